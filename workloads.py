@@ -1,0 +1,87 @@
+"""Seeded synthetic inputs for the five structured-sparse workloads.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark. It holds only random-number generation and the workload table
+(shapes, value distributions, seeds); none of the pruning, encoding or product
+arithmetic lives here.
+
+Every tensor is drawn as float64 ``standard_normal`` from
+``numpy.random.default_rng(seed)``, multiplied by the workload's sigma and
+rounded once to float16 (round to nearest even). Tensors of one workload are
+drawn from one generator in the order listed. The same float16 bits feed the
+oracle and the GPU.
+
+The pages measure on pruned BERT / GPT / OPT / Llama weights and on SQuAD
+attention; none of those is available, so these Gaussian tensors, at the
+shapes the pages use, stand in for them.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+def normal_f16(rng: np.random.Generator, shape, sigma: float = 1.0) -> np.ndarray:
+    """float64 standard normal x sigma, rounded once to float16 (RNE)."""
+    return (rng.standard_normal(size=shape) * sigma).astype(np.float16)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str                  # "nm", "vnm" or "attention"
+    seed: int
+    R: int = 0                 # rows of A (and of Y)
+    K: int = 0                 # reduction dimension, along which A is pruned
+    Cs: tuple = ()             # columns of B (one entry per B drawn)
+    sigma_a: float = 1.0
+    V: int = 0
+    M: int = 4
+    batch: int = 0
+    heads: int = 0
+    seq: int = 0
+    head_dim: int = 0
+    extra: dict = field(default_factory=dict)
+
+
+# The five workloads. Seeds of the last four are this library's choice.
+WORKLOADS = {
+    "nm_tiny": Workload("nm_tiny", "nm", seed=0, R=256, K=256, Cs=(64,), sigma_a=1.0),
+    "nm_decode": Workload("nm_decode", "nm", seed=1, R=4096, K=4096, Cs=(8, 16, 32), sigma_a=0.02),
+    "vnm_64_2_8": Workload("vnm_64_2_8", "vnm", seed=2, R=11008, K=4096, Cs=(256,), sigma_a=0.02,
+                           V=64, M=8),
+    "attention_2_4": Workload("attention_2_4", "attention", seed=3, batch=4, heads=16, seq=4096,
+                              head_dim=64),
+    "vnm_128_2_16": Workload("vnm_128_2_16", "vnm", seed=4, R=8192, K=8192, Cs=(4096,), sigma_a=0.02,
+                             V=128, M=16),
+}
+
+
+def weight_and_activations(w: Workload):
+    """A (R x K) then one B (K x C) per entry of ``w.Cs``, from one generator."""
+    rng = np.random.default_rng(w.seed)
+    A = normal_f16(rng, (w.R, w.K), w.sigma_a)
+    Bs = [normal_f16(rng, (w.K, c), 1.0) for c in w.Cs]
+    return A, Bs
+
+
+def attention_qkv(w: Workload):
+    """Q, K, V of shape [batch*heads, seq, head_dim], drawn in that order."""
+    rng = np.random.default_rng(w.seed)
+    shape = (w.batch * w.heads, w.seq, w.head_dim)
+    return tuple(normal_f16(rng, shape, 1.0) for _ in range(3))
+
+
+def small_matrix(seed: int, shape, sigma: float = 1.0) -> np.ndarray:
+    """One seeded float16 matrix, for small parity and edge cases."""
+    return normal_f16(np.random.default_rng(seed), shape, sigma)
+
+
+def ties_matrix(seed: int, shape, levels: int = 4) -> np.ndarray:
+    """float16 values drawn from a few magnitudes with random signs, so that many
+    groups hold exact magnitude ties and signed zeros."""
+    rng = np.random.default_rng(seed)
+    mags = rng.integers(0, levels, size=shape).astype(np.float64) * 0.5
+    sign = np.where(rng.integers(0, 2, size=shape) == 0, -1.0, 1.0)
+    return (mags * sign).astype(np.float16)
