@@ -1,0 +1,143 @@
+/*
+ * snm.h -- C ABI of libsnm: N:M and V:N:M structured-sparse x dense products and
+ * dynamic 2:4 attention on one AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Types      Element buffers are IEEE binary16 (fp16). Metadata buffers are bytes.
+ *            Everything is row-major. Leading dimensions (lda, ldb, ldy, ld) and
+ *            batch strides are counted in elements of the buffer they describe.
+ * Memory     Every pointer argument is DEVICE memory owned by the caller. The library
+ *            never allocates, frees or synchronises. Work is enqueued on `stream`
+ *            (a hipStream_t; NULL is the default stream) and the call returns at once.
+ * Alignment  Compressed arrays (values, meta, midx, colloc), A, Q and Kmat must be
+ *            16-byte aligned and A's leading dimension a multiple of 8 elements. Dense
+ *            B and Y accept any leading dimension (2-byte aligned pointers); B rows
+ *            that are 16-byte aligned are read 8 columns at a time.
+ * Errors     All argument checks run on the host before any HIP call. A failed check
+ *            returns its status with nothing enqueued. SNM_E_DEVICE means the current
+ *            device is not gfx950. SNM_E_LAUNCH reports the HIP error of the launch
+ *            itself; faults during execution surface at the caller's next
+ *            synchronisation. Nothing throws across this interface.
+ * Sizes      Empty problems (R, C or batch equal to 0) are valid and enqueue nothing.
+ * Threads    The library holds no mutable state besides a per-device architecture
+ *            check; calls from several host threads are safe.
+ *
+ * Canonical compressed layouts (identical on the host and the device; no reordering)
+ * -------------------------------------------------------------------------------
+ * 2:4 ("2:4 sparsity on sparse tensor cores", lecture notes: "The compressed format";
+ *      "Dynamic N:M ... attention", PPoPP'23, Sec. 4.2 Fig. 6(b) and Sec. 4.3):
+ *   values  fp16, R x K/2. Per group g of four consecutive elements along K, the two
+ *           kept elements in ascending slot order at columns 2g, 2g+1.
+ *   meta    uint8, R x K/8. Group code = s0 | s1 << 2 with slots s0 < s1 (one of
+ *           0x4 0x8 0x9 0xc 0xd 0xe). Group g sits in bits [4(g%4), 4(g%4)+3] of the
+ *           little-endian 16-bit word g/4; i.e. byte b holds group 2b (low nibble)
+ *           and group 2b+1 (high nibble).
+ *   Selection: the two largest magnitudes per group, magnitude = fp16 bits & 0x7FFF
+ *           (NaN > Inf > finite; +0 and -0 tie); on equal magnitude the lower slot
+ *           wins. Kept values are bit copies of the input.
+ * V:2:M ("VENOM: A vectorized N:M format ...", SC'23, Sec. 3 and Fig. 2-4):
+ *   values  fp16, R x 2K/M.   Two kept values per row per group of M columns.
+ *   midx    uint8, R x K/(2M). 2-bit positions (0..3) into the four selected columns,
+ *           packed exactly like the 2:4 meta.
+ *   colloc  uint8, (R/V) x (K/M) x 4. The four selected columns of each V x M block,
+ *           ascending, each in 0..M-1.
+ *   Selection: per V x M block, the four columns with the largest sum of squares over
+ *           the block's V rows (summed in float64, rows in ascending order; ties go to
+ *           the lower column); then, per row, 2:4 over the four selected values.
+ */
+#ifndef SNM_H
+#define SNM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SNM_OK = 0,
+  SNM_E_NULL = 1,        /* a required pointer is NULL */
+  SNM_E_SHAPE = 2,       /* a size, leading dimension or stride is invalid */
+  SNM_E_ALIGN = 3,       /* a pointer or leading dimension breaks the alignment rule */
+  SNM_E_UNSUPPORTED = 4, /* a pattern (V, M) or head_dim outside the supported set */
+  SNM_E_DEVICE = 5,      /* the current HIP device is not gfx950, or no device */
+  SNM_E_LAUNCH = 6       /* the kernel launch returned a HIP error */
+} snm_status;
+
+/* Version of this ABI and of the canonical layouts above. */
+int snm_abi_version(void);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* snm_status_string(int status);
+
+/* Sizes of the compressed 2:4 arrays of an R x K matrix: values elements (R*K/2) and
+ * meta bytes (R*K/8). Requires R >= 0, K >= 0, K % 16 == 0. Host only. */
+int snm_nm_sizes(int64_t R, int64_t K, int64_t* values_elems, int64_t* meta_bytes);
+
+/* Sizes of the V:2:M arrays of an R x K matrix. Requires R % V == 0, K % M == 0,
+ * (K/M) % 4 == 0, V in {1,...,256}, 4 <= M <= 256. Host only. */
+int snm_vnm_sizes(int64_t R, int64_t K, int V, int M, int64_t* values_elems,
+                  int64_t* midx_bytes, int64_t* colloc_bytes);
+
+/* 2:4 magnitude prune along K and compress (lecture notes, "The definition" and
+ * "The compressed format"; worked 2 x 8 example).
+ *   A       fp16 R x K, leading dimension lda >= K.
+ *   values  fp16 R x K/2 (contiguous), meta uint8 R x K/8 (contiguous): written.
+ * Requires K % 16 == 0. Output is bit-exactly the canonical layout above. */
+int snm_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda,
+                        void* values, void* meta, void* stream);
+
+/* V:2:M prune and compress (VENOM Sec. 3, Fig. 2 and Fig. 3).
+ *   A       fp16 R x K, leading dimension lda >= K.
+ *   values  fp16 R x 2K/M, midx uint8 R x K/(2M), colloc uint8 (R/V) x (K/M) x 4.
+ * Requires the shape rules of snm_vnm_sizes. */
+int snm_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
+                         void* values, void* midx, void* colloc, void* stream);
+
+/* Y = decode(values, meta) * B, batched (lecture notes, "How the tensor core uses it";
+ * the metadata selects, per kept value, the row of B it multiplies).
+ *   values, meta  2:4 arrays of an R x K matrix (canonical layout), per batch entry at
+ *                 values + b*stride_values (elements) and meta + b*stride_meta (bytes).
+ *   B             fp16 K x C, leading dimension ldb >= C, entry b at B + b*stride_B.
+ *   Y             fp16 R x C, leading dimension ldy >= C, entry b at Y + b*stride_Y.
+ * Products accumulate in fp32; Y is rounded to fp16 (round to nearest even). Requires
+ * K % 16 == 0, batch >= 1 (0 enqueues nothing). Strides are ignored when batch == 1. */
+int snm_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K,
+                const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                int64_t batch, int64_t stride_values, int64_t stride_meta,
+                int64_t stride_B, int64_t stride_Y, void* stream);
+
+/* Y = decode_vnm(values, midx, colloc) * B (VENOM Sec. 4 and Fig. 4: per block of V rows
+ * the K/M*4 rows of B named by colloc are gathered, then 2:4 is applied with midx).
+ *   values, midx, colloc  V:2:M arrays of an R x K matrix (canonical layout).
+ *   B  fp16 K x C (ldb >= C);  Y  fp16 R x C (ldy >= C).
+ * fp32 accumulation, fp16 output (RNE). Requires the shape rules of snm_vnm_sizes and
+ * V a multiple of 16. */
+int snm_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R,
+                 int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
+                 int64_t ldy, void* stream);
+
+/* Dynamic 2:4 SDDMM ("Dynamic N:M ... attention", Sec. 3.2 and Listing 1; Sec. 4.2-4.3):
+ * for each batch entry b, S = fp16_RNE((Q_b Kmat_b^T) * scale), then 2:4 prune and
+ * compress each row of S along the key axis, fused in one kernel.
+ *   Q       fp16 [batch, Lq, d] contiguous;  Kmat  fp16 [batch, Lk, d] contiguous.
+ *   values  fp16 [batch, Lq, Lk/2];  meta uint8 [batch, Lq, Lk/8]  (canonical 2:4).
+ *   S_dense optional fp16 [batch, Lq, Lk]: if not NULL it receives S before pruning.
+ * The product accumulates in fp32 and is scaled in fp32 before the single rounding to
+ * fp16. Requires Lk % 32 == 0 and d in {16, 32, 64, 128}. */
+int snm_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                       int64_t Lk, int64_t d, float scale, void* values, void* meta,
+                       void* S_dense, void* stream);
+
+/* In-place row softmax over the kept entries of compressed rows ("Dynamic N:M ...
+ * attention", Sec. 3.2: softmax runs only on each row's kept entries; dropped
+ * entries count as -inf). values: fp16 rows x kept, leading dimension ld >= kept.
+ * p = exp(v - max) / sum exp(v - max) per row, in fp32, rounded to fp16 (RNE). */
+int snm_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SNM_H */

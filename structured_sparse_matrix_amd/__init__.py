@@ -1,0 +1,199 @@
+"""Structured-sparse (2:4 and V:2:M) matrix products and dynamic 2:4 attention on MI355X.
+
+Thin binding over libsnm (include/snm.h). Each function takes and returns torch tensors on
+a ROCm device; torch provides device memory and the current stream, and every step of
+the computation runs in the library's HIP kernels. Functions keep the names of the
+C entry points without the ``snm_`` prefix.
+
+Layouts (canonical, see include/snm.h):
+  2:4     values fp16 [R, K/2], meta uint8 [R, K/8]
+  V:2:M   values fp16 [R, 2K/M], midx uint8 [R, K/(2M)], colloc uint8 [R/V, K/M, 4]
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+from ._lib import load, check, SnmError, LIB_PATH
+
+__all__ = [
+    "prune_encode_nm", "prune_encode_vnm", "spmm_nm", "spmm_vnm", "sddmm_prune_nm",
+    "softmax_nm_rows", "attention_nm", "nm_sizes", "vnm_sizes", "abi_version", "SnmError",
+    "LIB_PATH",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, dtype, dim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on a ROCm device")
+    if dim is not None and t.dim() not in (dim if isinstance(dim, tuple) else (dim,)):
+        raise ValueError(f"{name} must have {dim} dimensions, got {t.dim()}")
+
+
+def abi_version() -> int:
+    return load().snm_abi_version()
+
+
+def nm_sizes(R: int, K: int):
+    v, m = ctypes.c_int64(), ctypes.c_int64()
+    check("snm_nm_sizes", load().snm_nm_sizes(R, K, ctypes.byref(v), ctypes.byref(m)))
+    return v.value, m.value
+
+
+def vnm_sizes(R: int, K: int, V: int, M: int):
+    v, m, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    check("snm_vnm_sizes", load().snm_vnm_sizes(R, K, V, M, ctypes.byref(v), ctypes.byref(m), ctypes.byref(c)))
+    return v.value, m.value, c.value
+
+
+def prune_encode_nm(A, values=None, meta=None):
+    """2:4 magnitude prune of fp16 A [R, K] along K -> (values [R, K/2], meta [R, K/8])."""
+    torch = _torch()
+    _need(A, "A", torch.float16, 2)
+    if A.stride(1) != 1:
+        raise ValueError("A must be row-major (unit stride along K)")
+    R, K = A.shape
+    if values is None:
+        values = torch.empty((R, K // 2), dtype=torch.float16, device=A.device)
+    if meta is None:
+        meta = torch.empty((R, K // 8), dtype=torch.uint8, device=A.device)
+    check("snm_prune_encode_nm",
+          load().snm_prune_encode_nm(_ptr(A), R, K, A.stride(0), _ptr(values), _ptr(meta), _stream(A)))
+    return values, meta
+
+
+def prune_encode_vnm(A, V: int, M: int):
+    """V:2:M prune of fp16 A [R, K] -> (values [R, 2K/M], midx [R, K/(2M)], colloc [R/V, K/M, 4])."""
+    torch = _torch()
+    _need(A, "A", torch.float16, 2)
+    if A.stride(1) != 1:
+        raise ValueError("A must be row-major (unit stride along K)")
+    R, K = A.shape
+    G = K // M if M > 0 else 0
+    values = torch.empty((R, 2 * G), dtype=torch.float16, device=A.device)
+    midx = torch.empty((R, G // 2), dtype=torch.uint8, device=A.device)
+    colloc = torch.empty((R // V if V > 0 else 0, G, 4), dtype=torch.uint8, device=A.device)
+    check("snm_prune_encode_vnm",
+          load().snm_prune_encode_vnm(_ptr(A), R, K, A.stride(0), V, M, _ptr(values), _ptr(midx),
+                                      _ptr(colloc), _stream(A)))
+    return values, midx, colloc
+
+
+def spmm_nm(values, meta, B, out=None):
+    """Y = decode(values, meta) @ B. 2-D: values [R, K/2], meta [R, K/8], B [K, C] -> Y [R, C].
+    3-D (batched): values [b, R, K/2], meta [b, R, K/8], B [b, K, C] -> Y [b, R, C]."""
+    torch = _torch()
+    _need(values, "values", torch.float16, (2, 3))
+    _need(meta, "meta", torch.uint8, values.dim())
+    _need(B, "B", torch.float16, values.dim())
+    batched = values.dim() == 3
+    if not batched:
+        values, meta, B = values[None], meta[None], B[None]
+    nb, R, half_k = values.shape
+    K = 2 * half_k
+    if B.shape[0] != nb or B.shape[1] != K or meta.shape != (nb, R, K // 8):
+        raise ValueError(f"shape mismatch: values {tuple(values.shape)}, meta {tuple(meta.shape)}, "
+                         f"B {tuple(B.shape)}")
+    for t, n in ((values, "values"), (meta, "meta")):
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{n} must be contiguous per batch entry")
+    if B.stride(2) != 1:
+        raise ValueError("B must be row-major (unit stride along C)")
+    C = B.shape[2]
+    if out is None:
+        out = torch.empty((nb, R, C), dtype=torch.float16, device=B.device)
+    elif not batched:
+        out = out[None]
+    check("snm_spmm_nm",
+          load().snm_spmm_nm(_ptr(values), _ptr(meta), R, K, _ptr(B), C, B.stride(1), _ptr(out),
+                             out.stride(1), nb, values.stride(0), meta.stride(0), B.stride(0),
+                             out.stride(0), _stream(B)))
+    return out if batched else out[0]
+
+
+def spmm_vnm(values, midx, colloc, B, V: int, M: int, out=None):
+    """Y = decode_vnm(values, midx, colloc) @ B with B [K, C] -> Y [R, C]."""
+    torch = _torch()
+    _need(values, "values", torch.float16, 2)
+    _need(midx, "midx", torch.uint8, 2)
+    _need(colloc, "colloc", torch.uint8, 3)
+    _need(B, "B", torch.float16, 2)
+    R = values.shape[0]
+    K, C = B.shape
+    if not (values.is_contiguous() and midx.is_contiguous() and colloc.is_contiguous()):
+        raise ValueError("values, midx and colloc must be contiguous")
+    if B.stride(1) != 1:
+        raise ValueError("B must be row-major (unit stride along C)")
+    if M <= 0 or V <= 0 or values.shape[1] != 2 * (K // M) or tuple(colloc.shape) != (R // V, K // M, 4):
+        raise ValueError("shape mismatch between the V:2:M arrays and B")
+    if out is None:
+        out = torch.empty((R, C), dtype=torch.float16, device=B.device)
+    check("snm_spmm_vnm",
+          load().snm_spmm_vnm(_ptr(values), _ptr(midx), _ptr(colloc), R, K, V, M, _ptr(B), C,
+                              B.stride(0), _ptr(out), out.stride(0), _stream(B)))
+    return out
+
+
+def sddmm_prune_nm(Q, Kmat, scale=None, return_dense=False):
+    """Scores S = fp16((Q @ Kmat^T) * scale) pruned 2:4 along the key axis.
+    Q [b, Lq, d], Kmat [b, Lk, d] -> values [b, Lq, Lk/2], meta [b, Lq, Lk/8] (and S if asked)."""
+    torch = _torch()
+    _need(Q, "Q", torch.float16, 3)
+    _need(Kmat, "Kmat", torch.float16, 3)
+    if not (Q.is_contiguous() and Kmat.is_contiguous()):
+        raise ValueError("Q and Kmat must be contiguous")
+    nb, Lq, d = Q.shape
+    if Kmat.shape[0] != nb or Kmat.shape[2] != d:
+        raise ValueError("Q and Kmat disagree in batch or head_dim")
+    Lk = Kmat.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    values = torch.empty((nb, Lq, Lk // 2), dtype=torch.float16, device=Q.device)
+    meta = torch.empty((nb, Lq, Lk // 8), dtype=torch.uint8, device=Q.device)
+    S = torch.empty((nb, Lq, Lk), dtype=torch.float16, device=Q.device) if return_dense else None
+    check("snm_sddmm_prune_nm",
+          load().snm_sddmm_prune_nm(_ptr(Q), _ptr(Kmat), nb, Lq, Lk, d, float(scale), _ptr(values),
+                                    _ptr(meta), _ptr(S), _stream(Q)))
+    return (values, meta, S) if return_dense else (values, meta)
+
+
+def softmax_nm_rows(values):
+    """In-place softmax over the last axis of compressed rows (kept entries only)."""
+    torch = _torch()
+    _need(values, "values", torch.float16)
+    if values.stride(-1) != 1:
+        raise ValueError("values must have unit stride along the last axis")
+    kept = values.shape[-1]
+    rows = values.numel() // kept if kept else 0
+    ld = values.stride(-2) if values.dim() >= 2 else kept
+    if values.dim() > 2 and not values.is_contiguous():
+        raise ValueError("batched values must be contiguous")
+    check("snm_softmax_nm_rows", load().snm_softmax_nm_rows(_ptr(values), rows, kept, ld, _stream(values)))
+    return values
+
+
+def attention_nm(Q, Kmat, Vmat, scale=None):
+    """Dynamic 2:4 attention: SDDMM-prune, softmax over kept entries, 2:4 SpMM with V.
+    Q [b, Lq, d], Kmat [b, Lk, d], Vmat [b, Lk, dv] -> O [b, Lq, dv]."""
+    values, meta = sddmm_prune_nm(Q, Kmat, scale)
+    softmax_nm_rows(values)
+    return spmm_nm(values, meta, Vmat)

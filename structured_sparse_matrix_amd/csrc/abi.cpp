@@ -1,0 +1,128 @@
+// extern "C" entry points of libsnm: validate on the host (validate.cpp), check once per
+// device that it is a gfx950, then enqueue the kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "launch.hpp"
+#include "snm.h"
+#include "validate.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SNM_E_DEVICE;
+  int st = g_arch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SNM_E_DEVICE;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? SNM_OK : SNM_E_DEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? SNM_OK : SNM_E_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int snm_abi_version(void) { return 1; }
+
+const char* snm_status_string(int status) {
+  switch (status) {
+    case SNM_OK: return "ok";
+    case SNM_E_NULL: return "a required pointer is NULL";
+    case SNM_E_SHAPE: return "invalid size, leading dimension or stride";
+    case SNM_E_ALIGN: return "pointer or leading dimension breaks the 16-byte alignment rule";
+    case SNM_E_UNSUPPORTED: return "unsupported pattern parameters";
+    case SNM_E_DEVICE: return "current HIP device is not gfx950";
+    case SNM_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int snm_nm_sizes(int64_t R, int64_t K, int64_t* values_elems, int64_t* meta_bytes) {
+  int s = snm::check_nm_sizes(R, K);
+  if (s != SNM_OK) return s;
+  if (!values_elems || !meta_bytes) return SNM_E_NULL;
+  *values_elems = R * (K / 2);
+  *meta_bytes = R * (K / 8);
+  return SNM_OK;
+}
+
+int snm_vnm_sizes(int64_t R, int64_t K, int V, int M, int64_t* values_elems, int64_t* midx_bytes,
+                  int64_t* colloc_bytes) {
+  int s = snm::check_vnm_sizes(R, K, V, M);
+  if (s != SNM_OK) return s;
+  if (!values_elems || !midx_bytes || !colloc_bytes) return SNM_E_NULL;
+  const int64_t G = K / M;
+  *values_elems = R * 2 * G;
+  *midx_bytes = R * (G / 2);
+  *colloc_bytes = (R / V) * G * 4;
+  return SNM_OK;
+}
+
+int snm_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda, void* values, void* meta,
+                        void* stream) {
+  int s = snm::check_prune_encode_nm(A, R, K, lda, values, meta);
+  if (s != SNM_OK || R == 0 || K == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_prune_encode_nm(A, R, K, lda, values, meta, (hipStream_t)stream));
+}
+
+int snm_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
+                         void* values, void* midx, void* colloc, void* stream) {
+  int s = snm::check_prune_encode_vnm(A, R, K, lda, V, M, values, midx, colloc);
+  if (s != SNM_OK || R == 0 || K == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_prune_encode_vnm(A, R, K, lda, V, M, values, midx, colloc,
+                                               (hipStream_t)stream));
+}
+
+int snm_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
+                int64_t C, int64_t ldb, void* Y, int64_t ldy, int64_t batch,
+                int64_t stride_values, int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
+                void* stream) {
+  int s = snm::check_spmm_nm(values, meta, R, K, B, C, ldb, Y, ldy, batch, stride_values,
+                             stride_meta, stride_B, stride_Y);
+  if (s != SNM_OK || R == 0 || C == 0 || batch == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_spmm_nm(values, meta, R, K, B, C, ldb, Y, ldy, batch, stride_values,
+                                      stride_meta, stride_B, stride_Y, (hipStream_t)stream));
+}
+
+int snm_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R, int64_t K,
+                 int V, int M, const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                 void* stream) {
+  int s = snm::check_spmm_vnm(values, midx, colloc, R, K, V, M, B, C, ldb, Y, ldy);
+  if (s != SNM_OK || R == 0 || C == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_spmm_vnm(values, midx, colloc, R, K, V, M, B, C, ldb, Y, ldy,
+                                       (hipStream_t)stream));
+}
+
+int snm_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq, int64_t Lk,
+                       int64_t d, float scale, void* values, void* meta, void* S_dense,
+                       void* stream) {
+  int s = snm::check_sddmm_prune_nm(Q, Kmat, batch, Lq, Lk, d, values, meta, S_dense);
+  if (s != SNM_OK || batch == 0 || Lq == 0 || Lk == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_sddmm_prune_nm(Q, Kmat, batch, Lq, Lk, d, scale, values, meta,
+                                             S_dense, (hipStream_t)stream));
+}
+
+int snm_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream) {
+  int s = snm::check_softmax_nm_rows(values, rows, kept, ld);
+  if (s != SNM_OK || rows == 0 || kept == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_softmax_nm_rows(values, rows, kept, ld, (hipStream_t)stream));
+}
+
+}  // extern "C"

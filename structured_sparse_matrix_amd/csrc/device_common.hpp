@@ -1,0 +1,66 @@
+// Device-side building blocks for gfx950 (CDNA4): vector types, the sparse / dense
+// matrix-core instructions with the lane layouts measured on MI355X, and the LDS
+// transpose read. Every kernel of libsnm includes this header; nothing here is shared
+// with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace snm {
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16 __attribute__((ext_vector_type(16)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------------------
+// v_smfmac_f32_16x16x64_f16: D(16x16, fp32) += A(16x64, 2:4 sparse along k) * B(64x16).
+// Lane layout (lane l, quarter q = l / 16, i = l % 16):
+//   A: row i; 8 stored values covering dense k = 16q + [0, 16) = four groups of four;
+//      stored value j belongs to group j / 2 and its slot is bits [2j, 2j+1] of the
+//      16-bit index word -- exactly one canonical 2:4 metadata word. `abid` picks the
+//      low (0) or high (1) 16 bits of the 32-bit index register.
+//   B: column i; element e < 8 holds k = 8q + e, element e >= 8 holds k = 32 + 8q + e - 8.
+//   D: column i; element r holds row 4q + r.
+// So A quarter p pairs with B quarters 2(p%2), 2(p%2)+1, elements 8(p/2)..8(p/2)+7.
+// ---------------------------------------------------------------------------------------
+template <int ABID>
+__device__ __forceinline__ f4 smfmac16(const h8& a, const h16& b, const f4& c, uint32_t idx) {
+  return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, b, c, (int)idx, 0, ABID);
+}
+
+// v_mfma_f32_32x32x16_f16: D(32x32) += A(32x16) * B(16x32).
+//   A: row l % 32, k = 8 (l / 32) + [0, 8).  B: column l % 32, same k.
+//   D: column l % 32, element r holds row 8 (r / 4) + 4 (l / 32) + r % 4.
+__device__ __forceinline__ f16v mfma32x32x16(const h8& a, const h8& b, const f16v& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16. Within each group of 16 lanes, lane i receives element (i % 4) of
+// the 8 bytes read by lane 4r + i / 4, for r = 0..3. With lane L pointing at
+// &T[row0 + L / 4][c0 + 4 (L % 4)] of a row-major fp16 tile T, lane i therefore receives
+// T[row0 + r][c0 + i] for r = 0..3: four consecutive rows of one column.
+__device__ __forceinline__ h4 lds_read_tr16(uint32_t lds_byte_addr) {
+  typedef __fp16 fp4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+  typedef __attribute__((address_space(3))) fp4 lds_fp4;
+  lds_fp4* p = (lds_fp4*)(uintptr_t)lds_byte_addr;
+  return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(p));
+}
+
+// LDS byte address of a __shared__ object (address space 3 offset).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ uint16_t f16_bits(_Float16 x) { return __builtin_bit_cast(uint16_t, x); }
+__device__ __forceinline__ _Float16 bits_f16(uint16_t x) { return __builtin_bit_cast(_Float16, x); }
+
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default rounding mode).
+__device__ __forceinline__ _Float16 to_f16(float x) { return (_Float16)x; }
+
+}  // namespace snm

@@ -1,0 +1,182 @@
+// Pruning + compression kernels: 2:4 ("2:4 sparsity on sparse tensor cores", lecture
+// notes: "The definition", "The compressed format") and V:2:M ("VENOM: A vectorized N:M
+// format ...", SC'23, Sec. 3, Fig. 2 and Fig. 3). Both are HBM-streaming kernels: the
+// selection is local to a group and every output address is known in advance.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace snm {
+
+// Slots kept by 2:4 selection of four fp16 bit patterns: the two largest magnitudes
+// (bits & 0x7FFF), equal magnitudes resolved toward the lower slot. Returns the 4-bit
+// group code s0 | s1 << 2 (s0 < s1) and the two kept bit patterns.
+__device__ __forceinline__ uint32_t select_2of4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                                uint32_t& v0, uint32_t& v1) {
+  // Distinct composite keys: magnitude, then reversed slot (lower slot ranks higher).
+  const uint32_t c0 = ((a0 & 0x7FFFu) << 2) | 3u;
+  const uint32_t c1 = ((a1 & 0x7FFFu) << 2) | 2u;
+  const uint32_t c2 = ((a2 & 0x7FFFu) << 2) | 1u;
+  const uint32_t c3 = ((a3 & 0x7FFFu) << 2) | 0u;
+  const uint32_t g01 = c0 > c1, g02 = c0 > c2, g03 = c0 > c3;
+  const uint32_t g12 = c1 > c2, g13 = c1 > c3, g23 = c2 > c3;
+  // rank = number of larger keys; keep rank < 2
+  const uint32_t r0 = (1u - g01) + (1u - g02) + (1u - g03);
+  const uint32_t r1 = g01 + (1u - g12) + (1u - g13);
+  const uint32_t r2 = g02 + g12 + (1u - g23);
+  const uint32_t r3 = g03 + g13 + g23;
+  const uint32_t keep = (uint32_t)(r0 < 2) | ((uint32_t)(r1 < 2) << 1) | ((uint32_t)(r2 < 2) << 2) |
+                        ((uint32_t)(r3 < 2) << 3);
+  const uint32_t s0 = __builtin_ctz(keep);
+  const uint32_t s1 = 31u - __builtin_clz(keep);
+  v0 = s0 == 0 ? a0 : (s0 == 1 ? a1 : a2);   // s0 <= 2
+  v1 = s1 == 3 ? a3 : (s1 == 2 ? a2 : a1);   // s1 >= 1
+  return s0 | (s1 << 2);
+}
+
+// One thread per 16 consecutive elements of a row (four groups = one metadata word):
+// two 16-byte loads, one 16-byte value store and one 2-byte metadata store; a wave
+// covers 1 KiB of contiguous input.
+__global__ void __launch_bounds__(256)
+k_prune_encode_nm(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t lda,
+                  uint16_t* __restrict__ values, uint16_t* __restrict__ meta) {
+  const int64_t words_per_row = K >> 4;
+  const int64_t total = R * words_per_row;
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < total;
+       w += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = w / words_per_row;
+    const int64_t c = w - r * words_per_row;
+    const u4* src = reinterpret_cast<const u4*>(A + r * lda + (c << 4));
+    const u4 x0 = __builtin_nontemporal_load(src);
+    const u4 x1 = __builtin_nontemporal_load(src + 1);
+    uint32_t e[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    uint32_t out[4];
+    uint32_t word = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t lo = e[2 * g], hi = e[2 * g + 1];
+      uint32_t v0, v1;
+      const uint32_t code = select_2of4(lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16, v0, v1);
+      out[g] = v0 | (v1 << 16);
+      word |= code << (4 * g);
+    }
+    u4 o = {out[0], out[1], out[2], out[3]};
+    *reinterpret_cast<u4*>(values + r * (K >> 1) + (c << 3)) = o;
+    meta[r * words_per_row + c] = (uint16_t)word;
+  }
+}
+
+// V:2:M. One workgroup per (block of V rows, chunk of GC groups of M columns).
+//   Phase 1: one thread per column sums the squares of the block's V entries in float64,
+//            rows in ascending order (a fp16 square is exact in float64, so the sum is the
+//            same sequential float64 sum on any implementation).
+//   Phase 2: per group, the four columns of largest score (ties to the lower column),
+//            ascending -> column-loc.
+//   Phase 3: one thread per (row, four groups): 2:4 among the four selected values,
+//            16-byte value store + one 16-bit m-index word.
+constexpr int kVnmThreads = 256;
+constexpr int kVnmMaxCols = 1024;
+
+__global__ void __launch_bounds__(kVnmThreads)
+k_prune_encode_vnm(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t lda, int V, int M,
+                   int GC, uint16_t* __restrict__ values, uint16_t* __restrict__ midx,
+                   uint8_t* __restrict__ colloc) {
+  __shared__ double score[kVnmMaxCols];
+  __shared__ uint8_t keep[kVnmMaxCols];
+  __shared__ uint8_t sel[kVnmMaxCols / 4 * 4];   // [group in chunk][4]
+  const int64_t G = K / M;
+  const int64_t nchunks = (G + GC - 1) / GC;
+  const int64_t vb = blockIdx.x / nchunks;
+  const int64_t g0 = (blockIdx.x - vb * nchunks) * GC;
+  const int ng = (int)((G - g0) < GC ? (G - g0) : GC);   // groups in this chunk (multiple of 4)
+  const int ncols = ng * M;
+  const uint16_t* Ablk = A + vb * V * lda + g0 * M;
+
+  for (int c = threadIdx.x; c < ncols; c += kVnmThreads) {
+    double s = 0.0;
+    for (int r = 0; r < V; ++r) {
+      const double a = (double)bits_f16(Ablk[(int64_t)r * lda + c]);
+      s = __builtin_fma(a, a, s);     // a*a is exact, so this equals s + a*a rounded once
+    }
+    score[c] = s;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < ncols; c += kVnmThreads) {
+    const int gi = c / M;
+    const int base = gi * M;
+    const double sc = score[c];
+    int rank = 0;
+    for (int j = 0; j < M; ++j) {
+      const double sj = score[base + j];
+      rank += (sj > sc) | ((sj == sc) & (base + j < c));
+    }
+    keep[c] = rank < 4;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < ncols; c += kVnmThreads) {
+    if (!keep[c]) continue;
+    const int gi = c / M;
+    const int base = gi * M;
+    int p = 0;
+    for (int j = base; j < c; ++j) p += keep[j];
+    if (p < 4) {      // always true for finite scores; guards unspecified non-finite input
+      sel[gi * 4 + p] = (uint8_t)(c - base);
+      colloc[((vb * G) + g0 + gi) * 4 + p] = (uint8_t)(c - base);
+    }
+  }
+  __syncthreads();
+  const int words = ng >> 2;
+  const int64_t vals_per_row = 2 * G;
+  const int64_t midx_words_per_row = G >> 2;
+  for (int it = threadIdx.x; it < V * words; it += kVnmThreads) {
+    const int r = it / words;
+    const int w = it - r * words;
+    const uint16_t* arow = Ablk + (int64_t)r * lda;
+    uint32_t out[4];
+    uint32_t word = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int gi = 4 * w + q;
+      const uint16_t* ag = arow + gi * M;
+      uint32_t v0, v1;
+      const uint32_t code = select_2of4(ag[sel[gi * 4 + 0]], ag[sel[gi * 4 + 1]], ag[sel[gi * 4 + 2]],
+                                        ag[sel[gi * 4 + 3]], v0, v1);   // sel < M (phase 2)
+      out[q] = v0 | (v1 << 16);
+      word |= code << (4 * q);
+    }
+    const int64_t row = vb * V + r;
+    u4 o = {out[0], out[1], out[2], out[3]};
+    *reinterpret_cast<u4*>(values + row * vals_per_row + 2 * (g0 + 4 * w)) = o;
+    midx[row * midx_words_per_row + (g0 >> 2) + w] = (uint16_t)word;
+  }
+}
+
+hipError_t launch_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda, void* values,
+                                  void* meta, hipStream_t stream) {
+  const int64_t total = R * (K >> 4);
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;   // grid-stride beyond 64 workgroups per CU
+  hipLaunchKernelGGL(k_prune_encode_nm, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const uint16_t*)A, R, K, lda, (uint16_t*)values, (uint16_t*)meta);
+  return hipGetLastError();
+}
+
+int vnm_chunk_groups(int M) {
+  int gc = (256 / M) & ~3;
+  return gc < 4 ? 4 : gc;
+}
+
+hipError_t launch_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
+                                   void* values, void* midx, void* colloc, hipStream_t stream) {
+  if (R == 0 || K == 0) return hipSuccess;
+  const int GC = vnm_chunk_groups(M);
+  const int64_t G = K / M;
+  const int64_t nchunks = (G + GC - 1) / GC;
+  const int64_t blocks = (R / V) * nchunks;
+  hipLaunchKernelGGL(k_prune_encode_vnm, dim3((unsigned)blocks), dim3(kVnmThreads), 0, stream,
+                     (const uint16_t*)A, R, K, lda, V, M, GC, (uint16_t*)values, (uint16_t*)midx,
+                     (uint8_t*)colloc);
+  return hipGetLastError();
+}
+
+}  // namespace snm

@@ -1,0 +1,27 @@
+// Host-side launchers of the device kernels (implemented in the .hip files). They assume
+// arguments already passed validation and only enqueue work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace snm {
+
+hipError_t launch_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda, void* values,
+                                  void* meta, hipStream_t stream);
+hipError_t launch_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
+                                   void* values, void* midx, void* colloc, hipStream_t stream);
+hipError_t launch_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
+                          int64_t C, int64_t ldb, void* Y, int64_t ldy, int64_t batch,
+                          int64_t stride_values, int64_t stride_meta, int64_t stride_B,
+                          int64_t stride_Y, hipStream_t stream);
+hipError_t launch_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R,
+                           int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
+                           int64_t ldy, hipStream_t stream);
+hipError_t launch_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                                 int64_t Lk, int64_t d, float scale, void* values, void* meta,
+                                 void* S_dense, hipStream_t stream);
+hipError_t launch_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld,
+                                  hipStream_t stream);
+
+}  // namespace snm

@@ -1,0 +1,347 @@
+// Structured-sparse x dense products on the CDNA4 sparse matrix cores.
+//
+// Y = decode(values, meta) * B for 2:4 ("2:4 sparsity on sparse tensor cores", lecture
+// notes: "How the tensor core uses it" -- the 2-bit tags select which K/2 elements of
+// each B column are multiplied) and for V:2:M ("VENOM ...", SC'23, Sec. 4 and Fig. 4 --
+// per block of V rows the K/M*4 rows of B named by column-loc are gathered, which turns
+// the product into a 2:4 product over K' = 4K/M).
+//
+// One kernel template serves both: it runs 2:4 over a "compressed space" of length Kc
+// (Kc = K for 2:4, Kc = 4K/M for V:2:M). The only difference is how the rows of the B
+// tile are fetched: contiguous rows (2:4) or rows gathered through column-loc (V:2:M).
+//
+// Work decomposition
+//   workgroup tile  BM x BN outputs, BM = WM*TM*16 rows, BN = WN*TN*16 columns;
+//   WK waves split the reduction inside the workgroup (summed through LDS at the end).
+//   superchunk      KS = 64*KSUB consecutive positions of the compressed space. Lane
+//                   quarter p of a wave owns positions 16*KSUB*p + [0, 16*KSUB) of it,
+//                   i.e. KSUB consecutive sparse-MFMA operands that are one contiguous
+//                   32*KSUB-byte run of values and 2*KSUB bytes of metadata.
+//   A operand       loaded straight from HBM into registers (non-temporal, read once);
+//                   the canonical metadata word is the sparse-MFMA index operand as is.
+//   B operand       the KS x BN tile is staged in LDS (rows as stored, 32-byte cells
+//                   XOR-swizzled so that one transpose read touches every bank pair at
+//                   most twice) and read column-wise with ds_read_b64_tr_b16.
+//   pipelining      the next superchunk's A fragments and B rows are loaded into
+//                   registers while the current one is multiplied.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace snm {
+
+struct SpmmArgs {
+  const uint16_t* values;   // fp16 bits, R x Kc/2 per batch entry
+  const uint8_t* meta;      // R x Kc/8 bytes per batch entry
+  const uint16_t* B;        // fp16 bits, K x C (row-major, ldb)
+  uint16_t* Y;              // fp16 bits, R x C (ldy)
+  const uint8_t* colloc;    // V:2:M only: (R/V) x (K/M) x 4
+  int64_t R, Kc, K, C, ldb, ldy;
+  int64_t batch, stride_values, stride_meta, stride_B, stride_Y;
+  int64_t n_row_tiles, n_col_tiles;
+  int V, M;
+  int b_vec;                // B rows are 16-byte aligned: load 8 columns at a time
+};
+
+// Byte offset, inside a B tile of BN fp16 columns, of (row x, column c) with c a multiple
+// of 4. Cells of 32 bytes (16 columns) are XOR-permuted inside 256-byte lines (one line
+// spans all 64 LDS banks) so that the 16 rows one transpose read touches -- rows
+// {0..3, 8..11} + {0, 32*KSUB} (+16t) -- fall on 8 distinct cells, each at most twice.
+template <int BN>
+__device__ __forceinline__ uint32_t btile_offset(int x, int c) {
+  const int cr = c >> 4;
+  const uint32_t inner = (uint32_t)(c & 15) * 2u;
+  if constexpr (BN >= 128) {
+    const int hx = (x & 3) | ((x >> 1) & 4);
+    return (uint32_t)x * (BN * 2) + (uint32_t)((cr ^ hx) * 32) + inner;
+  } else if constexpr (BN == 64) {
+    const int L = x >> 1;
+    int u = ((x & 1) << 2) | cr;
+    u ^= (L & 1) | (((L >> 2) & 1) << 1);
+    return (uint32_t)L * 256u + (uint32_t)u * 32u + inner;
+  } else if constexpr (BN == 32) {
+    const int L = x >> 2;
+    int u = ((x & 3) << 1) | cr;
+    u ^= (L >> 1) & 1;
+    return (uint32_t)L * 256u + (uint32_t)u * 32u + inner;
+  } else {
+    static_assert(BN == 16, "BN must be 16, 32, 64 or a multiple of 128");
+    const int L = x >> 3;
+    int u = x & 7;
+    u ^= (L & 1) << 2;
+    return (uint32_t)L * 256u + (uint32_t)u * 32u + inner;
+  }
+}
+
+template <int WM, int WN, int WK, int TM, int TN, int KSUB, bool GATHER>
+struct SpmmCfg {
+  static constexpr int kWaves = WM * WN * WK;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int BM = WM * TM * 16;
+  static constexpr int BN = WN * TN * 16;
+  static constexpr int KS = 64 * KSUB;                 // compressed positions per superchunk
+  static constexpr int kTileRows = WK * KS;            // B rows staged per iteration
+  static constexpr int kChunksPerRow = BN / 8;         // 16-byte chunks per B row
+  static constexpr int kChunks = kTileRows * kChunksPerRow;
+  static constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
+  static constexpr int kLdsB = kTileRows * BN * 2;
+  static constexpr int kLdsRed = (WK - 1) * WM * WN * TM * TN * 64 * 16;
+  static constexpr int kLds = kLdsB > kLdsRed ? kLdsB : kLdsRed;
+  static_assert(kChunks % kThreads == 0, "B tile must split evenly over the workgroup");
+};
+
+template <int WM, int WN, int WK, int TM, int TN, int KSUB, bool GATHER>
+__global__ void __launch_bounds__(64 * WM * WN * WK)
+k_spmm(SpmmArgs a) {
+  using Cfg = SpmmCfg<WM, WN, WK, TM, TN, KSUB, GATHER>;
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, KS = Cfg::KS;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t lds_base = lds_addr(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wn = wave % WN;
+  const int wm = (wave / WN) % WM;
+  const int wk = wave / (WN * WM);
+  const int q = lane >> 4;      // lane quarter
+  const int li = lane & 15;
+
+  const int64_t tile = blockIdx.x;
+  const int64_t rt = tile % a.n_row_tiles;
+  const int64_t ct = tile / a.n_row_tiles;
+  const int64_t row0 = rt * BM;
+  const int64_t col0 = ct * BN;
+  const int64_t nsuper = (a.Kc + KS - 1) / KS;
+  const int64_t vals_row = a.Kc >> 1;     // elements
+  const int64_t meta_row = a.Kc >> 3;     // bytes
+  const int64_t G = GATHER ? a.K / a.M : 0;
+  const int64_t vb = GATHER ? row0 / a.V : 0;
+
+  for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
+    const uint16_t* __restrict__ vals = a.values + b * a.stride_values;
+    const uint8_t* __restrict__ meta = a.meta + b * a.stride_meta;
+    const uint16_t* __restrict__ Bm = a.B + b * a.stride_B;
+    uint16_t* __restrict__ Y = a.Y + b * a.stride_Y;
+
+    // ---- register staging ------------------------------------------------------------
+    u4 bstage[Cfg::kChunksPerThread];
+    h8 afrag[TM][KSUB];
+    uint32_t aidx[TM][KSUB];
+
+    auto load_b = [&](int64_t s0) {
+#pragma unroll
+      for (int i = 0; i < Cfg::kChunksPerThread; ++i) {
+        const int chunk = tid + i * Cfg::kThreads;
+        const int j = chunk / Cfg::kChunksPerRow;           // tile row
+        const int cc = chunk - j * Cfg::kChunksPerRow;      // 16-byte chunk in the row
+        const int64_t kg = s0 * KS + j;                     // compressed-space position
+        const int64_t col = col0 + cc * 8;
+        u4 v = {0u, 0u, 0u, 0u};
+        if (kg < a.Kc) {
+          int64_t brow;
+          if constexpr (GATHER) {
+            const int64_t g = kg >> 2;
+            const int cl = a.colloc[(vb * G + g) * 4 + (kg & 3)];
+            brow = g * a.M + (cl < a.M ? cl : a.M - 1);   // column-loc entries are < M by contract
+          } else {
+            brow = kg;
+          }
+          const uint16_t* src = Bm + brow * a.ldb + col;
+          if (a.b_vec && col + 8 <= a.C) {
+            v = *reinterpret_cast<const u4*>(src);
+          } else {
+            uint16_t e[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) e[t] = (col + t < a.C) ? src[t] : (uint16_t)0;
+            v[0] = e[0] | ((uint32_t)e[1] << 16);
+            v[1] = e[2] | ((uint32_t)e[3] << 16);
+            v[2] = e[4] | ((uint32_t)e[5] << 16);
+            v[3] = e[6] | ((uint32_t)e[7] << 16);
+          }
+        }
+        bstage[i] = v;
+      }
+    };
+    auto store_b = [&]() {
+#pragma unroll
+      for (int i = 0; i < Cfg::kChunksPerThread; ++i) {
+        const int chunk = tid + i * Cfg::kThreads;
+        const int j = chunk / Cfg::kChunksPerRow;
+        const int cc = chunk - j * Cfg::kChunksPerRow;
+        *reinterpret_cast<u4*>(smem + btile_offset<BN>(j, cc * 8)) = bstage[i];
+      }
+    };
+    auto load_a = [&](int64_t s0) {
+      const int64_t s = s0 + wk;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int64_t row = row0 + (wm * TM + tm) * 16 + li;
+#pragma unroll
+        for (int t = 0; t < KSUB; ++t) {
+          const int64_t kd = s * KS + 16 * KSUB * q + 16 * t;   // first dense position
+          h8 v = {};
+          uint32_t id = 0;
+          if (s < nsuper && kd < a.Kc && row < a.R) {
+            v = __builtin_bit_cast(h8, __builtin_nontemporal_load(
+                                           reinterpret_cast<const u4*>(vals + row * vals_row + (kd >> 1))));
+            id = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(meta + row * meta_row + (kd >> 3)));
+          }
+          afrag[tm][t] = v;
+          aidx[tm][t] = id;
+        }
+      }
+    };
+
+    f4 acc[TM][TN];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f4{0.f, 0.f, 0.f, 0.f};
+
+    load_a(0);
+    load_b(0);
+    for (int64_t s0 = 0; s0 < nsuper; s0 += WK) {
+      store_b();
+      __syncthreads();
+      h8 acur[TM][KSUB];
+      uint32_t icur[TM][KSUB];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int t = 0; t < KSUB; ++t) { acur[tm][t] = afrag[tm][t]; icur[tm][t] = aidx[tm][t]; }
+      if (s0 + WK < nsuper) {   // next superchunks in flight during this one's products
+        load_a(s0 + WK);
+        load_b(s0 + WK);
+      }
+      if (s0 + wk < nsuper) {
+        const int xbase = wk * KS;
+#pragma unroll
+        for (int t = 0; t < KSUB; ++t) {
+          const int r1 = 16 * KSUB * (q >> 1) + 16 * t + 8 * (q & 1) + (li >> 2);
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            const int c = (wn * TN + tn) * 16 + 4 * (li & 3);
+            const h4 b0 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1, c));
+            const h4 b1 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1 + 4, c));
+            const h4 b2 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1 + 32 * KSUB, c));
+            const h4 b3 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1 + 32 * KSUB + 4, c));
+            h16 bf;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              bf[e] = b0[e];
+              bf[4 + e] = b1[e];
+              bf[8 + e] = b2[e];
+              bf[12 + e] = b3[e];
+            }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) acc[tm][tn] = smfmac16<0>(acur[tm][t], bf, acc[tm][tn], icur[tm][t]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---- reduce the WK partial sums of the workgroup -------------------------------------
+    if constexpr (WK > 1) {
+      float* red = reinterpret_cast<float*>(smem);
+      const int slot = ((wm * WN + wn) * TM) * TN;
+      if (wk > 0) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+            *reinterpret_cast<f4*>(red + ((((wk - 1) * WM * WN * TM * TN) + slot + tm * TN + tn) * 64 + lane) * 4) =
+                acc[tm][tn];
+      }
+      __syncthreads();
+      if (wk == 0) {
+        for (int w = 1; w < WK; ++w)
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+              acc[tm][tn] += *reinterpret_cast<const f4*>(
+                  red + ((((w - 1) * WM * WN * TM * TN) + slot + tm * TN + tn) * 64 + lane) * 4);
+      }
+      __syncthreads();
+    }
+    if (wk == 0) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int64_t col = col0 + (wn * TN + tn) * 16 + li;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t row = row0 + (wm * TM + tm) * 16 + 4 * q + i;
+            if (row < a.R && col < a.C) Y[row * a.ldy + col] = f16_bits(to_f16(acc[tm][tn][i]));
+          }
+        }
+    }
+  }
+}
+
+// ---- host side: pick a tile shape for the problem and launch ------------------------------
+
+template <int WM, int WN, int WK, int TM, int TN, int KSUB, bool GATHER>
+static hipError_t launch_cfg(SpmmArgs a, hipStream_t stream) {
+  using Cfg = SpmmCfg<WM, WN, WK, TM, TN, KSUB, GATHER>;
+  a.n_row_tiles = (a.R + Cfg::BM - 1) / Cfg::BM;
+  a.n_col_tiles = (a.C + Cfg::BN - 1) / Cfg::BN;
+  const int64_t tiles = a.n_row_tiles * a.n_col_tiles;
+  if (tiles == 0 || a.batch == 0) return hipSuccess;
+  const unsigned gy = (unsigned)(a.batch < 65535 ? a.batch : 65535);
+  auto kern = k_spmm<WM, WN, WK, TM, TN, KSUB, GATHER>;
+  static bool attr_set = false;   // benign race: every thread sets the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles, gy), dim3(Cfg::kThreads), Cfg::kLds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
+                          int64_t C, int64_t ldb, void* Y, int64_t ldy, int64_t batch,
+                          int64_t stride_values, int64_t stride_meta, int64_t stride_B,
+                          int64_t stride_Y, hipStream_t stream) {
+  SpmmArgs a{};
+  a.values = (const uint16_t*)values;
+  a.meta = (const uint8_t*)meta;
+  a.B = (const uint16_t*)B;
+  a.Y = (uint16_t*)Y;
+  a.colloc = nullptr;
+  a.R = R; a.Kc = K; a.K = K; a.C = C; a.ldb = ldb; a.ldy = ldy;
+  a.batch = batch;
+  a.stride_values = stride_values; a.stride_meta = stride_meta;
+  a.stride_B = stride_B; a.stride_Y = stride_Y;
+  a.V = 0; a.M = 4;
+  a.b_vec = (ldb % 8 == 0) && (((uintptr_t)B & 15) == 0) && (batch <= 1 || stride_B % 8 == 0);
+  if (C <= 16) return launch_cfg<1, 1, 4, 1, 1, 4, false>(a, stream);
+  if (C <= 32) return launch_cfg<1, 1, 4, 1, 2, 4, false>(a, stream);
+  if (C <= 64) return launch_cfg<4, 1, 1, 2, 4, 4, false>(a, stream);
+  return launch_cfg<2, 2, 1, 2, 4, 2, false>(a, stream);
+}
+
+hipError_t launch_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R,
+                           int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
+                           int64_t ldy, hipStream_t stream) {
+  SpmmArgs a{};
+  a.values = (const uint16_t*)values;
+  a.meta = (const uint8_t*)midx;
+  a.B = (const uint16_t*)B;
+  a.Y = (uint16_t*)Y;
+  a.colloc = (const uint8_t*)colloc;
+  a.R = R; a.Kc = 4 * (K / M); a.K = K; a.C = C; a.ldb = ldb; a.ldy = ldy;
+  a.batch = 1;
+  a.stride_values = 0; a.stride_meta = 0; a.stride_B = 0; a.stride_Y = 0;
+  a.V = V; a.M = M;
+  a.b_vec = (ldb % 8 == 0) && (((uintptr_t)B & 15) == 0);
+  // The row tile must not straddle two V-blocks: BM divides V.
+  if (V % 64 == 0) return launch_cfg<2, 2, 1, 2, 4, 2, true>(a, stream);   // BM = 64, BN = 128
+  if (V % 32 == 0) return launch_cfg<2, 2, 1, 1, 4, 2, true>(a, stream);   // BM = 32, BN = 128
+  return launch_cfg<1, 4, 1, 1, 2, 2, true>(a, stream);                    // BM = 16, BN = 128
+}
+
+}  // namespace snm

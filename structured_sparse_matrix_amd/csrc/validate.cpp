@@ -1,0 +1,111 @@
+// Argument validation (host only, no HIP). Status values match snm_status in snm.h.
+#include "validate.hpp"
+
+#include <stdint.h>
+
+#include "snm.h"
+
+namespace snm {
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned2(const void* p) { return ((uintptr_t)p & 1u) == 0; }
+bool all_aligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !aligned16(p)) return false;
+  return true;
+}
+// Element counts above 2^47 are rejected so that every offset fits comfortably in int64.
+constexpr int64_t kMaxElems = (int64_t)1 << 47;
+bool fits(int64_t a, int64_t b) { return a >= 0 && b >= 0 && (b == 0 || a <= kMaxElems / b); }
+
+}  // namespace
+
+int check_nm_sizes(int64_t R, int64_t K) {
+  if (R < 0 || K < 0 || K % 16 != 0 || !fits(R, K)) return SNM_E_SHAPE;
+  return SNM_OK;
+}
+
+int check_vnm_sizes(int64_t R, int64_t K, int V, int M) {
+  if (V < 1 || V > 256 || M < 4 || M > 256) return SNM_E_UNSUPPORTED;
+  if (R < 0 || K < 0 || !fits(R, K)) return SNM_E_SHAPE;
+  if (R % V != 0 || K % M != 0 || (K / M) % 4 != 0) return SNM_E_SHAPE;
+  return SNM_OK;
+}
+
+int check_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda, const void* values,
+                          const void* meta) {
+  int s = check_nm_sizes(R, K);
+  if (s != SNM_OK) return s;
+  if (R == 0 || K == 0) return SNM_OK;
+  if (!A || !values || !meta) return SNM_E_NULL;
+  if (lda < K || !fits(R, lda)) return SNM_E_SHAPE;
+  if (lda % 8 != 0 || !all_aligned({A, values, meta})) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
+int check_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
+                           const void* values, const void* midx, const void* colloc) {
+  int s = check_vnm_sizes(R, K, V, M);
+  if (s != SNM_OK) return s;
+  if (R == 0 || K == 0) return SNM_OK;
+  if (!A || !values || !midx || !colloc) return SNM_E_NULL;
+  if (lda < K || !fits(R, lda)) return SNM_E_SHAPE;
+  if (lda % 8 != 0 || !all_aligned({A, values, midx, colloc})) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
+int check_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
+                  int64_t C, int64_t ldb, const void* Y, int64_t ldy, int64_t batch,
+                  int64_t stride_values, int64_t stride_meta, int64_t stride_B, int64_t stride_Y) {
+  int s = check_nm_sizes(R, K);
+  if (s != SNM_OK) return s;
+  if (C < 0 || batch < 0 || !fits(K, C) || !fits(R, C)) return SNM_E_SHAPE;
+  if (R == 0 || C == 0 || batch == 0) return SNM_OK;
+  if (!Y || (K > 0 && (!values || !meta || !B))) return SNM_E_NULL;
+  if (ldy < C || ldb < C || !fits(K, ldb) || !fits(R, ldy)) return SNM_E_SHAPE;
+  if (batch > 1) {
+    if (stride_values < R * (K / 2) || stride_meta < R * (K / 8) || stride_B < K * ldb ||
+        stride_Y < R * ldy || !fits(batch, stride_values) || !fits(batch, stride_B) ||
+        !fits(batch, stride_Y) || !fits(batch, stride_meta))
+      return SNM_E_SHAPE;
+    if (stride_values % 8 != 0 || stride_meta % 16 != 0) return SNM_E_ALIGN;
+  }
+  if (!all_aligned({values, meta}) || !aligned2(B) || !aligned2(Y)) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
+int check_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R, int64_t K,
+                   int V, int M, const void* B, int64_t C, int64_t ldb, const void* Y, int64_t ldy) {
+  int s = check_vnm_sizes(R, K, V, M);
+  if (s != SNM_OK) return s;
+  if (V % 16 != 0) return SNM_E_UNSUPPORTED;
+  if (C < 0 || !fits(K, C) || !fits(R, C)) return SNM_E_SHAPE;
+  if (R == 0 || C == 0) return SNM_OK;
+  if (!Y || (K > 0 && (!values || !midx || !colloc || !B))) return SNM_E_NULL;
+  if (ldy < C || ldb < C || !fits(K, ldb) || !fits(R, ldy)) return SNM_E_SHAPE;
+  if (!all_aligned({values, midx, colloc}) || !aligned2(B) || !aligned2(Y)) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
+int check_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq, int64_t Lk,
+                         int64_t d, const void* values, const void* meta, const void* S_dense) {
+  if (d != 16 && d != 32 && d != 64 && d != 128) return SNM_E_UNSUPPORTED;
+  if (batch < 0 || Lq < 0 || Lk < 0 || Lk % 32 != 0 || !fits(batch, Lq) || !fits(batch * Lq, Lk) ||
+      !fits(batch * Lk, d) || !fits(batch * Lq, d))
+    return SNM_E_SHAPE;
+  if (batch == 0 || Lq == 0 || Lk == 0) return SNM_OK;
+  if (!Q || !Kmat || !values || !meta) return SNM_E_NULL;
+  if (!all_aligned({Q, Kmat, values, meta, S_dense})) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
+int check_softmax_nm_rows(const void* values, int64_t rows, int64_t kept, int64_t ld) {
+  if (rows < 0 || kept < 0 || ld < kept || !fits(rows, ld)) return SNM_E_SHAPE;
+  if (rows == 0 || kept == 0) return SNM_OK;
+  if (!values) return SNM_E_NULL;
+  if (!aligned16(values)) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
+}  // namespace snm

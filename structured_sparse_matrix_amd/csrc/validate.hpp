@@ -1,0 +1,24 @@
+// Argument validation of every libsnm entry point. Pure host C++: no HIP call, so it is
+// compiled into the library and also into a host-only test binary.
+#pragma once
+
+#include <stdint.h>
+
+namespace snm {
+
+int check_nm_sizes(int64_t R, int64_t K);
+int check_vnm_sizes(int64_t R, int64_t K, int V, int M);
+int check_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda, const void* values,
+                          const void* meta);
+int check_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
+                           const void* values, const void* midx, const void* colloc);
+int check_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
+                  int64_t C, int64_t ldb, const void* Y, int64_t ldy, int64_t batch,
+                  int64_t stride_values, int64_t stride_meta, int64_t stride_B, int64_t stride_Y);
+int check_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R, int64_t K,
+                   int V, int M, const void* B, int64_t C, int64_t ldb, const void* Y, int64_t ldy);
+int check_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq, int64_t Lk,
+                         int64_t d, const void* values, const void* meta, const void* S_dense);
+int check_softmax_nm_rows(const void* values, int64_t rows, int64_t kept, int64_t ld);
+
+}  // namespace snm

@@ -1,0 +1,163 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol snm.h declares, and
+rejects bad arguments on the host before any HIP call (no compute runs here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "snm.h")
+
+
+def _lib():
+    from structured_sparse_matrix_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libsnm.so not built (run __graft_entry__.build())")
+    return L.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(snm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("snm_prune_encode_nm", "snm_prune_encode_vnm", "snm_spmm_nm", "snm_spmm_vnm",
+              "snm_sddmm_prune_nm", "snm_softmax_nm_rows"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    from structured_sparse_matrix_amd import _lib as L
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in snm.h but not exported"
+        assert name in L.SIGNATURES, f"{name} has no ctypes signature in the binding"
+
+
+def test_exported_symbols_are_c_linkage():
+    # nm -D lists dynamic symbols; every declared name must appear unmangled
+    import subprocess
+    from structured_sparse_matrix_amd import _lib as L
+    _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms
+
+
+def test_version_and_status_strings():
+    lib = _lib()
+    assert lib.snm_abi_version() == 1
+    for s in range(7):
+        assert lib.snm_status_string(s)
+    assert lib.snm_status_string(99) == b"unknown status"
+
+
+def test_size_queries():
+    from structured_sparse_matrix_amd import nm_sizes, vnm_sizes, SnmError
+    _lib()
+    assert nm_sizes(4096, 4096) == (4096 * 2048, 4096 * 512)
+    assert nm_sizes(2, 16) == (16, 4)
+    # V:2:M, V=128 M=16 on 8192 x 8192: values 8192 x 1024, midx 8192 x 256 B, colloc 64 x 512 x 4
+    assert vnm_sizes(8192, 8192, 128, 16) == (8192 * 1024, 8192 * 256, 64 * 512 * 4)
+    assert vnm_sizes(11008, 4096, 64, 8) == (11008 * 1024, 11008 * 256, 172 * 512 * 4)
+    with pytest.raises(SnmError):
+        nm_sizes(4, 8)            # K % 16 != 0
+    with pytest.raises(SnmError):
+        vnm_sizes(100, 64, 64, 8)  # R % V != 0
+    with pytest.raises(SnmError):
+        vnm_sizes(64, 48, 64, 8)   # (K/M) % 4 != 0
+    with pytest.raises(SnmError):
+        vnm_sizes(64, 1024, 64, 2)  # M < 4
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)          # never dereferenced: every call below fails validation first
+MISALIGNED = P(0x1008)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((P(0), 4, 16, 16, FAKE, FAKE, P(0)), 1),           # A NULL
+    ((FAKE, 4, 12, 16, FAKE, FAKE, P(0)), 2),           # K % 16
+    ((FAKE, 4, 16, 8, FAKE, FAKE, P(0)), 2),            # lda < K
+    ((FAKE, 4, 16, 20, FAKE, FAKE, P(0)), 3),           # lda % 8
+    ((MISALIGNED, 4, 16, 16, FAKE, FAKE, P(0)), 3),     # pointer alignment
+    ((FAKE, -1, 16, 16, FAKE, FAKE, P(0)), 2),          # negative R
+    ((P(0), 0, 16, 16, P(0), P(0), P(0)), 0),           # empty: ok, nothing enqueued
+])
+def test_prune_encode_nm_validation(args, status):
+    assert _lib().snm_prune_encode_nm(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 128, 64, 64, 64, 3, FAKE, FAKE, FAKE, P(0)), 4),     # M < 4
+    ((FAKE, 128, 64, 64, 0, 8, FAKE, FAKE, FAKE, P(0)), 4),      # V < 1
+    ((FAKE, 100, 64, 64, 64, 8, FAKE, FAKE, FAKE, P(0)), 2),     # R % V
+    ((FAKE, 128, 48, 48, 64, 8, FAKE, FAKE, FAKE, P(0)), 2),     # (K/M) % 4
+    ((FAKE, 128, 64, 64, 64, 8, P(0), FAKE, FAKE, P(0)), 1),     # values NULL
+])
+def test_prune_encode_vnm_validation(args, status):
+    assert _lib().snm_prune_encode_vnm(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, 16, 24, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 2),      # K % 16
+    ((FAKE, FAKE, 16, 32, FAKE, 8, 4, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 2),      # ldb < C
+    ((FAKE, FAKE, 16, 32, FAKE, 8, 8, P(0x1001), 12, 1, 0, 0, 0, 0, P(0)), 3),  # odd Y pointer
+    ((FAKE, P(0), 16, 32, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 1),      # meta NULL
+    ((FAKE, FAKE, 16, 32, FAKE, 8, 8, FAKE, 8, 2, 8, 64, 256, 128, P(0)), 2),  # stride_values too small
+    ((FAKE, FAKE, 16, 32, FAKE, 8, 8, FAKE, 8, -1, 0, 0, 0, 0, P(0)), 2),     # negative batch
+    ((P(0), P(0), 16, 32, P(0), 0, 0, P(0), 0, 1, 0, 0, 0, 0, P(0)), 0),      # C == 0: ok
+])
+def test_spmm_nm_validation(args, status):
+    assert _lib().snm_spmm_nm(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, FAKE, 64, 64, 8, 8, FAKE, 8, 8, FAKE, 8, P(0)), 4),    # V not a multiple of 16
+    ((FAKE, FAKE, FAKE, 64, 48, 64, 8, FAKE, 8, 8, FAKE, 8, P(0)), 2),   # (K/M) % 4
+    ((FAKE, FAKE, P(0), 64, 64, 64, 8, FAKE, 8, 8, FAKE, 8, P(0)), 1),   # colloc NULL
+])
+def test_spmm_vnm_validation(args, status):
+    assert _lib().snm_spmm_vnm(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, 1, 16, 32, 48, ctypes.c_float(0.125), FAKE, FAKE, P(0), P(0)), 4),   # d unsupported
+    ((FAKE, FAKE, 1, 16, 40, 64, ctypes.c_float(0.125), FAKE, FAKE, P(0), P(0)), 2),   # Lk % 32
+    ((FAKE, P(0), 1, 16, 32, 64, ctypes.c_float(0.125), FAKE, FAKE, P(0), P(0)), 1),   # Kmat NULL
+    ((FAKE, FAKE, 1, 16, 32, 64, ctypes.c_float(0.125), FAKE, FAKE, MISALIGNED, P(0)), 3),
+])
+def test_sddmm_validation(args, status):
+    assert _lib().snm_sddmm_prune_nm(*args) == status
+
+
+def test_softmax_validation():
+    lib = _lib()
+    assert lib.snm_softmax_nm_rows(FAKE, 4, 16, 8, P(0)) == 2       # ld < kept
+    assert lib.snm_softmax_nm_rows(P(0), 4, 16, 16, P(0)) == 1
+    assert lib.snm_softmax_nm_rows(MISALIGNED, 4, 16, 16, P(0)) == 3
+    assert lib.snm_softmax_nm_rows(P(0), 0, 16, 16, P(0)) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from structured_sparse_matrix_amd import _lib as L
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(ImportError):
+        L.load()
+
+
+def test_binding_never_imports_the_oracle():
+    # the product package must not reach the CPU oracle
+    pkg = os.path.join(ROOT, "structured_sparse_matrix_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+                assert not re.search(r"import_module\(\s*['\"]oracle", text), f
