@@ -2,7 +2,10 @@
 
 Workload (the shape the headline metric is quoted on): A 4096 x 4096 fp16 ~ N(0, 0.02),
 pruned 2:4 along K; B 4096 x N fp16 ~ N(0, 1) for N in {8, 16, 32}; fp32 accumulation,
-fp16 output. One step = prune_encode_nm(A) followed by spmm_nm with each of the three B.
+fp16 output. One step = 2:4 prune/encode of A followed by the SpMM with each of the
+three B. By default A is encoded into the operand-major layout (snm_prune_encode_nm_tiled
+/ snm_spmm_nm_tiled) and B is stored as decode activations X[N][K] (column-major B);
+--a-layout canonical and --b-layout row select the other paths.
 Inputs rotate over 32 independent copies (> 1.5 GiB) so that the 256 MiB last-level cache
 cannot serve them: every step streams its operands from HBM.
 
@@ -70,7 +73,7 @@ def cpu_baseline(min_seconds: float = 10.0) -> dict:
                       f"host {platform.processor() or platform.machine()}"}
 
 
-def run_gpu(steps: int, warmup: int):
+def run_gpu(steps: int, warmup: int, layout: str = "col", a_layout: str = "tiled"):
     import numpy as np
     import torch
     import structured_sparse_matrix_amd as snm
@@ -84,20 +87,35 @@ def run_gpu(steps: int, warmup: int):
     # 32 resident copies at distinct addresses
     As = [A0d.clone() for _ in range(NROT)]
     Bs = [[b.clone() for b in B0d] for _ in range(NROT)]
-    vals = [torch.empty((R, K // 2), dtype=torch.float16, device=dev) for _ in range(NROT)]
-    metas = [torch.empty((R, K // 8), dtype=torch.uint8, device=dev) for _ in range(NROT)]
+    # the same activations stored as X[N][K] (B column-major), the decode layout
+    Xs = [[b.t().contiguous().t() for b in B0d] for _ in range(NROT)]
+    if a_layout == "tiled":
+        nv, nm = snm.nm_tiled_sizes(R, K)
+        vals = [torch.empty((nv,), dtype=torch.float16, device=dev) for _ in range(NROT)]
+        metas = [torch.empty((nm,), dtype=torch.uint8, device=dev) for _ in range(NROT)]
+    else:
+        vals = [torch.empty((R, K // 2), dtype=torch.float16, device=dev) for _ in range(NROT)]
+        metas = [torch.empty((R, K // 8), dtype=torch.uint8, device=dev) for _ in range(NROT)]
     Ys = [[torch.empty((R, n), dtype=torch.float16, device=dev) for n in NS] for _ in range(NROT)]
     del A0d, B0d
+
+    Bsel = Xs if layout == "col" else Bs
 
     def step(i, ev=None):
         j = i % NROT
         if ev is not None:
             ev[0].record()
-        snm.prune_encode_nm(As[j], vals[j], metas[j])
+        if a_layout == "tiled":
+            snm.prune_encode_nm_tiled(As[j], vals[j], metas[j])
+        else:
+            snm.prune_encode_nm(As[j], vals[j], metas[j])
         if ev is not None:
             ev[1].record()
         for t in range(len(NS)):
-            snm.spmm_nm(vals[j], metas[j], Bs[j][t], out=Ys[j][t])
+            if a_layout == "tiled":
+                snm.spmm_nm_tiled(vals[j], metas[j], R, Bsel[j][t], out=Ys[j][t])
+            else:
+                snm.spmm_nm(vals[j], metas[j], Bsel[j][t], out=Ys[j][t])
             if ev is not None:
                 ev[2 + t].record()
 
@@ -127,6 +145,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--b-layout", choices=("col", "row"), default="col",
+                    help="B stored column-major (activations X[N][K], default) or row-major")
+    ap.add_argument("--a-layout", choices=("tiled", "canonical"), default="tiled",
+                    help="compressed A in the operand-major layout (default) or the canonical one")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -134,7 +156,7 @@ def main():
         sys.exit(2)
     import numpy as np
 
-    total_ms, wall, enc_ms, spmm_ms = run_gpu(args.steps, args.warmup)
+    total_ms, wall, enc_ms, spmm_ms = run_gpu(args.steps, args.warmup, args.b_layout, args.a_layout)
     ms_per_step = total_ms / args.steps
     flops_step = sum(2 * R * K * n for n in NS)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
@@ -170,8 +192,10 @@ def main():
         "config": {"workload": "2:4 SpMM decode-shaped: A 4096x4096 fp16 N(0,0.02) pruned 2:4 along K, "
                                "B 4096xN fp16 N(0,1), N in {8,16,32}; step = prune_encode_nm + 3 spmm_nm; "
                                "32 rotating input copies",
-                   "R": R, "K": K, "N": list(NS), "rotating_copies": NROT},
-        "roofline": {"bound": "hbm", "kernel": "spmm_nm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                   "R": R, "K": K, "N": list(NS), "rotating_copies": NROT,
+                   "B_storage": "column-major (X[N][K])" if args.b_layout == "col" else "row-major (K x N)",
+                   "A_storage": "operand-major (tiled)" if args.a_layout == "tiled" else "canonical"},
+        "roofline": {"bound": "hbm", "kernel": "spmm_nm_tiled" if args.a_layout == "tiled" else "spmm_nm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
         "kernels": kernels,
         "wall_s_timed_region": wall,

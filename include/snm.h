@@ -99,14 +99,42 @@ int snm_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V
  * the metadata selects, per kept value, the row of B it multiplies).
  *   values, meta  2:4 arrays of an R x K matrix (canonical layout), per batch entry at
  *                 values + b*stride_values (elements) and meta + b*stride_meta (bytes).
- *   B             fp16 K x C, leading dimension ldb >= C, entry b at B + b*stride_B.
- *   Y             fp16 R x C, leading dimension ldy >= C, entry b at Y + b*stride_Y.
+ *   B             fp16 K x C, entry b at B + b*stride_B. b_layout 0: row-major, element
+ *                 (k, c) at B[k*ldb + c], ldb >= C. b_layout 1: column-major, element
+ *                 (k, c) at B[c*ldb + k], ldb >= K (decode activations X[C][K] as stored).
+ *   Y             fp16 R x C, row-major, leading dimension ldy >= C, entry b at Y + b*stride_Y.
  * Products accumulate in fp32; Y is rounded to fp16 (round to nearest even). Requires
  * K % 16 == 0, batch >= 1 (0 enqueues nothing). Strides are ignored when batch == 1. */
 int snm_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K,
-                const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                const void* B, int64_t C, int64_t ldb, int b_layout, void* Y, int64_t ldy,
                 int64_t batch, int64_t stride_values, int64_t stride_meta,
                 int64_t stride_B, int64_t stride_Y, void* stream);
+
+/* Operand-major ("tiled") storage of the same 2:4 data, laid out for the CDNA4 sparse
+ * matrix instruction (the analogue of the fragment-ordered storage of VENOM Sec. 4.1.2,
+ * Fig. 7): the matrix is cut into blocks of 16 rows x 64 positions along K; block
+ * (rt, kc) is stored at index rt*ceil(K/64) + kc as
+ *   values_t  64 lanes x 8 fp16 (1 KiB): lane l = 16q + i holds row 16rt + i, positions
+ *             64kc + 16q + [0, 16) -- its four groups' kept values in canonical order;
+ *   meta_t    64 lanes x uint16 (128 B): lane l's canonical metadata word for the same
+ *             four groups.
+ * Rows past R and positions past K are stored as zero values and zero metadata. The
+ * content is a permutation (plus padding) of the canonical values and meta. */
+
+/* Sizes of the operand-major arrays: values elements and meta bytes for an R x K matrix
+ * (ceil(R/16)*ceil(K/64) blocks of 512 elements and 128 bytes). K % 16 == 0. Host only. */
+int snm_nm_tiled_sizes(int64_t R, int64_t K, int64_t* values_elems, int64_t* meta_bytes);
+
+/* 2:4 prune and compress straight into the operand-major layout. Same selection as
+ * snm_prune_encode_nm; A fp16 R x K (lda >= K, lda % 8 == 0); K % 16 == 0. */
+int snm_prune_encode_nm_tiled(const void* A, int64_t R, int64_t K, int64_t lda,
+                              void* values_t, void* meta_t, void* stream);
+
+/* Y = decode(values_t, meta_t) * B with A in the operand-major layout; B, b_layout, Y as
+ * in snm_spmm_nm (no batching). fp32 accumulation, fp16 output (RNE). */
+int snm_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                      const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
+                      int64_t ldy, void* stream);
 
 /* Y = decode_vnm(values, midx, colloc) * B (VENOM Sec. 4 and Fig. 4: per block of V rows
  * the K/M*4 rows of B named by colloc are gathered, then 2:4 is applied with midx).

@@ -19,6 +19,7 @@ from ._lib import load, check, SnmError, LIB_PATH
 __all__ = [
     "prune_encode_nm", "prune_encode_vnm", "spmm_nm", "spmm_vnm", "sddmm_prune_nm",
     "softmax_nm_rows", "attention_nm", "nm_sizes", "vnm_sizes", "abi_version", "SnmError",
+    "nm_tiled_sizes", "prune_encode_nm_tiled", "spmm_nm_tiled",
     "LIB_PATH",
 ]
 
@@ -81,6 +82,54 @@ def prune_encode_nm(A, values=None, meta=None):
     return values, meta
 
 
+def nm_tiled_sizes(R: int, K: int):
+    v, m = ctypes.c_int64(), ctypes.c_int64()
+    check("snm_nm_tiled_sizes", load().snm_nm_tiled_sizes(R, K, ctypes.byref(v), ctypes.byref(m)))
+    return v.value, m.value
+
+
+def prune_encode_nm_tiled(A, values_t=None, meta_t=None):
+    """2:4 prune of fp16 A [R, K] into the operand-major layout (see snm.h):
+    values_t fp16 [ceil(R/16)*ceil(K/64)*512], meta_t uint8 [.. *128]."""
+    torch = _torch()
+    _need(A, "A", torch.float16, 2)
+    if A.stride(1) != 1:
+        raise ValueError("A must be row-major (unit stride along K)")
+    R, K = A.shape
+    nv, nm = nm_tiled_sizes(R, K)
+    if values_t is None:
+        values_t = torch.empty((nv,), dtype=torch.float16, device=A.device)
+    if meta_t is None:
+        meta_t = torch.empty((nm,), dtype=torch.uint8, device=A.device)
+    if values_t.numel() < nv or meta_t.numel() < nm:
+        raise ValueError("output buffers too small for the operand-major layout")
+    check("snm_prune_encode_nm_tiled",
+          load().snm_prune_encode_nm_tiled(_ptr(A), R, K, A.stride(0), _ptr(values_t), _ptr(meta_t), _stream(A)))
+    return values_t, meta_t
+
+
+def spmm_nm_tiled(values_t, meta_t, R: int, B, out=None):
+    """Y = decode(values_t, meta_t) @ B for an R x K operand-major matrix; B [K, C]
+    (row-major, or column-major such as X.t())."""
+    torch = _torch()
+    _need(values_t, "values_t", torch.float16)
+    _need(meta_t, "meta_t", torch.uint8)
+    _need(B, "B", torch.float16, 2)
+    K, C = B.shape
+    nv, nm = nm_tiled_sizes(R, K)
+    if values_t.numel() < nv or meta_t.numel() < nm or not values_t.is_contiguous() or not meta_t.is_contiguous():
+        raise ValueError("operand-major arrays do not match R x K")
+    layout, ldb = _b_layout(B)
+    if out is None:
+        out = torch.empty((R, C), dtype=torch.float16, device=B.device)
+    if out.stride(1) != 1:
+        raise ValueError("out must be row-major")
+    check("snm_spmm_nm_tiled",
+          load().snm_spmm_nm_tiled(_ptr(values_t), _ptr(meta_t), R, K, _ptr(B), C, ldb, layout,
+                                   _ptr(out), out.stride(0), _stream(B)))
+    return out
+
+
 def prune_encode_vnm(A, V: int, M: int):
     """V:2:M prune of fp16 A [R, K] -> (values [R, 2K/M], midx [R, K/(2M)], colloc [R/V, K/M, 4])."""
     torch = _torch()
@@ -98,9 +147,20 @@ def prune_encode_vnm(A, V: int, M: int):
     return values, midx, colloc
 
 
+def _b_layout(B):
+    """(layout, ld) of a [..., K, C] tensor: 0 = row-major (unit stride along C),
+    1 = column-major (unit stride along K, e.g. X.t() for activations X [C, K])."""
+    if B.stride(-1) == 1 and (B.shape[-1] == 1 or B.stride(-2) >= B.shape[-1]):
+        return 0, B.stride(-2)
+    if B.stride(-2) == 1:
+        return 1, B.stride(-1)
+    raise ValueError("B must have unit stride along one of its last two axes")
+
+
 def spmm_nm(values, meta, B, out=None):
     """Y = decode(values, meta) @ B. 2-D: values [R, K/2], meta [R, K/8], B [K, C] -> Y [R, C].
-    3-D (batched): values [b, R, K/2], meta [b, R, K/8], B [b, K, C] -> Y [b, R, C]."""
+    3-D (batched): values [b, R, K/2], meta [b, R, K/8], B [b, K, C] -> Y [b, R, C].
+    B may be row-major or column-major (a transposed view such as X.t() with X [C, K])."""
     torch = _torch()
     _need(values, "values", torch.float16, (2, 3))
     _need(meta, "meta", torch.uint8, values.dim())
@@ -116,15 +176,16 @@ def spmm_nm(values, meta, B, out=None):
     for t, n in ((values, "values"), (meta, "meta")):
         if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
             raise ValueError(f"{n} must be contiguous per batch entry")
-    if B.stride(2) != 1:
-        raise ValueError("B must be row-major (unit stride along C)")
+    layout, ldb = _b_layout(B)
     C = B.shape[2]
     if out is None:
         out = torch.empty((nb, R, C), dtype=torch.float16, device=B.device)
     elif not batched:
         out = out[None]
+    if out.stride(2) != 1:
+        raise ValueError("out must be row-major")
     check("snm_spmm_nm",
-          load().snm_spmm_nm(_ptr(values), _ptr(meta), R, K, _ptr(B), C, B.stride(1), _ptr(out),
+          load().snm_spmm_nm(_ptr(values), _ptr(meta), R, K, _ptr(B), C, ldb, layout, _ptr(out),
                              out.stride(1), nb, values.stride(0), meta.stride(0), B.stride(0),
                              out.stride(0), _stream(B)))
     return out if batched else out[0]

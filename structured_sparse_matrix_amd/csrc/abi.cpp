@@ -77,6 +77,33 @@ int snm_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda, void* 
   return launched(snm::launch_prune_encode_nm(A, R, K, lda, values, meta, (hipStream_t)stream));
 }
 
+int snm_nm_tiled_sizes(int64_t R, int64_t K, int64_t* values_elems, int64_t* meta_bytes) {
+  int s = snm::check_nm_sizes(R, K);
+  if (s != SNM_OK) return s;
+  if (!values_elems || !meta_bytes) return SNM_E_NULL;
+  const int64_t blocks = ((R + 15) / 16) * ((K + 63) / 64);
+  *values_elems = blocks * 512;
+  *meta_bytes = blocks * 128;
+  return SNM_OK;
+}
+
+int snm_prune_encode_nm_tiled(const void* A, int64_t R, int64_t K, int64_t lda, void* values_t,
+                              void* meta_t, void* stream) {
+  int s = snm::check_prune_encode_nm(A, R, K, lda, values_t, meta_t);
+  if (s != SNM_OK || R == 0 || K == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_prune_encode_nm_tiled(A, R, K, lda, values_t, meta_t, (hipStream_t)stream));
+}
+
+int snm_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_t R, int64_t K, const void* B,
+                      int64_t C, int64_t ldb, int b_layout, void* Y, int64_t ldy, void* stream) {
+  int s = snm::check_spmm_nm(values_t, meta_t, R, K, B, C, ldb, b_layout, Y, ldy, 1, 0, 0, 0, 0);
+  if (s != SNM_OK || R == 0 || C == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_spmm_nm_tiled(values_t, meta_t, R, K, B, C, ldb, b_layout, Y, ldy,
+                                            (hipStream_t)stream));
+}
+
 int snm_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
                          void* values, void* midx, void* colloc, void* stream) {
   int s = snm::check_prune_encode_vnm(A, R, K, lda, V, M, values, midx, colloc);
@@ -87,15 +114,16 @@ int snm_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V
 }
 
 int snm_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
-                int64_t C, int64_t ldb, void* Y, int64_t ldy, int64_t batch,
+                int64_t C, int64_t ldb, int b_layout, void* Y, int64_t ldy, int64_t batch,
                 int64_t stride_values, int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
                 void* stream) {
-  int s = snm::check_spmm_nm(values, meta, R, K, B, C, ldb, Y, ldy, batch, stride_values,
-                             stride_meta, stride_B, stride_Y);
+  int s = snm::check_spmm_nm(values, meta, R, K, B, C, ldb, b_layout, Y, ldy, batch,
+                             stride_values, stride_meta, stride_B, stride_Y);
   if (s != SNM_OK || R == 0 || C == 0 || batch == 0) return s;
   if ((s = check_device()) != SNM_OK) return s;
-  return launched(snm::launch_spmm_nm(values, meta, R, K, B, C, ldb, Y, ldy, batch, stride_values,
-                                      stride_meta, stride_B, stride_Y, (hipStream_t)stream));
+  return launched(snm::launch_spmm_nm(values, meta, R, K, B, C, ldb, b_layout, Y, ldy, batch,
+                                      stride_values, stride_meta, stride_B, stride_Y,
+                                      (hipStream_t)stream));
 }
 
 int snm_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R, int64_t K,

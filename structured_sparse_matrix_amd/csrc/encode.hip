@@ -65,6 +65,46 @@ k_prune_encode_nm(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t 
   }
 }
 
+// 2:4 prune into the operand-major layout: block (rt, kc) holds the sparse-MFMA A operand
+// of rows 16rt..16rt+15 and positions 64kc..64kc+63 -- lane l = 16q + i carries row
+// 16rt + i, positions 64kc + 16q + [0, 16): 8 values (16 bytes) and one metadata word.
+// One thread per lane of a block: a wave reads 16 rows x 128 contiguous bytes and writes
+// one contiguous 1 KiB value block and one 128-byte metadata block. Rows past R and
+// positions past K are zero-filled (values 0, metadata word 0).
+__global__ void __launch_bounds__(256)
+k_prune_encode_nm_tiled(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t lda,
+                        uint16_t* __restrict__ values_t, uint16_t* __restrict__ meta_t) {
+  const int64_t KC = (K + 63) >> 6;
+  const int64_t total = ((R + 15) >> 4) * KC * 64;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(g & 63);
+    const int64_t blk = g >> 6;
+    const int64_t rt = blk / KC;
+    const int64_t kc = blk - rt * KC;
+    const int64_t row = rt * 16 + (lane & 15);
+    const int64_t pos = kc * 64 + 16 * (lane >> 4);
+    u4 o = {0u, 0u, 0u, 0u};
+    uint32_t word = 0;
+    if (row < R && pos < K) {
+      const u4* src = reinterpret_cast<const u4*>(A + row * lda + pos);
+      const u4 x0 = __builtin_nontemporal_load(src);
+      const u4 x1 = __builtin_nontemporal_load(src + 1);
+      const uint32_t e[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const uint32_t lo = e[2 * gi], hi = e[2 * gi + 1];
+        uint32_t v0, v1;
+        const uint32_t code = select_2of4(lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16, v0, v1);
+        o[gi] = v0 | (v1 << 16);
+        word |= code << (4 * gi);
+      }
+    }
+    *reinterpret_cast<u4*>(values_t + g * 8) = o;
+    meta_t[g] = (uint16_t)word;
+  }
+}
+
 // V:2:M. One workgroup per (block of V rows, chunk of GC groups of M columns).
 //   Phase 1: one thread per column sums the squares of the block's V entries in float64,
 //            rows in ascending order (a fp16 square is exact in float64, so the sum is the
@@ -158,6 +198,17 @@ hipError_t launch_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t l
   if (blocks > 256 * 64) blocks = 256 * 64;   // grid-stride beyond 64 workgroups per CU
   hipLaunchKernelGGL(k_prune_encode_nm, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint16_t*)A, R, K, lda, (uint16_t*)values, (uint16_t*)meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_prune_encode_nm_tiled(const void* A, int64_t R, int64_t K, int64_t lda, void* values_t,
+                                        void* meta_t, hipStream_t stream) {
+  const int64_t total = ((R + 15) >> 4) * ((K + 63) >> 6) * 64;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  hipLaunchKernelGGL(k_prune_encode_nm_tiled, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const uint16_t*)A, R, K, lda, (uint16_t*)values_t, (uint16_t*)meta_t);
   return hipGetLastError();
 }
 

@@ -9,12 +9,25 @@ namespace snm {
 
 hipError_t launch_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda, void* values,
                                   void* meta, hipStream_t stream);
+hipError_t launch_prune_encode_nm_tiled(const void* A, int64_t R, int64_t K, int64_t lda, void* values_t,
+                                        void* meta_t, hipStream_t stream);
+hipError_t launch_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                                const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
+                                int64_t ldy, hipStream_t stream);
+hipError_t launch_spmm_nm_tiled_skinny(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                                       const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
+                                       int64_t ldy, hipStream_t stream);
 hipError_t launch_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
                                    void* values, void* midx, void* colloc, hipStream_t stream);
 hipError_t launch_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
-                          int64_t C, int64_t ldb, void* Y, int64_t ldy, int64_t batch,
+                          int64_t C, int64_t ldb, int b_layout, void* Y, int64_t ldy, int64_t batch,
                           int64_t stride_values, int64_t stride_meta, int64_t stride_B,
                           int64_t stride_Y, hipStream_t stream);
+hipError_t launch_spmm_nm_skinny(const void* values, const void* meta, int64_t R, int64_t K,
+                                 const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
+                                 int64_t ldy, int64_t batch, int64_t stride_values,
+                                 int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
+                                 hipStream_t stream);
 hipError_t launch_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R,
                            int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
                            int64_t ldy, hipStream_t stream);

@@ -13,10 +13,10 @@
 // Work decomposition
 //   workgroup tile  BM x BN outputs, BM = WM*TM*16 rows, BN = WN*TN*16 columns;
 //   WK waves split the reduction inside the workgroup (summed through LDS at the end).
-//   superchunk      KS = 64*KSUB consecutive positions of the compressed space. Lane
-//                   quarter p of a wave owns positions 16*KSUB*p + [0, 16*KSUB) of it,
-//                   i.e. KSUB consecutive sparse-MFMA operands that are one contiguous
-//                   32*KSUB-byte run of values and 2*KSUB bytes of metadata.
+//   superchunk      KS = 64*KSUB consecutive positions of the compressed space, i.e.
+//                   KSUB sparse-MFMA operands; in operand t lane quarter q holds
+//                   positions 64t + 16q + [0, 16) (the instruction's own order, so the
+//                   operand-major storage of snm_spmm_nm_tiled is one 1 KiB block).
 //   A operand       loaded straight from HBM into registers (non-temporal, read once);
 //                   the canonical metadata word is the sparse-MFMA index operand as is.
 //   B operand       the KS x BN tile is staged in LDS (rows as stored, 32-byte cells
@@ -45,7 +45,7 @@ struct SpmmArgs {
 // Byte offset, inside a B tile of BN fp16 columns, of (row x, column c) with c a multiple
 // of 4. Cells of 32 bytes (16 columns) are XOR-permuted inside 256-byte lines (one line
 // spans all 64 LDS banks) so that the 16 rows one transpose read touches -- rows
-// {0..3, 8..11} + {0, 32*KSUB} (+16t) -- fall on 8 distinct cells, each at most twice.
+// {0..3, 8..11, 16..19, 24..27} + const -- fall on 8 distinct cells, each at most twice.
 template <int BN>
 __device__ __forceinline__ uint32_t btile_offset(int x, int c) {
   const int cr = c >> 4;
@@ -72,7 +72,7 @@ __device__ __forceinline__ uint32_t btile_offset(int x, int c) {
   }
 }
 
-template <int WM, int WN, int WK, int TM, int TN, int KSUB, bool GATHER>
+template <int WM, int WN, int WK, int TM, int TN, int KSUB, bool GATHER, bool BCOL, bool ATILED = false>
 struct SpmmCfg {
   static constexpr int kWaves = WM * WN * WK;
   static constexpr int kThreads = 64 * kWaves;
@@ -81,18 +81,22 @@ struct SpmmCfg {
   static constexpr int KS = 64 * KSUB;                 // compressed positions per superchunk
   static constexpr int kTileRows = WK * KS;            // B rows staged per iteration
   static constexpr int kChunksPerRow = BN / 8;         // 16-byte chunks per B row
+  static constexpr int kChunksPerCol = kTileRows / 8;  // 16-byte chunks per B column (BCOL)
   static constexpr int kChunks = kTileRows * kChunksPerRow;
   static constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
-  static constexpr int kLdsB = kTileRows * BN * 2;
+  // column-major B is staged as [column][k]: a 16-byte pad per column rotates the banks
+  static constexpr int kColPitch = kTileRows * 2 + 16;
+  static constexpr int kLdsB = BCOL ? BN * kColPitch : kTileRows * BN * 2;
   static constexpr int kLdsRed = (WK - 1) * WM * WN * TM * TN * 64 * 16;
   static constexpr int kLds = kLdsB > kLdsRed ? kLdsB : kLdsRed;
   static_assert(kChunks % kThreads == 0, "B tile must split evenly over the workgroup");
 };
 
-template <int WM, int WN, int WK, int TM, int TN, int KSUB, bool GATHER>
+template <int WM, int WN, int WK, int TM, int TN, int KSUB, bool GATHER, bool BCOL, bool ATILED>
 __global__ void __launch_bounds__(64 * WM * WN * WK)
 k_spmm(SpmmArgs a) {
-  using Cfg = SpmmCfg<WM, WN, WK, TM, TN, KSUB, GATHER>;
+  using Cfg = SpmmCfg<WM, WN, WK, TM, TN, KSUB, GATHER, BCOL, ATILED>;
+  static_assert(!(GATHER && BCOL), "gathered rows need row-major B");
   constexpr int BM = Cfg::BM, BN = Cfg::BN, KS = Cfg::KS;
   extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t lds_base = lds_addr(smem);
@@ -114,6 +118,7 @@ k_spmm(SpmmArgs a) {
   const int64_t nsuper = (a.Kc + KS - 1) / KS;
   const int64_t vals_row = a.Kc >> 1;     // elements
   const int64_t meta_row = a.Kc >> 3;     // bytes
+  const int64_t KCt = (a.Kc + 63) >> 6;   // operand-major: 64-position blocks per row tile
   const int64_t G = GATHER ? a.K / a.M : 0;
   const int64_t vb = GATHER ? row0 / a.V : 0;
 
@@ -132,31 +137,50 @@ k_spmm(SpmmArgs a) {
 #pragma unroll
       for (int i = 0; i < Cfg::kChunksPerThread; ++i) {
         const int chunk = tid + i * Cfg::kThreads;
-        const int j = chunk / Cfg::kChunksPerRow;           // tile row
-        const int cc = chunk - j * Cfg::kChunksPerRow;      // 16-byte chunk in the row
-        const int64_t kg = s0 * KS + j;                     // compressed-space position
-        const int64_t col = col0 + cc * 8;
         u4 v = {0u, 0u, 0u, 0u};
-        if (kg < a.Kc) {
-          int64_t brow;
-          if constexpr (GATHER) {
-            const int64_t g = kg >> 2;
-            const int cl = a.colloc[(vb * G + g) * 4 + (kg & 3)];
-            brow = g * a.M + (cl < a.M ? cl : a.M - 1);   // column-loc entries are < M by contract
-          } else {
-            brow = kg;
+        if constexpr (BCOL) {
+          // eight consecutive k of one column
+          const int c = chunk / Cfg::kChunksPerCol;
+          const int kc = chunk - c * Cfg::kChunksPerCol;
+          const int64_t kg = s0 * KS + kc * 8;
+          const int64_t col = col0 + c;
+          if (kg < a.Kc && col < a.C) {
+            const uint16_t* src = Bm + col * a.ldb + kg;
+            if (a.b_vec) {
+              v = *reinterpret_cast<const u4*>(src);
+            } else {
+              v[0] = src[0] | ((uint32_t)src[1] << 16);
+              v[1] = src[2] | ((uint32_t)src[3] << 16);
+              v[2] = src[4] | ((uint32_t)src[5] << 16);
+              v[3] = src[6] | ((uint32_t)src[7] << 16);
+            }
           }
-          const uint16_t* src = Bm + brow * a.ldb + col;
-          if (a.b_vec && col + 8 <= a.C) {
-            v = *reinterpret_cast<const u4*>(src);
-          } else {
-            uint16_t e[8];
+        } else {
+          const int j = chunk / Cfg::kChunksPerRow;           // tile row
+          const int cc = chunk - j * Cfg::kChunksPerRow;      // 16-byte chunk in the row
+          const int64_t kg = s0 * KS + j;                     // compressed-space position
+          const int64_t col = col0 + cc * 8;
+          if (kg < a.Kc) {
+            int64_t brow;
+            if constexpr (GATHER) {
+              const int64_t g = kg >> 2;
+              const int cl = a.colloc[(vb * G + g) * 4 + (kg & 3)];
+              brow = g * a.M + (cl < a.M ? cl : a.M - 1);   // column-loc entries are < M by contract
+            } else {
+              brow = kg;
+            }
+            const uint16_t* src = Bm + brow * a.ldb + col;
+            if (a.b_vec && col + 8 <= a.C) {
+              v = *reinterpret_cast<const u4*>(src);
+            } else {
+              uint16_t e[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) e[t] = (col + t < a.C) ? src[t] : (uint16_t)0;
-            v[0] = e[0] | ((uint32_t)e[1] << 16);
-            v[1] = e[2] | ((uint32_t)e[3] << 16);
-            v[2] = e[4] | ((uint32_t)e[5] << 16);
-            v[3] = e[6] | ((uint32_t)e[7] << 16);
+              for (int t = 0; t < 8; ++t) e[t] = (col + t < a.C) ? src[t] : (uint16_t)0;
+              v[0] = e[0] | ((uint32_t)e[1] << 16);
+              v[1] = e[2] | ((uint32_t)e[3] << 16);
+              v[2] = e[4] | ((uint32_t)e[5] << 16);
+              v[3] = e[6] | ((uint32_t)e[7] << 16);
+            }
           }
         }
         bstage[i] = v;
@@ -166,25 +190,43 @@ k_spmm(SpmmArgs a) {
 #pragma unroll
       for (int i = 0; i < Cfg::kChunksPerThread; ++i) {
         const int chunk = tid + i * Cfg::kThreads;
-        const int j = chunk / Cfg::kChunksPerRow;
-        const int cc = chunk - j * Cfg::kChunksPerRow;
-        *reinterpret_cast<u4*>(smem + btile_offset<BN>(j, cc * 8)) = bstage[i];
+        if constexpr (BCOL) {
+          const int c = chunk / Cfg::kChunksPerCol;
+          const int kc = chunk - c * Cfg::kChunksPerCol;
+          *reinterpret_cast<u4*>(smem + c * Cfg::kColPitch + kc * 16) = bstage[i];
+        } else {
+          const int j = chunk / Cfg::kChunksPerRow;
+          const int cc = chunk - j * Cfg::kChunksPerRow;
+          *reinterpret_cast<u4*>(smem + btile_offset<BN>(j, cc * 8)) = bstage[i];
+        }
       }
     };
     auto load_a = [&](int64_t s0) {
       const int64_t s = s0 + wk;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
-        const int64_t row = row0 + (wm * TM + tm) * 16 + li;
+        const int64_t rtile = (row0 >> 4) + wm * TM + tm;
+        const int64_t row = rtile * 16 + li;
 #pragma unroll
         for (int t = 0; t < KSUB; ++t) {
-          const int64_t kd = s * KS + 16 * KSUB * q + 16 * t;   // first dense position
+          const int64_t kd = s * KS + 64 * t + 16 * q;   // first dense position of this lane
           h8 v = {};
           uint32_t id = 0;
-          if (s < nsuper && kd < a.Kc && row < a.R) {
-            v = __builtin_bit_cast(h8, __builtin_nontemporal_load(
-                                           reinterpret_cast<const u4*>(vals + row * vals_row + (kd >> 1))));
-            id = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(meta + row * meta_row + (kd >> 3)));
+          if constexpr (ATILED) {
+            // operand-major: block (rtile, kd/64) is 64 lanes x 16 bytes (+ 64 metadata words);
+            // padded rows are stored as zeros, so only the tile and position range matter
+            if (s < nsuper && kd < a.Kc && rtile * 16 < a.R) {
+              const int64_t blk = rtile * KCt + (kd >> 6);
+              v = __builtin_bit_cast(h8, __builtin_nontemporal_load(
+                                             reinterpret_cast<const u4*>(vals + (blk * 64 + lane) * 8)));
+              id = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(meta + (blk * 64 + lane) * 2));
+            }
+          } else {
+            if (s < nsuper && kd < a.Kc && row < a.R) {
+              v = __builtin_bit_cast(h8, __builtin_nontemporal_load(
+                                             reinterpret_cast<const u4*>(vals + row * vals_row + (kd >> 1))));
+              id = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(meta + row * meta_row + (kd >> 3)));
+            }
           }
           afrag[tm][t] = v;
           aidx[tm][t] = id;
@@ -217,21 +259,32 @@ k_spmm(SpmmArgs a) {
         const int xbase = wk * KS;
 #pragma unroll
         for (int t = 0; t < KSUB; ++t) {
-          const int r1 = 16 * KSUB * (q >> 1) + 16 * t + 8 * (q & 1) + (li >> 2);
+          // operand rows: e < 8 -> 64t + 8q + e ; e >= 8 -> 64t + 32 + 8q + e - 8
+          const int r1 = 64 * t + 8 * q + (li >> 2);
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn) {
-            const int c = (wn * TN + tn) * 16 + 4 * (li & 3);
-            const h4 b0 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1, c));
-            const h4 b1 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1 + 4, c));
-            const h4 b2 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1 + 32 * KSUB, c));
-            const h4 b3 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1 + 32 * KSUB + 4, c));
             h16 bf;
+            if constexpr (BCOL) {
+              // [column][k] tile: eight consecutive k of one column are one 16-byte read
+              const int col = (wn * TN + tn) * 16 + li;
+              const int k1 = xbase + r1 - (li >> 2);
+              const h8 lo = *reinterpret_cast<const h8*>(smem + col * Cfg::kColPitch + k1 * 2);
+              const h8 hi = *reinterpret_cast<const h8*>(smem + col * Cfg::kColPitch + (k1 + 32) * 2);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              bf[e] = b0[e];
-              bf[4 + e] = b1[e];
-              bf[8 + e] = b2[e];
-              bf[12 + e] = b3[e];
+              for (int e = 0; e < 8; ++e) { bf[e] = lo[e]; bf[8 + e] = hi[e]; }
+            } else {
+              const int c = (wn * TN + tn) * 16 + 4 * (li & 3);
+              const h4 b0 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1, c));
+              const h4 b1 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1 + 4, c));
+              const h4 b2 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1 + 32, c));
+              const h4 b3 = lds_read_tr16(lds_base + btile_offset<BN>(xbase + r1 + 36, c));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                bf[e] = b0[e];
+                bf[4 + e] = b1[e];
+                bf[8 + e] = b2[e];
+                bf[12 + e] = b3[e];
+              }
             }
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) acc[tm][tn] = smfmac16<0>(acur[tm][t], bf, acc[tm][tn], icur[tm][t]);
@@ -283,15 +336,15 @@ k_spmm(SpmmArgs a) {
 
 // ---- host side: pick a tile shape for the problem and launch ------------------------------
 
-template <int WM, int WN, int WK, int TM, int TN, int KSUB, bool GATHER>
+template <int WM, int WN, int WK, int TM, int TN, int KSUB, bool GATHER, bool BCOL = false, bool ATILED = false>
 static hipError_t launch_cfg(SpmmArgs a, hipStream_t stream) {
-  using Cfg = SpmmCfg<WM, WN, WK, TM, TN, KSUB, GATHER>;
+  using Cfg = SpmmCfg<WM, WN, WK, TM, TN, KSUB, GATHER, BCOL, ATILED>;
   a.n_row_tiles = (a.R + Cfg::BM - 1) / Cfg::BM;
   a.n_col_tiles = (a.C + Cfg::BN - 1) / Cfg::BN;
   const int64_t tiles = a.n_row_tiles * a.n_col_tiles;
   if (tiles == 0 || a.batch == 0) return hipSuccess;
   const unsigned gy = (unsigned)(a.batch < 65535 ? a.batch : 65535);
-  auto kern = k_spmm<WM, WN, WK, TM, TN, KSUB, GATHER>;
+  auto kern = k_spmm<WM, WN, WK, TM, TN, KSUB, GATHER, BCOL, ATILED>;
   static bool attr_set = false;   // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLds);
@@ -303,9 +356,12 @@ static hipError_t launch_cfg(SpmmArgs a, hipStream_t stream) {
 }
 
 hipError_t launch_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
-                          int64_t C, int64_t ldb, void* Y, int64_t ldy, int64_t batch,
+                          int64_t C, int64_t ldb, int b_layout, void* Y, int64_t ldy, int64_t batch,
                           int64_t stride_values, int64_t stride_meta, int64_t stride_B,
                           int64_t stride_Y, hipStream_t stream) {
+  if (C <= 32)   // decode regime: weight streaming, see spmm_skinny.hip
+    return launch_spmm_nm_skinny(values, meta, R, K, B, C, ldb, b_layout, Y, ldy, batch,
+                                 stride_values, stride_meta, stride_B, stride_Y, stream);
   SpmmArgs a{};
   a.values = (const uint16_t*)values;
   a.meta = (const uint8_t*)meta;
@@ -318,10 +374,37 @@ hipError_t launch_spmm_nm(const void* values, const void* meta, int64_t R, int64
   a.stride_B = stride_B; a.stride_Y = stride_Y;
   a.V = 0; a.M = 4;
   a.b_vec = (ldb % 8 == 0) && (((uintptr_t)B & 15) == 0) && (batch <= 1 || stride_B % 8 == 0);
-  if (C <= 16) return launch_cfg<1, 1, 4, 1, 1, 4, false>(a, stream);
-  if (C <= 32) return launch_cfg<1, 1, 4, 1, 2, 4, false>(a, stream);
+  if (b_layout == 1) {
+    if (C <= 64) return launch_cfg<4, 1, 1, 2, 4, 4, false, true>(a, stream);
+    return launch_cfg<2, 2, 1, 2, 4, 2, false, true>(a, stream);
+  }
   if (C <= 64) return launch_cfg<4, 1, 1, 2, 4, 4, false>(a, stream);
   return launch_cfg<2, 2, 1, 2, 4, 2, false>(a, stream);
+}
+
+hipError_t launch_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                                const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
+                                int64_t ldy, hipStream_t stream) {
+  if (C <= 32)
+    return launch_spmm_nm_tiled_skinny(values_t, meta_t, R, K, B, C, ldb, b_layout, Y, ldy, stream);
+  SpmmArgs a{};
+  a.values = (const uint16_t*)values_t;
+  a.meta = (const uint8_t*)meta_t;
+  a.B = (const uint16_t*)B;
+  a.Y = (uint16_t*)Y;
+  a.colloc = nullptr;
+  a.R = R; a.Kc = K; a.K = K; a.C = C; a.ldb = ldb; a.ldy = ldy;
+  a.batch = 1;
+  a.V = 0; a.M = 4;
+  a.b_vec = (ldb % 8 == 0) && (((uintptr_t)B & 15) == 0);
+  // row tiles of a workgroup must be 16-row aligned tiles of the operand-major array: BM
+  // is a multiple of 16, which every configuration satisfies
+  if (b_layout == 1) {
+    if (C <= 64) return launch_cfg<4, 1, 1, 2, 4, 4, false, true, true>(a, stream);
+    return launch_cfg<2, 2, 1, 2, 4, 2, false, true, true>(a, stream);
+  }
+  if (C <= 64) return launch_cfg<4, 1, 1, 2, 4, 4, false, false, true>(a, stream);
+  return launch_cfg<2, 2, 1, 2, 4, 2, false, false, true>(a, stream);
 }
 
 hipError_t launch_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R,

@@ -1,0 +1,357 @@
+// 2:4 SpMM for skinny dense operands (C <= 32 columns): the decode regime, where the
+// product is bound by streaming the compressed weights from HBM ("2:4 sparsity on
+// sparse tensor cores", lecture notes: "Speedup: a staircase toward 2x" -- small GEMMs
+// are bound by memory traffic and fixed costs).
+//
+// Design for MI355X (gfx950), from rocprof timings and counters of earlier variants:
+//   * one workgroup per 16-row tile of A; its NW waves (up to 16) split the reduction
+//     into slices of S = 64*KSUB positions; K is walked in phases of P = NW*S.
+//   * every cache line is requested by exactly one wave: concurrent misses of several
+//     waves to one line are not merged and were measured to multiply HBM traffic (six
+//     times for scattered 2-byte metadata reads). So
+//       - A values: with the canonical layout one load covers 16 rows x 64 contiguous
+//         bytes; with the operand-major layout (snm_spmm_nm_tiled) every operand is one
+//         contiguous 1 KiB block, which streams about a quarter faster;
+//       - canonical metadata is loaded cooperatively (coalesced) into LDS; operand-major
+//         metadata is one contiguous 128-byte block per operand, loaded directly;
+//       - column-major B (decode activations X[C][K] as stored): each lane loads its
+//         operand half (eight consecutive k of one column) directly; the four lanes of
+//         a column together read whole 128-byte lines. Row-major B: the phase's B tile
+//         is loaded cooperatively into LDS as [k][CP] and read with ds_read_b64_tr_b16.
+//   * LDS staging (row-major B, canonical metadata) is requested before A, so the
+//     barrier waits for L2, not for the HBM stream.
+//   * the per-wave fp32 partial sums are added through LDS once; Y is written with
+//     consecutive threads on consecutive columns.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace snm {
+
+struct SkinnyArgs {
+  const uint16_t* values;
+  const uint8_t* meta;
+  const uint16_t* B;
+  uint16_t* Y;
+  int64_t R, Kc, C, ldb, ldy;
+  int64_t batch, stride_values, stride_meta, stride_B, stride_Y;
+  int b_vec;   // B rows (row-major) or B columns (column-major) are 16-byte aligned
+};
+
+template <int CP, int KSUB>
+struct SkinnyCfg {
+  static constexpr int S = 64 * KSUB;                        // positions per wave slice
+  static constexpr int CT = CP / 16;                         // 16-column MFMA tiles
+  // row-major B tile of one phase: NW*S rows x CP columns = NW*S*CP/8 chunks of 16 bytes
+  // over 64*NW threads -> S*CP/512 chunks per thread.
+  static constexpr int kBChunks = S * CP / 512;
+  // canonical metadata tile of one phase: 16 rows x NW*S/16 halfwords over 64*NW threads
+  static constexpr int kMetaHalves = S / 64;
+  static_assert(S * CP * 2 <= 16384, "phase B tile must fit in 160 KiB with 16 waves");
+};
+
+// Row-major [k][CP] tile with 32-byte cells XOR-placed so that one transpose read
+// (rows {0..3, 8..11, 16..19, 24..27} + const) hits each of the 8 cells of a 256-byte
+// line at most twice.
+template <int CP>
+__device__ __forceinline__ uint32_t rm_offset(int x, int c) {
+  const uint32_t inner = (uint32_t)(c & 15) * 2u;
+  if constexpr (CP == 16) {
+    const int L = x >> 3;
+    const int u = (x & 7) ^ ((L & 1) << 2);
+    return (uint32_t)L * 256u + (uint32_t)u * 32u + inner;
+  } else {
+    static_assert(CP == 32, "skinny tiles are 16 or 32 columns wide");
+    const int L = x >> 2;
+    const int u = (((x & 3) << 1) | (c >> 4)) ^ ((L >> 1) & 1);
+    return (uint32_t)L * 256u + (uint32_t)u * 32u + inner;
+  }
+}
+
+// ATILED: A (values, meta) in the operand-major layout; BCOL: B column-major;
+// BVEC: B lines are 16-byte aligned.
+template <int CP, int KSUB, bool ATILED, bool BCOL, bool BVEC>
+__global__ void __launch_bounds__(1024)
+k_spmm_skinny(SkinnyArgs a) {
+  using Cfg = SkinnyCfg<CP, KSUB>;
+  constexpr int S = Cfg::S, CT = Cfg::CT;
+  constexpr bool kStageB = !BCOL;          // row-major B goes through LDS
+  constexpr bool kStageMeta = !ATILED;     // canonical metadata goes through LDS
+  constexpr bool kBarrier = kStageB || kStageMeta;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t lds = lds_addr(smem);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int NW = blockDim.x >> 6;
+  const int nthreads = blockDim.x;
+  const int q = lane >> 4;
+  const int li = lane & 15;
+  const int64_t rt = blockIdx.x;
+  const int64_t row0 = rt * 16;
+  const int P = NW * S;                                     // positions per phase
+  const int nphases = (int)((a.Kc + P - 1) / P);
+  const int64_t KC = (a.Kc + 63) / 64;                      // 64-position operand chunks
+  const int64_t vals_row = a.Kc >> 1;
+  const int64_t meta_row = a.Kc >> 3;
+  const bool row_ok = row0 + li < a.R;
+  // LDS: [B tile (row-major B only) | canonical metadata tile (16 rows, pitch P/8 + 4 B)]
+  const uint32_t btile_bytes = kStageB ? (uint32_t)P * CP * 2u : 0u;
+  const uint32_t mpitch = (uint32_t)P / 8u + 4u;
+  const uint32_t mtile = btile_bytes;
+
+  // Cooperative staging geometry: chunk i of this thread is a fixed base plus a
+  // workgroup-uniform stride (CP/8 and P/16 divide the thread count).
+  const int bline0 = tid / (CP / 8);                        // B row within the phase
+  const int bcol0 = (tid - bline0 * (CP / 8)) * 8;
+  const int bstep = nthreads / (CP / 8);
+  const uint32_t boff0 = rm_offset<CP>(bline0, bcol0);
+  const uint32_t bofs_step = (uint32_t)bstep * CP * 2u;
+  const int mdiv = P / 16;
+  const int mrow0 = tid / mdiv;
+  const int mhw = tid - mrow0 * mdiv;
+  const int mstep = nthreads / mdiv;
+  const uint32_t moff0 = mtile + (uint32_t)mrow0 * mpitch + (uint32_t)mhw * 2u;
+
+  for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
+    const uint16_t* __restrict__ vals = a.values + b * a.stride_values;
+    const uint8_t* __restrict__ meta = a.meta + b * a.stride_meta;
+    const uint16_t* __restrict__ Bm = a.B + b * a.stride_B;
+    uint16_t* __restrict__ Y = a.Y + b * a.stride_Y;
+
+    f4 acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+
+    for (int ph = 0; ph < nphases; ++ph) {
+      const int64_t pbase = (int64_t)ph * P;
+      // ---- cooperative staging requests (L2), issued before the HBM stream ------------
+      u4 bst[kStageB ? Cfg::kBChunks : 1];
+      if constexpr (kStageB) {
+        const int col = bcol0;
+        const uint16_t* src0 = Bm + (pbase + bline0) * a.ldb + col;
+        const int64_t sstep = (int64_t)bstep * a.ldb;
+#pragma unroll
+        for (int i = 0; i < Cfg::kBChunks; ++i) {
+          u4 v = {0u, 0u, 0u, 0u};
+          const uint16_t* src = src0 + i * sstep;
+          if (pbase + bline0 + i * bstep < a.Kc) {
+            if (BVEC && col + 8 <= a.C) {
+              v = *reinterpret_cast<const u4*>(src);
+            } else if (col < a.C) {
+              uint32_t e[8];
+#pragma unroll
+              for (int t = 0; t < 8; ++t) e[t] = (col + t < a.C) ? src[t] : 0u;
+              v[0] = e[0] | (e[1] << 16);
+              v[1] = e[2] | (e[3] << 16);
+              v[2] = e[4] | (e[5] << 16);
+              v[3] = e[6] | (e[7] << 16);
+            }
+          }
+          bst[i] = v;
+        }
+      }
+      uint32_t mst[kStageMeta ? Cfg::kMetaHalves : 1];
+      if constexpr (kStageMeta) {
+        const int64_t k = pbase + mhw * 16;
+        const uint8_t* src0 = meta + (row0 + mrow0) * meta_row + (k >> 3);
+        const int64_t sstep = (int64_t)mstep * meta_row;
+#pragma unroll
+        for (int i = 0; i < Cfg::kMetaHalves; ++i) {
+          uint32_t v = 0;
+          if (row0 + mrow0 + i * mstep < a.R && k < a.Kc) v = *reinterpret_cast<const uint16_t*>(src0 + i * sstep);
+          mst[i] = v;
+        }
+      }
+      // ---- this wave's A operands: operand t of quarter q = positions w*S + 64t + 16q + [0,16)
+      h8 av[KSUB];
+      uint32_t ai[KSUB];
+#pragma unroll
+      for (int t = 0; t < KSUB; ++t) {
+        const int64_t kd = pbase + w * S + 64 * t + 16 * q;
+        h8 v = {};
+        uint32_t id = 0;
+        if constexpr (ATILED) {
+          const int64_t blk = rt * KC + (kd >> 6);   // the tiled arrays are padded: rows and chunks exist
+          if (kd < a.Kc) {
+            v = *reinterpret_cast<const h8*>(vals + blk * 512 + lane * 8);
+            id = *reinterpret_cast<const uint16_t*>(meta + (blk * 64 + lane) * 2);
+          }
+        } else {
+          if (row_ok && kd < a.Kc) v = *reinterpret_cast<const h8*>(vals + (row0 + li) * vals_row + (kd >> 1));
+        }
+        av[t] = v;
+        ai[t] = id;
+      }
+      // ---- column-major B: operand halves straight from memory -------------------------
+      h16 bdir[BCOL ? KSUB : 1][BCOL ? CT : 1];
+      if constexpr (BCOL) {
+#pragma unroll
+        for (int t = 0; t < KSUB; ++t) {
+          const int64_t k1 = pbase + w * S + 64 * t + 8 * q;   // rows k1 + e, k1 + 32 + e - 8
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const int64_t col = 16 * ct + li;
+            const uint16_t* colp = Bm + col * a.ldb;
+            h8 lo = {}, hi = {};
+            // K is a multiple of 16 and k1 of 8: each 8-row half is wholly inside or outside
+            if (col < a.C) {
+              if constexpr (BVEC) {
+                if (k1 < a.Kc) lo = *reinterpret_cast<const h8*>(colp + k1);
+                if (k1 + 32 < a.Kc) hi = *reinterpret_cast<const h8*>(colp + k1 + 32);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                  if (k1 < a.Kc) lo[e] = bits_f16(colp[k1 + e]);
+                  if (k1 + 32 < a.Kc) hi[e] = bits_f16(colp[k1 + 32 + e]);
+                }
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { bdir[t][ct][e] = lo[e]; bdir[t][ct][8 + e] = hi[e]; }
+          }
+        }
+      }
+      // ---- publish staged tiles ----------------------------------------------------------
+      if constexpr (kStageB) {
+#pragma unroll
+        for (int i = 0; i < Cfg::kBChunks; ++i) *reinterpret_cast<u4*>(smem + boff0 + i * bofs_step) = bst[i];
+      }
+      if constexpr (kStageMeta) {
+#pragma unroll
+        for (int i = 0; i < Cfg::kMetaHalves; ++i)
+          *reinterpret_cast<uint16_t*>(smem + moff0 + i * mstep * mpitch) = (uint16_t)mst[i];
+      }
+      if constexpr (kBarrier) __syncthreads();
+      // ---- sparse MFMAs over the slice ---------------------------------------------------
+      const int xs = w * S;
+      const int r1_0 = xs + 8 * q + (li >> 2);
+      const uint32_t tr0 = rm_offset<CP>(r1_0, 4 * (li & 3));
+      const uint32_t tr4 = rm_offset<CP>(r1_0 + 4, 4 * (li & 3));
+      constexpr uint32_t kRow64 = 64u * CP * 2u;       // +64 rows
+      constexpr uint32_t kRow32 = 32u * CP * 2u;       // +32 rows
+      const uint32_t ct_step = CP == 32 ? rm_offset<CP>(r1_0, 16 + 4 * (li & 3)) - tr0 : 0u;
+#pragma unroll
+      for (int t = 0; t < KSUB; ++t) {
+        uint32_t idx = ai[t];
+        if constexpr (kStageMeta)
+          idx = *reinterpret_cast<const uint16_t*>(
+              smem + mtile + (uint32_t)li * mpitch + (uint32_t)((xs + 64 * t + 16 * q) >> 3));
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          h16 bf;
+          if constexpr (BCOL) {
+            bf = bdir[t][ct];
+          } else {
+            // transpose reads: the swizzle turns +64 rows and +32 rows into constant byte
+            // offsets and +4 rows / +16 columns into per-lane constants
+            const uint32_t o0 = lds + tr0 + ct * ct_step + t * kRow64;
+            const uint32_t o4 = lds + tr4 + ct * ct_step + t * kRow64;
+            const h4 b0 = lds_read_tr16(o0);
+            const h4 b1 = lds_read_tr16(o4);
+            const h4 b2 = lds_read_tr16(o0 + kRow32);
+            const h4 b3 = lds_read_tr16(o4 + kRow32);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              bf[e] = b0[e]; bf[4 + e] = b1[e]; bf[8 + e] = b2[e]; bf[12 + e] = b3[e];
+            }
+          }
+          acc[ct] = smfmac16<0>(av[t], bf, acc[ct], idx);
+        }
+      }
+      if constexpr (kBarrier) __syncthreads();
+    }
+
+    // ---- sum the NW partial tiles and store Y ----------------------------------------------
+    f4* red = reinterpret_cast<f4*>(smem);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) red[(w * CT + ct) * 64 + lane] = acc[ct];
+    __syncthreads();
+    for (int e = tid; e < 16 * CP; e += nthreads) {
+      const int r = e / CP;
+      const int c = e - r * CP;
+      const int ct = c >> 4;
+      const int ln = ((r >> 2) << 4) | (c & 15);
+      const float* rp = reinterpret_cast<const float*>(red);
+      float s = 0.f;
+      for (int ww = 0; ww < NW; ++ww) s += rp[((ww * CT + ct) * 64 + ln) * 4 + (r & 3)];
+      const int64_t orow = row0 + r;
+      if (orow < a.R && c < a.C) Y[orow * a.ldy + c] = f16_bits(to_f16(s));
+    }
+    __syncthreads();
+  }
+}
+
+template <int CP, int KSUB, bool ATILED, bool BCOL, bool BVEC>
+static hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
+  using Cfg = SkinnyCfg<CP, KSUB>;
+  const int64_t nslices = (a.Kc + Cfg::S - 1) / Cfg::S;
+  int nw = (int)(nslices < 16 ? nslices : 16);
+  if (nw < 1) nw = 1;
+  const size_t P = (size_t)nw * Cfg::S;
+  const size_t btile = BCOL ? 0 : P * CP * 2;
+  const size_t mtile = ATILED ? 0 : 16 * (P / 8 + 4);
+  const size_t red = (size_t)nw * Cfg::CT * 64 * 16;
+  const size_t lds = btile + mtile > red ? btile + mtile : red;
+  auto kern = k_spmm_skinny<CP, KSUB, ATILED, BCOL, BVEC>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const unsigned gx = (unsigned)((a.R + 15) / 16);
+  const unsigned gy = (unsigned)(a.batch < 65535 ? a.batch : 65535);
+  hipLaunchKernelGGL(kern, dim3(gx, gy), dim3(64 * nw), lds, stream, a);
+  return hipGetLastError();
+}
+
+// CP = 16: phases of up to 4096 positions (S = 256); CP = 32: up to 2048 (S = 128).
+template <bool ATILED>
+static hipError_t dispatch_skinny(const SkinnyArgs& a, int b_layout, hipStream_t stream) {
+  const bool narrow = a.C <= 16;
+  if (b_layout == 1) {
+    if (a.b_vec)
+      return narrow ? launch_skinny<16, 4, ATILED, true, true>(a, stream) : launch_skinny<32, 2, ATILED, true, true>(a, stream);
+    return narrow ? launch_skinny<16, 4, ATILED, true, false>(a, stream) : launch_skinny<32, 2, ATILED, true, false>(a, stream);
+  }
+  if (a.b_vec)
+    return narrow ? launch_skinny<16, 4, ATILED, false, true>(a, stream) : launch_skinny<32, 2, ATILED, false, true>(a, stream);
+  return narrow ? launch_skinny<16, 4, ATILED, false, false>(a, stream) : launch_skinny<32, 2, ATILED, false, false>(a, stream);
+}
+
+static SkinnyArgs skinny_args(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
+                              int64_t C, int64_t ldb, void* Y, int64_t ldy, int64_t batch,
+                              int64_t stride_values, int64_t stride_meta, int64_t stride_B,
+                              int64_t stride_Y) {
+  SkinnyArgs a{};
+  a.values = (const uint16_t*)values;
+  a.meta = (const uint8_t*)meta;
+  a.B = (const uint16_t*)B;
+  a.Y = (uint16_t*)Y;
+  a.R = R; a.Kc = K; a.C = C; a.ldb = ldb; a.ldy = ldy;
+  a.batch = batch;
+  a.stride_values = stride_values; a.stride_meta = stride_meta;
+  a.stride_B = stride_B; a.stride_Y = stride_Y;
+  a.b_vec = (ldb % 8 == 0) && (((uintptr_t)B & 15) == 0) && (batch <= 1 || stride_B % 8 == 0);
+  return a;
+}
+
+hipError_t launch_spmm_nm_skinny(const void* values, const void* meta, int64_t R, int64_t K,
+                                 const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
+                                 int64_t ldy, int64_t batch, int64_t stride_values,
+                                 int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
+                                 hipStream_t stream) {
+  const SkinnyArgs a = skinny_args(values, meta, R, K, B, C, ldb, Y, ldy, batch, stride_values,
+                                   stride_meta, stride_B, stride_Y);
+  return dispatch_skinny<false>(a, b_layout, stream);
+}
+
+hipError_t launch_spmm_nm_tiled_skinny(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                                       const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
+                                       int64_t ldy, hipStream_t stream) {
+  const SkinnyArgs a = skinny_args(values_t, meta_t, R, K, B, C, ldb, Y, ldy, 1, 0, 0, 0, 0);
+  return dispatch_skinny<true>(a, b_layout, stream);
+}
+
+}  // namespace snm

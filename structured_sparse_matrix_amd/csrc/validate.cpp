@@ -56,16 +56,20 @@ int check_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int
 }
 
 int check_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
-                  int64_t C, int64_t ldb, const void* Y, int64_t ldy, int64_t batch,
+                  int64_t C, int64_t ldb, int b_layout, const void* Y, int64_t ldy, int64_t batch,
                   int64_t stride_values, int64_t stride_meta, int64_t stride_B, int64_t stride_Y) {
   int s = check_nm_sizes(R, K);
   if (s != SNM_OK) return s;
+  if (b_layout != 0 && b_layout != 1) return SNM_E_UNSUPPORTED;
   if (C < 0 || batch < 0 || !fits(K, C) || !fits(R, C)) return SNM_E_SHAPE;
   if (R == 0 || C == 0 || batch == 0) return SNM_OK;
   if (!Y || (K > 0 && (!values || !meta || !B))) return SNM_E_NULL;
-  if (ldy < C || ldb < C || !fits(K, ldb) || !fits(R, ldy)) return SNM_E_SHAPE;
+  // row-major B: K rows of ldb >= C; column-major B: C columns of ldb >= K
+  const int64_t b_lines = b_layout == 0 ? K : C;
+  const int64_t b_min_ld = b_layout == 0 ? C : K;
+  if (ldy < C || ldb < b_min_ld || !fits(b_lines, ldb) || !fits(R, ldy)) return SNM_E_SHAPE;
   if (batch > 1) {
-    if (stride_values < R * (K / 2) || stride_meta < R * (K / 8) || stride_B < K * ldb ||
+    if (stride_values < R * (K / 2) || stride_meta < R * (K / 8) || stride_B < b_lines * ldb ||
         stride_Y < R * ldy || !fits(batch, stride_values) || !fits(batch, stride_B) ||
         !fits(batch, stride_Y) || !fits(batch, stride_meta))
       return SNM_E_SHAPE;

@@ -13,7 +13,7 @@ int check_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda, cons
 int check_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
                            const void* values, const void* midx, const void* colloc);
 int check_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
-                  int64_t C, int64_t ldb, const void* Y, int64_t ldy, int64_t batch,
+                  int64_t C, int64_t ldb, int b_layout, const void* Y, int64_t ldy, int64_t batch,
                   int64_t stride_values, int64_t stride_meta, int64_t stride_B, int64_t stride_Y);
 int check_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R, int64_t K,
                    int V, int M, const void* B, int64_t C, int64_t ldb, const void* Y, int64_t ldy);

@@ -105,13 +105,15 @@ def test_prune_encode_vnm_validation(args, status):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((FAKE, FAKE, 16, 24, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 2),      # K % 16
-    ((FAKE, FAKE, 16, 32, FAKE, 8, 4, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 2),      # ldb < C
-    ((FAKE, FAKE, 16, 32, FAKE, 8, 8, P(0x1001), 12, 1, 0, 0, 0, 0, P(0)), 3),  # odd Y pointer
-    ((FAKE, P(0), 16, 32, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 1),      # meta NULL
-    ((FAKE, FAKE, 16, 32, FAKE, 8, 8, FAKE, 8, 2, 8, 64, 256, 128, P(0)), 2),  # stride_values too small
-    ((FAKE, FAKE, 16, 32, FAKE, 8, 8, FAKE, 8, -1, 0, 0, 0, 0, P(0)), 2),     # negative batch
-    ((P(0), P(0), 16, 32, P(0), 0, 0, P(0), 0, 1, 0, 0, 0, 0, P(0)), 0),      # C == 0: ok
+    ((FAKE, FAKE, 16, 24, FAKE, 8, 8, 0, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 2),      # K % 16
+    ((FAKE, FAKE, 16, 32, FAKE, 8, 4, 0, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 2),      # ldb < C
+    ((FAKE, FAKE, 16, 32, FAKE, 8, 16, 1, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 2),     # column-major: ldb < K
+    ((FAKE, FAKE, 16, 32, FAKE, 8, 8, 2, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 4),      # unknown layout
+    ((FAKE, FAKE, 16, 32, FAKE, 8, 8, 0, P(0x1001), 12, 1, 0, 0, 0, 0, P(0)), 3),  # odd Y pointer
+    ((FAKE, P(0), 16, 32, FAKE, 8, 8, 0, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 1),      # meta NULL
+    ((FAKE, FAKE, 16, 32, FAKE, 8, 8, 0, FAKE, 8, 2, 8, 64, 256, 128, P(0)), 2),  # stride_values too small
+    ((FAKE, FAKE, 16, 32, FAKE, 8, 8, 0, FAKE, 8, -1, 0, 0, 0, 0, P(0)), 2),     # negative batch
+    ((P(0), P(0), 16, 32, P(0), 0, 0, 0, P(0), 0, 1, 0, 0, 0, 0, P(0)), 0),      # C == 0: ok
 ])
 def test_spmm_nm_validation(args, status):
     assert _lib().snm_spmm_nm(*args) == status

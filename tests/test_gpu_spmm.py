@@ -33,6 +33,37 @@ def test_spmm_nm_shapes(R, K, C):
     assert_fp16_close(to_host(Y), oracle.spmm_nm(ov, om, B), f"{R}x{K}x{C}")
 
 
+@pytest.mark.parametrize("R,K,C", [
+    (16, 64, 16), (1, 16, 1), (5, 48, 3), (100, 256, 8), (33, 272, 17), (64, 512, 32),
+    (130, 1040, 40), (200, 320, 100), (64, 2048, 260), (300, 4096, 24),
+])
+def test_spmm_nm_column_major_b(R, K, C):
+    # B given as the transpose of a contiguous C x K activation matrix
+    snm = _snm()
+    ov, om, B = _nm_case(R, K, C, R * 17 + K + C)
+    Bcm = to_dev(np.ascontiguousarray(B.T)).t()
+    assert Bcm.stride(0) == 1
+    Y = snm.spmm_nm(to_dev(ov), to_dev(om), Bcm)
+    assert_fp16_close(to_host(Y), oracle.spmm_nm(ov, om, B), f"col-major {R}x{K}x{C}")
+
+
+@pytest.mark.parametrize("C", [8, 32, 72])
+def test_spmm_nm_column_major_padded_ld(C):
+    snm = _snm()
+    import torch
+    R, K = 48, 512
+    ov, om, B = _nm_case(R, K, C, 500 + C)
+    X = torch.zeros((C, K + 24), dtype=torch.float16, device="cuda")
+    X[:, :K] = to_dev(np.ascontiguousarray(B.T))
+    Y = snm.spmm_nm(to_dev(ov), to_dev(om), X[:, :K].t())
+    assert_fp16_close(to_host(Y), oracle.spmm_nm(ov, om, B), f"col-major ld {K + 24}")
+    # odd leading dimension: unaligned columns take the scalar path
+    X2 = torch.zeros((C, K + 3), dtype=torch.float16, device="cuda")
+    X2[:, :K] = to_dev(np.ascontiguousarray(B.T))
+    Y2 = snm.spmm_nm(to_dev(ov), to_dev(om), X2[:, :K].t())
+    assert_fp16_close(to_host(Y2), oracle.spmm_nm(ov, om, B), f"col-major ld {K + 3}")
+
+
 def test_spmm_nm_identity_is_exact_decode():
     snm = _snm()
     A = workloads.small_matrix(21, (48, 128))
@@ -41,6 +72,17 @@ def test_spmm_nm_identity_is_exact_decode():
     dense = oracle.decode_nm(ov, om, 128)
     got = to_host(Y)
     assert np.array_equal(got.astype(np.float64), dense.astype(np.float64))
+
+
+def test_spmm_nm_batched_column_major():
+    snm = _snm()
+    nb, R, K, C = 4, 64, 1024, 16
+    cases = [_nm_case(R, K, C, 900 + i) for i in range(nb)]
+    X = np.stack([np.ascontiguousarray(c[2].T) for c in cases])            # [b, C, K]
+    Y = snm.spmm_nm(to_dev(np.stack([c[0] for c in cases])), to_dev(np.stack([c[1] for c in cases])),
+                    to_dev(X).transpose(1, 2))
+    ref = np.stack([oracle.spmm_nm(*c) for c in cases])
+    assert_fp16_close(to_host(Y), ref, "batched column-major")
 
 
 def test_spmm_nm_batched_and_strided():
@@ -79,8 +121,11 @@ def test_spmm_nm_workload_decode_full():
     ov, om = oracle.prune_encode_nm(A)
     assert_bits_equal(to_host(v), ov, "decode values")
     for B in Bs:
+        ref = oracle.spmm_nm(ov, om, B)
         Y = snm.spmm_nm(v, m, to_dev(B))
-        assert_fp16_close(to_host(Y), oracle.spmm_nm(ov, om, B), f"decode N={B.shape[1]}")
+        assert_fp16_close(to_host(Y), ref, f"decode N={B.shape[1]}")
+        Ycm = snm.spmm_nm(v, m, to_dev(np.ascontiguousarray(B.T)).t())   # activations X[N][K]
+        assert_fp16_close(to_host(Ycm), ref, f"decode N={B.shape[1]} column-major B")
 
 
 def _vnm_case(R, K, C, V, M, seed):
