@@ -46,7 +46,6 @@ struct SkinnyCfg {
   static constexpr int kBChunks = S * CP / 512;
   // canonical metadata tile of one phase: 16 rows x NW*S/16 halfwords over 64*NW threads
   static constexpr int kMetaHalves = S / 64;
-  static_assert(S * CP * 2 <= 16384, "phase B tile must fit in 160 KiB with 16 waves");
 };
 
 // Row-major [k][CP] tile with 32-byte cells XOR-placed so that one transpose read
@@ -77,6 +76,7 @@ k_spmm_skinny(SkinnyArgs a) {
   constexpr bool kStageB = !BCOL;          // row-major B goes through LDS
   constexpr bool kStageMeta = !ATILED;     // canonical metadata goes through LDS
   constexpr bool kBarrier = kStageB || kStageMeta;
+  static_assert(!kStageB || S * CP * 2 <= 16384, "phase B tile must fit in 160 KiB with 16 waves");
   extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t lds = lds_addr(smem);
   const int tid = threadIdx.x;
@@ -306,14 +306,15 @@ static hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// CP = 16: phases of up to 4096 positions (S = 256); CP = 32: up to 2048 (S = 128).
+// Phases of up to 4096 positions (S = 256); row-major B with 32 columns uses phases of
+// 2048 (S = 128) so that its LDS tile fits.
 template <bool ATILED>
 static hipError_t dispatch_skinny(const SkinnyArgs& a, int b_layout, hipStream_t stream) {
   const bool narrow = a.C <= 16;
   if (b_layout == 1) {
     if (a.b_vec)
-      return narrow ? launch_skinny<16, 4, ATILED, true, true>(a, stream) : launch_skinny<32, 2, ATILED, true, true>(a, stream);
-    return narrow ? launch_skinny<16, 4, ATILED, true, false>(a, stream) : launch_skinny<32, 2, ATILED, true, false>(a, stream);
+      return narrow ? launch_skinny<16, 4, ATILED, true, true>(a, stream) : launch_skinny<32, 4, ATILED, true, true>(a, stream);
+    return narrow ? launch_skinny<16, 4, ATILED, true, false>(a, stream) : launch_skinny<32, 4, ATILED, true, false>(a, stream);
   }
   if (a.b_vec)
     return narrow ? launch_skinny<16, 4, ATILED, false, true>(a, stream) : launch_skinny<32, 2, ATILED, false, true>(a, stream);

@@ -1,0 +1,113 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+  python -m structured_sparse_matrix_amd.profiling kernels TRACE_CSV [--match snm] [--skip N]
+      Markdown table of kernel dispatch durations (calls, mean, median, min, max) from a
+      `rocprofv3 --kernel-trace -f csv` run.
+
+  python -m structured_sparse_matrix_amd.profiling traffic --fetch FETCH_CSV --write WRITE_CSV
+         --match NAME --calibration-bytes N [--command CMD]
+      HBM traffic per launch of the kernels whose name contains NAME, from two
+      `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of the same program. Each
+      counter is scaled by what it reads for the largest plain copy kernel (N bytes read
+      and N bytes written) dispatched before the first matching kernel. Prints JSON with
+      the kernel-source hash that bench.py compares against.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+DECODE_KERNEL_SOURCES = ("spmm_skinny.hip", "device_common.hpp")
+
+
+def kernel_source_hash(files=DECODE_KERNEL_SOURCES) -> str:
+    """Hash of the kernel sources a counter summary was taken on."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _durations(path, match, skip):
+    by = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        if match and match not in name:
+            continue
+        by.setdefault(name, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return {k: v[skip:] if len(v) > skip else v for k, v in by.items()}
+
+
+def kernels_table(path, match, skip):
+    rows = ["| kernel | calls | mean us | median us | min us | max us |", "|---|---|---|---|---|---|"]
+    for name, ds in sorted(_durations(path, match, skip).items(), key=lambda kv: -sum(kv[1])):
+        short = name if len(name) < 110 else name[:107] + "..."
+        rows.append(f"| `{short}` | {len(ds)} | {statistics.mean(ds) / 1e3:.2f} | "
+                    f"{statistics.median(ds) / 1e3:.2f} | {min(ds) / 1e3:.2f} | {max(ds) / 1e3:.2f} |")
+    return "\n".join(rows)
+
+
+def _counter_rows(path, counter):
+    out = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0))
+    out.sort()
+    return out
+
+
+def traffic(fetch_csv, write_csv, match, calibration_bytes):
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+    first = next(i for i, (_, n, _) in enumerate(fetch) if match in n)
+    calib_f = max((b, n) for _, n, b in fetch[:first] if "snm" not in n)
+    firstw = next(i for i, (_, n, _) in enumerate(write) if match in n)
+    calib_w = max((b, n) for _, n, b in write[:firstw] if "snm" not in n)
+    ff = calib_f[0] / calibration_bytes
+    fw = calib_w[0] / calibration_bytes
+    kf = [b / ff for _, n, b in fetch if match in n]
+    kw = [b / fw for _, n, b in write if match in n]
+    n = min(len(kf), len(kw))
+    per = [kf[i] + kw[i] for i in range(n)]
+    return {
+        "kernel_match": match,
+        "launches": n,
+        "fetch_bytes_per_launch_avg": statistics.mean(kf[:n]),
+        "write_bytes_per_launch_avg": statistics.mean(kw[:n]),
+        "bytes_per_launch_avg": statistics.mean(per),
+        "calibration": {"bytes": calibration_bytes, "fetch_factor": ff, "write_factor": fw,
+                        "fetch_kernel": calib_f[1][:80], "write_kernel": calib_w[1][:80]},
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    k = sub.add_parser("kernels")
+    k.add_argument("trace")
+    k.add_argument("--match", default="")
+    k.add_argument("--skip", type=int, default=0)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--match", required=True)
+    t.add_argument("--calibration-bytes", type=int, required=True)
+    t.add_argument("--command", default="")
+    a = ap.parse_args(argv)
+    if a.cmd == "kernels":
+        print(kernels_table(a.trace, a.match, a.skip))
+    else:
+        out = traffic(a.fetch, a.write, a.match, a.calibration_bytes)
+        out["kernel_source_hash"] = kernel_source_hash()
+        out["command"] = a.command
+        print(json.dumps(out, indent=1))
+
+
+if __name__ == "__main__":
+    main()
