@@ -185,6 +185,73 @@ def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_c
     return total_ms, wall, enc_ms, spmm_ms
 
 
+def bench_other(workload: str, steps: int, warmup: int) -> dict:
+    """Per-kernel timings of the other workloads (not the headline line): each kernel is
+    timed over K back-to-back launches with one HIP event pair."""
+    import numpy as np
+    import torch
+    import structured_sparse_matrix_amd as snm
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS[workload]
+    nrot = 4
+
+    def timed(launch):
+        for i in range(warmup):
+            launch(i % nrot)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            launch(i % nrot)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps * 1e-3   # seconds per launch
+
+    out = {"workload": workload, "kernels": {}}
+    if w.kind == "vnm":
+        A, (B,) = workloads.weight_and_activations(w)
+        Ad = [torch.from_numpy(A).to(dev) for _ in range(nrot)]
+        Bd = [torch.from_numpy(B).to(dev) for _ in range(nrot)]
+        enc = [snm.prune_encode_vnm(a, w.V, w.M) for a in Ad]
+        Ys = [torch.empty((w.R, B.shape[1]), dtype=torch.float16, device=dev) for _ in range(nrot)]
+        t_enc = timed(lambda j: snm.prune_encode_vnm(Ad[j], w.V, w.M))
+        t_mm = timed(lambda j: snm.spmm_vnm(*enc[j], Bd[j], w.V, w.M, out=Ys[j]))
+        C = B.shape[1]
+        Kp = 4 * (w.K // w.M)
+        bytes_mm = w.R * (2 * w.K // w.M) * 2 + w.R * (w.K // w.M) // 2 + (w.R // w.V) * (w.K // w.M) * 4 \
+            + w.K * C * 2 + w.R * C * 2
+        bytes_enc = w.R * w.K * 2 + w.R * (2 * w.K // w.M) * 2 + w.R * (w.K // w.M) // 2 + (w.R // w.V) * (w.K // w.M) * 4
+        out["kernels"]["prune_encode_vnm"] = {"avg_us": t_enc * 1e6, "GB/s": bytes_enc / t_enc / 1e9}
+        out["kernels"]["spmm_vnm"] = {
+            "avg_us": t_mm * 1e6, "GB/s": bytes_mm / t_mm / 1e9,
+            "dense_equiv_TFLOP/s": 2 * w.R * w.K * C / t_mm / 1e12,
+            "smfmac_TFLOP/s": 2 * w.R * Kp * C / t_mm / 1e12,
+            "sparse_mfma_frac": 2 * w.R * Kp * C / t_mm / 1e12 / 5000.0,
+            "hbm_frac": bytes_mm / t_mm / 1e9 / HBM_PEAK_GBS}
+    elif w.kind == "attention":
+        Q, Km, V = workloads.attention_qkv(w)
+        Qd, Kd, Vd = (torch.from_numpy(x).to(dev) for x in (Q, Km, V))
+        nb, L, d = Q.shape
+        vals, meta = snm.sddmm_prune_nm(Qd, Kd, 1.0 / np.sqrt(d))
+        O = torch.empty((nb, L, d), dtype=torch.float16, device=dev)
+        nrot = 1
+        t_sd = timed(lambda j: snm.sddmm_prune_nm(Qd, Kd, 1.0 / np.sqrt(d)))
+        t_sm = timed(lambda j: snm.softmax_nm_rows(vals))
+        t_pv = timed(lambda j: snm.spmm_nm(vals, meta, Vd, out=O))
+        vbytes = nb * L * (L // 2) * 2
+        mbytes = nb * L * (L // 8)
+        out["kernels"]["sddmm_prune_nm"] = {"avg_us": t_sd * 1e6, "GB/s": (vbytes + mbytes + 2 * nb * L * d * 2) / t_sd / 1e9,
+                                            "dense_TFLOP/s": 2 * nb * L * L * d / t_sd / 1e12}
+        out["kernels"]["softmax_nm_rows"] = {"avg_us": t_sm * 1e6, "GB/s": 2 * vbytes / t_sm / 1e9}
+        out["kernels"]["spmm_nm_PV"] = {"avg_us": t_pv * 1e6, "GB/s": (vbytes + mbytes + 2 * nb * L * d * 2) / t_pv / 1e9,
+                                        "smfmac_TFLOP/s": 2 * nb * L * L * d / t_pv / 1e12}
+        out["attention_total_us"] = (t_sd + t_sm + t_pv) * 1e6
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,7 +265,13 @@ def main():
                     help="compressed A in the operand-major layout (default) or the canonical one")
     ap.add_argument("--calibration-copy", action="store_true",
                     help=f"copy {CALIBRATION_BYTES >> 20} MiB once before timing (counter calibration)")
+    ap.add_argument("--workload", default="nm_decode",
+                    help="nm_decode (the headline line) or vnm_64_2_8 / vnm_128_2_16 / attention_2_4 "
+                         "(per-kernel timings only)")
     args = ap.parse_args()
+    if args.workload != "nm_decode":
+        print(json.dumps(bench_other(args.workload, args.steps, args.warmup)))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
