@@ -31,6 +31,15 @@ hipError_t launch_spmm_nm_skinny(const void* values, const void* meta, int64_t R
 hipError_t launch_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R,
                            int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
                            int64_t ldy, hipStream_t stream);
+// Wide-output SpMM (spmm_wide.hip): row-major B, C > 32. V > 0 selects V:2:M with
+// column-loc gathering (Kc = 4K/M); V == 0 is plain 2:4 (Kc = K), optionally batched.
+bool spmm_wide_eligible(int64_t R, int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb,
+                        int64_t batch, int64_t stride_B);
+hipError_t launch_spmm_wide(const void* values, const void* meta, const void* colloc, int64_t R,
+                            int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb,
+                            void* Y, int64_t ldy, int64_t batch, int64_t stride_values,
+                            int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
+                            hipStream_t stream);
 hipError_t launch_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
                                  int64_t Lk, int64_t d, float scale, void* values, void* meta,
                                  void* S_dense, hipStream_t stream);

@@ -362,6 +362,9 @@ hipError_t launch_spmm_nm(const void* values, const void* meta, int64_t R, int64
   if (C <= 32)   // decode regime: weight streaming, see spmm_skinny.hip
     return launch_spmm_nm_skinny(values, meta, R, K, B, C, ldb, b_layout, Y, ldy, batch,
                                  stride_values, stride_meta, stride_B, stride_Y, stream);
+  if (b_layout == 0 && spmm_wide_eligible(R, K, 0, 4, B, C, ldb, batch, stride_B))
+    return launch_spmm_wide(values, meta, nullptr, R, K, 0, 4, B, C, ldb, Y, ldy, batch,
+                            stride_values, stride_meta, stride_B, stride_Y, stream);
   SpmmArgs a{};
   a.values = (const uint16_t*)values;
   a.meta = (const uint8_t*)meta;
@@ -410,6 +413,9 @@ hipError_t launch_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_
 hipError_t launch_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R,
                            int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
                            int64_t ldy, hipStream_t stream) {
+  if (spmm_wide_eligible(R, 4 * (K / M), V, M, B, C, ldb, 1, 0))
+    return launch_spmm_wide(values, midx, colloc, R, 4 * (K / M), V, M, B, C, ldb, Y, ldy, 1, 0, 0,
+                            0, 0, stream);
   SpmmArgs a{};
   a.values = (const uint16_t*)values;
   a.meta = (const uint8_t*)midx;

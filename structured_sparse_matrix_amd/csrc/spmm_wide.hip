@@ -1,0 +1,447 @@
+// Structured-sparse x dense products with wide outputs (C > 32): the compute-heavy regime
+// of V:2:M ("VENOM ...", SC'23, Sec. 4 and Fig. 4: per block of V rows, the K/M*4 rows
+// of B named by column-loc are gathered and the product becomes 2:4 over K' = 4K/M) and of
+// 2:4 with many columns ("2:4 sparsity on sparse tensor cores", lecture notes: "How the
+// tensor core uses it"), including the batched P.V product of dynamic 2:4 attention.
+//
+// Design for MI355X (gfx950), from measurements on the device:
+//   * math: v_smfmac_f32_32x32x32_f16 -- the 32x32 form sustains about 5% more than the
+//     16x16x64 form and needs half the operand bytes per flop.
+//   * reuse: a gathered B row is shared only by the V rows of its V-block, so the L2->CU
+//     stream of B is 1/BM bytes per flop whatever else is done; the workgroup tile is
+//     therefore as tall as the V-block allows (BM = 128 or 64) and as wide as the register
+//     file allows (BN up to 256, 128 fp32 accumulators per lane).
+//   * feeding: an LDS ring of NST stages is filled by the global->LDS DMA path
+//     (global_load_lds_dwordx4 and the 2-byte form) NST-1 stages ahead, with no register
+//     staging; each wave waits only for its own DMA of the stage about to be read
+//     (s_waitcnt vmcnt) and one barrier per stage publishes it and frees the oldest slot.
+//   * every LDS destination of a DMA instruction is 64 consecutive lanes x 16 bytes, so
+//     the B tile's bank swizzle is applied on the source side (wide_layout.hpp), the A
+//     operand blocks are stored exactly in the instruction's lane order and read with one
+//     ds_read_b128, and B operands are read with ds_read_b64_tr_b16.
+//   * workgroups are spread over the 8 XCDs round-robin by the hardware; tiles are
+//     renumbered so that the workgroups resident on one XCD share a column strip of B
+//     (V:2:M: all V-blocks of one strip) and hit in that XCD's L2.
+//   * ragged edges: DMA sources are clamped into the operands (rows >= R, columns >= C
+//     and positions >= K' read valid memory whose products are never stored or are
+//     multiplied by zeroed operands), so no lane ever skips a DMA and every wave's
+//     vmcnt bookkeeping stays exact.
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "wide_layout.hpp"
+
+#include <type_traits>
+
+namespace snm {
+namespace {
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+struct WideArgs {
+  const uint16_t* values;   // fp16 bits, R x Kc/2 per batch entry
+  const uint8_t* meta;      // R x Kc/8 bytes per batch entry
+  const uint16_t* B;        // fp16 bits, row-major, ldb (a multiple of 8)
+  uint16_t* Y;              // fp16 bits, R x C (ldy)
+  const uint8_t* colloc;    // V:2:M: (R/V) x Kc bytes (Kc/4 groups x 4 column indices)
+  int64_t R, Kc, C, ldb, ldy;
+  int64_t stride_values, stride_meta, stride_B, stride_Y, batch;
+  int64_t n_row_tiles, n_tiles;   // tiles per batch entry = n_row_tiles * column tiles
+  int V, M;
+  int xcd_remap;                  // total workgroups are a multiple of 8
+};
+
+template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER>
+struct WideCfg {
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int BM = 32 * TM * WM;
+  static constexpr int BN = 32 * TN * WN;
+  static constexpr int KS = 32 * KSTEPS;            // compressed positions per stage
+  static constexpr int kBBytes = KS * BN * 2;
+  static constexpr int kBlocks = (BM / 32) * KSTEPS; // A blocks (1 KiB) = metadata blocks (256 B)
+  static constexpr int kAOff = kBBytes;
+  static constexpr int kMOff = kBBytes + kBlocks * 1024;
+  static constexpr int kStage = kMOff + kBlocks * 256;
+  static constexpr int kRing = NST * kStage;
+  static constexpr int nB = kBBytes / 1024 / kWaves;   // DMA instructions per wave per stage
+  static constexpr int nA = kBlocks / kWaves;
+  static constexpr int kDma = nB + 2 * nA;
+  static_assert(kBBytes % (1024 * kWaves) == 0, "B stage must split into whole DMA rows per wave");
+  static_assert(kBlocks % kWaves == 0, "A blocks must split evenly over the waves");
+  static_assert(NST >= 2, "the ring needs a stage in flight");
+  static_assert(kDma * (NST - 2) < 64, "vmcnt holds at most 63 outstanding operations");
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// All LDS reads of this wave are complete, then the workgroup barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Global -> LDS DMA of 16 bytes (or 2 bytes, zero-extended to a dword) per lane: lane l
+// writes LDS bytes [lds_byte + 16 l, +16) (or [lds_byte + 4 l, +4)); lds_byte is
+// wave-uniform and goes through M0. dma_s addresses a wave-uniform base (SGPR pair) plus a
+// per-lane 32-bit byte offset, dma_v a per-lane 64-bit address. Issued from inline assembly
+// on purpose: the compiler's waitcnt pass would otherwise make every later LDS read it
+// cannot disambiguate (the transpose reads) wait for all DMA in flight, i.e. drain the
+// prefetch ring each stage. Completion is tracked by hand with s_waitcnt vmcnt before the
+// barrier that publishes a stage. No "memory" clobber: a DMA writes a ring slot no wave is
+// reading, and the waits and barriers that order it are memory-clobbering statements.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is set inside the statement
+template <int SIZE>
+__device__ __forceinline__ void dma_s(const void* sbase, uint32_t voff, uint32_t lds_byte) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0) : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff), "s"(sbase), "s"(m0) : "m0");
+}
+template <int SIZE>
+__device__ __forceinline__ void dma_v(const void* src, uint32_t lds_byte) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(src), "s"(m0) : "m0");
+}
+#pragma clang diagnostic pop
+
+// ds_read_b64_tr_b16 (lane layout as lds_read_tr16) addressed from the dynamic LDS array
+// itself, so that constant parts of the offset fold into the instruction.
+__device__ __forceinline__ h4 tr16_at(uint8_t* smem, uint32_t byte_off) {
+  typedef __fp16 fp4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+  typedef __attribute__((address_space(3))) fp4 lds_fp4;
+  lds_fp4* p = (lds_fp4*)((lds_u8*)smem + byte_off);
+  return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(p));
+}
+
+__device__ __forceinline__ f16v smfmac32(const h8& a, const h16& b, const f16v& c, uint32_t idx) {
+  return __builtin_amdgcn_smfmac_f32_32x32x32_f16(a, b, c, (int)idx, 0, 0);
+}
+
+template <int I>
+using cint = std::integral_constant<int, I>;
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(cint<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Two workgroups per CU (two waves per SIMD): one workgroup's barrier and LDS latency hide
+// behind the other's matrix-core work; this caps a lane at 256 registers.
+//
+// Per step (32 positions) a wave issues TM*TN sparse-MFMAs and almost no other vector
+// work: DMA sources are a per-stage scalar base plus per-lane offsets fixed at start-up
+// (only a gathered B row needs one multiply-add), the stage loop is unrolled by the ring
+// depth so every LDS read is a lane-constant register plus an immediate, and all clamping
+// of ragged edges is confined to the last, partial stage.
+template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER>
+__global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
+k_spmm_wide(WideArgs a) {
+  using Cfg = WideCfg<WM, WN, TM, TN, KSTEPS, NST, GATHER>;
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, KS = Cfg::KS;
+  constexpr int nB = Cfg::nB, nA = Cfg::nA;
+  constexpr int kRowsPerDma = 1024 / (2 * BN);   // B tile rows one DMA instruction fills
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t lds0 = lds_addr(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wn = wave % WN;
+  const int wm = wave / WN;
+
+  // ---- tile of this workgroup (XCD-aware numbering) ------------------------------------
+  int64_t L = blockIdx.x;
+  if (a.xcd_remap) L = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int64_t bt = L / a.n_tiles;
+  const int64_t rem = L - bt * a.n_tiles;
+  const int64_t ct = rem / a.n_row_tiles;
+  const int64_t rt = rem - ct * a.n_row_tiles;
+  const int64_t row0 = rt * BM;
+  const int64_t col0 = ct * BN;
+
+  const uint8_t* __restrict__ vals = reinterpret_cast<const uint8_t*>(a.values + bt * a.stride_values);
+  const uint8_t* __restrict__ meta = a.meta + bt * a.stride_meta;
+  const uint16_t* __restrict__ Bm = a.B + bt * a.stride_B;
+  uint16_t* __restrict__ Y = a.Y + bt * a.stride_Y;
+  const int64_t Kc = a.Kc;
+  const int64_t nst = (Kc + KS - 1) / KS;
+  const int64_t nfull = Kc / KS;   // stages whose sources need no clamping
+  const int64_t mrow = Kc >> 3;    // metadata bytes per row; a values row is Kc bytes
+  const int64_t ldb2 = a.ldb * 2;
+
+  if constexpr (GATHER) {   // this V-block's column-loc bytes after the ring, zero-padded
+    const uint8_t* cl = a.colloc + (row0 / a.V) * Kc;
+    for (int64_t i = (int64_t)tid * 16; i < Kc + 2 * KS; i += Cfg::kThreads * 16)
+      *reinterpret_cast<u4*>(smem + Cfg::kRing + i) = i < Kc ? *reinterpret_cast<const u4*>(cl + i) : u4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+
+  // ---- per-lane DMA source offsets (stage-invariant) -------------------------------------
+  const uint32_t o0 = (uint32_t)(wave * nB * 1024 + lane * 16);
+  const int bx0 = wide::b_row_of<BN>(o0);   // chunk j covers tile row bx0 + j*kRowsPerDma
+  uint32_t boff[nB];
+#pragma unroll
+  for (int j = 0; j < nB; ++j) {
+    const uint32_t o = o0 + (uint32_t)(j * 1024);
+    const int x = wide::b_row_of<BN>(o);
+    int64_t c = col0 + wide::b_col_of<BN>(o);
+    c = c < a.C ? c : 0;
+    boff[j] = GATHER ? (uint32_t)(((int64_t)(x >> 2) * a.M * a.ldb + c) * 2) : (uint32_t)(((int64_t)x * a.ldb + c) * 2);
+  }
+  uint32_t aoff[nA], moff[nA];
+#pragma unroll
+  for (int j = 0; j < nA; ++j) {
+    const int bi = wave * nA + j;   // block = tile * KSTEPS + step
+    int64_t r = (bi / KSTEPS) * 32 + (lane & 31);
+    r = row0 + r < a.R ? r : a.R - 1 - row0;
+    const int pos = (bi % KSTEPS) * 32 + 16 * (lane >> 5);
+    aoff[j] = (uint32_t)(r * Kc + pos);
+    moff[j] = (uint32_t)(r * mrow + pos / 8);
+  }
+
+  // column-loc bytes of the B rows a stage gathers: read from LDS one stage ahead of the
+  // DMA that needs them, so the issue path never waits on LDS
+  int gcl[nB];
+  auto fetch_colloc = [&](int64_t s) {
+    if (GATHER && s < nst) {
+#pragma unroll
+      for (int j = 0; j < nB; ++j) gcl[j] = smem[Cfg::kRing + s * KS + bx0 + j * kRowsPerDma];
+    }
+  };
+  auto issue = [&](int64_t s, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    const uint32_t sb = lds0 + (uint32_t)(slot * Cfg::kStage);
+    if (s < nfull) {
+      const uint16_t* bs = Bm + (GATHER ? s * (KS / 4) * a.M * a.ldb : s * KS * a.ldb);
+#pragma unroll
+      for (int j = 0; j < nB; ++j) {
+        const uint32_t v = GATHER ? boff[j] + (uint32_t)gcl[j] * (uint32_t)ldb2 : boff[j];
+        dma_s<16>(bs, v, sb + (uint32_t)((wave * nB + j) * 1024));
+      }
+      const uint8_t* vs = vals + row0 * Kc + s * KS;
+      const uint8_t* ms = meta + row0 * mrow + s * (KS / 8);
+#pragma unroll
+      for (int j = 0; j < nA; ++j) {
+        dma_s<16>(vs, aoff[j], sb + (uint32_t)(Cfg::kAOff + (wave * nA + j) * 1024));
+        dma_s<2>(ms, moff[j], sb + (uint32_t)(Cfg::kMOff + (wave * nA + j) * 256));
+      }
+    } else {
+      // last, partial stage: every source clamped into the operands
+#pragma unroll
+      for (int j = 0; j < nB; ++j) {
+        const uint32_t o = o0 + (uint32_t)(j * 1024);
+        int64_t kg = s * KS + wide::b_row_of<BN>(o);
+        kg = kg < Kc ? kg : Kc - 1;
+        int64_t c = col0 + wide::b_col_of<BN>(o);
+        c = c < a.C ? c : 0;
+        int64_t brow = kg;
+        if constexpr (GATHER) {
+          const int cl = smem[Cfg::kRing + kg];
+          brow = (kg >> 2) * a.M + (cl < a.M ? cl : a.M - 1);   // column-loc entries are < M by contract
+        }
+        dma_v<16>(Bm + brow * a.ldb + c, sb + (uint32_t)((wave * nB + j) * 1024));
+      }
+#pragma unroll
+      for (int j = 0; j < nA; ++j) {
+        const int bi = wave * nA + j;
+        int64_t r = row0 + (bi / KSTEPS) * 32 + (lane & 31);
+        r = r < a.R ? r : a.R - 1;
+        int64_t p = s * KS + (bi % KSTEPS) * 32 + 16 * (lane >> 5);
+        p = p < Kc ? p : Kc - 16;
+        dma_v<16>(vals + r * Kc + p, sb + (uint32_t)(Cfg::kAOff + (wave * nA + j) * 1024));
+        dma_v<2>(meta + r * mrow + p / 8, sb + (uint32_t)(Cfg::kMOff + (wave * nA + j) * 256));
+      }
+    }
+  };
+
+  f16v acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[tm][tn][i] = 0.f;
+
+  // lane-constant LDS offsets of the operand reads
+  const uint32_t a_lds = (uint32_t)(lane * 16 + wm * TM * KSTEPS * 1024);
+  const uint32_t m_lds = (uint32_t)(lane * 4 + wm * TM * KSTEPS * 256);
+  uint32_t tr_lds[TN][4];
+  {
+    const int x = 8 * (lane >> 5) + ((lane & 15) >> 2);                       // row in a step
+    const int cb = wn * TN * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // column
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      tr_lds[tn][0] = wide::b_offset<BN>(x, cb + tn * 32);
+      tr_lds[tn][1] = wide::b_offset<BN>(x + 4, cb + tn * 32);
+      tr_lds[tn][2] = wide::b_offset<BN>(x + 16, cb + tn * 32);
+      tr_lds[tn][3] = wide::b_offset<BN>(x + 20, cb + tn * 32);
+    }
+  }
+
+  auto compute = [&](int64_t s, auto slot_c) {
+    constexpr uint32_t sb = (uint32_t)(decltype(slot_c)::value * Cfg::kStage);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int64_t kb = s * KS + ks * 32;
+      if (kb >= Kc) break;
+      h8 af[TM];
+      uint32_t ix[TM];
+      h16 bf[TN];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        af[tm] = *reinterpret_cast<const h8*>(smem + a_lds + (sb + Cfg::kAOff + (tm * KSTEPS + ks) * 1024));
+        ix[tm] = *reinterpret_cast<const uint32_t*>(smem + m_lds + (sb + Cfg::kMOff + (tm * KSTEPS + ks) * 256));
+      }
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const uint32_t so = sb + (uint32_t)(ks * 64 * BN);   // 32 rows of 2*BN bytes
+        const h4 b0 = tr16_at(smem, tr_lds[tn][0] + so);
+        const h4 b1 = tr16_at(smem, tr_lds[tn][1] + so);
+        const h4 b2 = tr16_at(smem, tr_lds[tn][2] + so);
+        const h4 b3 = tr16_at(smem, tr_lds[tn][3] + so);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf[tn][e] = b0[e];
+          bf[tn][4 + e] = b1[e];
+          bf[tn][8 + e] = b2[e];
+          bf[tn][12 + e] = b3[e];
+        }
+      }
+      if (kb + 32 > Kc) {
+        // last, partial step (K' is a multiple of 16): only its first 16 positions exist.
+        // Zero the A values of the missing half and the B rows there, so clamped DMA
+        // sources contribute exact zeros.
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+          if (lane >= 32) af[tm] = h8{};
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int e = 8; e < 16; ++e) bf[tn][e] = (_Float16)0.f;
+      }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = smfmac32(af[tm], bf[tn], acc[tm][tn], ix[tm]);
+    }
+  };
+
+  // ---- the ring: stage s lives in slot s % NST; the loop is unrolled by NST -------------
+  static_for<0, NST - 1>([&](auto p) {
+    constexpr int P = decltype(p)::value;
+    if (P < nst) {
+      fetch_colloc(P);
+      issue(P, cint<P>{});
+    }
+  });
+  fetch_colloc(NST - 1);
+  for (int64_t s0 = 0; s0 < nst; s0 += NST) {
+    static_for<0, NST>([&](auto u) {
+      constexpr int U = decltype(u)::value;
+      const int64_t s = s0 + U;
+      if (s < nst) {
+        // wait for this wave's DMA of stage s; the barrier publishes every wave's and
+        // retires all reads of slot (s - 1) % NST, which is refilled with stage s + NST - 1
+        if (s + NST - 2 < nst) wait_vmcnt<Cfg::kDma * (NST - 2)>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (s + NST - 1 < nst) {
+          issue(s + NST - 1, cint<(U + NST - 1) % NST>{});
+          fetch_colloc(s + NST);
+        }
+        compute(s, u);
+      }
+    });
+  }
+
+  // ---- epilogue: fp32 -> fp16 (RNE) ------------------------------------------------------
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const int64_t col = col0 + (wn * TN + tn) * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t row = row0 + (wm * TM + tm) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (row < a.R && col < a.C) Y[row * a.ldy + col] = f16_bits(to_f16(acc[tm][tn][i]));
+      }
+    }
+}
+
+template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER>
+hipError_t launch_wide(WideArgs a, hipStream_t stream) {
+  using Cfg = WideCfg<WM, WN, TM, TN, KSTEPS, NST, GATHER>;
+  a.n_row_tiles = (a.R + Cfg::BM - 1) / Cfg::BM;
+  const int64_t n_col_tiles = (a.C + Cfg::BN - 1) / Cfg::BN;
+  a.n_tiles = a.n_row_tiles * n_col_tiles;
+  const int64_t total = a.n_tiles * a.batch;
+  if (total == 0) return hipSuccess;
+  if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  a.xcd_remap = (total % 8) == 0;
+  const size_t lds = (size_t)Cfg::kRing + (GATHER ? (size_t)(a.Kc + 2 * Cfg::KS) : 0);
+  auto kern = k_spmm_wide<WM, WN, TM, TN, KSTEPS, NST, GATHER>;
+  static bool attr_set = false;   // benign race: every caller sets the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(Cfg::kThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+constexpr int64_t kMaxGatherKc = 16384;   // column-loc of one V-block staged in LDS
+
+}  // namespace
+
+bool spmm_wide_eligible(int64_t R, int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb,
+                        int64_t batch, int64_t stride_B) {
+  if (R <= 0 || Kc <= 0 || C <= 32 || C % 8 != 0 || ldb % 8 != 0) return false;
+  if (((uintptr_t)B & 15) != 0) return false;
+  if (batch > 1 && stride_B % 8 != 0) return false;
+  if (V > 0 && (V % 64 != 0 || Kc > kMaxGatherKc)) return false;
+  // per-lane DMA offsets are 32-bit: one tile's A rows, one stage's B rows
+  constexpr int64_t kLim = (int64_t)1 << 31;
+  if (128 * Kc >= kLim) return false;
+  const int64_t b_stage_rows = V > 0 ? 16 * (int64_t)M : 64;
+  if ((b_stage_rows * ldb + C) * 2 >= kLim) return false;
+  return true;
+}
+
+hipError_t launch_spmm_wide(const void* values, const void* meta, const void* colloc, int64_t R,
+                            int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb,
+                            void* Y, int64_t ldy, int64_t batch, int64_t stride_values,
+                            int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
+                            hipStream_t stream) {
+  WideArgs a{};
+  a.values = (const uint16_t*)values;
+  a.meta = (const uint8_t*)meta;
+  a.B = (const uint16_t*)B;
+  a.Y = (uint16_t*)Y;
+  a.colloc = (const uint8_t*)colloc;
+  a.R = R; a.Kc = Kc; a.C = C; a.ldb = ldb; a.ldy = ldy;
+  a.batch = batch < 1 ? 1 : batch;
+  a.stride_values = stride_values; a.stride_meta = stride_meta;
+  a.stride_B = stride_B; a.stride_Y = stride_Y;
+  a.V = V; a.M = M;
+  if (V > 0) {
+    if (V % 128 == 0) {
+      if (C > 128) return launch_wide<1, 4, 4, 2, 1, 3, true>(a, stream);   // 128 x 256
+      return launch_wide<1, 4, 4, 1, 2, 3, true>(a, stream);                // 128 x 128
+    }
+    return launch_wide<1, 4, 2, 1, 2, 3, true>(a, stream);                  // 64 x 128
+  }
+  if (C <= 64) return launch_wide<4, 1, 1, 2, 2, 4, false>(a, stream);      // 128 x 64
+  if (C <= 128) return launch_wide<1, 4, 4, 1, 2, 3, false>(a, stream);     // 128 x 128
+  return launch_wide<1, 4, 4, 2, 1, 3, false>(a, stream);                   // 128 x 256
+}
+
+}  // namespace snm

@@ -191,3 +191,68 @@ def test_spmm_vnm_workload_128_2_16_sampled_rows():
     dense = oracle.decode_vnm(ov, omi, ocl, 128, 16, 8192)[rows]
     ref = dense.astype(np.float64) @ B.astype(np.float64)
     assert_fp16_close(Yh, ref, "vnm_128_2_16 sampled rows")
+
+
+# ---- wide outputs (C > 32, row-major B, C % 8 == 0): the LDS-ring sparse-MFMA path ------
+
+@pytest.mark.parametrize("R,K,C", [
+    (128, 64, 40), (130, 1040, 64), (257, 2080, 136), (96, 528, 256), (384, 4096, 264),
+    (33, 16, 512), (1, 48, 48),
+])
+def test_spmm_nm_wide_shapes(R, K, C):
+    snm = _snm()
+    ov, om, B = _nm_case(R, K, C, R * 7 + K * 3 + C)
+    Y = snm.spmm_nm(to_dev(ov), to_dev(om), to_dev(B))
+    assert_fp16_close(to_host(Y), oracle.spmm_nm(ov, om, B), f"wide {R}x{K}x{C}")
+
+
+@pytest.mark.parametrize("C", [64, 128])
+def test_spmm_nm_wide_batched_padded(C):
+    snm = _snm()
+    import torch
+    nb, R, K = 3, 200, 1056
+    vs, ms, Bs, refs = [], [], [], []
+    for i in range(nb):
+        ov, om, B = _nm_case(R, K, C, 900 + i + C)
+        vs.append(ov); ms.append(om); Bs.append(B); refs.append(oracle.spmm_nm(ov, om, B))
+    Y = snm.spmm_nm(to_dev(np.stack(vs)), to_dev(np.stack(ms)), to_dev(np.stack(Bs)))
+    assert_fp16_close(to_host(Y), np.stack(refs), f"wide batched C={C}")
+    # B with a padded leading dimension (a multiple of 8) and Y inside a wider buffer
+    Bp = torch.zeros((K, C + 16), dtype=torch.float16, device="cuda")
+    Bp[:, :C] = to_dev(Bs[1])
+    Yp = torch.full((R, C + 8), 7.0, dtype=torch.float16, device="cuda")
+    snm.spmm_nm(to_dev(vs[1]), to_dev(ms[1]), Bp[:, :C], out=Yp[:, :C])
+    got = to_host(Yp)
+    assert_fp16_close(got[:, :C], refs[1], "wide strided")
+    assert np.all(got[:, C:] == 7.0), "wrote outside the output view"
+
+
+def test_spmm_nm_wide_identity_is_exact_decode():
+    snm = _snm()
+    A = workloads.small_matrix(78, (160, 320))
+    ov, om = oracle.prune_encode_nm(A)
+    dense = oracle.decode_nm(ov, om, 320).astype(np.float64)
+    for C in (64, 128, 320):
+        Y = snm.spmm_nm(to_dev(ov), to_dev(om), to_dev(np.eye(320, dtype=np.float16)[:, :C].copy()))
+        assert np.array_equal(to_host(Y).astype(np.float64), dense[:, :C]), f"C={C}"
+
+
+@pytest.mark.parametrize("V,M,K,C", [(128, 16, 1024, 256), (128, 8, 512, 128), (64, 8, 768, 256),
+                                     (256, 16, 2048, 72), (64, 12, 960, 48), (64, 8, 96, 64)])
+def test_spmm_vnm_wide_identity_is_exact_decode(V, M, K, C):
+    snm = _snm()
+    A = workloads.small_matrix(V + M + K, (2 * V, K))
+    ov, omi, ocl = oracle.prune_encode_vnm(A, V, M)
+    dense = oracle.decode_vnm(ov, omi, ocl, V, M, K).astype(np.float64)
+    B = np.eye(K, dtype=np.float16)[:, :C].copy()
+    Y = snm.spmm_vnm(to_dev(ov), to_dev(omi), to_dev(ocl), to_dev(B), V, M)
+    assert np.array_equal(to_host(Y).astype(np.float64), dense[:, :C])
+
+
+@pytest.mark.parametrize("R,K,C,V,M", [(256, 1024, 200, 128, 16), (384, 640, 136, 128, 10),
+                                       (192, 2048, 64, 64, 8), (128, 204, 520, 64, 17)])
+def test_spmm_vnm_wide_shapes(R, K, C, V, M):
+    snm = _snm()
+    ov, omi, ocl, B = _vnm_case(R, K, C, V, M, R * 3 + K + C + V + M)
+    Y = snm.spmm_vnm(to_dev(ov), to_dev(omi), to_dev(ocl), to_dev(B), V, M)
+    assert_fp16_close(to_host(Y), oracle.spmm_vnm(ov, omi, ocl, V, M, B), f"wide vnm {R}x{K}x{C} V{V} M{M}")

@@ -1,0 +1,68 @@
+"""Host-side checks of the wide-tile SpMM's LDS layout (csrc/wide_layout.hpp), compiled
+with the host C++ compiler: the DMA chunk placement must be a bijection onto the B tile,
+and every ds_read_b64_tr_b16 of a half-wave must touch each of the 64 four-byte banks
+exactly once."""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "..", "structured_sparse_matrix_amd", "csrc")
+
+CHECKER = r"""
+#include "wide_layout.hpp"
+#include <cstdio>
+#include <set>
+using namespace snm::wide;
+
+template <int BN, int KS>
+int check() {
+  int bad = 0;
+  // 1) chunk o -> (x, c) -> b_offset(x, c) == o, and every (x, c) reached once
+  std::set<std::pair<int, int>> seen;
+  for (unsigned o = 0; o < (unsigned)(KS * BN * 2); o += 16) {
+    const int x = b_row_of<BN>(o), c = b_col_of<BN>(o);
+    if (x < 0 || x >= KS || c < 0 || c + 8 > BN || c % 8) { ++bad; continue; }
+    if (b_offset<BN>(x, c) != o) ++bad;
+    if (!seen.insert({x, c}).second) ++bad;
+  }
+  if ((int)seen.size() != KS * BN / 8) ++bad;
+  // 2) transpose reads of one 32-column operand: half-wave = lanes 0..31 reading rows
+  //    x0 + lane%16/4 at columns c0 + 16*(lane/16) + 4*(lane%4); 8 bytes = 2 banks each
+  for (int x0 = 0; x0 + 4 <= KS; x0 += 4)
+    for (int c0 = 0; c0 + 32 <= BN; c0 += 32) {
+      int hits[64] = {0};
+      for (int l = 0; l < 32; ++l) {
+        const unsigned a = b_offset<BN>(x0 + (l & 15) / 4, c0 + 16 * (l / 16) + 4 * (l & 3));
+        if (a % 8) ++bad;
+        ++hits[(a / 4) % 64];
+        ++hits[(a / 4 + 1) % 64];
+      }
+      for (int b = 0; b < 64; ++b)
+        if (hits[b] != 1) { ++bad; break; }
+    }
+  std::printf("BN=%d KS=%d bad=%d\n", BN, KS, bad);
+  return bad;
+}
+
+int main() {
+  int bad = check<64, 32>() + check<64, 64>() + check<128, 32>() + check<128, 64>() +
+            check<256, 32>() + check<256, 64>();
+  return bad ? 1 : 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs a host C++ compiler")
+def test_wide_lds_layout():
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "check.cpp")
+        exe = os.path.join(d, "check")
+        with open(src, "w") as f:
+            f.write(CHECKER)
+        subprocess.run(["g++", "-std=c++17", "-O1", "-I", CSRC, src, "-o", exe], check=True)
+        r = subprocess.run([exe], capture_output=True, text=True)
+        assert r.returncode == 0, r.stdout + r.stderr
