@@ -14,47 +14,87 @@
 
 namespace snm {
 
-__device__ __forceinline__ uint32_t select_2of4_attn(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
-                                                     uint32_t& v0, uint32_t& v1) {
-  const uint32_t c0 = ((a0 & 0x7FFFu) << 2) | 3u;
-  const uint32_t c1 = ((a1 & 0x7FFFu) << 2) | 2u;
-  const uint32_t c2 = ((a2 & 0x7FFFu) << 2) | 1u;
-  const uint32_t c3 = ((a3 & 0x7FFFu) << 2) | 0u;
-  const uint32_t g01 = c0 > c1, g02 = c0 > c2, g03 = c0 > c3;
-  const uint32_t g12 = c1 > c2, g13 = c1 > c3, g23 = c2 > c3;
-  const uint32_t r0 = (1u - g01) + (1u - g02) + (1u - g03);
-  const uint32_t r1 = g01 + (1u - g12) + (1u - g13);
-  const uint32_t r2 = g02 + g12 + (1u - g23);
-  const uint32_t r3 = g03 + g13 + g23;
-  const uint32_t keep = (uint32_t)(r0 < 2) | ((uint32_t)(r1 < 2) << 1) | ((uint32_t)(r2 < 2) << 2) |
-                        ((uint32_t)(r3 < 2) << 3);
-  const uint32_t s0 = __builtin_ctz(keep);
-  const uint32_t s1 = 31u - __builtin_clz(keep);
-  v0 = s0 == 0 ? a0 : (s0 == 1 ? a1 : a2);
-  v1 = s1 == 3 ? a3 : (s1 == 2 ? a2 : a1);
+// 2 of 4 by magnitude on composite keys: key_i = |h_i| << 2 | (3 - i), where |h| is the
+// fp16 pattern without its sign (orders like the magnitude; NaN > Inf > finite), so a
+// larger key means a larger magnitude or, on equal magnitudes, a lower slot -- the
+// lower-slot-wins tie rule. The two largest keys are the kept slots (a 6-operation
+// max/min network instead of pairwise ranks). Inputs are the group's four fp16 patterns
+// packed in pairs (p01 = h0 | h1 << 16, p23 = h2 | h3 << 16); the kept pair, ascending
+// slot order, comes back packed the same way, gathered with one byte permute.
+__device__ __forceinline__ uint32_t select_2of4_keys(uint32_t p01, uint32_t p23, uint32_t& kept) {
+  const uint32_t c0 = ((p01 & 0x7FFFu) << 2) | 3u;
+  const uint32_t c1 = ((p01 >> 14) & 0x1FFFCu) | 2u;
+  const uint32_t c2 = ((p23 & 0x7FFFu) << 2) | 1u;
+  const uint32_t c3 = (p23 >> 14) & 0x1FFFCu;
+  const uint32_t m01 = c0 > c1 ? c0 : c1, n01 = c0 > c1 ? c1 : c0;
+  const uint32_t m23 = c2 > c3 ? c2 : c3, n23 = c2 > c3 ? c3 : c2;
+  const uint32_t t1 = m01 > m23 ? m01 : m23;
+  const uint32_t lo_m = m01 > m23 ? m23 : m01;
+  const uint32_t hi_n = n01 > n23 ? n01 : n23;
+  const uint32_t t2 = lo_m > hi_n ? lo_m : hi_n;
+  const uint32_t x = t1 & 3u, y = t2 & 3u;   // 3 - slot of the two kept entries
+  const uint32_t s0 = 3u - (x > y ? x : y);
+  const uint32_t s1 = 3u - (x > y ? y : x);
+  // bytes 2 s0, 2 s0 + 1, 2 s1, 2 s1 + 1 of {p23 : p01}
+  kept = __builtin_amdgcn_perm(p23, p01, (s0 | (s1 << 16)) * 0x0202u + 0x01000100u);
   return s0 | (s1 << 2);
 }
 
-// Workgroup: 4 waves x QT query tiles of 32 queries; the waves walk the same key tiles
-// (32 keys each) so K rows are shared through L1.
+// Workgroup: 8 waves (two per SIMD); each wave owns QT tiles of 32 queries and walks all
+// keys in tiles of 32. The product is formed transposed (S^T = K Q^T, dense 32x32x16 MFMA)
+// so each lane holds four consecutive keys of one query per group. Per tile and lane:
+// scale in fp32, round to fp16 (packed RNE conversion), select 2 of 4, and stage the kept
+// pairs and the metadata nibbles in the wave's LDS buffers.
+//   * values leave every 4 key tiles (128 keys = one 128-byte line per query row), and
+//     metadata every 32 key tiles (1024 keys = one 128-byte line per row): only whole
+//     lines are written, so the L2 never evicts partly written lines (measured: 16-byte
+//     metadata pieces cost as much as the 8x larger value stream).
+//   * K tiles rotate through a 4-deep register ring loaded 3 tiles ahead. Vector loads and
+//     stores retire in issue order on this architecture, so a load issued after a flush
+//     cannot be waited for without waiting for the flush; the ring keeps every wait on a
+//     load issued well before the last flush.
+//   * the MFMA chain of query tile qt+1 is issued before the epilogue of tile qt.
 template <int D, int QT>
-__global__ void __launch_bounds__(256)
+struct SddmmCfg {
+  static constexpr int kWaves = 8;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int KT = 4;                  // key tiles per values flush
+  static constexpr int MT = 32;                 // key tiles per metadata flush
+  static constexpr int VP = 144;                // staged value bytes per query row: 128 + pad
+  static constexpr int MP = 144;                // staged metadata bytes per query row: 128 + pad
+  static constexpr int kWaveV = QT * 32 * VP;
+  static constexpr int kWaveM = QT * 32 * MP;
+  static constexpr int kLds = kWaves * (kWaveV + kWaveM);
+  static constexpr int kQueries = kWaves * 32 * QT;   // per workgroup
+};
+
+// DENSE: also write the pre-prune fp16 S (the optional debug output).
+template <int D, int QT, bool DENSE>
+__global__ void __launch_bounds__(512)
 k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, int64_t batch,
               int64_t Lq, int64_t Lk, float scale, uint16_t* __restrict__ values,
               uint16_t* __restrict__ meta, uint16_t* __restrict__ S) {
-  constexpr int KSTEPS = D / 16;
+  using Cfg = SddmmCfg<D, QT>;
+  constexpr int KSTEPS = Cfg::KSTEPS, KT = Cfg::KT, MT = Cfg::MT, VP = Cfg::VP, MP = Cfg::MP;
+  extern __shared__ __align__(16) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;          // which 8-wide d slice / which 4-key subgroup
   const int l32 = lane & 31;
-  const int64_t q_wave = (int64_t)blockIdx.x * (4 * 32 * QT) + (int64_t)wave * 32 * QT;
+  uint8_t* const sv = smem + wave * Cfg::kWaveV;
+  uint8_t* const sm = smem + Cfg::kWaves * Cfg::kWaveV + wave * Cfg::kWaveM;
+  const int64_t q_wave = (int64_t)blockIdx.x * Cfg::kQueries + (int64_t)wave * 32 * QT;
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
+  const int64_t nkt = Lk >> 5;         // key tiles (Lk % 32 == 0)
 
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    if (q_wave >= Lq) break;   // whole wave past the end (uniform per wave; no barriers)
     const uint16_t* Qb = Q + b * Lq * D;
     const uint16_t* Kb = Km + b * Lk * D;
     uint16_t* vals_b = values + b * Lq * (Lk >> 1);
-    uint16_t* meta_b = meta + b * Lq * (Lk >> 4);
-    uint16_t* S_b = S ? S + b * Lq * Lk : nullptr;
+    uint8_t* meta_b = reinterpret_cast<uint8_t*>(meta) + b * Lq * (Lk >> 3);
+    uint16_t* S_b = DENSE ? S + b * Lq * Lk : nullptr;
 
     // Q^T operand: column = query, k = d. Lane holds d = 8*half + 16j + [0, 8).
     h8 qf[QT][KSTEPS];
@@ -68,62 +108,101 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
         qf[qt][j] = v;
       }
     }
-    if (q_wave >= Lq) continue;   // whole wave past the end (uniform per wave)
 
-    auto load_k = [&](int64_t k0, h8 (&kf)[KSTEPS]) {
+    // K ring: slot t % 4 holds key tile t; tile t + 3 is requested while tile t is used
+    h8 kr[4][KSTEPS];
+    auto load_k = [&](int64_t t, h8 (&kf)[KSTEPS]) {
+      if (t < nkt) {
 #pragma unroll
-      for (int j = 0; j < KSTEPS; ++j)
-        kf[j] = *reinterpret_cast<const h8*>(Kb + (k0 + l32) * D + 16 * j + 8 * half);
+        for (int j = 0; j < KSTEPS; ++j)
+          kf[j] = *reinterpret_cast<const h8*>(Kb + (t * 32 + l32) * D + 16 * j + 8 * half);
+      }
     };
-    h8 kcur[KSTEPS], knext[KSTEPS];
-    load_k(0, kcur);
-    for (int64_t k0 = 0; k0 < Lk; k0 += 32) {
-      if (k0 + 32 < Lk) load_k(k0 + 32, knext);
+    load_k(0, kr[0]);
+    load_k(1, kr[1]);
+    load_k(2, kr[2]);
+
+    for (int64_t t0 = 0; t0 < nkt; t0 += KT) {
+      const int nk = (int)(nkt - t0 < KT ? nkt - t0 : KT);
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        f16v acc = {};
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt >= nk) break;
+        const int64_t t = t0 + kt;
+        const int64_t kk = t * 32;
+        load_k(t + 3, kr[(kt + 3) % 4]);
+        auto chain = [&](int qt) {
+          f16v acc = {};
 #pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) acc = mfma32x32x16(kcur[j], qf[qt][j], acc);
-        // acc[i] = S[query l32][key k0 + 8(i/4) + 4 half + i%4]
-        const int64_t qi = q_wave + qt * 32 + l32;
-        uint32_t out[4];
-        uint32_t codes = 0;   // code of this lane's group gi at bits [8 gi, 8 gi + 3]
+          for (int j = 0; j < KSTEPS; ++j) acc = mfma32x32x16(kr[kt][j], qf[qt][j], acc);
+          return acc;
+        };
+        const int mcol = (int)(t % MT);   // metadata word column of this tile
+        f16v acc_next = chain(0);
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          uint32_t h[4];
+        for (int qt = 0; qt < QT; ++qt) {
+          const f16v acc = acc_next;
+          if (qt + 1 < QT) acc_next = chain(qt + 1);
+          // acc[i] = S[query l32][key kk + 8(i/4) + 4 half + i%4]
+          const int64_t qi = q_wave + qt * 32 + l32;
+          uint32_t mword = 0;   // nibble of group 2gi+half at bits 8gi + 4half
 #pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = f16_bits(to_f16(acc[4 * gi + e] * scale));
-          if (S_b && qi < Lq) {
-            u2 pk = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-            *reinterpret_cast<u2*>(S_b + qi * Lk + k0 + 8 * gi + 4 * half) = pk;
+          for (int gi = 0; gi < 4; ++gi) {
+            const f2 x01 = {acc[4 * gi] * scale, acc[4 * gi + 1] * scale};
+            const f2 x23 = {acc[4 * gi + 2] * scale, acc[4 * gi + 3] * scale};
+            const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(x01, hh2));
+            const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(x23, hh2));
+            if (DENSE && qi < Lq) {
+              const u2 pk = {p01, p23};
+              *reinterpret_cast<u2*>(S_b + qi * Lk + kk + 8 * gi + 4 * half) = pk;
+            }
+            uint32_t kept;
+            const uint32_t code = select_2of4_keys(p01, p23, kept);
+            // kept pair of group (kk + 8gi + 4half)/4 -> value position kt*16 + 4gi + 2half
+            *reinterpret_cast<uint32_t*>(sv + (qt * 32 + l32) * VP + (kt * 16 + 4 * gi + 2 * half) * 2) = kept;
+            mword |= code << (8 * gi + 4 * half);
           }
-          uint32_t v0, v1;
-          const uint32_t code = select_2of4_attn(h[0], h[1], h[2], h[3], v0, v1);
-          out[gi] = v0 | (v1 << 16);
-          codes |= code << (8 * gi);
-        }
-        // Lanes l and l+32 hold the even and odd groups of the 8 groups of this query's
-        // 32 keys. Swap so that lane l holds groups 0-3 and lane l+32 groups 4-7.
-        const uint32_t send0 = half ? out[0] : out[2];
-        const uint32_t send1 = half ? out[1] : out[3];
-        const uint32_t recv0 = (uint32_t)__shfl_xor((int)send0, 32);
-        const uint32_t recv1 = (uint32_t)__shfl_xor((int)send1, 32);
-        const uint32_t pcodes = (uint32_t)__shfl_xor((int)codes, 32);
-        u4 o;
-        if (!half) { o[0] = out[0]; o[1] = recv0; o[2] = out[1]; o[3] = recv1; }
-        else       { o[0] = recv0; o[1] = out[2]; o[2] = recv1; o[3] = out[3]; }
-        const uint32_t ev = half ? pcodes : codes;
-        const uint32_t od = half ? codes : pcodes;
-        const uint32_t sh = half ? 16u : 0u;
-        const uint32_t word = ((ev >> sh) & 0xF0Fu) | (((od >> sh) & 0xF0Fu) << 4);
-        if (qi < Lq) {
-          *reinterpret_cast<u4*>(vals_b + qi * (Lk >> 1) + (k0 >> 1) + 8 * half) = o;
-          meta_b[qi * (Lk >> 4) + (k0 >> 4) + half] = (uint16_t)word;
+          mword |= (uint32_t)__shfl_xor((int)mword, 32);
+          if (!half) *reinterpret_cast<uint32_t*>(sm + (qt * 32 + l32) * MP + mcol * 4) = mword;
         }
       }
-      if (k0 + 32 < Lk) {
+      // ---- values: the 4 staged tiles of every row as one 128-byte line
 #pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) kcur[j] = knext[j];
+      for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 8 * i + (lane >> 3);
+          const int ch = lane & 7;             // 16-byte chunk = 8 kept values
+          const int64_t qi = q_wave + qt * 32 + row;
+          if (ch < 2 * nk && qi < Lq) {
+            const u4 v = *reinterpret_cast<const u4*>(sv + (qt * 32 + row) * VP + ch * 16);
+            *reinterpret_cast<u4*>(vals_b + qi * (Lk >> 1) + t0 * 16 + ch * 8) = v;
+          }
+        }
+      }
+      // ---- metadata: every 32 tiles (or at the end) the staged words of every row
+      const int64_t tend = t0 + nk;   // tiles done
+      if (tend % MT == 0 || tend == nkt) {
+        const int64_t m0 = (tend - 1) / MT * MT;   // first tile of this metadata line
+        const int nw = (int)(tend - m0);           // 4-byte words staged per row
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 8 * i + (lane >> 3);
+            const int ch = lane & 7;           // 16-byte chunk = 4 words = 4 key tiles
+            const int64_t qi = q_wave + qt * 32 + row;
+            if (qi < Lq) {
+              const uint8_t* src = sm + (qt * 32 + row) * MP + ch * 16;
+              uint8_t* dst = meta_b + qi * (Lk >> 3) + m0 * 4 + ch * 16;
+              if (4 * ch + 4 <= nw && (Lk & 127) == 0) {
+                *reinterpret_cast<u4*>(dst) = *reinterpret_cast<const u4*>(src);
+              } else {
+                for (int w = 4 * ch; w < 4 * ch + 4 && w < nw; ++w)
+                  reinterpret_cast<uint32_t*>(dst)[w - 4 * ch] = reinterpret_cast<const uint32_t*>(src)[w - 4 * ch];
+              }
+            }
+          }
+        }
       }
     }
   }
@@ -189,24 +268,45 @@ k_softmax_rows(uint16_t* __restrict__ vals, int64_t rows, int64_t kept, int64_t 
   for (int64_t e = lane; e < kept; e += 64) v[e] = f16_bits(to_f16(__expf((float)bits_f16(v[e]) - mx) * inv));
 }
 
+template <int D, int QT, bool DENSE>
+static hipError_t launch_sddmm_cfg1(const uint16_t* q, const uint16_t* k, int64_t batch, int64_t Lq,
+                                   int64_t Lk, float scale, uint16_t* vv, uint16_t* mm, uint16_t* ss,
+                                   hipStream_t stream) {
+  using Cfg = SddmmCfg<D, QT>;
+  const int64_t qblocks = (Lq + Cfg::kQueries - 1) / Cfg::kQueries;
+  const dim3 grid((unsigned)qblocks, (unsigned)(batch < 65535 ? batch : 65535));
+  auto kern = k_sddmm_prune<D, QT, DENSE>;
+  static bool attr_set = false;   // benign race: every caller sets the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(64 * Cfg::kWaves), Cfg::kLds, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss);
+  return hipGetLastError();
+}
+template <int D, int QT>
+static hipError_t launch_sddmm_cfg(const uint16_t* q, const uint16_t* k, int64_t batch, int64_t Lq,
+                                   int64_t Lk, float scale, uint16_t* vv, uint16_t* mm, uint16_t* ss,
+                                   hipStream_t stream) {
+  if (ss) return launch_sddmm_cfg1<D, QT, true>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
+  return launch_sddmm_cfg1<D, QT, false>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
+}
+
 hipError_t launch_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
                                  int64_t Lk, int64_t d, float scale, void* values, void* meta,
                                  void* S_dense, hipStream_t stream) {
-  constexpr int QT = 2;
-  const int64_t qblocks = (Lq + 4 * 32 * QT - 1) / (4 * 32 * QT);
-  const dim3 grid((unsigned)qblocks, (unsigned)(batch < 65535 ? batch : 65535));
   const uint16_t* q = (const uint16_t*)Q;
   const uint16_t* k = (const uint16_t*)Kmat;
   uint16_t* vv = (uint16_t*)values;
   uint16_t* mm = (uint16_t*)meta;
   uint16_t* ss = (uint16_t*)S_dense;
   switch (d) {
-    case 16: hipLaunchKernelGGL((k_sddmm_prune<16, QT>), grid, dim3(256), 0, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss); break;
-    case 32: hipLaunchKernelGGL((k_sddmm_prune<32, QT>), grid, dim3(256), 0, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss); break;
-    case 64: hipLaunchKernelGGL((k_sddmm_prune<64, QT>), grid, dim3(256), 0, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss); break;
-    default: hipLaunchKernelGGL((k_sddmm_prune<128, QT>), grid, dim3(256), 0, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss); break;
+    case 16: return launch_sddmm_cfg<16, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
+    case 32: return launch_sddmm_cfg<32, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
+    case 64: return launch_sddmm_cfg<64, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
+    default: return launch_sddmm_cfg<128, 1>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld,
