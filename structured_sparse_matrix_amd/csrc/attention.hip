@@ -14,32 +14,6 @@
 
 namespace snm {
 
-// 2 of 4 by magnitude on composite keys: key_i = |h_i| << 2 | (3 - i), where |h| is the
-// fp16 pattern without its sign (orders like the magnitude; NaN > Inf > finite), so a
-// larger key means a larger magnitude or, on equal magnitudes, a lower slot -- the
-// lower-slot-wins tie rule. The two largest keys are the kept slots (a 6-operation
-// max/min network instead of pairwise ranks). Inputs are the group's four fp16 patterns
-// packed in pairs (p01 = h0 | h1 << 16, p23 = h2 | h3 << 16); the kept pair, ascending
-// slot order, comes back packed the same way, gathered with one byte permute.
-__device__ __forceinline__ uint32_t select_2of4_keys(uint32_t p01, uint32_t p23, uint32_t& kept) {
-  const uint32_t c0 = ((p01 & 0x7FFFu) << 2) | 3u;
-  const uint32_t c1 = ((p01 >> 14) & 0x1FFFCu) | 2u;
-  const uint32_t c2 = ((p23 & 0x7FFFu) << 2) | 1u;
-  const uint32_t c3 = (p23 >> 14) & 0x1FFFCu;
-  const uint32_t m01 = c0 > c1 ? c0 : c1, n01 = c0 > c1 ? c1 : c0;
-  const uint32_t m23 = c2 > c3 ? c2 : c3, n23 = c2 > c3 ? c3 : c2;
-  const uint32_t t1 = m01 > m23 ? m01 : m23;
-  const uint32_t lo_m = m01 > m23 ? m23 : m01;
-  const uint32_t hi_n = n01 > n23 ? n01 : n23;
-  const uint32_t t2 = lo_m > hi_n ? lo_m : hi_n;
-  const uint32_t x = t1 & 3u, y = t2 & 3u;   // 3 - slot of the two kept entries
-  const uint32_t s0 = 3u - (x > y ? x : y);
-  const uint32_t s1 = 3u - (x > y ? y : x);
-  // bytes 2 s0, 2 s0 + 1, 2 s1, 2 s1 + 1 of {p23 : p01}
-  kept = __builtin_amdgcn_perm(p23, p01, (s0 | (s1 << 16)) * 0x0202u + 0x01000100u);
-  return s0 | (s1 << 2);
-}
-
 // Workgroup: 8 waves (two per SIMD); each wave owns QT tiles of 32 queries and walks all
 // keys in tiles of 32. The product is formed transposed (S^T = K Q^T, dense 32x32x16 MFMA)
 // so each lane holds four consecutive keys of one query per group. Per tile and lane:

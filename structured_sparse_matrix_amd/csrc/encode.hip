@@ -133,9 +133,20 @@ k_prune_encode_vnm(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t
 
   for (int c = threadIdx.x; c < ncols; c += kVnmThreads) {
     double s = 0.0;
-    for (int r = 0; r < V; ++r) {
+    int r = 0;
+    for (; r + 8 <= V; r += 8) {     // eight independent loads in flight, sums in row order
+      uint16_t h[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) h[t] = Ablk[(int64_t)(r + t) * lda + c];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const double a = (double)bits_f16(h[t]);
+        s = __builtin_fma(a, a, s);   // a*a is exact, so this equals s + a*a rounded once
+      }
+    }
+    for (; r < V; ++r) {
       const double a = (double)bits_f16(Ablk[(int64_t)r * lda + c]);
-      s = __builtin_fma(a, a, s);     // a*a is exact, so this equals s + a*a rounded once
+      s = __builtin_fma(a, a, s);
     }
     score[c] = s;
   }
@@ -190,6 +201,175 @@ k_prune_encode_vnm(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t
   }
 }
 
+// V:2:M with the workgroup's V x (GC*M) tile of A staged in LDS first (batches of eight
+// 16-byte loads in flight per thread), then the column scores (float64, rows in ascending
+// order), the column-loc selection and the 2:4 encoding all read LDS: one HBM read of A,
+// no dependent global loads. Used whenever a tile of at least one metadata word of groups
+// fits. Tiles of up to 64 KiB for tall blocks (V >= 128: fewer, longer score chains) and
+// 32 KiB otherwise (more workgroups per CU to overlap the phases); measured on MI355X.
+constexpr int kVnmTileBytes = 64 * 1024;
+static int vnm_tile_bytes(int V) { return V >= 128 ? kVnmTileBytes : kVnmTileBytes / 2; }
+
+__global__ void __launch_bounds__(kVnmThreads)
+k_prune_encode_vnm_lds(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t lda, int V,
+                       int M, int GC, uint16_t* __restrict__ values, uint16_t* __restrict__ midx,
+                       uint8_t* __restrict__ colloc) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int64_t G = K / M;
+  const int64_t nchunks = (G + GC - 1) / GC;
+  const int64_t vb = blockIdx.x / nchunks;
+  const int64_t g0 = (blockIdx.x - vb * nchunks) * GC;
+  const int ng = (int)((G - g0) < GC ? (G - g0) : GC);   // groups in this chunk (multiple of 4)
+  const int ncols = ng * M;
+  const int pitch = GC * M;                              // elements per staged row
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+  double* score = reinterpret_cast<double*>(smem + (size_t)V * pitch * 2);
+  uint8_t* sel = reinterpret_cast<uint8_t*>(score + pitch);   // [group in chunk][4]
+  uint8_t* keep = sel + GC * 4;
+  const uint16_t* Ablk = A + vb * V * lda + g0 * M;
+
+  // ---- stage the tile
+  if ((((uintptr_t)Ablk) & 15) == 0 && (ncols & 7) == 0 && (lda & 7) == 0) {
+    // eight 16-byte loads in flight per thread before their LDS writes
+    const int c8 = ncols >> 3;
+    const int n = V * c8;
+    for (int i0 = threadIdx.x; i0 < n; i0 += 8 * kVnmThreads) {
+      u4 v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int i = i0 + t * kVnmThreads;
+        if (i < n) {
+          const int r = i / c8;
+          const int c = (i - r * c8) * 8;
+          v[t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(Ablk + (int64_t)r * lda + c));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int i = i0 + t * kVnmThreads;
+        if (i < n) {
+          const int r = i / c8;
+          const int c = (i - r * c8) * 8;
+          *reinterpret_cast<u4*>(tile + r * pitch + c) = v[t];
+        }
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < V * ncols; i += kVnmThreads) {
+      const int r = i / ncols;
+      const int c = i - r * ncols;
+      tile[r * pitch + c] = Ablk[(int64_t)r * lda + c];
+    }
+  }
+  __syncthreads();
+  // ---- phase 1: column scores; eight LDS reads in flight, sums in row order
+  for (int c = threadIdx.x; c < ncols; c += kVnmThreads) {
+    double s = 0.0;
+    int r = 0;
+    for (; r + 8 <= V; r += 8) {
+      uint16_t h[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) h[t] = tile[(r + t) * pitch + c];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const double a = (double)bits_f16(h[t]);
+        s = __builtin_fma(a, a, s);   // a*a is exact, so this equals s + a*a rounded once
+      }
+    }
+    for (; r < V; ++r) {
+      const double a = (double)bits_f16(tile[r * pitch + c]);
+      s = __builtin_fma(a, a, s);
+    }
+    score[c] = s;
+  }
+  __syncthreads();
+  // ---- phase 2: the four columns of largest score per group (ties to the lower column)
+  for (int c = threadIdx.x; c < ncols; c += kVnmThreads) {
+    const int gi = c / M;
+    const int base = gi * M;
+    const double sc = score[c];
+    int rank = 0;
+    int j = 0;
+    for (; j + 4 <= M; j += 4) {
+      double sj[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sj[t] = score[base + j + t];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) rank += (sj[t] > sc) | ((sj[t] == sc) & (base + j + t < c));
+    }
+    for (; j < M; ++j) {
+      const double sj = score[base + j];
+      rank += (sj > sc) | ((sj == sc) & (base + j < c));
+    }
+    keep[c] = rank < 4;
+  }
+  __syncthreads();
+  // position of each kept column among its group's kept columns (ascending column order)
+  const bool wave_groups = (64 % M) == 0;   // groups never straddle a wave
+  for (int c0 = 0; c0 < ncols; c0 += kVnmThreads) {
+    const int c = c0 + (int)threadIdx.x;
+    const bool kc = c < ncols && keep[c];
+    int p;
+    const int gi = c / M;
+    const int base = gi * M;
+    if (wave_groups) {
+      const uint64_t kb = __ballot(kc);
+      const int lane = threadIdx.x & 63;
+      const int lb = lane - (c - base);              // lane of the group's first column
+      const uint64_t below = ((uint64_t)1 << lane) - 1;
+      const uint64_t grp = lb > 0 ? ~(((uint64_t)1 << lb) - 1) : ~(uint64_t)0;
+      p = __popcll(kb & below & grp);
+    } else {
+      p = 0;
+      if (kc)
+        for (int j = base; j < c; ++j) p += keep[j];
+    }
+    if (kc && p < 4) {   // p < 4 always for finite scores; guards unspecified non-finite input
+      sel[gi * 4 + p] = (uint8_t)(c - base);
+      colloc[((vb * G) + g0 + gi) * 4 + p] = (uint8_t)(c - base);
+    }
+  }
+  __syncthreads();
+  // ---- phase 3: 2:4 among the selected columns, one thread per (row, group), four items
+  // in flight per thread. Consecutive threads take consecutive groups of a row (ng is a
+  // multiple of 4), so the four groups of a metadata word sit in one lane quad and their
+  // codes are combined with two quad permutes.
+  const int64_t vals_per_row = 2 * G;
+  const int64_t midx_words_per_row = G >> 2;
+  const int nitems = V * ng;
+  const int lane = threadIdx.x & 63;
+  for (int i0 = threadIdx.x; i0 < nitems + 3 * kVnmThreads; i0 += 4 * kVnmThreads) {
+    if (i0 - (int)threadIdx.x >= nitems) break;   // uniform: the whole batch is past the end
+    uint32_t sw[4];
+    int rr[4], gg[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int it = i0 + t * kVnmThreads;
+      const int itc = it < nitems ? it : nitems - 1;
+      rr[t] = itc / ng;
+      gg[t] = itc - rr[t] * ng;
+      sw[t] = *reinterpret_cast<const uint32_t*>(sel + gg[t] * 4);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int it = i0 + t * kVnmThreads;
+      const uint16_t* ag = tile + rr[t] * pitch + gg[t] * M;
+      const uint32_t p01 = (uint32_t)ag[sw[t] & 0xFFu] | ((uint32_t)ag[(sw[t] >> 8) & 0xFFu] << 16);
+      const uint32_t p23 = (uint32_t)ag[(sw[t] >> 16) & 0xFFu] | ((uint32_t)ag[sw[t] >> 24] << 16);
+      uint32_t kept;
+      const uint32_t code = select_2of4_keys(p01, p23, kept);
+      uint32_t w = code << (4 * (lane & 3));
+      w |= (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+      w |= (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
+      if (it < nitems) {
+        const int64_t row = vb * V + rr[t];
+        *reinterpret_cast<uint32_t*>(values + row * vals_per_row + 2 * (g0 + gg[t])) = kept;
+        if ((lane & 3) == 0) midx[row * midx_words_per_row + ((g0 + gg[t]) >> 2)] = (uint16_t)w;
+      }
+    }
+  }
+}
+
 hipError_t launch_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda, void* values,
                                   void* meta, hipStream_t stream) {
   const int64_t total = R * (K >> 4);
@@ -217,9 +397,39 @@ int vnm_chunk_groups(int M) {
   return gc < 4 ? 4 : gc;
 }
 
+// Groups per workgroup of the LDS-staged kernel: the most whose V x GC*M tile fits
+// kVnmTileBytes with the score arrays, in steps of 4 groups (one metadata word; with M
+// even that also keeps every chunk on a 16-byte boundary) or of 8 for odd M; 0 if not
+// even one step fits.
+static int vnm_lds_groups(int V, int M) {
+  const int per_group = M * (V * 2 + 8 + 2);   // tile column + score + keep/sel bytes
+  const int step = (M % 2 == 0) ? 4 : 8;
+  int gc = vnm_tile_bytes(V) / per_group / step * step;
+  if (gc > 256) gc = 256;
+  return gc >= step ? gc : 0;
+}
+
 hipError_t launch_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
                                    void* values, void* midx, void* colloc, hipStream_t stream) {
   if (R == 0 || K == 0) return hipSuccess;
+  const int GL = vnm_lds_groups(V, M);
+  if (GL > 0) {
+    const int64_t G = K / M;
+    const int64_t nchunks = (G + GL - 1) / GL;
+    const int64_t blocks = (R / V) * nchunks;
+    const size_t lds = (size_t)V * GL * M * 2 + (size_t)GL * M * (8 + 1) + (size_t)GL * 4;   // tile, score, sel, keep
+    static bool attr_set = false;   // benign race: every caller sets the same value
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void*)k_prune_encode_vnm_lds,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(k_prune_encode_vnm_lds, dim3((unsigned)blocks), dim3(kVnmThreads), lds, stream,
+                       (const uint16_t*)A, R, K, lda, V, M, GL, (uint16_t*)values, (uint16_t*)midx,
+                       (uint8_t*)colloc);
+    return hipGetLastError();
+  }
   const int GC = vnm_chunk_groups(M);
   const int64_t G = K / M;
   const int64_t nchunks = (G + GC - 1) / GC;

@@ -73,9 +73,27 @@ def _check_vnm(A, V, M, what):
 @pytest.mark.parametrize("R,K,V,M", [
     (64, 64, 64, 8), (128, 512, 64, 8), (256, 1024, 128, 16), (32, 160, 32, 10),
     (16, 4096, 16, 256), (8, 64, 1, 4), (4, 128, 2, 8), (96, 256, 32, 4), (128, 320, 64, 5),
+    # the largest V; an odd V
+    (512, 256, 256, 16), (6, 64, 3, 8),
 ])
 def test_vnm_small(R, K, V, M):
     _check_vnm(workloads.small_matrix(R + K + V + M, (R, K), 0.02), V, M, f"{R}x{K} V{V} M{M}")
+
+
+def test_vnm_padded_rows_odd_m():
+    # K = 460, M = 5: several workgroup chunks, the last one 12 groups = 60 columns (not a
+    # multiple of 8 elements); A is a view with leading dimension 464
+    import torch
+    snm = _snm()
+    R, K, V, M = 128, 460, 64, 5
+    A = workloads.small_matrix(77, (R, K), 0.02)
+    buf = torch.zeros((R, 464), dtype=torch.float16, device="cuda")
+    buf[:, :K] = to_dev(A)
+    v, mi, cl = snm.prune_encode_vnm(buf[:, :K], V, M)
+    ov, omi, ocl = oracle.prune_encode_vnm(A, V, M)
+    assert_bits_equal(to_host(cl), ocl, "padded colloc")
+    assert_bits_equal(to_host(mi), omi, "padded midx")
+    assert_bits_equal(to_host(v), ov, "padded values")
 
 
 def test_vnm_ties():
