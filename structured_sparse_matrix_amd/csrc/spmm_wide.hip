@@ -196,15 +196,16 @@ k_spmm_wide(WideArgs a) {
     c = c < a.C ? c : 0;
     boff[j] = GATHER ? (uint32_t)(((int64_t)(x >> 2) * a.M * a.ldb + c) * 2) : (uint32_t)(((int64_t)x * a.ldb + c) * 2);
   }
-  uint32_t aoff[nA], moff[nA];
+  uint32_t aoff[nA], moff[nA];   // A chunk (16 bytes = 16 positions) and index word sources
 #pragma unroll
   for (int j = 0; j < nA; ++j) {
-    const int bi = wave * nA + j;   // block = tile * KSTEPS + step
-    int64_t r = (bi / KSTEPS) * 32 + (lane & 31);
+    const int bi = wave * nA + j;
+    int64_t r = wide::a_dma_row<KS>(bi, lane);
     r = row0 + r < a.R ? r : a.R - 1 - row0;
-    const int pos = (bi % KSTEPS) * 32 + 16 * (lane >> 5);
-    aoff[j] = (uint32_t)(r * Kc + pos);
-    moff[j] = (uint32_t)(r * mrow + pos / 8);
+    aoff[j] = (uint32_t)(r * Kc + wide::a_dma_chunk<KS>(lane) * 16);
+    int64_t rm = wide::m_dma_row<KS>(bi, lane);
+    rm = row0 + rm < a.R ? rm : a.R - 1 - row0;
+    moff[j] = (uint32_t)(rm * mrow + wide::m_dma_word<KS>(lane) * 2);
   }
 
   // column-loc bytes of the B rows a stage gathers: read from LDS one stage ahead of the
@@ -252,12 +253,16 @@ k_spmm_wide(WideArgs a) {
 #pragma unroll
       for (int j = 0; j < nA; ++j) {
         const int bi = wave * nA + j;
-        int64_t r = row0 + (bi / KSTEPS) * 32 + (lane & 31);
+        int64_t r = row0 + wide::a_dma_row<KS>(bi, lane);
         r = r < a.R ? r : a.R - 1;
-        int64_t p = s * KS + (bi % KSTEPS) * 32 + 16 * (lane >> 5);
+        int64_t p = s * KS + wide::a_dma_chunk<KS>(lane) * 16;   // first position of the chunk
         p = p < Kc ? p : Kc - 16;
-        dma_v<16>(vals + r * Kc + p, sb + (uint32_t)(Cfg::kAOff + (wave * nA + j) * 1024));
-        dma_v<2>(meta + r * mrow + p / 8, sb + (uint32_t)(Cfg::kMOff + (wave * nA + j) * 256));
+        dma_v<16>(vals + r * Kc + p, sb + (uint32_t)(Cfg::kAOff + bi * 1024));
+        int64_t rm = row0 + wide::m_dma_row<KS>(bi, lane);
+        rm = rm < a.R ? rm : a.R - 1;
+        int64_t wd = s * (KS / 16) + wide::m_dma_word<KS>(lane);   // index word of the row
+        wd = wd < Kc / 16 ? wd : Kc / 16 - 1;
+        dma_v<2>(meta + rm * mrow + wd * 2, sb + (uint32_t)(Cfg::kMOff + bi * 256));
       }
     }
   };
@@ -270,9 +275,17 @@ k_spmm_wide(WideArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[tm][tn][i] = 0.f;
 
-  // lane-constant LDS offsets of the operand reads
-  const uint32_t a_lds = (uint32_t)(lane * 16 + wm * TM * KSTEPS * 1024);
-  const uint32_t m_lds = (uint32_t)(lane * 4 + wm * TM * KSTEPS * 256);
+  // lane-constant LDS offsets of the operand reads: A operand of tile tm, step ks = row
+  // (wm*TM + tm)*32 + lane%32, chunk 2 ks + lane/32; its index word likewise
+  uint32_t a_lds[TM][KSTEPS], m_lds[TM][KSTEPS];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int R = (wm * TM + tm) * 32 + (lane & 31);
+      a_lds[tm][ks] = wide::a_offset<KS>(R, 2 * ks + (lane >> 5));
+      m_lds[tm][ks] = wide::m_offset<KS>(R, 2 * ks + (lane >> 5));
+    }
   uint32_t tr_lds[TN][4];
   {
     const int x = 8 * (lane >> 5) + ((lane & 15) >> 2);                       // row in a step
@@ -297,8 +310,8 @@ k_spmm_wide(WideArgs a) {
       h16 bf[TN];
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
-        af[tm] = *reinterpret_cast<const h8*>(smem + a_lds + (sb + Cfg::kAOff + (tm * KSTEPS + ks) * 1024));
-        ix[tm] = *reinterpret_cast<const uint32_t*>(smem + m_lds + (sb + Cfg::kMOff + (tm * KSTEPS + ks) * 256));
+        af[tm] = *reinterpret_cast<const h8*>(smem + a_lds[tm][ks] + (sb + Cfg::kAOff));
+        ix[tm] = *reinterpret_cast<const uint32_t*>(smem + m_lds[tm][ks] + (sb + Cfg::kMOff));
       }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {

@@ -8,11 +8,15 @@
 //               ds_read_b64_tr_b16 -- which touches rows x0..x0+3 of one 16-column cell in
 //               each 16-lane group, and cells 2j, 2j+1 in the two groups of a half-wave --
 //               hits every bank at most once per half-wave.
-//   A blocks    (BM/32) * KSTEPS blocks of 1 KiB: the 32x32x32 sparse-MFMA A operand of one
-//               32-row tile and one 32-position step, lane-major (lane l's 16 bytes at
-//               16*l), exactly as one 16-byte-per-lane DMA instruction writes them.
-//   metadata    the same number of 256-byte blocks: lane l's 16-bit index word at 4*l (the
-//               2-byte DMA form writes one zero-extended dword per lane).
+//   A values    a stage holds KS bytes of every row (KS/2 values); one 16-byte-per-lane DMA
+//               instruction fills a 1 KiB block of RPD = 1024/KS consecutive rows, row-major,
+//               whose 16-byte chunks are XOR-permuted by a function of the row so that the
+//               sparse-MFMA operand read (16 bytes of rows r..r+15 at one logical chunk per
+//               quarter-wave) touches every bank once. With KS = 64 one instruction reads 16
+//               rows x 64 bytes of the canonical array instead of 32 rows x 32 bytes.
+//   metadata    WPR = KS/16 index words per row; one 2-byte-per-lane DMA instruction (which
+//               writes one zero-extended dword per lane) fills a 256-byte block of RPM =
+//               64/WPR rows, lane = row * WPR + word.
 #pragma once
 
 #include <stdint.h>
@@ -46,6 +50,42 @@ constexpr int b_col_of(uint32_t o) {
   const int p = (int)(o % (2u * BN));
   return (((p >> 5) ^ cell_xor<BN>(x)) << 4) + ((p >> 4) & 1) * 8;
 }
+
+// ---- A values: stage of KS positions (KS bytes per row), blocks of RPD rows ----------------
+template <int KS>
+constexpr int a_rows_per_block() { return 1024 / KS; }
+// XOR applied to the 16-byte chunk index of row r (0 <= r < RPD) of a block
+template <int KS>
+constexpr int a_chunk_xor(int r) { return (r / (256 / KS)) % (KS / 16); }
+// byte offset inside the stage's A region of (row R of the tile, logical 16-byte chunk c)
+template <int KS>
+constexpr uint32_t a_offset(int R, int c) {
+  return (uint32_t)(R / a_rows_per_block<KS>()) * 1024u +
+         (uint32_t)(R % a_rows_per_block<KS>()) * (uint32_t)KS +
+         (uint32_t)((c ^ a_chunk_xor<KS>(R % a_rows_per_block<KS>())) * 16);
+}
+// DMA lane l of block b: tile row and logical chunk it fetches
+template <int KS>
+constexpr int a_dma_row(int b, int l) { return b * a_rows_per_block<KS>() + l / (KS / 16); }
+template <int KS>
+constexpr int a_dma_chunk(int l) {
+  return (l % (KS / 16)) ^ a_chunk_xor<KS>(l / (KS / 16));
+}
+
+// ---- metadata: WPR words per row per stage, blocks of RPM rows ------------------------------
+template <int KS>
+constexpr int m_words_per_row() { return KS / 16; }
+template <int KS>
+constexpr int m_rows_per_block() { return 64 / m_words_per_row<KS>(); }
+template <int KS>
+constexpr uint32_t m_offset(int R, int w) {
+  return (uint32_t)(R / m_rows_per_block<KS>()) * 256u +
+         (uint32_t)((R % m_rows_per_block<KS>()) * m_words_per_row<KS>() + w) * 4u;
+}
+template <int KS>
+constexpr int m_dma_row(int b, int l) { return b * m_rows_per_block<KS>() + l / m_words_per_row<KS>(); }
+template <int KS>
+constexpr int m_dma_word(int l) { return l % m_words_per_row<KS>(); }
 
 }  // namespace wide
 }  // namespace snm

@@ -48,9 +48,51 @@ int check() {
   return bad;
 }
 
+// A and metadata regions of a stage of KS positions for a BM-row tile: the DMA writes must
+// cover each (row, chunk) / (row, word) exactly once at the offset the operand reads use,
+// and a quarter-wave of operand reads (rows r0..r0+15 of a 32-row tile, one chunk) must
+// hit each 16-byte bank group of a 256-byte line once.
+template <int KS, int BM>
+int check_a() {
+  int bad = 0;
+  const int nblk = BM * KS / 1024;
+  std::set<unsigned> offs;
+  for (int b = 0; b < nblk; ++b)
+    for (int l = 0; l < 64; ++l) {
+      const int R = a_dma_row<KS>(b, l), c = a_dma_chunk<KS>(l);
+      if (R < 0 || R >= BM || c < 0 || c >= KS / 16) { ++bad; continue; }
+      if (a_offset<KS>(R, c) != (unsigned)(b * 1024 + l * 16)) ++bad;
+      offs.insert(a_offset<KS>(R, c));
+    }
+  if ((int)offs.size() != nblk * 64) ++bad;
+  for (int t = 0; t < BM / 32; ++t)
+    for (int c = 0; c < KS / 16; ++c)
+      for (int q = 0; q < 2; ++q) {
+        int hits[16] = {0};
+        for (int i = 0; i < 16; ++i) ++hits[(a_offset<KS>(t * 32 + 16 * q + i, c) / 16) % 16];
+        for (int k = 0; k < 16; ++k)
+          if (hits[k] != 1) { ++bad; break; }
+      }
+  std::set<unsigned> moffs;
+  const int nm = BM / m_rows_per_block<KS>();
+  if (nm != nblk) ++bad;
+  for (int b = 0; b < nm; ++b)
+    for (int l = 0; l < 64; ++l) {
+      const int R = m_dma_row<KS>(b, l), w = m_dma_word<KS>(l);
+      if (R >= BM || w >= KS / 16) { ++bad; continue; }
+      if (m_offset<KS>(R, w) != (unsigned)(b * 256 + l * 4)) ++bad;
+      moffs.insert(m_offset<KS>(R, w));
+    }
+  if ((int)moffs.size() != nm * 64) ++bad;
+  std::printf("A/meta KS=%d BM=%d bad=%d\n", KS, BM, bad);
+  return bad;
+}
+
 int main() {
   int bad = check<64, 32>() + check<64, 64>() + check<128, 32>() + check<128, 64>() +
             check<256, 32>() + check<256, 64>();
+  bad += check_a<32, 128>() + check_a<64, 128>() + check_a<64, 64>() + check_a<32, 64>() +
+         check_a<128, 128>() + check_a<128, 64>();
   return bad ? 1 : 0;
 }
 """
