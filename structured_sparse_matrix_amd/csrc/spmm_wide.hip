@@ -202,7 +202,7 @@ k_spmm_wide(WideArgs a) {
     const int bi = wave * nA + j;
     int64_t r = wide::a_dma_row<KS>(bi, lane);
     r = row0 + r < a.R ? r : a.R - 1 - row0;
-    aoff[j] = (uint32_t)(r * Kc + wide::a_dma_chunk<KS>(lane) * 16);
+    aoff[j] = (uint32_t)(r * Kc + wide::a_dma_chunk<KS>(bi, lane) * 16);
     int64_t rm = wide::m_dma_row<KS>(bi, lane);
     rm = row0 + rm < a.R ? rm : a.R - 1 - row0;
     moff[j] = (uint32_t)(rm * mrow + wide::m_dma_word<KS>(lane) * 2);
@@ -255,7 +255,7 @@ k_spmm_wide(WideArgs a) {
         const int bi = wave * nA + j;
         int64_t r = row0 + wide::a_dma_row<KS>(bi, lane);
         r = r < a.R ? r : a.R - 1;
-        int64_t p = s * KS + wide::a_dma_chunk<KS>(lane) * 16;   // first position of the chunk
+        int64_t p = s * KS + wide::a_dma_chunk<KS>(bi, lane) * 16;   // first position of the chunk
         p = p < Kc ? p : Kc - 16;
         dma_v<16>(vals + r * Kc + p, sb + (uint32_t)(Cfg::kAOff + bi * 1024));
         int64_t rm = row0 + wide::m_dma_row<KS>(bi, lane);

@@ -54,22 +54,23 @@ constexpr int b_col_of(uint32_t o) {
 // ---- A values: stage of KS positions (KS bytes per row), blocks of RPD rows ----------------
 template <int KS>
 constexpr int a_rows_per_block() { return 1024 / KS; }
-// XOR applied to the 16-byte chunk index of row r (0 <= r < RPD) of a block
+// XOR applied to the 16-byte chunk index of tile row R (16 consecutive rows get distinct
+// 16-byte slots of a 256-byte bank line)
 template <int KS>
-constexpr int a_chunk_xor(int r) { return (r / (256 / KS)) % (KS / 16); }
+constexpr int a_chunk_xor(int R) { return (R / (256 / KS)) % (KS / 16); }
 // byte offset inside the stage's A region of (row R of the tile, logical 16-byte chunk c)
 template <int KS>
 constexpr uint32_t a_offset(int R, int c) {
   return (uint32_t)(R / a_rows_per_block<KS>()) * 1024u +
          (uint32_t)(R % a_rows_per_block<KS>()) * (uint32_t)KS +
-         (uint32_t)((c ^ a_chunk_xor<KS>(R % a_rows_per_block<KS>())) * 16);
+         (uint32_t)((c ^ a_chunk_xor<KS>(R)) * 16);
 }
 // DMA lane l of block b: tile row and logical chunk it fetches
 template <int KS>
 constexpr int a_dma_row(int b, int l) { return b * a_rows_per_block<KS>() + l / (KS / 16); }
 template <int KS>
-constexpr int a_dma_chunk(int l) {
-  return (l % (KS / 16)) ^ a_chunk_xor<KS>(l / (KS / 16));
+constexpr int a_dma_chunk(int b, int l) {
+  return (l % (KS / 16)) ^ a_chunk_xor<KS>(a_dma_row<KS>(b, l));
 }
 
 // ---- metadata: WPR words per row per stage, blocks of RPM rows ------------------------------

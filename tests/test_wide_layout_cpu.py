@@ -59,7 +59,7 @@ int check_a() {
   std::set<unsigned> offs;
   for (int b = 0; b < nblk; ++b)
     for (int l = 0; l < 64; ++l) {
-      const int R = a_dma_row<KS>(b, l), c = a_dma_chunk<KS>(l);
+      const int R = a_dma_row<KS>(b, l), c = a_dma_chunk<KS>(b, l);
       if (R < 0 || R >= BM || c < 0 || c >= KS / 16) { ++bad; continue; }
       if (a_offset<KS>(R, c) != (unsigned)(b * 1024 + l * 16)) ++bad;
       offs.insert(a_offset<KS>(R, c));
