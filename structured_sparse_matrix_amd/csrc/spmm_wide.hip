@@ -93,7 +93,15 @@ __device__ __forceinline__ void lds_barrier() {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // m0 is set inside the statement
 template <int SIZE>
-__device__ __forceinline__ void dma_s(const void* sbase, uint32_t voff, uint32_t lds_byte) {
+__device__ __forceinline__ void dma_s(const void* sbase_in, uint32_t voff, uint32_t lds_byte) {
+  // the base is wave-uniform by construction; readfirstlane makes that explicit so the
+  // operand always lands in an SGPR pair
+  // (the builtin returns a signed int: widen through uint32_t, never sign-extend)
+  const uint64_t bv = (uint64_t)(uintptr_t)sbase_in;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bv >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bv);
+  const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const void* sbase = (const void*)(uintptr_t)bu;
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_byte);
   if constexpr (SIZE == 16)
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0) : "m0");
@@ -424,7 +432,7 @@ bool spmm_wide_eligible(int64_t R, int64_t Kc, int V, int M, const void* B, int6
   // per-lane DMA offsets are 32-bit: one tile's A rows, one stage's B rows
   constexpr int64_t kLim = (int64_t)1 << 31;
   if (128 * Kc >= kLim) return false;
-  const int64_t b_stage_rows = V > 0 ? 16 * (int64_t)M : 64;
+  const int64_t b_stage_rows = V > 0 ? 16 * (int64_t)M : 256;   // largest stage of any tile shape
   if ((b_stage_rows * ldb + C) * 2 >= kLim) return false;
   return true;
 }
@@ -452,7 +460,7 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
     }
     return launch_wide<1, 4, 2, 1, 2, 3, true>(a, stream);                  // 64 x 128
   }
-  if (C <= 64) return launch_wide<4, 1, 1, 2, 2, 4, false>(a, stream);      // 128 x 64
+  if (C <= 64) return launch_wide<4, 1, 1, 2, 4, 2, false>(a, stream);      // 128 x 64, 128-position stages
   if (C <= 128) return launch_wide<1, 4, 4, 1, 2, 3, false>(a, stream);     // 128 x 128
   return launch_wide<1, 4, 4, 2, 1, 3, false>(a, stream);                   // 128 x 256
 }
