@@ -295,7 +295,7 @@ def main():
         print(json.dumps(bench_other(args.workload, args.steps, args.warmup)))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import numpy as np
