@@ -271,6 +271,16 @@ def bench_other(workload: str, steps: int, warmup: int) -> dict:
         out["kernels"]["spmm_nm_PV"] = {"avg_us": t_pv * 1e6, "GB/s": (vbytes + mbytes + 2 * nb * L * d * 2) / t_pv / 1e9,
                                         "smfmac_TFLOP/s": 2 * nb * L * L * d / t_pv / 1e12}
         out["attention_total_us"] = (t_sd + t_sm + t_pv) * 1e6
+        # fused-softmax variant: the SDDMM also writes each row's largest kept score, the
+        # SpMM exponentiates and normalises on the fly (no separate pass over the scores)
+        vals2, meta2, rmax = snm.sddmm_prune_nm_rowmax(Qd, Kd, 1.0 / np.sqrt(d))
+        t_sdr = timed(lambda j: snm.sddmm_prune_nm_rowmax(Qd, Kd, 1.0 / np.sqrt(d)))
+        t_pvs = timed(lambda j: snm.spmm_nm_softmax(vals2, meta2, rmax, Vd, out=O))
+        out["kernels"]["sddmm_prune_nm_rowmax"] = {
+            "avg_us": t_sdr * 1e6, "GB/s": (vbytes + mbytes + 4 * nb * L + 2 * nb * L * d * 2) / t_sdr / 1e9}
+        out["kernels"]["spmm_nm_softmax_PV"] = {
+            "avg_us": t_pvs * 1e6, "GB/s": (vbytes + mbytes + 4 * nb * L + 2 * nb * L * d * 2) / t_pvs / 1e9}
+        out["attention_fused_total_us"] = (t_sdr + t_pvs) * 1e6
     return out
 
 

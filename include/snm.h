@@ -158,6 +158,36 @@ int snm_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t L
                        int64_t Lk, int64_t d, float scale, void* values, void* meta,
                        void* S_dense, void* stream);
 
+/* Fused-softmax variant of dynamic 2:4 attention ("Dynamic N:M ... attention", Sec. 3.2:
+ * softmax acts on each row's kept entries only, and the SDDMM epilogue is the place that
+ * sees a whole row of scores). Instead of a separate softmax pass over the compressed
+ * scores, the SDDMM also reports each row's largest kept score and the SpMM turns the
+ * scores into probabilities as it multiplies.
+ *
+ * snm_sddmm_prune_nm_rowmax: exactly snm_sddmm_prune_nm (no S_dense) and, in addition,
+ *   row_max  fp32 [batch, Lq]: the largest kept (fp16) score of each row, widened exactly.
+ * Requires what snm_sddmm_prune_nm requires; row_max 4-byte aligned. */
+int snm_sddmm_prune_nm_rowmax(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                              int64_t Lk, int64_t d, float scale, void* values, void* meta,
+                              float* row_max, void* stream);
+
+/* snm_spmm_nm_softmax: Y = P * B with P the row softmax of the kept scores (dropped entries
+ * count as -inf), decoded through meta: per row, p = fp16_RNE(exp(v - row_max)) for each
+ * kept score v (exp in fp32), the products accumulate in fp32, and the output row is
+ * divided by the fp32 sum of its p values before rounding to fp16 (RNE).
+ *   values, meta  2:4 scores as written by snm_sddmm_prune_nm (canonical layout), per batch
+ *                 entry at values + b*stride_values and meta + b*stride_meta (bytes).
+ *   row_max       fp32, R per batch entry at row_max + b*stride_row_max: a value >= every
+ *                 kept score of the row (snm_sddmm_prune_nm_rowmax writes the maximum);
+ *                 any such value gives the same P up to rounding.
+ *   B, Y          as in snm_spmm_nm with b_layout 0 (row-major B).
+ * Requires K % 16 == 0 and K > 0, C % 8 == 0, ldb % 8 == 0, B 16-byte aligned (and
+ * stride_B % 8 == 0 when batch > 1), 128*K < 2^31 and (256*ldb + C)*2 < 2^31. */
+int snm_spmm_nm_softmax(const void* values, const void* meta, const float* row_max, int64_t R,
+                        int64_t K, const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                        int64_t batch, int64_t stride_values, int64_t stride_meta,
+                        int64_t stride_row_max, int64_t stride_B, int64_t stride_Y, void* stream);
+
 /* In-place row softmax over the kept entries of compressed rows ("Dynamic N:M ...
  * attention", Sec. 3.2: softmax runs only on each row's kept entries; dropped
  * entries count as -inf). values: fp16 rows x kept, leading dimension ld >= kept.

@@ -20,6 +20,7 @@ __all__ = [
     "prune_encode_nm", "prune_encode_vnm", "spmm_nm", "spmm_vnm", "sddmm_prune_nm",
     "softmax_nm_rows", "attention_nm", "nm_sizes", "vnm_sizes", "abi_version", "SnmError",
     "nm_tiled_sizes", "prune_encode_nm_tiled", "spmm_nm_tiled",
+    "sddmm_prune_nm_rowmax", "spmm_nm_softmax", "attention_nm_fused",
     "LIB_PATH",
 ]
 
@@ -237,6 +238,66 @@ def sddmm_prune_nm(Q, Kmat, scale=None, return_dense=False):
     return (values, meta, S) if return_dense else (values, meta)
 
 
+def sddmm_prune_nm_rowmax(Q, Kmat, scale=None):
+    """As sddmm_prune_nm, plus row_max fp32 [b, Lq]: the largest kept score of each row."""
+    torch = _torch()
+    _need(Q, "Q", torch.float16, 3)
+    _need(Kmat, "Kmat", torch.float16, 3)
+    if not (Q.is_contiguous() and Kmat.is_contiguous()):
+        raise ValueError("Q and Kmat must be contiguous")
+    nb, Lq, d = Q.shape
+    if Kmat.shape[0] != nb or Kmat.shape[2] != d:
+        raise ValueError("Q and Kmat disagree in batch or head_dim")
+    Lk = Kmat.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    values = torch.empty((nb, Lq, Lk // 2), dtype=torch.float16, device=Q.device)
+    meta = torch.empty((nb, Lq, Lk // 8), dtype=torch.uint8, device=Q.device)
+    row_max = torch.empty((nb, Lq), dtype=torch.float32, device=Q.device)
+    check("snm_sddmm_prune_nm_rowmax",
+          load().snm_sddmm_prune_nm_rowmax(_ptr(Q), _ptr(Kmat), nb, Lq, Lk, d, float(scale), _ptr(values),
+                                           _ptr(meta), _ptr(row_max), _stream(Q)))
+    return values, meta, row_max
+
+
+def spmm_nm_softmax(values, meta, row_max, B, out=None):
+    """Y = softmax_kept(values) decoded through meta, times B: the row softmax over the kept
+    scores is applied inside the product. 2-D: values [R, K/2], meta [R, K/8], row_max [R],
+    B [K, C] -> Y [R, C]; 3-D: one more leading batch axis on every argument."""
+    torch = _torch()
+    _need(values, "values", torch.float16, (2, 3))
+    _need(meta, "meta", torch.uint8, values.dim())
+    _need(row_max, "row_max", torch.float32, values.dim() - 1)
+    _need(B, "B", torch.float16, values.dim())
+    batched = values.dim() == 3
+    if not batched:
+        values, meta, row_max, B = values[None], meta[None], row_max[None], B[None]
+    nb, R, half_k = values.shape
+    K = 2 * half_k
+    if B.shape[0] != nb or B.shape[1] != K or meta.shape != (nb, R, K // 8) or row_max.shape != (nb, R):
+        raise ValueError(f"shape mismatch: values {tuple(values.shape)}, meta {tuple(meta.shape)}, "
+                         f"row_max {tuple(row_max.shape)}, B {tuple(B.shape)}")
+    for t, n in ((values, "values"), (meta, "meta")):
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{n} must be contiguous per batch entry")
+    if row_max.stride(1) != 1:
+        raise ValueError("row_max must be contiguous per batch entry")
+    if B.stride(2) != 1:
+        raise ValueError("B must be row-major (unit stride along C)")
+    C = B.shape[2]
+    if out is None:
+        out = torch.empty((nb, R, C), dtype=torch.float16, device=B.device)
+    elif not batched:
+        out = out[None]
+    if out.stride(2) != 1:
+        raise ValueError("out must be row-major")
+    check("snm_spmm_nm_softmax",
+          load().snm_spmm_nm_softmax(_ptr(values), _ptr(meta), _ptr(row_max), R, K, _ptr(B), C, B.stride(1),
+                                     _ptr(out), out.stride(1), nb, values.stride(0), meta.stride(0),
+                                     row_max.stride(0), B.stride(0), out.stride(0), _stream(B)))
+    return out if batched else out[0]
+
+
 def softmax_nm_rows(values):
     """In-place softmax over the last axis of compressed rows (kept entries only)."""
     torch = _torch()
@@ -258,3 +319,11 @@ def attention_nm(Q, Kmat, Vmat, scale=None):
     values, meta = sddmm_prune_nm(Q, Kmat, scale)
     softmax_nm_rows(values)
     return spmm_nm(values, meta, Vmat)
+
+
+def attention_nm_fused(Q, Kmat, Vmat, scale=None):
+    """Dynamic 2:4 attention with the softmax folded into the two kernels: the SDDMM also
+    writes each row's largest kept score, and the SpMM exponentiates and normalises.
+    Same arguments and result as attention_nm."""
+    values, meta, row_max = sddmm_prune_nm_rowmax(Q, Kmat, scale)
+    return spmm_nm_softmax(values, meta, row_max, Vmat)

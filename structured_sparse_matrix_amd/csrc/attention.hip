@@ -43,11 +43,13 @@ struct SddmmCfg {
 };
 
 // DENSE: also write the pre-prune fp16 S (the optional debug output).
-template <int D, int QT, bool DENSE>
+// RMAX: also write, per query row, the largest kept score (the fused-softmax variant's
+// statistic; a packed fp16 running maximum per lane, two lanes per row).
+template <int D, int QT, bool DENSE, bool RMAX>
 __global__ void __launch_bounds__(512)
 k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, int64_t batch,
               int64_t Lq, int64_t Lk, float scale, uint16_t* __restrict__ values,
-              uint16_t* __restrict__ meta, uint16_t* __restrict__ S) {
+              uint16_t* __restrict__ meta, uint16_t* __restrict__ S, float* __restrict__ rowmax) {
   using Cfg = SddmmCfg<D, QT>;
   constexpr int KSTEPS = Cfg::KSTEPS, KT = Cfg::KT, MT = Cfg::MT, VP = Cfg::VP, MP = Cfg::MP;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -58,8 +60,6 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
   uint8_t* const sv = smem + wave * Cfg::kWaveV;
   uint8_t* const sm = smem + Cfg::kWaves * Cfg::kWaveV + wave * Cfg::kWaveM;
   const int64_t q_wave = (int64_t)blockIdx.x * Cfg::kQueries + (int64_t)wave * 32 * QT;
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
   const int64_t nkt = Lk >> 5;         // key tiles (Lk % 32 == 0)
 
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
@@ -95,6 +95,9 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
     load_k(0, kr[0]);
     load_k(1, kr[1]);
     load_k(2, kr[2]);
+    hh2 rmx[QT];   // running max of the kept scores of each query tile's row (RMAX)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) rmx[qt] = hh2{(_Float16)-__builtin_inff(), (_Float16)-__builtin_inff()};
 
     for (int64_t t0 = 0; t0 < nkt; t0 += KT) {
       const int nk = (int)(nkt - t0 < KT ? nkt - t0 : KT);
@@ -131,6 +134,7 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
             }
             uint32_t kept;
             const uint32_t code = select_2of4_keys(p01, p23, kept);
+            if constexpr (RMAX) rmx[qt] = __builtin_elementwise_max(rmx[qt], __builtin_bit_cast(hh2, kept));
             // kept pair of group (kk + 8gi + 4half)/4 -> value position kt*16 + 4gi + 2half
             *reinterpret_cast<uint32_t*>(sv + (qt * 32 + l32) * VP + (kt * 16 + 4 * gi + 2 * half) * 2) = kept;
             mword |= code << (8 * gi + 4 * half);
@@ -177,6 +181,15 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
             }
           }
         }
+      }
+    }
+    if constexpr (RMAX) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float m = fmaxf((float)rmx[qt][0], (float)rmx[qt][1]);
+        m = fmaxf(m, __shfl_xor(m, 32));   // lanes l and l+32 hold the two halves of a row
+        const int64_t qi = q_wave + qt * 32 + l32;
+        if (!half && qi < Lq) rowmax[b * Lq + qi] = m;
       }
     }
   }
@@ -242,44 +255,46 @@ k_softmax_rows(uint16_t* __restrict__ vals, int64_t rows, int64_t kept, int64_t 
   for (int64_t e = lane; e < kept; e += 64) v[e] = f16_bits(to_f16(__expf((float)bits_f16(v[e]) - mx) * inv));
 }
 
-template <int D, int QT, bool DENSE>
+template <int D, int QT, bool DENSE, bool RMAX>
 static hipError_t launch_sddmm_cfg1(const uint16_t* q, const uint16_t* k, int64_t batch, int64_t Lq,
                                    int64_t Lk, float scale, uint16_t* vv, uint16_t* mm, uint16_t* ss,
-                                   hipStream_t stream) {
+                                   float* rmax, hipStream_t stream) {
   using Cfg = SddmmCfg<D, QT>;
   const int64_t qblocks = (Lq + Cfg::kQueries - 1) / Cfg::kQueries;
   const dim3 grid((unsigned)qblocks, (unsigned)(batch < 65535 ? batch : 65535));
-  auto kern = k_sddmm_prune<D, QT, DENSE>;
+  auto kern = k_sddmm_prune<D, QT, DENSE, RMAX>;
   static bool attr_set = false;   // benign race: every caller sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, grid, dim3(64 * Cfg::kWaves), Cfg::kLds, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * Cfg::kWaves), Cfg::kLds, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax);
   return hipGetLastError();
 }
 template <int D, int QT>
 static hipError_t launch_sddmm_cfg(const uint16_t* q, const uint16_t* k, int64_t batch, int64_t Lq,
                                    int64_t Lk, float scale, uint16_t* vv, uint16_t* mm, uint16_t* ss,
-                                   hipStream_t stream) {
-  if (ss) return launch_sddmm_cfg1<D, QT, true>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
-  return launch_sddmm_cfg1<D, QT, false>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
+                                   float* rmax, hipStream_t stream) {
+  if (ss && rmax) return launch_sddmm_cfg1<D, QT, true, true>(q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax, stream);
+  if (ss) return launch_sddmm_cfg1<D, QT, true, false>(q, k, batch, Lq, Lk, scale, vv, mm, ss, nullptr, stream);
+  if (rmax) return launch_sddmm_cfg1<D, QT, false, true>(q, k, batch, Lq, Lk, scale, vv, mm, nullptr, rmax, stream);
+  return launch_sddmm_cfg1<D, QT, false, false>(q, k, batch, Lq, Lk, scale, vv, mm, nullptr, nullptr, stream);
 }
 
 hipError_t launch_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
                                  int64_t Lk, int64_t d, float scale, void* values, void* meta,
-                                 void* S_dense, hipStream_t stream) {
+                                 void* S_dense, float* row_max, hipStream_t stream) {
   const uint16_t* q = (const uint16_t*)Q;
   const uint16_t* k = (const uint16_t*)Kmat;
   uint16_t* vv = (uint16_t*)values;
   uint16_t* mm = (uint16_t*)meta;
   uint16_t* ss = (uint16_t*)S_dense;
   switch (d) {
-    case 16: return launch_sddmm_cfg<16, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
-    case 32: return launch_sddmm_cfg<32, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
-    case 64: return launch_sddmm_cfg<64, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
-    default: return launch_sddmm_cfg<128, 1>(q, k, batch, Lq, Lk, scale, vv, mm, ss, stream);
+    case 16: return launch_sddmm_cfg<16, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, row_max, stream);
+    case 32: return launch_sddmm_cfg<32, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, row_max, stream);
+    case 64: return launch_sddmm_cfg<64, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, row_max, stream);
+    default: return launch_sddmm_cfg<128, 1>(q, k, batch, Lq, Lk, scale, vv, mm, ss, row_max, stream);
   }
 }
 

@@ -31,8 +31,12 @@ hipError_t launch_spmm_nm_skinny(const void* values, const void* meta, int64_t R
 hipError_t launch_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R,
                            int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
                            int64_t ldy, hipStream_t stream);
-// Wide-output SpMM (spmm_wide.hip): row-major B, C > 32. V > 0 selects V:2:M with
-// column-loc gathering (Kc = 4K/M); V == 0 is plain 2:4 (Kc = K), optionally batched.
+// Wide-output SpMM (spmm_wide.hip): row-major B. V > 0 selects V:2:M with column-loc
+// gathering (Kc = 4K/M); V == 0 is plain 2:4 (Kc = K), optionally batched.
+// supported: the kernel can run the shape (C % 8 == 0, 16-byte B rows, 32-bit offsets);
+// eligible: supported and C > 32, where it is the fastest kernel.
+bool spmm_wide_supported(int64_t R, int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb,
+                         int64_t batch, int64_t stride_B);
 bool spmm_wide_eligible(int64_t R, int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb,
                         int64_t batch, int64_t stride_B);
 hipError_t launch_spmm_wide(const void* values, const void* meta, const void* colloc, int64_t R,
@@ -40,9 +44,15 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
                             void* Y, int64_t ldy, int64_t batch, int64_t stride_values,
                             int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
                             hipStream_t stream);
+// 2:4 SpMM that applies the softmax over each row's kept scores (wide kernel, softmax mode).
+hipError_t launch_spmm_nm_softmax(const void* values, const void* meta, const float* row_max,
+                                  int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb,
+                                  void* Y, int64_t ldy, int64_t batch, int64_t stride_values,
+                                  int64_t stride_meta, int64_t stride_row_max, int64_t stride_B,
+                                  int64_t stride_Y, hipStream_t stream);
 hipError_t launch_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
                                  int64_t Lk, int64_t d, float scale, void* values, void* meta,
-                                 void* S_dense, hipStream_t stream);
+                                 void* S_dense, float* row_max, hipStream_t stream);
 hipError_t launch_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld,
                                   hipStream_t stream);
 

@@ -43,8 +43,9 @@ struct WideArgs {
   const uint16_t* B;        // fp16 bits, row-major, ldb (a multiple of 8)
   uint16_t* Y;              // fp16 bits, R x C (ldy)
   const uint8_t* colloc;    // V:2:M: (R/V) x Kc bytes (Kc/4 groups x 4 column indices)
+  const float* rowmax;      // softmax mode: fp32 per row (R per batch entry, stride_rowmax)
   int64_t R, Kc, C, ldb, ldy;
-  int64_t stride_values, stride_meta, stride_B, stride_Y, batch;
+  int64_t stride_values, stride_meta, stride_B, stride_Y, stride_rowmax, batch;
   int64_t n_row_tiles, n_tiles;   // tiles per batch entry = n_row_tiles * column tiles
   int V, M;
   int xcd_remap;                  // total workgroups are a multiple of 8
@@ -149,9 +150,16 @@ __device__ __forceinline__ void static_for(F&& f) {
 // (only a gathered B row needs one multiply-add), the stage loop is unrolled by the ring
 // depth so every LDS read is a lane-constant register plus an immediate, and all clamping
 // of ragged edges is confined to the last, partial stage.
-template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER>
+//
+// SMAX (2:4 only): the stored values are attention scores and the product applies the
+// softmax over each row's kept entries on the fly. Every A operand value v becomes
+// fp16(exp(v - rowmax)) in registers before it enters the matrix core, the lane keeps an
+// fp32 sum of exactly those fp16 numbers for its row, and the epilogue divides each
+// output row by its sum. With WN == 1 no two waves exponentiate the same operand.
+template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER, bool SMAX>
 __global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
 k_spmm_wide(WideArgs a) {
+  static_assert(!(SMAX && GATHER), "the softmax mode is defined for 2:4 scores only");
   using Cfg = WideCfg<WM, WN, TM, TN, KSTEPS, NST, GATHER>;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, KS = Cfg::KS;
   constexpr int nB = Cfg::nB, nA = Cfg::nA;
@@ -283,6 +291,21 @@ k_spmm_wide(WideArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[tm][tn][i] = 0.f;
 
+  // softmax mode: row maximum in log2 units and the running sum of this lane's share of
+  // its row (lanes l and l + 32 hold the two halves of row l of each 32-row tile)
+  constexpr float kLog2e = 1.4426950408889634f;
+  float mx2[TM], rsum[TM];
+  if constexpr (SMAX) {
+    const float* __restrict__ rmx = a.rowmax + bt * a.stride_rowmax;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      int64_t r = row0 + (wm * TM + tm) * 32 + (lane & 31);
+      r = r < a.R ? r : a.R - 1;
+      mx2[tm] = rmx[r] * kLog2e;
+      rsum[tm] = 0.f;
+    }
+  }
+
   // lane-constant LDS offsets of the operand reads: A operand of tile tm, step ks = row
   // (wm*TM + tm)*32 + lane%32, chunk 2 ks + lane/32; its index word likewise
   uint32_t a_lds[TM][KSTEPS], m_lds[TM][KSTEPS];
@@ -321,6 +344,19 @@ k_spmm_wide(WideArgs a) {
         af[tm] = *reinterpret_cast<const h8*>(smem + a_lds[tm][ks] + (sb + Cfg::kAOff));
         ix[tm] = *reinterpret_cast<const uint32_t*>(smem + m_lds[tm][ks] + (sb + Cfg::kMOff));
       }
+      if constexpr (SMAX) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            f2 x;
+            x[0] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)af[tm][e], kLog2e, -mx2[tm]));
+            x[1] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)af[tm][e + 1], kLog2e, -mx2[tm]));
+            const hh2 p = __builtin_convertvector(x, hh2);
+            af[tm][e] = p[0];
+            af[tm][e + 1] = p[1];
+          }
+      }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
         const uint32_t so = sb + (uint32_t)(ks * 64 * BN);   // 32 rows of 2*BN bytes
@@ -347,6 +383,14 @@ k_spmm_wide(WideArgs a) {
         for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
           for (int e = 8; e < 16; ++e) bf[tn][e] = (_Float16)0.f;
+      }
+      if constexpr (SMAX) {   // sum of the fp16 probabilities the matrix core multiplies
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            rsum[tm] = __builtin_amdgcn_fdot2(hh2{af[tm][e], af[tm][e + 1]}, hh2{(_Float16)1.f, (_Float16)1.f},
+                                              rsum[tm], false);
       }
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
@@ -385,19 +429,30 @@ k_spmm_wide(WideArgs a) {
 
   // ---- epilogue: fp32 -> fp16 (RNE) ------------------------------------------------------
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
+  for (int tm = 0; tm < TM; ++tm) {
+    // softmax mode: 1 / row sum for each of the lane's 16 output rows (row 8(i/4) + 4(l/32)
+    // + i%4 of the tile, whose sum lanes r and r + 32 share)
+    float inv[16];
+    if constexpr (SMAX) {
+      const float tot = rsum[tm] + __shfl_xor(rsum[tm], 32);
+      const float rinv = 1.0f / tot;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) inv[i] = __shfl(rinv, 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3));
+    }
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       const int64_t col = col0 + (wn * TN + tn) * 32 + (lane & 31);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int64_t row = row0 + (wm * TM + tm) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (row < a.R && col < a.C) Y[row * a.ldy + col] = f16_bits(to_f16(acc[tm][tn][i]));
+        const float y = SMAX ? acc[tm][tn][i] * inv[i] : acc[tm][tn][i];
+        if (row < a.R && col < a.C) Y[row * a.ldy + col] = f16_bits(to_f16(y));
       }
     }
+  }
 }
 
-template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER>
+template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER, bool SMAX = false>
 hipError_t launch_wide(WideArgs a, hipStream_t stream) {
   using Cfg = WideCfg<WM, WN, TM, TN, KSTEPS, NST, GATHER>;
   a.n_row_tiles = (a.R + Cfg::BM - 1) / Cfg::BM;
@@ -408,7 +463,7 @@ hipError_t launch_wide(WideArgs a, hipStream_t stream) {
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
   a.xcd_remap = (total % 8) == 0;
   const size_t lds = (size_t)Cfg::kRing + (GATHER ? (size_t)(a.Kc + 2 * Cfg::KS) : 0);
-  auto kern = k_spmm_wide<WM, WN, TM, TN, KSTEPS, NST, GATHER>;
+  auto kern = k_spmm_wide<WM, WN, TM, TN, KSTEPS, NST, GATHER, SMAX>;
   static bool attr_set = false;   // benign race: every caller sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -425,7 +480,12 @@ constexpr int64_t kMaxGatherKc = 16384;   // column-loc of one V-block staged in
 
 bool spmm_wide_eligible(int64_t R, int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb,
                         int64_t batch, int64_t stride_B) {
-  if (R <= 0 || Kc <= 0 || C <= 32 || C % 8 != 0 || ldb % 8 != 0) return false;
+  return C > 32 && spmm_wide_supported(R, Kc, V, M, B, C, ldb, batch, stride_B);
+}
+
+bool spmm_wide_supported(int64_t R, int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb,
+                         int64_t batch, int64_t stride_B) {
+  if (R <= 0 || Kc <= 0 || C <= 0 || C % 8 != 0 || ldb % 8 != 0) return false;
   if (((uintptr_t)B & 15) != 0) return false;
   if (batch > 1 && stride_B % 8 != 0) return false;
   if (V > 0 && (V % 64 != 0 || Kc > kMaxGatherKc)) return false;
@@ -463,6 +523,33 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
   if (C <= 64) return launch_wide<4, 1, 1, 2, 4, 2, false>(a, stream);      // 128 x 64, 128-position stages
   if (C <= 128) return launch_wide<1, 4, 4, 1, 2, 3, false>(a, stream);     // 128 x 128
   return launch_wide<1, 4, 4, 2, 1, 3, false>(a, stream);                   // 128 x 256
+}
+
+}  // namespace snm
+
+namespace snm {
+
+hipError_t launch_spmm_nm_softmax(const void* values, const void* meta, const float* row_max,
+                                  int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb,
+                                  void* Y, int64_t ldy, int64_t batch, int64_t stride_values,
+                                  int64_t stride_meta, int64_t stride_row_max, int64_t stride_B,
+                                  int64_t stride_Y, hipStream_t stream) {
+  if (!spmm_wide_supported(R, K, 0, 4, B, C, ldb, batch, stride_B)) return hipErrorInvalidValue;
+  WideArgs a{};
+  a.values = (const uint16_t*)values;
+  a.meta = (const uint8_t*)meta;
+  a.B = (const uint16_t*)B;
+  a.Y = (uint16_t*)Y;
+  a.rowmax = row_max;
+  a.R = R; a.Kc = K; a.C = C; a.ldb = ldb; a.ldy = ldy;
+  a.batch = batch < 1 ? 1 : batch;
+  a.stride_values = stride_values; a.stride_meta = stride_meta;
+  a.stride_B = stride_B; a.stride_Y = stride_Y; a.stride_rowmax = stride_row_max;
+  a.V = 0; a.M = 4;
+  // one wave column (WN = 1) so each score is exponentiated once per column tile
+  if (C <= 64) return launch_wide<4, 1, 1, 2, 4, 2, false, true>(a, stream);    // 128 x 64
+  if (C <= 128) return launch_wide<4, 1, 1, 4, 2, 3, false, true>(a, stream);   // 128 x 128
+  return launch_wide<4, 1, 1, 4, 2, 3, false, true>(a, stream);                 // 128 x 128 strips
 }
 
 }  // namespace snm

@@ -19,6 +19,13 @@ int check_spmm_vnm(const void* values, const void* midx, const void* colloc, int
                    int V, int M, const void* B, int64_t C, int64_t ldb, const void* Y, int64_t ldy);
 int check_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq, int64_t Lk,
                          int64_t d, const void* values, const void* meta, const void* S_dense);
+int check_sddmm_prune_nm_rowmax(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                                int64_t Lk, int64_t d, const void* values, const void* meta,
+                                const void* row_max);
+int check_spmm_nm_softmax(const void* values, const void* meta, const void* row_max, int64_t R,
+                          int64_t K, const void* B, int64_t C, int64_t ldb, const void* Y,
+                          int64_t ldy, int64_t batch, int64_t stride_values, int64_t stride_meta,
+                          int64_t stride_row_max, int64_t stride_B, int64_t stride_Y);
 int check_softmax_nm_rows(const void* values, int64_t rows, int64_t kept, int64_t ld);
 
 }  // namespace snm

@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("snm_prune_encode_nm", "snm_prune_encode_vnm", "snm_spmm_nm", "snm_spmm_vnm",
-              "snm_sddmm_prune_nm", "snm_softmax_nm_rows"):
+              "snm_sddmm_prune_nm", "snm_softmax_nm_rows", "snm_sddmm_prune_nm_rowmax",
+              "snm_spmm_nm_softmax"):
         assert n in names
 
 
@@ -136,6 +137,33 @@ def test_spmm_vnm_validation(args, status):
 ])
 def test_sddmm_validation(args, status):
     assert _lib().snm_sddmm_prune_nm(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, 1, 16, 32, 48, ctypes.c_float(0.125), FAKE, FAKE, FAKE, P(0)), 4),   # d unsupported
+    ((FAKE, FAKE, 1, 16, 32, 64, ctypes.c_float(0.125), FAKE, FAKE, P(0), P(0)), 1),   # row_max NULL
+    ((FAKE, FAKE, 1, 16, 32, 64, ctypes.c_float(0.125), FAKE, FAKE, P(0x1002), P(0)), 3),  # row_max % 4
+    ((P(0), P(0), 0, 16, 32, 64, ctypes.c_float(0.125), P(0), P(0), P(0), P(0)), 0),   # empty batch
+])
+def test_sddmm_rowmax_validation(args, status):
+    assert _lib().snm_sddmm_prune_nm_rowmax(*args) == status
+
+
+# values, meta, row_max, R, K, B, C, ldb, Y, ldy, batch, s_values, s_meta, s_rowmax, s_B, s_Y, stream
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, FAKE, 16, 24, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)), 2),      # K % 16
+    ((FAKE, FAKE, P(0), 16, 32, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)), 1),      # row_max NULL
+    ((FAKE, FAKE, FAKE, 16, 32, FAKE, 12, 12, FAKE, 12, 1, 0, 0, 0, 0, 0, P(0)), 3),   # C % 8
+    ((FAKE, FAKE, FAKE, 16, 32, FAKE, 8, 12, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)), 3),     # ldb % 8
+    ((FAKE, FAKE, FAKE, 16, 32, P(0x1008), 8, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)), 3),  # B 16-byte alignment
+    ((FAKE, FAKE, P(0x1002), 16, 32, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)), 3),  # row_max % 4
+    ((FAKE, FAKE, FAKE, 16, 0, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)), 2),       # K == 0: no softmax
+    ((FAKE, FAKE, FAKE, 16, 32, FAKE, 8, 8, FAKE, 8, 2, 256, 64, 8, 256, 128, P(0)), 2),  # stride_row_max < R
+    ((FAKE, FAKE, FAKE, 16, 1 << 24, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)), 2),  # 128*K >= 2^31
+    ((P(0), P(0), P(0), 0, 32, P(0), 8, 8, P(0), 8, 1, 0, 0, 0, 0, 0, P(0)), 0),       # R == 0: ok
+])
+def test_spmm_softmax_validation(args, status):
+    assert _lib().snm_spmm_nm_softmax(*args) == status
 
 
 def test_softmax_validation():

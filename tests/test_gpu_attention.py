@@ -136,3 +136,112 @@ def test_attention_workload_sampled_heads():
         assert_fp16_close(O[h:h + 1, qrows], O_ref, f"O head {h}")
         if h in (0, 37):
             assert_fp16_close(to_host(P[h:h + 1]), P_ref, f"P head {h}")
+
+
+# ---- fused-softmax variant: SDDMM emits each row's largest kept score, SpMM normalises ----
+
+@pytest.mark.parametrize("b,lq,lk,d", [(1, 32, 32, 64), (2, 100, 64, 64), (3, 257, 96, 16),
+                                       (2, 64, 128, 32), (1, 40, 64, 128), (2, 512, 512, 64)])
+def test_sddmm_rowmax(b, lq, lk, d):
+    # values and meta are those of the plain entry point, bit for bit; row_max is exactly the
+    # largest kept fp16 score of each row, widened to fp32
+    snm = _snm()
+    Q, K, _ = _qkv(b * 1000 + lq + lk + d, b, lq, lk, d)
+    scale = 1.0 / np.sqrt(d)
+    dQ, dK = to_dev(Q), to_dev(K)
+    v0, m0 = snm.sddmm_prune_nm(dQ, dK, scale)
+    v, m, rmax = snm.sddmm_prune_nm_rowmax(dQ, dK, scale)
+    v, m, rmax = to_host(v), to_host(m), to_host(rmax)
+    assert_bits_equal(v, to_host(v0), "values")
+    assert_bits_equal(m, to_host(m0), "meta")
+    assert rmax.dtype == np.float32 and rmax.shape == (b, lq)
+    assert_bits_equal(rmax, v.astype(np.float32).max(-1), "row_max")
+
+
+def _scores_problem(seed, b, R, K, C, sigma):
+    """Random fp16 scores S [b, R, K] pruned 2:4 by the oracle, and B [b, K, C]."""
+    rng = np.random.default_rng(seed)
+    S = workloads.normal_f16(rng, (b, R, K), sigma)
+    B = workloads.normal_f16(rng, (b, K, C))
+    values, meta = oracle.prune_encode_nm(S.reshape(b * R, K))
+    return S, values.reshape(b, R, K // 2), meta.reshape(b, R, K // 8), B
+
+
+@pytest.mark.parametrize("b,R,K,C,sigma", [
+    (1, 32, 32, 64, 1.0), (2, 100, 64, 64, 2.0), (1, 130, 48, 72, 1.0), (1, 257, 80, 8, 1.0), (3, 64, 80, 24, 1.0),
+    (2, 64, 128, 16, 4.0), (1, 40, 256, 128, 1.0), (1, 200, 512, 136, 1.0), (2, 129, 2048, 64, 8.0),
+    (1, 64, 4096, 32, 1.0)])
+def test_spmm_softmax_vs_oracle(b, R, K, C, sigma):
+    # inputs made by the oracle (2:4 of random scores); the oracle's float64 softmax over the
+    # kept entries times B is the reference; row_max is the true maximum
+    snm = _snm()
+    S, values, meta, B = _scores_problem(R * 7 + K + C, b, R, K, C, sigma)
+    _, O_ref = oracle.attention.attention_from_pattern(S, meta, B)
+    rmax = values.astype(np.float32).max(-1)
+    Y = snm.spmm_nm_softmax(to_dev(values), to_dev(meta), to_dev(rmax), to_dev(B))
+    assert_fp16_close(to_host(Y), O_ref, f"spmm_softmax {b}x{R}x{K}x{C}")
+
+
+def test_spmm_softmax_shift_invariant():
+    # any row_max >= the row's largest kept score gives the same probabilities
+    snm = _snm()
+    S, values, meta, B = _scores_problem(11, 2, 96, 256, 64, 2.0)
+    _, O_ref = oracle.attention.attention_from_pattern(S, meta, B)
+    rmax = values.astype(np.float32).max(-1) + np.float32(3.0)
+    Y = snm.spmm_nm_softmax(to_dev(values), to_dev(meta), to_dev(rmax), to_dev(B))
+    assert_fp16_close(to_host(Y), O_ref, "shifted row_max")
+
+
+def test_spmm_softmax_constant_rows():
+    # equal kept scores: every exponential is 1 and the row sum is kept = 128, a power of
+    # two, so the output is the exact mean of the kept rows of B, rounded once
+    snm = _snm()
+    b, R, K, C = 1, 64, 256, 64
+    values = np.full((b, R, K // 2), 0.75, dtype=np.float16)
+    codes = np.full((b * R, K // 4), 0x4, dtype=np.int64)           # slots 0 and 1 of each group
+    meta = oracle.nm._pack_codes(codes).reshape(b, R, K // 8)
+    # multiples of 1/64 below 8 in magnitude: every fp32 partial sum is exact
+    B = (np.round(workloads.small_matrix(5, (b, K, C)).astype(np.float64) * 64) / 64).astype(np.float16)
+    rmax = np.full((b, R), 0.75, dtype=np.float32)
+    Y = to_host(snm.spmm_nm_softmax(to_dev(values), to_dev(meta), to_dev(rmax), to_dev(B)))
+    kept_rows = (np.arange(K) % 4) < 2
+    mean = B[0][kept_rows].astype(np.float64).mean(0)
+    assert_bits_equal(Y[0], np.broadcast_to(mean.astype(np.float16), (R, C)), "constant rows")
+
+
+@pytest.mark.parametrize("b,lq,lk,d", [(2, 128, 128, 64), (1, 512, 512, 64), (3, 96, 96, 32),
+                                       (2, 160, 256, 128), (1, 64, 64, 16), (2, 100, 256, 64)])
+def test_attention_fused_end_to_end(b, lq, lk, d):
+    snm = _snm()
+    Q, K, V = _qkv(91 + lq + lk + d, b, lq, lk, d)
+    Q = Q[:, :lq].copy()
+    scale = 1.0 / np.sqrt(d)
+    dQ, dK, dV = to_dev(Q), to_dev(K), to_dev(V)
+    O = to_host(snm.attention_nm_fused(dQ, dK, dV, scale))
+    # the oracle's float64 softmax and product on the GPU's own pattern (see above)
+    _, m = snm.sddmm_prune_nm(dQ, dK, scale)
+    S_ref = oracle.attention.scores_f16(Q, K, scale)
+    _, O_ref = oracle.attention.attention_from_pattern(S_ref, to_host(m), V)
+    assert_fp16_close(O, O_ref, f"fused attention {b}x{lq}x{lk}x{d}")
+    # and the unfused pipeline agrees with it to the same bar
+    O_unfused = to_host(snm.attention_nm(dQ, dK, dV, scale))
+    assert_fp16_close(O, O_unfused.astype(np.float64), "fused vs unfused")
+
+
+def test_attention_fused_workload_sampled_heads():
+    # 4 x 16 heads, seq 4096, head_dim 64 in the launch configuration the benchmark times;
+    # two heads checked in full, 64 sampled query rows of every other head
+    snm = _snm()
+    w = workloads.WORKLOADS["attention_2_4"]
+    Q, K, V = workloads.attention_qkv(w)
+    scale = 0.125
+    dQ, dK, dV = to_dev(Q), to_dev(K), to_dev(V)
+    vals, meta, rmax = snm.sddmm_prune_nm_rowmax(dQ, dK, scale)
+    O = to_host(snm.spmm_nm_softmax(vals, meta, rmax, dV))
+    meta_h = to_host(meta)
+    rng = np.random.default_rng(6)
+    for h in range(Q.shape[0]):
+        qrows = np.arange(4096) if h in (1, 50) else np.sort(rng.choice(4096, 64, replace=False))
+        S_ref = oracle.attention.scores_f16(Q[h:h + 1, qrows], K[h:h + 1], scale)
+        _, O_ref = oracle.attention.attention_from_pattern(S_ref, meta_h[h:h + 1, qrows], V[h:h + 1])
+        assert_fp16_close(O[h:h + 1, qrows], O_ref, f"fused O head {h}")
