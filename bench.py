@@ -284,6 +284,84 @@ def bench_other(workload: str, steps: int, warmup: int) -> dict:
     return out
 
 
+def bench_sweep(steps: int, warmup: int, families=None) -> dict:
+    """The general V:N:M sweep (VENOM, Sec. 4, Fig. 9 and Fig. 10 shapes, plus the GPT-3
+    layer): per point, the V:2:M encode and the SpMM, each timed over K back-to-back
+    launches of its C entry point with one event pair, and the dense fp16 product of the
+    same shape (torch.matmul) for the speedup the pages report. Timing only: parity of
+    every (V, M) is covered by the GPU tests. Inputs are drawn on the device from a seeded
+    torch generator (A ~ N(0, 0.02), B ~ N(0, 1), fp16); they stay cache-warm between
+    launches, as in the pages' microbenchmarks."""
+    import torch
+    import workloads
+    from structured_sparse_matrix_amd import vnm_sizes
+    from structured_sparse_matrix_amd._lib import load as load_lib, check
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = load_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def bind(name, *args):
+        fn = getattr(lib, name)
+        check(name, fn(*args))
+        return lambda: fn(*args)
+
+    def timed(launch):
+        for _ in range(warmup):
+            launch()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            launch()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps * 1e-3
+
+    gen = torch.Generator(device=dev)
+    points = []
+    for idx, (fam, R, K, C, V, M) in enumerate(workloads.vnm_sweep()):
+        if families and fam not in families:
+            continue
+        gen.manual_seed(1000 + idx)
+        lda = -(-K // 8) * 8
+        Abuf = torch.zeros((R, lda), dtype=torch.float16, device=dev)
+        Abuf[:, :K] = (torch.randn((R, K), generator=gen, device=dev) * 0.02).half()
+        B = torch.randn((K, C), generator=gen, device=dev).half()
+        nv, nmi, ncl = vnm_sizes(R, K, V, M)
+        values = torch.empty((nv,), dtype=torch.float16, device=dev)
+        midx = torch.empty((nmi,), dtype=torch.uint8, device=dev)
+        colloc = torch.empty((ncl,), dtype=torch.uint8, device=dev)
+        Y = torch.empty((R, C), dtype=torch.float16, device=dev)
+        enc = bind("snm_prune_encode_vnm", Abuf.data_ptr(), R, K, lda, V, M, values.data_ptr(),
+                   midx.data_ptr(), colloc.data_ptr(), stream)
+        mm = bind("snm_spmm_vnm", values.data_ptr(), midx.data_ptr(), colloc.data_ptr(), R, K, V, M,
+                  B.data_ptr(), C, C, Y.data_ptr(), C, stream)
+        t_enc = timed(enc)
+        t_mm = timed(mm)
+        Ad = Abuf[:, :K].contiguous()
+        Yd = torch.empty((R, C), dtype=torch.float16, device=dev)
+        t_dense = timed(lambda: torch.matmul(Ad, B, out=Yd))
+        Kc = 4 * (K // M)
+        mm_bytes = R * (2 * K // M) * 2 + R * (K // M) // 2 + (R // V) * (K // M) * 4 + K * C * 2 + R * C * 2
+        enc_bytes = R * K * 2 + R * (2 * K // M) * 2 + R * (K // M) // 2 + (R // V) * (K // M) * 4
+        smf = 2 * R * Kc * C / t_mm / 1e12
+        points.append({
+            "family": fam, "R": R, "K": K, "C": C, "V": V, "M": M,
+            "spmm_us": round(t_mm * 1e6, 2), "encode_us": round(t_enc * 1e6, 2),
+            "dense_gemm_us": round(t_dense * 1e6, 2),
+            "smfmac_TFLOP/s": round(smf, 1), "sparse_mfma_frac": round(smf / 5000.0, 4),
+            "dense_equiv_TFLOP/s": round(2 * R * K * C / t_mm / 1e12, 1),
+            "spmm_GB/s": round(mm_bytes / t_mm / 1e9, 1), "encode_GB/s": round(enc_bytes / t_enc / 1e9, 1),
+            "speedup_vs_dense": round(t_dense / t_mm, 2), "ideal_speedup": M / 2})
+        print(f"{fam:6s} {R:6d}x{K:6d}x{C:5d} V{V:<4d}M{M:<4d} spmm {t_mm * 1e6:8.1f} us  "
+              f"{smf:7.1f} TF/s smfmac  dense {t_dense * 1e6:8.1f} us  x{t_dense / t_mm:5.2f} "
+              f"(ideal {M / 2:g})  encode {t_enc * 1e6:7.1f} us", file=sys.stderr, flush=True)
+        del Abuf, Ad, B, Y, Yd, values, midx, colloc
+    return {"workload": "vnm_sweep", "points": points}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -299,8 +377,14 @@ def main():
                     help=f"copy {CALIBRATION_BYTES >> 20} MiB once before timing (counter calibration)")
     ap.add_argument("--workload", default="nm_decode",
                     help="nm_decode (the headline line) or vnm_64_2_8 / vnm_128_2_16 / attention_2_4 "
-                         "(per-kernel timings only)")
+                         "(per-kernel timings only) or vnm_sweep (the general V:N:M sweep)")
+    ap.add_argument("--families", default="",
+                    help="with --workload vnm_sweep: comma-separated subset of fig9,fig10,gpt3")
     args = ap.parse_args()
+    if args.workload == "vnm_sweep":
+        fams = args.families.split(",") if args.families else None
+        print(json.dumps(bench_sweep(args.steps, args.warmup, fams)))
+        return
     if args.workload != "nm_decode":
         print(json.dumps(bench_other(args.workload, args.steps, args.warmup)))
         return

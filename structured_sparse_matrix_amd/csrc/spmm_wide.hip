@@ -488,11 +488,11 @@ bool spmm_wide_supported(int64_t R, int64_t Kc, int V, int M, const void* B, int
   if (R <= 0 || Kc <= 0 || C <= 0 || C % 8 != 0 || ldb % 8 != 0) return false;
   if (((uintptr_t)B & 15) != 0) return false;
   if (batch > 1 && stride_B % 8 != 0) return false;
-  if (V > 0 && (V % 64 != 0 || Kc > kMaxGatherKc)) return false;
+  if (V > 0 && (V % 32 != 0 || Kc > kMaxGatherKc)) return false;
   // per-lane DMA offsets are 32-bit: one tile's A rows, one stage's B rows
   constexpr int64_t kLim = (int64_t)1 << 31;
   if (128 * Kc >= kLim) return false;
-  const int64_t b_stage_rows = V > 0 ? 16 * (int64_t)M : 256;   // largest stage of any tile shape
+  const int64_t b_stage_rows = V > 0 ? 32 * (int64_t)M : 256;   // largest stage of any tile shape (128 positions)
   if ((b_stage_rows * ldb + C) * 2 >= kLim) return false;
   return true;
 }
@@ -518,7 +518,8 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
       if (C > 128) return launch_wide<1, 4, 4, 2, 1, 3, true>(a, stream);   // 128 x 256
       return launch_wide<1, 4, 4, 1, 2, 3, true>(a, stream);                // 128 x 128
     }
-    return launch_wide<1, 4, 2, 1, 2, 3, true>(a, stream);                  // 64 x 128
+    if (V % 64 == 0) return launch_wide<1, 4, 2, 1, 2, 3, true>(a, stream);  // 64 x 128
+    return launch_wide<1, 4, 1, 1, 4, 2, true>(a, stream);                  // 32 x 128, 128-position stages
   }
   if (C <= 64) return launch_wide<4, 1, 1, 2, 4, 2, false>(a, stream);      // 128 x 64, 128-position stages
   if (C <= 128) return launch_wide<1, 4, 4, 1, 2, 3, false>(a, stream);     // 128 x 128

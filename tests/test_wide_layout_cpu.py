@@ -90,9 +90,9 @@ int check_a() {
 
 int main() {
   int bad = check<64, 32>() + check<64, 64>() + check<64, 128>() + check<64, 256>() + check<128, 32>() + check<128, 64>() +
-            check<256, 32>() + check<256, 64>();
+            check<128, 128>() + check<256, 32>() + check<256, 64>();
   bad += check_a<32, 128>() + check_a<64, 128>() + check_a<64, 64>() + check_a<32, 64>() +
-         check_a<128, 128>() + check_a<128, 64>() + check_a<256, 128>();
+         check_a<128, 128>() + check_a<128, 64>() + check_a<128, 32>() + check_a<256, 128>();
   return bad ? 1 : 0;
 }
 """

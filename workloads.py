@@ -58,6 +58,39 @@ WORKLOADS = {
 }
 
 
+# ---- the general V:N:M sweep (VENOM, Sec. 4 ablations, Fig. 9 and Fig. 10) ---------------
+# Problem sizes are R x K x C (A is R x K, B is K x C). The pages' K values are not all
+# multiples of 4M, which the format needs (K/M groups, in sets of 4 for whole metadata
+# words); K is padded with zero columns of A and zero rows of B up to the next multiple
+# of 4M, which changes neither the pruning nor the product.
+SWEEP_V = (32, 64, 128)
+SWEEP_M = (5, 7, 8, 10, 20, 40, 100)
+
+
+def pad_k(K: int, M: int) -> int:
+    """Smallest multiple of 4M that is >= K."""
+    q = 4 * M
+    return -(-K // q) * q
+
+
+def vnm_sweep():
+    """(family, R, K_padded, C, V, M) of every sweep point:
+    fig9:  1024 x K x 4096, K = 768, 1536, ..., 12288, V = 128, M in {10, 20, 40, 100};
+    fig10: 1024 x 4096 x 4096, V in {32, 64, 128}, M in {5, 7, 8, 10, 20, 40, 100};
+    gpt3:  36864 x 12288 x 4096, V = 128, M in {8, 10, 20} (the larger problem the
+           pages repeat the study on)."""
+    pts = []
+    for M in (10, 20, 40, 100):
+        for K in range(768, 12288 + 1, 768):
+            pts.append(("fig9", 1024, pad_k(K, M), 4096, 128, M))
+    for V in SWEEP_V:
+        for M in SWEEP_M:
+            pts.append(("fig10", 1024, pad_k(4096, M), 4096, V, M))
+    for M in (8, 10, 20):
+        pts.append(("gpt3", 36864, pad_k(12288, M), 4096, 128, M))
+    return pts
+
+
 def weight_and_activations(w: Workload):
     """A (R x K) then one B (K x C) per entry of ``w.Cs``, from one generator."""
     rng = np.random.default_rng(w.seed)
