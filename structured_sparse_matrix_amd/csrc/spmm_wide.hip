@@ -49,6 +49,7 @@ struct WideArgs {
   int64_t n_row_tiles, n_tiles;   // tiles per batch entry = n_row_tiles * column tiles
   int V, M;
   int xcd_remap;                  // total workgroups are a multiple of 8
+  int y_vec;                      // Y rows start 16-byte aligned (16-byte output stores)
 };
 
 template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER>
@@ -64,6 +65,10 @@ struct WideCfg {
   static constexpr int kMOff = kBBytes + kBlocks * 1024;
   static constexpr int kStage = kMOff + kBlocks * 256;
   static constexpr int kRing = NST * kStage;
+  // output tile staged as fp16 rows; the 64-byte pad makes rows r and r + 4 (written by one
+  // transposing store instruction) fall on different banks
+  static constexpr int kOutPitch = 2 * BN + 64;
+  static constexpr int kOut = BM * kOutPitch;
   static constexpr int nB = kBBytes / 1024 / kWaves;   // DMA instructions per wave per stage
   static constexpr int nA = kBlocks / kWaves;
   static constexpr int kDma = nB + 2 * nA;
@@ -156,7 +161,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 // fp16(exp(v - rowmax)) in registers before it enters the matrix core, the lane keeps an
 // fp32 sum of exactly those fp16 numbers for its row, and the epilogue divides each
 // output row by its sum. With WN == 1 no two waves exponentiate the same operand.
-template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER, bool SMAX>
+// PIPE: issue each step's products one step late (two operand buffers), so that the
+// operand reads of the next step -- across a stage barrier too -- overlap the matrix core;
+// off where the second buffer does not fit in the register file.
+template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER, bool SMAX, bool PIPE>
 __global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
 k_spmm_wide(WideArgs a) {
   static_assert(!(SMAX && GATHER), "the softmax mode is defined for 2:4 scores only");
@@ -307,99 +315,110 @@ k_spmm_wide(WideArgs a) {
   }
 
   // lane-constant LDS offsets of the operand reads: A operand of tile tm, step ks = row
-  // (wm*TM + tm)*32 + lane%32, chunk 2 ks + lane/32; its index word likewise
-  uint32_t a_lds[TM][KSTEPS], m_lds[TM][KSTEPS];
+  // (wm*TM + tm)*32 + lane%32, chunk 2 ks + lane/32; its index word likewise. The layout
+  // makes tile tm + 1 a constant offset away (32 KS bytes of A, 8 KS of metadata), and the
+  // index word of step ks + 1 too (8 bytes), so only the first tile's offsets are registers
+  // and the rest fold into the read instructions (checked on the host with the layout).
+  uint32_t a_lds[KSTEPS];
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int R = (wm * TM + tm) * 32 + (lane & 31);
-      a_lds[tm][ks] = wide::a_offset<KS>(R, 2 * ks + (lane >> 5));
-      m_lds[tm][ks] = wide::m_offset<KS>(R, 2 * ks + (lane >> 5));
-    }
-  uint32_t tr_lds[TN][4];
+  for (int ks = 0; ks < KSTEPS; ++ks)
+    a_lds[ks] = wide::a_offset<KS>(wm * TM * 32 + (lane & 31), 2 * ks + (lane >> 5));
+  const uint32_t m_lds = wide::m_offset<KS>(wm * TM * 32 + (lane & 31), lane >> 5);
+  constexpr uint32_t kATile = wide::a_tile_delta<KS>();
+  constexpr uint32_t kMTile = wide::m_tile_delta<KS>();
+  // transpose reads: rows x, x + 4, x + 16, x + 20 of a step share the cell swizzle, so
+  // they are one register plus constant row offsets
+  uint32_t tr_lds[TN];
   {
     const int x = 8 * (lane >> 5) + ((lane & 15) >> 2);                       // row in a step
     const int cb = wn * TN * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // column
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      tr_lds[tn][0] = wide::b_offset<BN>(x, cb + tn * 32);
-      tr_lds[tn][1] = wide::b_offset<BN>(x + 4, cb + tn * 32);
-      tr_lds[tn][2] = wide::b_offset<BN>(x + 16, cb + tn * 32);
-      tr_lds[tn][3] = wide::b_offset<BN>(x + 20, cb + tn * 32);
-    }
+    for (int tn = 0; tn < TN; ++tn) tr_lds[tn] = wide::b_offset<BN>(x, cb + tn * 32);
   }
 
-  auto compute = [&](int64_t s, auto slot_c) {
-    constexpr uint32_t sb = (uint32_t)(decltype(slot_c)::value * Cfg::kStage);
+  // Operands of one 32-position step, read from the ring; the step's products are issued
+  // one step later, so that the reads of step t + 1 (across a stage barrier too) are in
+  // flight while the matrix core works on step t.
+  struct Frag {
+    h8 af[TM];
+    uint32_t ix[TM];
+    h16 bf[TN];
+  };
+  auto read_frag = [&](Frag& f, uint32_t sb, int ks) {
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int64_t kb = s * KS + ks * 32;
-      if (kb >= Kc) break;
-      h8 af[TM];
-      uint32_t ix[TM];
-      h16 bf[TN];
+    for (int tm = 0; tm < TM; ++tm) {
+      f.af[tm] = *reinterpret_cast<const h8*>(smem + a_lds[ks] + (sb + Cfg::kAOff + tm * kATile));
+      f.ix[tm] = *reinterpret_cast<const uint32_t*>(smem + m_lds + (sb + Cfg::kMOff + tm * kMTile + ks * 8));
+    }
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        af[tm] = *reinterpret_cast<const h8*>(smem + a_lds[tm][ks] + (sb + Cfg::kAOff));
-        ix[tm] = *reinterpret_cast<const uint32_t*>(smem + m_lds[tm][ks] + (sb + Cfg::kMOff));
+    for (int tn = 0; tn < TN; ++tn) {
+      const uint32_t so = sb + (uint32_t)(ks * 64 * BN);   // 32 rows of 2*BN bytes
+      const h4 b0 = tr16_at(smem, tr_lds[tn] + so);
+      const h4 b1 = tr16_at(smem, tr_lds[tn] + (so + 4 * 2 * BN));
+      const h4 b2 = tr16_at(smem, tr_lds[tn] + (so + 16 * 2 * BN));
+      const h4 b3 = tr16_at(smem, tr_lds[tn] + (so + 20 * 2 * BN));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f.bf[tn][e] = b0[e];
+        f.bf[tn][4 + e] = b1[e];
+        f.bf[tn][8 + e] = b2[e];
+        f.bf[tn][12 + e] = b3[e];
       }
-      if constexpr (SMAX) {
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            f2 x;
-            x[0] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)af[tm][e], kLog2e, -mx2[tm]));
-            x[1] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)af[tm][e + 1], kLog2e, -mx2[tm]));
-            const hh2 p = __builtin_convertvector(x, hh2);
-            af[tm][e] = p[0];
-            af[tm][e + 1] = p[1];
-          }
-      }
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const uint32_t so = sb + (uint32_t)(ks * 64 * BN);   // 32 rows of 2*BN bytes
-        const h4 b0 = tr16_at(smem, tr_lds[tn][0] + so);
-        const h4 b1 = tr16_at(smem, tr_lds[tn][1] + so);
-        const h4 b2 = tr16_at(smem, tr_lds[tn][2] + so);
-        const h4 b3 = tr16_at(smem, tr_lds[tn][3] + so);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bf[tn][e] = b0[e];
-          bf[tn][4 + e] = b1[e];
-          bf[tn][8 + e] = b2[e];
-          bf[tn][12 + e] = b3[e];
-        }
-      }
-      if (kb + 32 > Kc) {
-        // last, partial step (K' is a multiple of 16): only its first 16 positions exist.
-        // Zero the A values of the missing half and the B rows there, so clamped DMA
-        // sources contribute exact zeros.
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-          if (lane >= 32) af[tm] = h8{};
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int e = 8; e < 16; ++e) bf[tn][e] = (_Float16)0.f;
-      }
-      if constexpr (SMAX) {   // sum of the fp16 probabilities the matrix core multiplies
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2)
-            rsum[tm] = __builtin_amdgcn_fdot2(hh2{af[tm][e], af[tm][e + 1]}, hh2{(_Float16)1.f, (_Float16)1.f},
-                                              rsum[tm], false);
-      }
+    }
+  };
+  auto mma = [&](Frag& f) {
+    if constexpr (SMAX) {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = smfmac32(af[tm], bf[tn], acc[tm][tn], ix[tm]);
+        for (int e = 0; e < 8; e += 2) {
+          f2 x;
+          x[0] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)f.af[tm][e], kLog2e, -mx2[tm]));
+          x[1] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)f.af[tm][e + 1], kLog2e, -mx2[tm]));
+          const hh2 p = __builtin_convertvector(x, hh2);
+          f.af[tm][e] = p[0];
+          f.af[tm][e + 1] = p[1];
+        }
     }
+    if constexpr (SMAX) {   // sum of the fp16 probabilities the matrix core multiplies
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          rsum[tm] = __builtin_amdgcn_fdot2(hh2{f.af[tm][e], f.af[tm][e + 1]}, hh2{(_Float16)1.f, (_Float16)1.f},
+                                            rsum[tm], false);
+    }
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = smfmac32(f.af[tm], f.bf[tn], acc[tm][tn], f.ix[tm]);
   };
 
-  // ---- the ring: stage s lives in slot s % NST; the loop is unrolled by NST -------------
+  // The last stage of a ragged K' (a multiple of 16 positions) holds clamped DMA sources
+  // past K': once it has landed, its A values there become 0 (-inf in the softmax mode,
+  // whose exponential is 0) and its B rows there become 0, so that every stage runs the
+  // same unchecked step loop and the extra positions contribute exact zeros.
+  const int krem = (int)(Kc - nfull * KS);   // valid positions of the last stage, or 0
+  auto clean_tail = [&](uint32_t sb) {
+    constexpr int kChunks = KS / 16;
+    const int c0 = krem / 16;
+    const uint32_t fill = SMAX ? 0xFC00FC00u : 0u;
+    for (int e = tid; e < BM * kChunks; e += Cfg::kThreads) {
+      const int R = e / kChunks;
+      const int c = e - R * kChunks;
+      if (c >= c0)
+        *reinterpret_cast<u4*>(smem + sb + Cfg::kAOff + wide::a_offset<KS>(R, c)) = u4{fill, fill, fill, fill};
+    }
+    for (int e = krem * (BN / 8) + tid; e < KS * (BN / 8); e += Cfg::kThreads)   // rows >= krem
+      *reinterpret_cast<u4*>(smem + sb + (uint32_t)e * 16u) = u4{0u, 0u, 0u, 0u};
+  };
+
+  // ---- the ring: stage s lives in slot s % NST. The loop is unrolled by NST (by 2 NST if
+  // a pass of NST stages has an odd number of steps) so that slots and the two operand
+  // buffers (global step g uses fr[g % 2]) are compile-time constants. ---------------------
+  constexpr int UNR = PIPE && (NST * KSTEPS) % 2 ? 2 * NST : NST;
+  Frag fr[2];
+  bool pending = false;   // the previous step's operands are waiting for their products
   static_for<0, NST - 1>([&](auto p) {
     constexpr int P = decltype(p)::value;
     if (P < nst) {
@@ -408,9 +427,11 @@ k_spmm_wide(WideArgs a) {
     }
   });
   fetch_colloc(NST - 1);
-  for (int64_t s0 = 0; s0 < nst; s0 += NST) {
-    static_for<0, NST>([&](auto u) {
+  for (int64_t s0 = 0; s0 < nst; s0 += UNR) {
+    static_for<0, UNR>([&](auto u) {
       constexpr int U = decltype(u)::value;
+      constexpr int SLOT = U % NST;
+      constexpr uint32_t sb = (uint32_t)(SLOT * Cfg::kStage);
       const int64_t s = s0 + U;
       if (s < nst) {
         // wait for this wave's DMA of stage s; the barrier publishes every wave's and
@@ -419,15 +440,37 @@ k_spmm_wide(WideArgs a) {
         else wait_vmcnt<0>();
         lds_barrier();
         if (s + NST - 1 < nst) {
-          issue(s + NST - 1, cint<(U + NST - 1) % NST>{});
+          issue(s + NST - 1, cint<(SLOT + NST - 1) % NST>{});
           fetch_colloc(s + NST);
         }
-        compute(s, u);
+        if (s == nfull) {   // only a ragged last stage gets here
+          clean_tail(sb);
+          lds_barrier();
+        }
+        static_for<0, KSTEPS>([&](auto k) {
+          constexpr int KK = decltype(k)::value;
+          if constexpr (PIPE) {
+            constexpr int P = (U * KSTEPS + KK) % 2;
+            read_frag(fr[P], sb, KK);
+            if (pending) mma(fr[P ^ 1]);
+            pending = true;
+          } else {
+            read_frag(fr[0], sb, KK);
+            mma(fr[0]);
+          }
+        });
       }
     });
   }
+  if (pending) {   // the last step: g = nst * KSTEPS - 1
+    if ((nst * KSTEPS) & 1) mma(fr[0]);
+    else mma(fr[1]);
+  }
 
-  // ---- epilogue: fp32 -> fp16 (RNE) ------------------------------------------------------
+  // ---- epilogue: fp32 -> fp16 (RNE), staged through LDS so that output rows leave as
+  // whole 128-byte lines of 16-byte stores ([VENOM] Sec. 4.2, Fig. 8: wide output stores)
+  __syncthreads();   // every wave is done with the ring (and the column-loc bytes)
+  uint8_t* const otile = smem;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     // softmax mode: 1 / row sum for each of the lane's 16 output rows (row 8(i/4) + 4(l/32)
@@ -441,18 +484,44 @@ k_spmm_wide(WideArgs a) {
     }
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
-      const int64_t col = col0 + (wn * TN + tn) * 32 + (lane & 31);
+      const int ct = (wn * TN + tn) * 32 + (lane & 31);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int64_t row = row0 + (wm * TM + tm) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const int rt = (wm * TM + tm) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
         const float y = SMAX ? acc[tm][tn][i] * inv[i] : acc[tm][tn][i];
-        if (row < a.R && col < a.C) Y[row * a.ldy + col] = f16_bits(to_f16(y));
+        *reinterpret_cast<uint16_t*>(otile + rt * Cfg::kOutPitch + ct * 2) = f16_bits(to_f16(y));
+      }
+      // scheduling fence: convert and store tile by tile (hoisting every conversion above
+      // the first store would need a second register copy of the accumulators)
+      asm volatile("" ::: "memory");
+    }
+  }
+  __syncthreads();
+  constexpr int kChunksPerRow = BN / 8;   // 16-byte chunks of a tile row; C % 8 == 0, so a
+                                          // chunk is wholly inside or outside the output
+  for (int e = tid; e < BM * kChunksPerRow; e += Cfg::kThreads) {
+    const int r = e / kChunksPerRow;
+    const int ch = e - r * kChunksPerRow;
+    const int64_t row = row0 + r;
+    const int64_t col = col0 + ch * 8;
+    if (row < a.R && col < a.C) {
+      const u4 v = *reinterpret_cast<const u4*>(otile + r * Cfg::kOutPitch + ch * 16);
+      uint16_t* dst = Y + row * a.ldy + col;
+      if (a.y_vec) {
+        *reinterpret_cast<u4*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          dst[2 * w] = (uint16_t)(v[w] & 0xFFFFu);
+          dst[2 * w + 1] = (uint16_t)(v[w] >> 16);
+        }
       }
     }
   }
 }
 
-template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER, bool SMAX = false>
+template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER, bool SMAX = false,
+          bool PIPE = true>
 hipError_t launch_wide(WideArgs a, hipStream_t stream) {
   using Cfg = WideCfg<WM, WN, TM, TN, KSTEPS, NST, GATHER>;
   a.n_row_tiles = (a.R + Cfg::BM - 1) / Cfg::BM;
@@ -462,8 +531,10 @@ hipError_t launch_wide(WideArgs a, hipStream_t stream) {
   if (total == 0) return hipSuccess;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
   a.xcd_remap = (total % 8) == 0;
-  const size_t lds = (size_t)Cfg::kRing + (GATHER ? (size_t)(a.Kc + 2 * Cfg::KS) : 0);
-  auto kern = k_spmm_wide<WM, WN, TM, TN, KSTEPS, NST, GATHER, SMAX>;
+  const size_t ring = (size_t)Cfg::kRing + (GATHER ? (size_t)(a.Kc + 2 * Cfg::KS) : 0);
+  const size_t lds = ring > (size_t)Cfg::kOut ? ring : (size_t)Cfg::kOut;
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  auto kern = k_spmm_wide<WM, WN, TM, TN, KSTEPS, NST, GATHER, SMAX, PIPE>;
   static bool attr_set = false;   // benign race: every caller sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -475,6 +546,10 @@ hipError_t launch_wide(WideArgs a, hipStream_t stream) {
 }
 
 constexpr int64_t kMaxGatherKc = 16384;   // column-loc of one V-block staged in LDS
+
+bool y_rows_aligned(const void* Y, int64_t ldy, int64_t batch, int64_t stride_Y) {
+  return ((uintptr_t)Y & 15) == 0 && ldy % 8 == 0 && (batch <= 1 || stride_Y % 8 == 0);
+}
 
 }  // namespace
 
@@ -513,17 +588,20 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
   a.stride_values = stride_values; a.stride_meta = stride_meta;
   a.stride_B = stride_B; a.stride_Y = stride_Y;
   a.V = V; a.M = M;
+  a.y_vec = y_rows_aligned(Y, ldy, a.batch, stride_Y);
+  // 128 x 256 tiles where they still give every CU two workgroups; 128 x 128 otherwise
+  const bool wide_grid = a.batch * ((R + 127) / 128) * ((C + 255) / 256) >= 512;
   if (V > 0) {
     if (V % 128 == 0) {
-      if (C > 128) return launch_wide<1, 4, 4, 2, 1, 3, true>(a, stream);   // 128 x 256
+      if (C > 128 && wide_grid) return launch_wide<1, 4, 4, 2, 1, 3, true, false, false>(a, stream);   // 128 x 256
       return launch_wide<1, 4, 4, 1, 2, 3, true>(a, stream);                // 128 x 128
     }
     if (V % 64 == 0) return launch_wide<1, 4, 2, 1, 2, 3, true>(a, stream);  // 64 x 128
     return launch_wide<1, 4, 1, 1, 4, 2, true>(a, stream);                  // 32 x 128, 128-position stages
   }
   if (C <= 64) return launch_wide<4, 1, 1, 2, 4, 2, false>(a, stream);      // 128 x 64, 128-position stages
-  if (C <= 128) return launch_wide<1, 4, 4, 1, 2, 3, false>(a, stream);     // 128 x 128
-  return launch_wide<1, 4, 4, 2, 1, 3, false>(a, stream);                   // 128 x 256
+  if (C <= 128 || !wide_grid) return launch_wide<1, 4, 4, 1, 2, 3, false>(a, stream);   // 128 x 128
+  return launch_wide<1, 4, 4, 2, 1, 3, false, false, false>(a, stream);     // 128 x 256
 }
 
 }  // namespace snm
@@ -547,6 +625,7 @@ hipError_t launch_spmm_nm_softmax(const void* values, const void* meta, const fl
   a.stride_values = stride_values; a.stride_meta = stride_meta;
   a.stride_B = stride_B; a.stride_Y = stride_Y; a.stride_rowmax = stride_row_max;
   a.V = 0; a.M = 4;
+  a.y_vec = y_rows_aligned(Y, ldy, a.batch, stride_Y);
   // one wave column (WN = 1) so each score is exponentiated once per column tile
   if (C <= 64) return launch_wide<4, 1, 1, 2, 4, 2, false, true>(a, stream);    // 128 x 64
   if (C <= 128) return launch_wide<4, 1, 1, 4, 2, 3, false, true>(a, stream);   // 128 x 128

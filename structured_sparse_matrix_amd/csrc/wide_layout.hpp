@@ -88,5 +88,14 @@ constexpr int m_dma_row(int b, int l) { return b * m_rows_per_block<KS>() + l / 
 template <int KS>
 constexpr int m_dma_word(int l) { return l % m_words_per_row<KS>(); }
 
+// Constant distances used by the kernels' operand reads: row R + 32 of A lies 32 KS bytes
+// after row R (same chunk), its metadata 8 KS bytes after; the index word w + 2 of a row
+// lies 8 bytes after word w; in the B tile, rows x + 4, x + 16 and x + 20 of a row x with
+// x % 8 < 4 share x's cell swizzle, so they lie 4, 16 and 20 rows (times 2 BN bytes) after.
+template <int KS>
+constexpr uint32_t a_tile_delta() { return 32u * KS; }
+template <int KS>
+constexpr uint32_t m_tile_delta() { return 8u * KS; }
+
 }  // namespace wide
 }  // namespace snm

@@ -44,6 +44,15 @@ int check() {
       for (int b = 0; b < 64; ++b)
         if (hits[b] != 1) { ++bad; break; }
     }
+  // 3) rows x + 4, x + 16, x + 20 (x % 8 < 4) are constant row offsets from row x
+  for (int x = 0; x + 20 < KS; ++x) {
+    if (x % 8 >= 4) continue;
+    for (int c = 0; c < BN; c += 4) {
+      if (b_offset<BN>(x + 4, c) != b_offset<BN>(x, c) + 4u * 2u * BN) ++bad;
+      if (b_offset<BN>(x + 16, c) != b_offset<BN>(x, c) + 16u * 2u * BN) ++bad;
+      if (b_offset<BN>(x + 20, c) != b_offset<BN>(x, c) + 20u * 2u * BN) ++bad;
+    }
+  }
   std::printf("BN=%d KS=%d bad=%d\n", BN, KS, bad);
   return bad;
 }
@@ -84,6 +93,13 @@ int check_a() {
       moffs.insert(m_offset<KS>(R, w));
     }
   if ((int)moffs.size() != nm * 64) ++bad;
+  // constant distances between the operand reads of tiles 32 rows apart and of steps
+  for (int R = 0; R + 32 < BM; ++R)
+    for (int c = 0; c < KS / 16; ++c) {
+      if (a_offset<KS>(R + 32, c) != a_offset<KS>(R, c) + a_tile_delta<KS>()) ++bad;
+      if (m_offset<KS>(R + 32, c) != m_offset<KS>(R, c) + m_tile_delta<KS>()) ++bad;
+      if (c + 2 < KS / 16 && m_offset<KS>(R, c + 2) != m_offset<KS>(R, c) + 8u) ++bad;
+    }
   std::printf("A/meta KS=%d BM=%d bad=%d\n", KS, BM, bad);
   return bad;
 }
