@@ -12,7 +12,9 @@ every step streams its operands from HBM.
 Timed regions, each bracketed by synchronisation and one HIP event pair on the launch
 stream:
   1. K whole steps -> ms_per_step and `value` (dense-equivalent TFLOP/s of the whole
-     step: 2*R*K*N summed over the three products / step time, encode included);
+     step: 2*R*K*N summed over the three products / step time, encode included). Steps
+     are independent, so step i runs on stream i % S (--streams, default 2): two steps
+     in flight hide one kernel's launch ramp and tail behind the other's work;
   2. for each kernel of the step, K back-to-back launches of that kernel alone over the
      same rotating inputs -> its average launch duration (an event between every launch
      would drain the queue and add a gap of its own). `roofline` is the SpMM kernel's:
@@ -94,7 +96,8 @@ def cpu_baseline(min_seconds: float = 10.0) -> dict:
                       f"BLAS threads={threads}; host {platform.processor() or platform.machine()}"}
 
 
-def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_copy: bool):
+def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_copy: bool,
+            nstreams: int = 2):
     import torch
     import structured_sparse_matrix_amd as snm
     import workloads
@@ -134,7 +137,12 @@ def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_c
     # leave the GPU waiting between back-to-back launches.
     from structured_sparse_matrix_amd._lib import load as load_lib, check
     lib = load_lib()
-    stream = torch.cuda.current_stream().cuda_stream
+    # Steps are independent (each has its own rotating copy), so step i is enqueued on
+    # stream i % nstreams: two steps in flight overlap one kernel's ramp and tail with the
+    # other's work. A copy is reused every NROT steps, always on the same stream.
+    assert NROT % nstreams == 0
+    main_stream = torch.cuda.current_stream()
+    streams = [main_stream] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
 
     def bind(name, *args):
         fn = getattr(lib, name)
@@ -143,6 +151,7 @@ def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_c
 
     enc_calls, mm_calls = [], []
     for j in range(NROT):
+        stream = streams[j % nstreams].cuda_stream
         if a_layout == "tiled":
             enc_calls.append(bind("snm_prune_encode_nm_tiled", As[j].data_ptr(), R, K, K,
                                   vals[j].data_ptr(), metas[j].data_ptr(), stream))
@@ -172,22 +181,27 @@ def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_c
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        start.record()
+        start.record(main_stream)
+        for st in streams[1:]:
+            st.wait_stream(main_stream)
         for i in range(steps):
             step(warmup + i)
-        stop.record()
+        for st in streams[1:]:
+            main_stream.wait_stream(st)
+        stop.record(main_stream)
         torch.cuda.synchronize()
         return start.elapsed_time(stop), time.perf_counter() - t0
 
     def timed_kernel(launch):
-        """K back-to-back launches of one kernel over the rotating inputs, one event pair:
-        an event between every launch would drain the queue and add its own gap."""
+        """K back-to-back launches of one kernel over the rotating copies of the main stream,
+        one event pair on that stream: an event between every launch would drain the queue
+        and add its own gap."""
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        start.record()
+        start.record(main_stream)
         for i in range(steps):
-            launch((warmup + i) % NROT)
-        stop.record()
+            launch((i * nstreams) % NROT)
+        stop.record(main_stream)
         torch.cuda.synchronize()
         return start.elapsed_time(stop) / steps
 
@@ -378,6 +392,8 @@ def main():
     ap.add_argument("--workload", default="nm_decode",
                     help="nm_decode (the headline line) or vnm_64_2_8 / vnm_128_2_16 / attention_2_4 "
                          "(per-kernel timings only) or vnm_sweep (the general V:N:M sweep)")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="decode steps in flight (step i on stream i %% S); kernel timings use one")
     ap.add_argument("--families", default="",
                     help="with --workload vnm_sweep: comma-separated subset of fig9,fig10,gpt3")
     args = ap.parse_args()
@@ -395,7 +411,7 @@ def main():
     import numpy as np
 
     total_ms, wall, enc_ms, spmm_ms = run_gpu(args.steps, args.warmup, args.b_layout, args.a_layout,
-                                              args.calibration_copy)
+                                              args.calibration_copy, args.streams)
     ms_per_step = total_ms / args.steps
     flops_step = sum(2 * R * K * n for n in NS)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
@@ -434,6 +450,7 @@ def main():
                                "B 4096xN fp16 N(0,1), N in {8,16,32}; step = 2:4 prune/encode + 3 SpMM; "
                                "32 rotating input copies",
                    "R": R, "K": K, "N": list(NS), "rotating_copies": NROT,
+                   "streams": args.streams,
                    "B_storage": "column-major (X[N][K])" if args.b_layout == "col" else "row-major (K x N)",
                    "A_storage": "operand-major (tiled)" if args.a_layout == "tiled" else "canonical"},
         "roofline": {"bound": "hbm", "kernel": spmm_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
