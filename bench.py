@@ -376,6 +376,54 @@ def bench_sweep(steps: int, warmup: int, families=None) -> dict:
     return {"workload": "vnm_sweep", "points": points}
 
 
+def bench_energy(steps: int, warmup: int) -> dict:
+    """Energy of the V:2:M encodings the GPU produces (VENOM, Sec. 5, Fig. 11): a 768 x 768
+    Gaussian weight (seed 5; the size of the page's BERT-base query weight), V in
+    {1, 16, 32, 64, 128}, N:M in {2:4, 2:5, 2:8, 2:10, 2:20, 2:40}, K zero-padded to a
+    multiple of 4M. energy = sum |kept| / sum |A| in float64 on the host, from the
+    encoder's output; each encode is also timed."""
+    import numpy as np
+    import torch
+    import workloads
+    from structured_sparse_matrix_amd import vnm_sizes
+    from structured_sparse_matrix_amd._lib import load as load_lib, check
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = load_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    A = workloads.normal_f16(np.random.default_rng(5), (768, 768))
+    total = float(np.abs(A.astype(np.float64)).sum())
+    points = []
+    for V in (1, 16, 32, 64, 128):
+        for M in (4, 5, 8, 10, 20, 40):
+            K = -(-768 // (4 * M)) * (4 * M)
+            lda = -(-K // 8) * 8
+            buf = torch.zeros((768, lda), dtype=torch.float16, device=dev)
+            buf[:, :768] = torch.from_numpy(A).to(dev)
+            nv, nmi, ncl = vnm_sizes(768, K, V, M)
+            values = torch.empty((nv,), dtype=torch.float16, device=dev)
+            midx = torch.empty((nmi,), dtype=torch.uint8, device=dev)
+            colloc = torch.empty((ncl,), dtype=torch.uint8, device=dev)
+            args = (buf.data_ptr(), 768, K, lda, V, M, values.data_ptr(), midx.data_ptr(),
+                    colloc.data_ptr(), stream)
+            check("snm_prune_encode_vnm", lib.snm_prune_encode_vnm(*args))
+            for _ in range(warmup):
+                lib.snm_prune_encode_vnm(*args)
+            start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record()
+            for _ in range(steps):
+                lib.snm_prune_encode_vnm(*args)
+            stop.record()
+            torch.cuda.synchronize()
+            kept = values.cpu().numpy().astype(np.float64)
+            points.append({"V": V, "M": M, "sparsity": 1.0 - 2.0 / M,
+                           "energy": float(np.abs(kept).sum()) / total,
+                           "encode_us": start.elapsed_time(stop) / steps * 1e3})
+    return {"workload": "energy", "matrix": "768x768 fp16 N(0,1), seed 5", "points": points}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,12 +439,16 @@ def main():
                     help=f"copy {CALIBRATION_BYTES >> 20} MiB once before timing (counter calibration)")
     ap.add_argument("--workload", default="nm_decode",
                     help="nm_decode (the headline line) or vnm_64_2_8 / vnm_128_2_16 / attention_2_4 "
-                         "(per-kernel timings only) or vnm_sweep (the general V:N:M sweep)")
+                         "(per-kernel timings only) or vnm_sweep (the general V:N:M sweep) or energy "
+                         "(energy of the GPU's V:2:M encodings)")
     ap.add_argument("--streams", type=int, default=2,
                     help="decode steps in flight (step i on stream i %% S); kernel timings use one")
     ap.add_argument("--families", default="",
                     help="with --workload vnm_sweep: comma-separated subset of fig9,fig10,gpt3")
     args = ap.parse_args()
+    if args.workload == "energy":
+        print(json.dumps(bench_energy(args.steps, args.warmup)))
+        return
     if args.workload == "vnm_sweep":
         fams = args.families.split(",") if args.families else None
         print(json.dumps(bench_sweep(args.steps, args.warmup, fams)))
