@@ -16,6 +16,8 @@ function names the passage of the pages it follows:
   (PPoPP'23, Chinese text): Sec. 3.2, Listing 1, Sec. 4.2 Fig. 6(b), Sec. 4.3.
 * VENOM Sec. 5 and Fig. 11: the energy (magnitude preservation) metric
   (oracle/energy.py).
+* "Coruscant: Co-Designing GPU Kernel and Sparse Tensor Core ...", Sec. 3.1,
+  Fig. 7 and Sec. 3.2: the bitmap sparse format (oracle/bitmap.py).
 
 Every function here is pinned by at least one CPU test against a printed
 worked example, a closed form, an invariant, a reduction to a textbook case or
@@ -26,6 +28,7 @@ from .nm import (magnitude_key, select_top_n, prune_encode_nm, decode_nm, spmm_n
 from .vnm import column_scores, prune_encode_vnm, decode_vnm, spmm_vnm
 from .attention import sddmm_prune_nm, softmax_nm_rows, attention_nm, full_attention
 from . import energy
+from . import bitmap
 
 __all__ = [
     "magnitude_key", "select_top_n", "prune_encode_nm", "decode_nm", "spmm_nm", "NM_LEGAL_CODES",
