@@ -188,6 +188,42 @@ int snm_spmm_nm_softmax(const void* values, const void* meta, const float* row_m
                         int64_t batch, int64_t stride_values, int64_t stride_meta,
                         int64_t stride_row_max, int64_t stride_B, int64_t stride_Y, void* stream);
 
+/* Bitmap format for unstructured sparsity ("Coruscant: Co-Designing GPU Kernel and Sparse
+ * Tensor Core ...", Sec. 3.1 and Fig. 7; Sec. 3.2 for the padding). An R x K fp16 matrix
+ * (K % 64 == 0, R*K < 2^31) is cut into tiles of 64 consecutive positions along K of one
+ * row, in row-major tile order (tile t = r*K/64 + k/64):
+ *   bitmaps       uint64 [R*K/64]: bit i of tile t is set iff position i of the tile holds
+ *                 a non-zero (fp16 magnitude bits not all zero: +0 and -0 are not stored);
+ *   tile_offsets  uint32 [R*K/64 + 1]: element index in values of tile t's first non-zero
+ *                 (the exclusive prefix sum of the padded counts); the last entry is the
+ *                 number of values;
+ *   values        fp16 [tile_offsets[R*K/64]]: each tile's non-zeros in ascending position
+ *                 order, padded with +0 to a multiple of 8 (every tile starts 16-byte
+ *                 aligned).
+ * Sizes of the fixed arrays (host only). */
+int snm_bitmap_sizes(int64_t R, int64_t K, int64_t* n_tiles, int64_t* n_offsets);
+
+/* Encoder, pass 1: bitmaps and tile_offsets of A (fp16 R x K row-major, lda >= K,
+ * lda % 8 == 0, A 16-byte aligned; bitmaps 8-byte and tile_offsets 4-byte aligned). After
+ * the stream reaches this call, tile_offsets[R*K/64] is the number of values to allocate. */
+int snm_bitmap_count(const void* A, int64_t R, int64_t K, int64_t lda, void* bitmaps,
+                     void* tile_offsets, void* stream);
+
+/* Encoder, pass 2: the packed values (fp16 [tile_offsets[R*K/64]]) from A and the arrays of
+ * pass 1. values may be NULL when that count is 0 (it is then never touched). */
+int snm_bitmap_encode(const void* A, int64_t R, int64_t K, int64_t lda, const void* bitmaps,
+                      const void* tile_offsets, void* values, void* stream);
+
+/* Y = decode(bitmaps, tile_offsets, values) * B for a decode-shaped B with C <= 32 columns
+ * (Coruscant Sec. 3.2: the product of a bitmap-compressed weight with few activations).
+ * B, b_layout, Y as in snm_spmm_nm; column-major B (b_layout 1) needs ldb % 8 == 0 and a
+ * 16-byte aligned B (row-major B is supported, slower). values 16-byte aligned. fp32
+ * accumulation, fp16 output (RNE). C > 32 returns SNM_E_UNSUPPORTED. values may be NULL when
+ * the encoding holds no non-zeros. */
+int snm_spmm_bitmap(const void* bitmaps, const void* tile_offsets, const void* values, int64_t R,
+                    int64_t K, const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
+                    int64_t ldy, void* stream);
+
 /* In-place row softmax over the kept entries of compressed rows ("Dynamic N:M ...
  * attention", Sec. 3.2: softmax runs only on each row's kept entries; dropped
  * entries count as -inf). values: fp16 rows x kept, leading dimension ld >= kept.

@@ -8,6 +8,8 @@ C entry points without the ``snm_`` prefix.
 Layouts (canonical, see include/snm.h):
   2:4     values fp16 [R, K/2], meta uint8 [R, K/8]
   V:2:M   values fp16 [R, 2K/M], midx uint8 [R, K/(2M)], colloc uint8 [R/V, K/M, 4]
+  bitmap  bitmaps [R, K/64] (64-bit words, held in int64), tile_offsets [R*K/64 + 1]
+          (uint32 values, held in int32), values fp16 [tile_offsets[-1]]
 """
 from __future__ import annotations
 
@@ -21,6 +23,7 @@ __all__ = [
     "softmax_nm_rows", "attention_nm", "nm_sizes", "vnm_sizes", "abi_version", "SnmError",
     "nm_tiled_sizes", "prune_encode_nm_tiled", "spmm_nm_tiled",
     "sddmm_prune_nm_rowmax", "spmm_nm_softmax", "attention_nm_fused",
+    "bitmap_sizes", "bitmap_encode", "spmm_bitmap",
     "LIB_PATH",
 ]
 
@@ -296,6 +299,60 @@ def spmm_nm_softmax(values, meta, row_max, B, out=None):
                                      _ptr(out), out.stride(1), nb, values.stride(0), meta.stride(0),
                                      row_max.stride(0), B.stride(0), out.stride(0), _stream(B)))
     return out if batched else out[0]
+
+
+def bitmap_sizes(R: int, K: int):
+    n, m = ctypes.c_int64(), ctypes.c_int64()
+    check("snm_bitmap_sizes", load().snm_bitmap_sizes(R, K, ctypes.byref(n), ctypes.byref(m)))
+    return n.value, m.value
+
+
+def bitmap_encode(A):
+    """Bitmap format of fp16 A [R, K] (K % 64 == 0) -> (bitmaps int64 [R, K/64],
+    tile_offsets int32 [R*K/64 + 1], values fp16 [n]). Two passes; the value count is read
+    back between them (one synchronisation)."""
+    torch = _torch()
+    _need(A, "A", torch.float16, 2)
+    if A.stride(1) != 1:
+        raise ValueError("A must be row-major (unit stride along K)")
+    R, K = A.shape
+    nt, no = bitmap_sizes(R, K)
+    bitmaps = torch.empty((R, K // 64), dtype=torch.int64, device=A.device)
+    offsets = torch.empty((no,), dtype=torch.int32, device=A.device)
+    lib = load()
+    check("snm_bitmap_count", lib.snm_bitmap_count(_ptr(A), R, K, A.stride(0), _ptr(bitmaps), _ptr(offsets),
+                                                   _stream(A)))
+    n = int(offsets[-1].item())
+    values = torch.empty((n,), dtype=torch.float16, device=A.device)
+    check("snm_bitmap_encode", lib.snm_bitmap_encode(_ptr(A), R, K, A.stride(0), _ptr(bitmaps), _ptr(offsets),
+                                                     _ptr(values), _stream(A)))
+    return bitmaps, offsets, values
+
+
+def spmm_bitmap(bitmaps, tile_offsets, values, B, out=None):
+    """Y = decode(bitmap format) @ B with B [K, C], C <= 32 (row-major, or column-major
+    such as X.t() for activations X [C, K])."""
+    torch = _torch()
+    _need(bitmaps, "bitmaps", torch.int64, 2)
+    _need(tile_offsets, "tile_offsets", torch.int32, 1)
+    _need(values, "values", torch.float16, 1)
+    _need(B, "B", torch.float16, 2)
+    R, T = bitmaps.shape
+    K, C = B.shape
+    if 64 * T != K or tile_offsets.numel() != R * T + 1:
+        raise ValueError("bitmap arrays do not match B's K")
+    for t, n in ((bitmaps, "bitmaps"), (tile_offsets, "tile_offsets"), (values, "values")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    layout, ldb = _b_layout(B)
+    if out is None:
+        out = torch.empty((R, C), dtype=torch.float16, device=B.device)
+    if out.stride(1) != 1:
+        raise ValueError("out must be row-major")
+    check("snm_spmm_bitmap", load().snm_spmm_bitmap(_ptr(bitmaps), _ptr(tile_offsets), _ptr(values), R, K,
+                                                    _ptr(B), C,
+                                                    ldb, layout, _ptr(out), out.stride(0), _stream(B)))
+    return out
 
 
 def softmax_nm_rows(values):

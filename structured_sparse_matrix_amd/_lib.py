@@ -30,6 +30,10 @@ SIGNATURES = {
     "snm_spmm_vnm": [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
     "snm_sddmm_prune_nm": [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp],
     "snm_softmax_nm_rows": [_vp, _i64, _i64, _i64, _vp],
+    "snm_bitmap_sizes": [_i64, _i64, _p64, _p64],
+    "snm_bitmap_count": [_vp, _i64, _i64, _i64, _vp, _vp, _vp],
+    "snm_bitmap_encode": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "snm_spmm_bitmap": [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _vp, _i64, _vp],
     "snm_sddmm_prune_nm_rowmax": [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp],
     "snm_spmm_nm_softmax": [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
                             _i64, _i64, _vp],

@@ -170,6 +170,47 @@ int snm_spmm_nm_softmax(const void* values, const void* meta, const float* row_m
                                               stride_B, stride_Y, (hipStream_t)stream));
 }
 
+int snm_bitmap_sizes(int64_t R, int64_t K, int64_t* n_tiles, int64_t* n_offsets) {
+  int s = snm::check_bitmap_sizes(R, K);
+  if (s != SNM_OK) return s;
+  if (!n_tiles || !n_offsets) return SNM_E_NULL;
+  *n_tiles = R * (K / 64);
+  *n_offsets = R * (K / 64) + 1;
+  return SNM_OK;
+}
+
+int snm_bitmap_count(const void* A, int64_t R, int64_t K, int64_t lda, void* bitmaps,
+                     void* tile_offsets, void* stream) {
+  int s = snm::check_bitmap_encode(A, R, K, lda, bitmaps, tile_offsets, nullptr, false);
+  if (s != SNM_OK) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  // an empty matrix still gets its single offset (0)
+  const int64_t Rl = (R == 0 || K == 0) ? 0 : R;
+  return launched(snm::launch_bitmap_count(A, Rl, Rl ? K : 0, lda, (uint64_t*)bitmaps,
+                                           (uint32_t*)tile_offsets, (hipStream_t)stream));
+}
+
+int snm_bitmap_encode(const void* A, int64_t R, int64_t K, int64_t lda, const void* bitmaps,
+                      const void* tile_offsets, void* values, void* stream) {
+  int s = snm::check_bitmap_encode(A, R, K, lda, bitmaps, tile_offsets, values, true);
+  if (s != SNM_OK || R == 0 || K == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_bitmap_values(A, R, K, lda, (const uint64_t*)bitmaps,
+                                            (const uint32_t*)tile_offsets, values,
+                                            (hipStream_t)stream));
+}
+
+int snm_spmm_bitmap(const void* bitmaps, const void* tile_offsets, const void* values, int64_t R,
+                    int64_t K, const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
+                    int64_t ldy, void* stream) {
+  int s = snm::check_spmm_bitmap(bitmaps, tile_offsets, values, R, K, B, C, ldb, b_layout, Y, ldy);
+  if (s != SNM_OK || R == 0 || C == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_spmm_bitmap((const uint64_t*)bitmaps, (const uint32_t*)tile_offsets,
+                                          values, R, K, B, C, ldb, b_layout, Y, ldy,
+                                          (hipStream_t)stream));
+}
+
 int snm_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream) {
   int s = snm::check_softmax_nm_rows(values, rows, kept, ld);
   if (s != SNM_OK || rows == 0 || kept == 0) return s;

@@ -53,6 +53,19 @@ __device__ __forceinline__ h4 lds_read_tr16(uint32_t lds_byte_addr) {
   return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(p));
 }
 
+// Global -> LDS DMA of 16 bytes per active lane: lane l writes LDS bytes
+// [lds_byte + 16 l, + 16) from its own 64-bit address (global_load_lds_dwordx4; lds_byte is
+// wave-uniform and goes through M0). Inactive lanes neither read nor write. Completion is
+// tracked with s_waitcnt vmcnt by the caller; from inline assembly so that the compiler's
+// waitcnt pass does not make unrelated LDS reads wait for it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is set inside the statement
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_byte) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "m0");
+}
+#pragma clang diagnostic pop
+
 // LDS byte address of a __shared__ object (address space 3 offset).
 template <typename T>
 __device__ __forceinline__ uint32_t lds_addr(T* p) {

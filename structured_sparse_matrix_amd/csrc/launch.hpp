@@ -53,6 +53,15 @@ hipError_t launch_spmm_nm_softmax(const void* values, const void* meta, const fl
 hipError_t launch_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
                                  int64_t Lk, int64_t d, float scale, void* values, void* meta,
                                  void* S_dense, float* row_max, hipStream_t stream);
+// Bitmap (Coruscant) format: encoder passes and the decode-shaped product (bitmap.hip).
+hipError_t launch_bitmap_count(const void* A, int64_t R, int64_t K, int64_t lda, uint64_t* bitmaps,
+                               uint32_t* offsets, hipStream_t stream);
+hipError_t launch_bitmap_values(const void* A, int64_t R, int64_t K, int64_t lda,
+                                const uint64_t* bitmaps, const uint32_t* offsets, void* values,
+                                hipStream_t stream);
+hipError_t launch_spmm_bitmap(const uint64_t* bitmaps, const uint32_t* offsets, const void* values,
+                              int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb,
+                              int b_layout, void* Y, int64_t ldy, hipStream_t stream);
 hipError_t launch_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld,
                                   hipStream_t stream);
 

@@ -133,6 +133,47 @@ int check_spmm_nm_softmax(const void* values, const void* meta, const void* row_
   return SNM_OK;
 }
 
+int check_bitmap_sizes(int64_t R, int64_t K) {
+  if (R < 0 || K < 0 || K % 64 != 0 || !fits(R, K)) return SNM_E_SHAPE;
+  if (R * K >= ((int64_t)1 << 31)) return SNM_E_SHAPE;   // 32-bit tile offsets
+  return SNM_OK;
+}
+
+int check_bitmap_encode(const void* A, int64_t R, int64_t K, int64_t lda, const void* bitmaps,
+                        const void* offsets, const void* values, bool need_values) {
+  int s = check_bitmap_sizes(R, K);
+  if (s != SNM_OK) return s;
+  if (!offsets) return SNM_E_NULL;
+  if (((uintptr_t)offsets & 3u) != 0) return SNM_E_ALIGN;
+  if (R == 0 || K == 0) return SNM_OK;
+  // values may be NULL: an encoding with no non-zeros never touches it
+  if (!A || !bitmaps) return SNM_E_NULL;
+  if (lda < K || !fits(R, lda)) return SNM_E_SHAPE;
+  if (lda % 8 != 0 || !aligned16(A) || ((uintptr_t)bitmaps & 7u) != 0) return SNM_E_ALIGN;
+  if (need_values && !aligned2(values)) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
+int check_spmm_bitmap(const void* bitmaps, const void* offsets, const void* values, int64_t R,
+                      int64_t K, const void* B, int64_t C, int64_t ldb, int b_layout, const void* Y,
+                      int64_t ldy) {
+  int s = check_bitmap_sizes(R, K);
+  if (s != SNM_OK) return s;
+  if (b_layout != 0 && b_layout != 1) return SNM_E_UNSUPPORTED;
+  if (C < 0 || !fits(K, C) || !fits(R, C)) return SNM_E_SHAPE;
+  if (C > 32) return SNM_E_UNSUPPORTED;
+  if (R == 0 || C == 0) return SNM_OK;
+  if (!Y || (K > 0 && (!bitmaps || !offsets || !B))) return SNM_E_NULL;   // values may be NULL (no non-zeros)
+  const int64_t b_lines = b_layout == 0 ? K : C;
+  const int64_t b_min_ld = b_layout == 0 ? C : K;
+  if (ldy < C || ldb < b_min_ld || !fits(b_lines, ldb) || !fits(R, ldy)) return SNM_E_SHAPE;
+  if (!aligned16(values) || ((uintptr_t)bitmaps & 7u) != 0 || ((uintptr_t)offsets & 3u) != 0 ||
+      !aligned2(B) || !aligned2(Y))
+    return SNM_E_ALIGN;
+  if (b_layout == 1 && (ldb % 8 != 0 || !aligned16(B))) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
 int check_softmax_nm_rows(const void* values, int64_t rows, int64_t kept, int64_t ld) {
   if (rows < 0 || kept < 0 || ld < kept || !fits(rows, ld)) return SNM_E_SHAPE;
   if (rows == 0 || kept == 0) return SNM_OK;

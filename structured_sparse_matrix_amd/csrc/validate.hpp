@@ -26,6 +26,12 @@ int check_spmm_nm_softmax(const void* values, const void* meta, const void* row_
                           int64_t K, const void* B, int64_t C, int64_t ldb, const void* Y,
                           int64_t ldy, int64_t batch, int64_t stride_values, int64_t stride_meta,
                           int64_t stride_row_max, int64_t stride_B, int64_t stride_Y);
+int check_bitmap_sizes(int64_t R, int64_t K);
+int check_bitmap_encode(const void* A, int64_t R, int64_t K, int64_t lda, const void* bitmaps,
+                        const void* offsets, const void* values, bool need_values);
+int check_spmm_bitmap(const void* bitmaps, const void* offsets, const void* values, int64_t R,
+                      int64_t K, const void* B, int64_t C, int64_t ldb, int b_layout, const void* Y,
+                      int64_t ldy);
 int check_softmax_nm_rows(const void* values, int64_t rows, int64_t kept, int64_t ld);
 
 }  // namespace snm

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("snm_prune_encode_nm", "snm_prune_encode_vnm", "snm_spmm_nm", "snm_spmm_vnm",
               "snm_sddmm_prune_nm", "snm_softmax_nm_rows", "snm_sddmm_prune_nm_rowmax",
-              "snm_spmm_nm_softmax"):
+              "snm_spmm_nm_softmax", "snm_bitmap_sizes", "snm_bitmap_count", "snm_bitmap_encode",
+              "snm_spmm_bitmap"):
         assert n in names
 
 
@@ -164,6 +165,34 @@ def test_sddmm_rowmax_validation(args, status):
 ])
 def test_spmm_softmax_validation(args, status):
     assert _lib().snm_spmm_nm_softmax(*args) == status
+
+
+def test_bitmap_sizes_and_validation():
+    from structured_sparse_matrix_amd import bitmap_sizes, SnmError
+    _lib()
+    assert bitmap_sizes(9216, 9216) == (9216 * 144, 9216 * 144 + 1)
+    assert bitmap_sizes(0, 64) == (0, 1)
+    with pytest.raises(SnmError):
+        bitmap_sizes(4, 100)                     # K % 64
+    with pytest.raises(SnmError):
+        bitmap_sizes(1 << 16, 1 << 15)           # R*K >= 2^31
+    lib = _lib()
+    # count: A, R, K, lda, bitmaps, offsets, stream
+    assert lib.snm_bitmap_count(FAKE, 4, 96, 96, FAKE, FAKE, P(0)) == 2          # K % 64
+    assert lib.snm_bitmap_count(FAKE, 4, 64, 64, FAKE, P(0), P(0)) == 1          # offsets NULL
+    assert lib.snm_bitmap_count(FAKE, 4, 64, 60, FAKE, FAKE, P(0)) == 2          # lda < K
+    assert lib.snm_bitmap_count(FAKE, 4, 64, 72, P(0x1004), FAKE, P(0)) == 3     # bitmaps % 8
+    assert lib.snm_bitmap_count(MISALIGNED, 4, 64, 64, FAKE, FAKE, P(0)) == 3    # A % 16
+    # encode: A, R, K, lda, bitmaps, offsets, values, stream
+    assert lib.snm_bitmap_encode(FAKE, 4, 64, 64, P(0), FAKE, FAKE, P(0)) == 1   # bitmaps NULL
+    assert lib.snm_bitmap_encode(P(0), 0, 64, 64, P(0), FAKE, P(0), P(0)) == 0   # empty
+    # spmm: bitmaps, offsets, values, R, K, B, C, ldb, b_layout, Y, ldy, stream
+    assert lib.snm_spmm_bitmap(FAKE, FAKE, FAKE, 16, 64, FAKE, 40, 64, 1, FAKE, 40, P(0)) == 4   # C > 32
+    assert lib.snm_spmm_bitmap(FAKE, FAKE, FAKE, 16, 64, FAKE, 8, 64, 2, FAKE, 8, P(0)) == 4     # layout
+    assert lib.snm_spmm_bitmap(FAKE, FAKE, MISALIGNED, 16, 64, FAKE, 8, 64, 1, FAKE, 8, P(0)) == 3
+    assert lib.snm_spmm_bitmap(FAKE, FAKE, FAKE, 16, 64, FAKE, 8, 68, 1, FAKE, 8, P(0)) == 3     # ldb % 8
+    assert lib.snm_spmm_bitmap(FAKE, FAKE, FAKE, 16, 64, FAKE, 8, 32, 1, FAKE, 8, P(0)) == 2     # ldb < K
+    assert lib.snm_spmm_bitmap(P(0), P(0), P(0), 0, 64, P(0), 8, 64, 1, P(0), 8, P(0)) == 0      # R == 0
 
 
 def test_softmax_validation():

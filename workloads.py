@@ -91,6 +91,25 @@ def vnm_sweep():
     return pts
 
 
+# ---- unstructured sparsity in the bitmap format (Coruscant, Sec. 4 and 5.2) ----------------
+# The pages measure the kernel on OPT-30B / OPT-66B weight matrices (7168 x 7168 and
+# 9216 x 9216) pruned to 30-70 % unstructured sparsity, at N = 8 activations. Stand-in:
+# A ~ N(0, 0.02) with every entry below the s-quantile of |A| set to zero (magnitude
+# pruning over the whole matrix); B ~ N(0, 1).
+BITMAP_SHAPES = (7168, 9216)
+BITMAP_SPARSITY = (0.3, 0.5, 0.7)
+
+
+def pruned_unstructured(seed: int, R: int, K: int, sparsity: float, sigma: float = 0.02) -> np.ndarray:
+    """Gaussian fp16 matrix with the smallest-magnitude fraction `sparsity` zeroed."""
+    A = normal_f16(np.random.default_rng(seed), (R, K), sigma)
+    if sparsity > 0:
+        mag = np.abs(A.astype(np.float32))
+        t = np.quantile(mag, sparsity)
+        A[mag <= t] = 0
+    return A
+
+
 def weight_and_activations(w: Workload):
     """A (R x K) then one B (K x C) per entry of ``w.Cs``, from one generator."""
     rng = np.random.default_rng(w.seed)
