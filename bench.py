@@ -376,6 +376,89 @@ def bench_sweep(steps: int, warmup: int, families=None) -> dict:
     return {"workload": "vnm_sweep", "points": points}
 
 
+def bench_bitmap(steps: int, warmup: int) -> dict:
+    """Unstructured sparsity in the bitmap format (Coruscant, Sec. 3 and 5.2): OPT-30B /
+    OPT-66B weight shapes (7168 and 9216 square) at 30 / 50 / 70 % sparsity, activations
+    N = 8 / 16 / 32 stored column-major. Per point: the encoder (count + values), the
+    SpMM, and the dense fp16 product of the same shape (torch.matmul, the pages' dense
+    baseline), each over K back-to-back launches with one event pair. Inputs rotate over
+    enough copies (> 256 MiB) that the last-level cache cannot hold them. A is drawn on the
+    device (N(0, 0.02), seeded) and its smallest magnitudes are zeroed."""
+    import torch
+    from structured_sparse_matrix_amd import bitmap_sizes
+    from structured_sparse_matrix_amd._lib import load as load_lib, check
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = load_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(launch, nrot):
+        for i in range(warmup):
+            launch(i % nrot)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            launch(i % nrot)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps * 1e-3
+
+    gen = torch.Generator(device=dev)
+    points = []
+    for n in (7168, 9216):
+        for sp in (0.3, 0.5, 0.7):
+            gen.manual_seed(int(n + 100 * sp))
+            A = (torch.randn((n, n), generator=gen, device=dev) * 0.02).half()
+            mag = A.float().abs().flatten()
+            k = int(sp * mag.numel())
+            thr = mag.kthvalue(k).values if k > 0 else torch.tensor(-1.0, device=dev)
+            A[A.float().abs() <= thr] = 0
+            del mag
+            nt, no = bitmap_sizes(n, n)
+            bm = torch.empty((nt,), dtype=torch.int64, device=dev)
+            off = torch.empty((no,), dtype=torch.int32, device=dev)
+            check("snm_bitmap_count", lib.snm_bitmap_count(A.data_ptr(), n, n, n, bm.data_ptr(), off.data_ptr(), stream))
+            nv = int(off[-1].item())
+            fmt_bytes = nv * 2 + nt * 8 + no * 4
+            nrot = max(2, -(-(300 << 20) // fmt_bytes))
+            copies = []
+            for _ in range(nrot):
+                vals = torch.empty((nv,), dtype=torch.float16, device=dev)
+                check("snm_bitmap_encode", lib.snm_bitmap_encode(A.data_ptr(), n, n, n, bm.data_ptr(),
+                                                                 off.data_ptr(), vals.data_ptr(), stream))
+                copies.append((bm.clone(), off.clone(), vals))
+            enc = [(A.data_ptr(), bm.data_ptr(), off.data_ptr(), copies[0][2].data_ptr())]
+            t_enc = timed(lambda j: (lib.snm_bitmap_count(enc[0][0], n, n, n, enc[0][1], enc[0][2], stream),
+                                     lib.snm_bitmap_encode(enc[0][0], n, n, n, enc[0][1], enc[0][2], enc[0][3], stream)), 1)
+            point = {"n": n, "sparsity": sp, "values": nv,
+                     "format_bytes": fmt_bytes, "compression": fmt_bytes / (n * n * 2),
+                     "encode_us": t_enc * 1e6, "N": {}}
+            for N in (8, 16, 32):
+                X = [torch.randn((N, n), generator=gen, device=dev).half() for _ in range(nrot)]
+                Y = torch.empty((n, N), dtype=torch.float16, device=dev)
+                args = [(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr(), n, n, X[j].data_ptr(), N, n, 1,
+                         Y.data_ptr(), N, stream) for j, c in enumerate(copies)]
+                check("snm_spmm_bitmap", lib.snm_spmm_bitmap(*args[0]))
+                t_mm = timed(lambda j: lib.snm_spmm_bitmap(*args[j]), nrot)
+                Ad = [A] + [A.clone() for _ in range(min(nrot, 3) - 1)]
+                Yd = torch.empty((n, N), dtype=torch.float16, device=dev)
+                t_dense = timed(lambda j: torch.matmul(Ad[j % len(Ad)], X[j].t(), out=Yd), nrot)
+                byts = fmt_bytes + n * N * 2 + n * N * 2
+                point["N"][str(N)] = {"spmm_us": t_mm * 1e6, "GB/s": byts / t_mm / 1e9,
+                                      "hbm_frac": byts / t_mm / 1e9 / HBM_PEAK_GBS,
+                                      "dense_gemm_us": t_dense * 1e6, "speedup_vs_dense": t_dense / t_mm}
+                print(f"bitmap {n}x{n} s={sp} N={N}: spmm {t_mm * 1e6:7.1f} us {byts / t_mm / 1e9:7.0f} GB/s  "
+                      f"dense {t_dense * 1e6:7.1f} us  x{t_dense / t_mm:4.2f}  (compression {fmt_bytes / (n * n * 2):.3f})",
+                      file=sys.stderr, flush=True)
+                del Ad, X
+            points.append(point)
+            del A, copies
+            torch.cuda.empty_cache()
+    return {"workload": "bitmap", "points": points}
+
+
 def bench_energy(steps: int, warmup: int) -> dict:
     """Energy of the V:2:M encodings the GPU produces (VENOM, Sec. 5, Fig. 11): a 768 x 768
     Gaussian weight (seed 5; the size of the page's BERT-base query weight), V in
@@ -440,12 +523,16 @@ def main():
     ap.add_argument("--workload", default="nm_decode",
                     help="nm_decode (the headline line) or vnm_64_2_8 / vnm_128_2_16 / attention_2_4 "
                          "(per-kernel timings only) or vnm_sweep (the general V:N:M sweep) or energy "
-                         "(energy of the GPU's V:2:M encodings)")
+                         "(energy of the GPU's V:2:M encodings) or bitmap (unstructured sparsity, "
+                         "bitmap format)")
     ap.add_argument("--streams", type=int, default=2,
                     help="decode steps in flight (step i on stream i %% S); kernel timings use one")
     ap.add_argument("--families", default="",
                     help="with --workload vnm_sweep: comma-separated subset of fig9,fig10,gpt3")
     args = ap.parse_args()
+    if args.workload == "bitmap":
+        print(json.dumps(bench_bitmap(args.steps, args.warmup)))
+        return
     if args.workload == "energy":
         print(json.dumps(bench_energy(args.steps, args.warmup)))
         return

@@ -11,7 +11,7 @@
 //   * the encoder runs in three steps -- per-row bitmaps, padded counts and in-row
 //     offsets; one workgroup scanning the row totals; the final offsets -- then writes
 //     the values in a separate call, once the caller has allocated them.
-//   * the product: one workgroup per 16 rows, four waves splitting K; each wave copies its
+//   * the product: one workgroup per 16 rows, eight waves splitting K; each wave copies its
 //     rows' packed values for a phase of 4 tiles (16-byte aligned spans, because every
 //     tile starts at a multiple of 8 values) into its own LDS region with the
 //     global->LDS DMA, then expands each 8-position chunk through its bitmap byte with
@@ -171,8 +171,9 @@ __device__ __forceinline__ f4 mfma16x16x32(const h8& a, const h8& b, const f4& c
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// One workgroup (4 waves) per 16-row tile; wave w takes a contiguous quarter of the row's
-// tiles and walks it in phases of 4 tiles (256 positions). Lane l = 16q + i works on row
+// One workgroup (kBmWaves waves) per 16-row tile; wave w takes a contiguous 1/kBmWaves of
+// the row's tiles and walks it in phases of 4 tiles (256 positions). Eight waves and two
+// workgroups per CU keep sixteen phases' loads in flight per CU. Lane l = 16q + i works on row
 // i; in tile t it covers positions 32 blk + 8q + [0, 8), blk = 0, 1 (bitmap byte
 // 4 blk + q) -- the dense MFMA A operand of k-block (t, blk).
 // Per phase: (1) the packed values of the phase's 4 tiles of every row of the tile (a
@@ -182,9 +183,34 @@ __device__ __forceinline__ f4 mfma16x16x32(const h8& a, const h8& b, const f4& c
 // loaded; (3) each chunk is expanded through its bitmap byte -- the e-th set bit takes
 // the next value of the span, at LDS byte 512 i + 2 (tile offset - span start + rank) --
 // and multiplied on the matrix core.
+constexpr int kBmWaves = 8;
+constexpr int kWaveBytes = 8192;                      // staged values of one wave
+constexpr int kLutOff = kBmWaves * kWaveBytes + 16;   // + a pad that over-reads may touch
+constexpr int kLutBytes = 256 * 16 + 256 * 8;
+constexpr int kBitmapLds = kLutOff + kLutBytes;
+
 template <int CT, bool BCOL>
-__global__ void __launch_bounds__(256) k_spmm_bitmap(BitmapArgs a) {
-  __shared__ __align__(16) uint8_t smem[4 * 8192];
+__global__ void __launch_bounds__(64 * kBmWaves) __attribute__((amdgpu_waves_per_eu(4)))
+k_spmm_bitmap(BitmapArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];   // 8 KiB per wave, then the expansion table
+  // Expansion table, one entry per bitmap byte m: four dwords of 16-bit keep masks (0xFFFF
+  // where bit e of m is set) and two dwords of eight byte offsets (2 rank_e, rank_e = set
+  // bits of m below e). Expanding a chunk is then one address add and one read per
+  // position, and one AND per pair of positions.
+  for (int m = threadIdx.x; m < 256; m += 64 * kBmWaves) {
+    uint32_t mk[4], rk[2] = {0u, 0u}, r = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      rk[e >> 2] |= (2u * r) << (8 * (e & 3));
+      r += (m >> e) & 1;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      mk[i] = (((m >> (2 * i)) & 1) ? 0xFFFFu : 0u) | (((m >> (2 * i + 1)) & 1) ? 0xFFFF0000u : 0u);
+    *reinterpret_cast<u4*>(smem + kLutOff + 16 * m) = u4{mk[0], mk[1], mk[2], mk[3]};
+    *reinterpret_cast<u2*>(smem + kLutOff + 4096 + 8 * m) = u2{rk[0], rk[1]};
+  }
+  __syncthreads();
   constexpr int kPhaseTiles = 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -195,10 +221,10 @@ __global__ void __launch_bounds__(256) k_spmm_bitmap(BitmapArgs a) {
   const int64_t row = row0 + li;
   const bool row_ok = row < a.R;
   const int64_t T = a.K / kTile;
-  const int64_t tw = (T + 3) / 4;                       // tiles per wave
+  const int64_t tw = (T + kBmWaves - 1) / kBmWaves;     // tiles per wave
   const int64_t tbeg = (int64_t)w * tw;
   const int64_t tend = tbeg + tw < T ? tbeg + tw : T;
-  uint8_t* const wl = smem + w * 8192;
+  uint8_t* const wl = smem + w * kWaveBytes;
   const uint32_t wl_lds = lds_addr(wl);
 
   f4 acc[CT];
@@ -260,17 +286,22 @@ __global__ void __launch_bounds__(256) k_spmm_bitmap(BitmapArgs a) {
       for (int blk = 0; blk < 2; ++blk) {
         const int byte = 4 * blk + q;
         const uint64_t below = byte == 0 ? 0ull : (bm[t] & ((1ull << (8 * byte)) - 1ull));
-        uint32_t e_idx = (off[t] - span0) + (uint32_t)__popcll(below);
+        // first value of the chunk; a position past the last set bit reads at most one
+        // value beyond the row's span (inside the wave region, or the pad after the last)
+        const uint32_t a0 = rbase + 2u * ((off[t] - span0) + (uint32_t)__popcll(below));
         const uint32_t m = (uint32_t)(bm[t] >> (8 * byte)) & 0xFFu;
-        h8 av;
+        const u4 keep = *reinterpret_cast<const u4*>(smem + kLutOff + 16u * m);
+        const u2 rk = *reinterpret_cast<const u2*>(smem + kLutOff + 4096u + 8u * m);
+        u4 pk;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t bit = (m >> e) & 1u;
-          const uint32_t ix = e_idx < 256u ? e_idx : 255u;   // always inside the row's 512 bytes
-          const uint16_t x = *reinterpret_cast<const uint16_t*>(wl + rbase + 2u * ix);
-          av[e] = bits_f16(bit ? x : (uint16_t)0);
-          e_idx += bit;
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = rk[i >> 1];
+          const int sh = 16 * (i & 1);
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(wl + a0 + ((w >> sh) & 0xFFu));
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(wl + a0 + ((w >> (sh + 8)) & 0xFFu));
+          pk[i] = (lo | (hi << 16)) & keep[i];
         }
+        const h8 av = __builtin_bit_cast(h8, pk);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma16x16x32(av, bop[t][blk][ct], acc[ct]);
         // scheduling fence: expand block by block (hoisting every block's LDS reads would
@@ -281,14 +312,14 @@ __global__ void __launch_bounds__(256) k_spmm_bitmap(BitmapArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // LDS reads done before the next DMA
   }
 
-  // ---- sum the 4 partial tiles and store Y --------------------------------------------------
+  // ---- sum the partial tiles of the waves and store Y -------------------------------------
   __syncthreads();
   f4* red = reinterpret_cast<f4*>(smem);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) red[(w * CT + ct) * 64 + lane] = acc[ct];
   __syncthreads();
   // D layout of the 16x16 MFMA: column l % 16, element r -> row 4 (l / 16) + r
-  for (int e = tid; e < 16 * 16 * CT; e += 256) {
+  for (int e = tid; e < 16 * 16 * CT; e += 64 * kBmWaves) {
     const int rr = e / (16 * CT);
     const int cc = e - rr * 16 * CT;
     const int ct = cc >> 4;
@@ -296,7 +327,7 @@ __global__ void __launch_bounds__(256) k_spmm_bitmap(BitmapArgs a) {
     const float* rp = reinterpret_cast<const float*>(red);
     float s = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) s += rp[((ww * CT + ct) * 64 + ln) * 4 + (rr & 3)];
+    for (int ww = 0; ww < kBmWaves; ++ww) s += rp[((ww * CT + ct) * 64 + ln) * 4 + (rr & 3)];
     const int64_t orow = row0 + rr;
     if (orow < a.R && cc < a.C) a.Y[orow * a.ldy + cc] = f16_bits(to_f16(s));
   }
@@ -341,14 +372,21 @@ hipError_t launch_spmm_bitmap(const uint64_t* bitmaps, const uint32_t* offsets, 
   a.R = R; a.K = K; a.C = C; a.ldb = ldb; a.ldy = ldy;
   a.b_col = b_layout == 1;
   const unsigned g = (unsigned)((R + 15) / 16);
-  if (b_layout == 1) {
-    if (C > 16) hipLaunchKernelGGL((k_spmm_bitmap<2, true>), dim3(g), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((k_spmm_bitmap<1, true>), dim3(g), dim3(256), 0, stream, a);
-  } else {
-    if (C > 16) hipLaunchKernelGGL((k_spmm_bitmap<2, false>), dim3(g), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((k_spmm_bitmap<1, false>), dim3(g), dim3(256), 0, stream, a);
-  }
-  return hipGetLastError();
+  const size_t lds = (size_t)kBitmapLds;   // 69 KiB: two workgroups per CU
+  const dim3 blk(64 * kBmWaves);
+  auto go = [&](auto kern) -> hipError_t {
+    static bool set[2][2] = {};
+    bool& done = set[C > 16][b_layout == 1];
+    if (!done) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      done = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(g), blk, lds, stream, a);
+    return hipGetLastError();
+  };
+  if (b_layout == 1) return C > 16 ? go(k_spmm_bitmap<2, true>) : go(k_spmm_bitmap<1, true>);
+  return C > 16 ? go(k_spmm_bitmap<2, false>) : go(k_spmm_bitmap<1, false>);
 }
 
 }  // namespace snm
