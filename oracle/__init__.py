@@ -18,6 +18,8 @@ function names the passage of the pages it follows:
   (oracle/energy.py).
 * "Coruscant: Co-Designing GPU Kernel and Sparse Tensor Core ...", Sec. 3.1,
   Fig. 7 and Sec. 3.2: the bitmap sparse format (oracle/bitmap.py).
+* The attention page's data-type variants, Sec. 1, Fig. 1-3 and Sec. 4.2:
+  bf16 scores with 2:4 and fp32 scores with 1:2 (oracle/variants.py).
 
 Every function here is pinned by at least one CPU test against a printed
 worked example, a closed form, an invariant, a reduction to a textbook case or
@@ -29,6 +31,7 @@ from .vnm import column_scores, prune_encode_vnm, decode_vnm, spmm_vnm
 from .attention import sddmm_prune_nm, softmax_nm_rows, attention_nm, full_attention
 from . import energy
 from . import bitmap
+from . import variants
 
 __all__ = [
     "magnitude_key", "select_top_n", "prune_encode_nm", "decode_nm", "spmm_nm", "NM_LEGAL_CODES",
