@@ -230,6 +230,39 @@ int snm_spmm_bitmap(const void* bitmaps, const void* tile_offsets, const void* v
  * p = exp(v - max) / sum exp(v - max) per row, in fp32, rounded to fp16 (RNE). */
 int snm_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream);
 
+/* bf16 variant of dynamic 2:4 attention ("Dynamic N:M ... attention", Sec. 4.2: 16-bit
+ * scores of either fp16 or bf16 are pruned 2 of 4 in every 8 bytes). Every element buffer
+ * below holds bf16 instead of fp16; layouts, metadata, the selection rule (on the 16-bit
+ * patterns: magnitude bits, lower slot wins ties) and all requirements are those of the
+ * fp16 call of the same name. Every bf16 result is one round-to-nearest-even of an fp32
+ * value; products and sums are in fp32.
+ *
+ * snm_sddmm_prune_nm_bf16: snm_sddmm_prune_nm on bf16 Q, Kmat, values (and S_dense);
+ *   row_max optional (NULL: not written): as in snm_sddmm_prune_nm_rowmax. */
+int snm_sddmm_prune_nm_bf16(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                            int64_t Lk, int64_t d, float scale, void* values, void* meta,
+                            void* S_dense, float* row_max, void* stream);
+
+/* snm_softmax_nm_rows_bf16: snm_softmax_nm_rows on bf16 rows. */
+int snm_softmax_nm_rows_bf16(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream);
+
+/* snm_spmm_nm_bf16: snm_spmm_nm with b_layout 0 on bf16 values, B and Y, batched the same
+ * way. Requires, beyond the rules of snm_spmm_nm: C % 8 == 0, ldb % 8 == 0, B 16-byte
+ * aligned (and stride_B % 8 == 0 when batch > 1), 128*K < 2^31 and (256*ldb + C)*2 < 2^31;
+ * otherwise SNM_E_ALIGN or SNM_E_SHAPE. K == 0 writes zeros. */
+int snm_spmm_nm_bf16(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
+                     int64_t C, int64_t ldb, void* Y, int64_t ldy, int64_t batch,
+                     int64_t stride_values, int64_t stride_meta, int64_t stride_B,
+                     int64_t stride_Y, void* stream);
+
+/* snm_spmm_nm_softmax_bf16: snm_spmm_nm_softmax on bf16 values, B and Y; the probabilities
+ * are p = bf16_RNE(exp(v - row_max)). */
+int snm_spmm_nm_softmax_bf16(const void* values, const void* meta, const float* row_max,
+                             int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb, void* Y,
+                             int64_t ldy, int64_t batch, int64_t stride_values,
+                             int64_t stride_meta, int64_t stride_row_max, int64_t stride_B,
+                             int64_t stride_Y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,7 @@ Layouts (canonical, see include/snm.h):
   V:2:M   values fp16 [R, 2K/M], midx uint8 [R, K/(2M)], colloc uint8 [R/V, K/M, 4]
   bitmap  bitmaps [R, K/64] (64-bit words, held in int64), tile_offsets [R*K/64 + 1]
           (uint32 values, held in int32), values fp16 [tile_offsets[-1]]
+The ``*_bf16`` functions are the same operations on bf16 tensors (same layouts).
 """
 from __future__ import annotations
 
@@ -24,6 +25,8 @@ __all__ = [
     "nm_tiled_sizes", "prune_encode_nm_tiled", "spmm_nm_tiled",
     "sddmm_prune_nm_rowmax", "spmm_nm_softmax", "attention_nm_fused",
     "bitmap_sizes", "bitmap_encode", "spmm_bitmap",
+    "sddmm_prune_nm_bf16", "softmax_nm_rows_bf16", "spmm_nm_bf16", "spmm_nm_softmax_bf16",
+    "attention_nm_bf16", "attention_nm_fused_bf16",
     "LIB_PATH",
 ]
 
@@ -178,7 +181,7 @@ def spmm_nm(values, meta, B, out=None):
         raise ValueError(f"shape mismatch: values {tuple(values.shape)}, meta {tuple(meta.shape)}, "
                          f"B {tuple(B.shape)}")
     for t, n in ((values, "values"), (meta, "meta")):
-        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        if t.shape[2] and (t.stride(2) != 1 or t.stride(1) != t.shape[2]):
             raise ValueError(f"{n} must be contiguous per batch entry")
     layout, ldb = _b_layout(B)
     C = B.shape[2]
@@ -281,7 +284,7 @@ def spmm_nm_softmax(values, meta, row_max, B, out=None):
         raise ValueError(f"shape mismatch: values {tuple(values.shape)}, meta {tuple(meta.shape)}, "
                          f"row_max {tuple(row_max.shape)}, B {tuple(B.shape)}")
     for t, n in ((values, "values"), (meta, "meta")):
-        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        if t.shape[2] and (t.stride(2) != 1 or t.stride(1) != t.shape[2]):
             raise ValueError(f"{n} must be contiguous per batch entry")
     if row_max.stride(1) != 1:
         raise ValueError("row_max must be contiguous per batch entry")
@@ -384,3 +387,121 @@ def attention_nm_fused(Q, Kmat, Vmat, scale=None):
     Same arguments and result as attention_nm."""
     values, meta, row_max = sddmm_prune_nm_rowmax(Q, Kmat, scale)
     return spmm_nm_softmax(values, meta, row_max, Vmat)
+
+
+# ---------------------------------------------------------------------------------------
+# bf16 variants (same layouts; every element buffer holds bf16)
+
+def _qk(Q, Kmat, dtype, scale):
+    _need(Q, "Q", dtype, 3)
+    _need(Kmat, "Kmat", dtype, 3)
+    if not (Q.is_contiguous() and Kmat.is_contiguous()):
+        raise ValueError("Q and Kmat must be contiguous")
+    nb, Lq, d = Q.shape
+    if Kmat.shape[0] != nb or Kmat.shape[2] != d:
+        raise ValueError("Q and Kmat disagree in batch or head_dim")
+    return nb, Lq, Kmat.shape[1], d, (1.0 / math.sqrt(d) if scale is None else float(scale))
+
+
+def sddmm_prune_nm_bf16(Q, Kmat, scale=None, return_dense=False, return_rowmax=False):
+    """bf16 scores S = bf16((Q @ Kmat^T) * scale) pruned 2:4 along the key axis.
+    Returns (values, meta), plus S [b, Lq, Lk] if return_dense and row_max fp32 [b, Lq]
+    (largest kept score per row) if return_rowmax, in that order."""
+    torch = _torch()
+    nb, Lq, Lk, d, scale = _qk(Q, Kmat, torch.bfloat16, scale)
+    values = torch.empty((nb, Lq, Lk // 2), dtype=torch.bfloat16, device=Q.device)
+    meta = torch.empty((nb, Lq, Lk // 8), dtype=torch.uint8, device=Q.device)
+    S = torch.empty((nb, Lq, Lk), dtype=torch.bfloat16, device=Q.device) if return_dense else None
+    rmax = torch.empty((nb, Lq), dtype=torch.float32, device=Q.device) if return_rowmax else None
+    check("snm_sddmm_prune_nm_bf16",
+          load().snm_sddmm_prune_nm_bf16(_ptr(Q), _ptr(Kmat), nb, Lq, Lk, d, scale, _ptr(values), _ptr(meta),
+                                         _ptr(S), _ptr(rmax), _stream(Q)))
+    return (values, meta) + ((S,) if return_dense else ()) + ((rmax,) if return_rowmax else ())
+
+
+def softmax_nm_rows_bf16(values):
+    """In-place softmax over the last axis of compressed bf16 rows (kept entries only)."""
+    torch = _torch()
+    _need(values, "values", torch.bfloat16)
+    if values.stride(-1) != 1:
+        raise ValueError("values must have unit stride along the last axis")
+    kept = values.shape[-1]
+    rows = values.numel() // kept if kept else 0
+    ld = values.stride(-2) if values.dim() >= 2 else kept
+    if values.dim() > 2 and not values.is_contiguous():
+        raise ValueError("batched values must be contiguous")
+    check("snm_softmax_nm_rows_bf16", load().snm_softmax_nm_rows_bf16(_ptr(values), rows, kept, ld,
+                                                                      _stream(values)))
+    return values
+
+
+def _rowmajor_spmm_args(values, meta, B, out, dtype, row_max=None):
+    """Shapes of a batched 2:4 product with row-major B; adds the batch axis to 2-D input."""
+    torch = _torch()
+    _need(values, "values", dtype, (2, 3))
+    _need(meta, "meta", torch.uint8, values.dim())
+    _need(B, "B", dtype, values.dim())
+    if row_max is not None:
+        _need(row_max, "row_max", torch.float32, values.dim() - 1)
+    batched = values.dim() == 3
+    if not batched:
+        values, meta, B = values[None], meta[None], B[None]
+        row_max = row_max[None] if row_max is not None else None
+        out = out[None] if out is not None else None
+    nb, R, half_k = values.shape
+    K = 2 * half_k
+    if B.shape[0] != nb or B.shape[1] != K or meta.shape != (nb, R, K // 8) or \
+            (row_max is not None and row_max.shape != (nb, R)):
+        raise ValueError(f"shape mismatch: values {tuple(values.shape)}, meta {tuple(meta.shape)}, "
+                         f"B {tuple(B.shape)}")
+    for t, n in ((values, "values"), (meta, "meta")):
+        if t.shape[2] and (t.stride(2) != 1 or t.stride(1) != t.shape[2]):
+            raise ValueError(f"{n} must be contiguous per batch entry")
+    if row_max is not None and row_max.stride(1) != 1:
+        raise ValueError("row_max must be contiguous per batch entry")
+    if B.stride(2) != 1:
+        raise ValueError("B must be row-major (unit stride along C)")
+    C = B.shape[2]
+    if out is None:
+        out = torch.empty((nb, R, C), dtype=dtype, device=B.device)
+    if out.stride(2) != 1:
+        raise ValueError("out must be row-major")
+    return batched, values, meta, B, out, row_max, nb, R, K, C
+
+
+def spmm_nm_bf16(values, meta, B, out=None):
+    """Y = decode(values, meta) @ B on bf16 (row-major B). 2-D: values [R, K/2], meta [R, K/8],
+    B [K, C] -> Y [R, C]; 3-D: one more leading batch axis."""
+    torch = _torch()
+    batched, values, meta, B, out, _, nb, R, K, C = _rowmajor_spmm_args(values, meta, B, out, torch.bfloat16)
+    check("snm_spmm_nm_bf16",
+          load().snm_spmm_nm_bf16(_ptr(values), _ptr(meta), R, K, _ptr(B), C, B.stride(1), _ptr(out),
+                                  out.stride(1), nb, values.stride(0), meta.stride(0), B.stride(0),
+                                  out.stride(0), _stream(B)))
+    return out if batched else out[0]
+
+
+def spmm_nm_softmax_bf16(values, meta, row_max, B, out=None):
+    """spmm_nm_softmax on bf16 scores, B and Y."""
+    torch = _torch()
+    batched, values, meta, B, out, row_max, nb, R, K, C = _rowmajor_spmm_args(values, meta, B, out,
+                                                                             torch.bfloat16, row_max)
+    check("snm_spmm_nm_softmax_bf16",
+          load().snm_spmm_nm_softmax_bf16(_ptr(values), _ptr(meta), _ptr(row_max), R, K, _ptr(B), C,
+                                          B.stride(1), _ptr(out), out.stride(1), nb, values.stride(0),
+                                          meta.stride(0), row_max.stride(0), B.stride(0), out.stride(0),
+                                          _stream(B)))
+    return out if batched else out[0]
+
+
+def attention_nm_bf16(Q, Kmat, Vmat, scale=None):
+    """attention_nm on bf16 Q, Kmat, Vmat: SDDMM-prune, softmax over kept entries, 2:4 SpMM."""
+    values, meta = sddmm_prune_nm_bf16(Q, Kmat, scale)
+    softmax_nm_rows_bf16(values)
+    return spmm_nm_bf16(values, meta, Vmat)
+
+
+def attention_nm_fused_bf16(Q, Kmat, Vmat, scale=None):
+    """attention_nm_fused on bf16: the SDDMM writes row maxima, the SpMM applies the softmax."""
+    values, meta, row_max = sddmm_prune_nm_bf16(Q, Kmat, scale, return_rowmax=True)
+    return spmm_nm_softmax_bf16(values, meta, row_max, Vmat)

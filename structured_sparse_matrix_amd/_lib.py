@@ -37,6 +37,11 @@ SIGNATURES = {
     "snm_sddmm_prune_nm_rowmax": [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp],
     "snm_spmm_nm_softmax": [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
                             _i64, _i64, _vp],
+    "snm_sddmm_prune_nm_bf16": [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp],
+    "snm_softmax_nm_rows_bf16": [_vp, _i64, _i64, _i64, _vp],
+    "snm_spmm_nm_bf16": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
+    "snm_spmm_nm_softmax_bf16": [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64,
+                                 _i64, _i64, _i64, _vp],
 }
 
 STATUS = {0: "SNM_OK", 1: "SNM_E_NULL", 2: "SNM_E_SHAPE", 3: "SNM_E_ALIGN",

@@ -143,7 +143,7 @@ int snm_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t L
   if (s != SNM_OK || batch == 0 || Lq == 0 || Lk == 0) return s;
   if ((s = check_device()) != SNM_OK) return s;
   return launched(snm::launch_sddmm_prune_nm(Q, Kmat, batch, Lq, Lk, d, scale, values, meta,
-                                             S_dense, nullptr, (hipStream_t)stream));
+                                             S_dense, nullptr, false, (hipStream_t)stream));
 }
 
 int snm_sddmm_prune_nm_rowmax(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
@@ -153,7 +153,30 @@ int snm_sddmm_prune_nm_rowmax(const void* Q, const void* Kmat, int64_t batch, in
   if (s != SNM_OK || batch == 0 || Lq == 0 || Lk == 0) return s;
   if ((s = check_device()) != SNM_OK) return s;
   return launched(snm::launch_sddmm_prune_nm(Q, Kmat, batch, Lq, Lk, d, scale, values, meta,
-                                             nullptr, row_max, (hipStream_t)stream));
+                                             nullptr, row_max, false, (hipStream_t)stream));
+}
+
+int snm_sddmm_prune_nm_bf16(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                            int64_t Lk, int64_t d, float scale, void* values, void* meta,
+                            void* S_dense, float* row_max, void* stream) {
+  int s = snm::check_sddmm_prune_nm_bf16(Q, Kmat, batch, Lq, Lk, d, values, meta, S_dense, row_max);
+  if (s != SNM_OK || batch == 0 || Lq == 0 || Lk == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_sddmm_prune_nm(Q, Kmat, batch, Lq, Lk, d, scale, values, meta,
+                                             S_dense, row_max, true, (hipStream_t)stream));
+}
+
+int snm_spmm_nm_bf16(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
+                     int64_t C, int64_t ldb, void* Y, int64_t ldy, int64_t batch,
+                     int64_t stride_values, int64_t stride_meta, int64_t stride_B,
+                     int64_t stride_Y, void* stream) {
+  int s = snm::check_spmm_nm_bf16(values, meta, R, K, B, C, ldb, Y, ldy, batch, stride_values,
+                                  stride_meta, stride_B, stride_Y);
+  if (s != SNM_OK || R == 0 || C == 0 || batch == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_spmm_nm_bf16(values, meta, R, K, B, C, ldb, Y, ldy, batch,
+                                           stride_values, stride_meta, stride_B, stride_Y,
+                                           (hipStream_t)stream));
 }
 
 int snm_spmm_nm_softmax(const void* values, const void* meta, const float* row_max, int64_t R,
@@ -167,7 +190,22 @@ int snm_spmm_nm_softmax(const void* values, const void* meta, const float* row_m
   if ((s = check_device()) != SNM_OK) return s;
   return launched(snm::launch_spmm_nm_softmax(values, meta, row_max, R, K, B, C, ldb, Y, ldy,
                                               batch, stride_values, stride_meta, stride_row_max,
-                                              stride_B, stride_Y, (hipStream_t)stream));
+                                              stride_B, stride_Y, false, (hipStream_t)stream));
+}
+
+int snm_spmm_nm_softmax_bf16(const void* values, const void* meta, const float* row_max,
+                             int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb, void* Y,
+                             int64_t ldy, int64_t batch, int64_t stride_values,
+                             int64_t stride_meta, int64_t stride_row_max, int64_t stride_B,
+                             int64_t stride_Y, void* stream) {
+  int s = snm::check_spmm_nm_softmax(values, meta, row_max, R, K, B, C, ldb, Y, ldy, batch,
+                                     stride_values, stride_meta, stride_row_max, stride_B,
+                                     stride_Y);
+  if (s != SNM_OK || R == 0 || C == 0 || batch == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_spmm_nm_softmax(values, meta, row_max, R, K, B, C, ldb, Y, ldy,
+                                              batch, stride_values, stride_meta, stride_row_max,
+                                              stride_B, stride_Y, true, (hipStream_t)stream));
 }
 
 int snm_bitmap_sizes(int64_t R, int64_t K, int64_t* n_tiles, int64_t* n_offsets) {
@@ -215,7 +253,14 @@ int snm_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, vo
   int s = snm::check_softmax_nm_rows(values, rows, kept, ld);
   if (s != SNM_OK || rows == 0 || kept == 0) return s;
   if ((s = check_device()) != SNM_OK) return s;
-  return launched(snm::launch_softmax_nm_rows(values, rows, kept, ld, (hipStream_t)stream));
+  return launched(snm::launch_softmax_nm_rows(values, rows, kept, ld, false, (hipStream_t)stream));
+}
+
+int snm_softmax_nm_rows_bf16(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream) {
+  int s = snm::check_softmax_nm_rows(values, rows, kept, ld);
+  if (s != SNM_OK || rows == 0 || kept == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_softmax_nm_rows(values, rows, kept, ld, true, (hipStream_t)stream));
 }
 
 }  // extern "C"

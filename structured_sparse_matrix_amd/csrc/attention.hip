@@ -9,7 +9,10 @@
 // operands are rows of Q and K read as stored (d contiguous).
 //
 // k_softmax_rows: row softmax over the kept values only, in place.
-#include "device_common.hpp"
+//
+// Both kernels take fp16 or bf16 (template BF): the page prunes 16-bit scores of either
+// type 2:4 (Sec. 4.2); the selection works on bit patterns and is the same for both.
+#include "elem.hpp"
 #include "launch.hpp"
 
 namespace snm {
@@ -42,15 +45,17 @@ struct SddmmCfg {
   static constexpr int kQueries = kWaves * 32 * QT;   // per workgroup
 };
 
-// DENSE: also write the pre-prune fp16 S (the optional debug output).
+// DENSE: also write the pre-prune 16-bit S (the optional debug output).
 // RMAX: also write, per query row, the largest kept score (the fused-softmax variant's
-// statistic; a packed fp16 running maximum per lane, two lanes per row).
-template <int D, int QT, bool DENSE, bool RMAX>
+// statistic; a running maximum per lane, two lanes per row: packed fp16, or fp32 for bf16).
+// BF: bf16 operands and scores instead of fp16.
+template <int D, int QT, bool DENSE, bool RMAX, bool BF>
 __global__ void __launch_bounds__(512)
 k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, int64_t batch,
               int64_t Lq, int64_t Lk, float scale, uint16_t* __restrict__ values,
               uint16_t* __restrict__ meta, uint16_t* __restrict__ S, float* __restrict__ rowmax) {
   using Cfg = SddmmCfg<D, QT>;
+  using E = Elem<BF>;
   constexpr int KSTEPS = Cfg::KSTEPS, KT = Cfg::KT, MT = Cfg::MT, VP = Cfg::VP, MP = Cfg::MP;
   extern __shared__ __align__(16) uint8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -95,9 +100,13 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
     load_k(0, kr[0]);
     load_k(1, kr[1]);
     load_k(2, kr[2]);
-    hh2 rmx[QT];   // running max of the kept scores of each query tile's row (RMAX)
+    hh2 rmx[QT];     // running max of the kept scores of each query tile's row (RMAX, fp16)
+    float rmf[QT];   // the same for bf16
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) rmx[qt] = hh2{(_Float16)-__builtin_inff(), (_Float16)-__builtin_inff()};
+    for (int qt = 0; qt < QT; ++qt) {
+      rmx[qt] = hh2{(_Float16)-__builtin_inff(), (_Float16)-__builtin_inff()};
+      rmf[qt] = -__builtin_inff();
+    }
 
     for (int64_t t0 = 0; t0 < nkt; t0 += KT) {
       const int nk = (int)(nkt - t0 < KT ? nkt - t0 : KT);
@@ -110,7 +119,7 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
         auto chain = [&](int qt) {
           f16v acc = {};
 #pragma unroll
-          for (int j = 0; j < KSTEPS; ++j) acc = mfma32x32x16(kr[kt][j], qf[qt][j], acc);
+          for (int j = 0; j < KSTEPS; ++j) acc = E::mfma32x32x16(kr[kt][j], qf[qt][j], acc);
           return acc;
         };
         const int mcol = (int)(t % MT);   // metadata word column of this tile
@@ -126,15 +135,16 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
           for (int gi = 0; gi < 4; ++gi) {
             const f2 x01 = {acc[4 * gi] * scale, acc[4 * gi + 1] * scale};
             const f2 x23 = {acc[4 * gi + 2] * scale, acc[4 * gi + 3] * scale};
-            const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(x01, hh2));
-            const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(x23, hh2));
+            const uint32_t p01 = E::pack2(x01);
+            const uint32_t p23 = E::pack2(x23);
             if (DENSE && qi < Lq) {
               const u2 pk = {p01, p23};
               *reinterpret_cast<u2*>(S_b + qi * Lk + kk + 8 * gi + 4 * half) = pk;
             }
             uint32_t kept;
             const uint32_t code = select_2of4_keys(p01, p23, kept);
-            if constexpr (RMAX) rmx[qt] = __builtin_elementwise_max(rmx[qt], __builtin_bit_cast(hh2, kept));
+            if constexpr (RMAX && !BF) rmx[qt] = __builtin_elementwise_max(rmx[qt], __builtin_bit_cast(hh2, kept));
+            if constexpr (RMAX && BF) rmf[qt] = fmaxf(rmf[qt], fmaxf(E::lo(kept), E::hi(kept)));
             // kept pair of group (kk + 8gi + 4half)/4 -> value position kt*16 + 4gi + 2half
             *reinterpret_cast<uint32_t*>(sv + (qt * 32 + l32) * VP + (kt * 16 + 4 * gi + 2 * half) * 2) = kept;
             mword |= code << (8 * gi + 4 * half);
@@ -186,7 +196,7 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
     if constexpr (RMAX) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        float m = fmaxf((float)rmx[qt][0], (float)rmx[qt][1]);
+        float m = BF ? rmf[qt] : fmaxf((float)rmx[qt][0], (float)rmx[qt][1]);
         m = fmaxf(m, __shfl_xor(m, 32));   // lanes l and l+32 hold the two halves of a row
         const int64_t qi = q_wave + qt * 32 + l32;
         if (!half && qi < Lq) rowmax[b * Lq + qi] = m;
@@ -196,24 +206,25 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
 }
 
 // Row softmax over kept values, one wave per row. Rows of up to 64*8*CH elements stay in
-// registers (one read, one write); longer rows are streamed three times.
-template <int CH>
+// registers (one read, one write); longer rows are streamed three times. BF: bf16 values.
+template <int CH, bool BF>
 __global__ void __launch_bounds__(256)
 k_softmax_rows(uint16_t* __restrict__ vals, int64_t rows, int64_t kept, int64_t ld, int vec) {
+  using E = Elem<BF>;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   uint16_t* v = vals + row * ld;
   float mx = -__builtin_inff();
   if (vec && kept <= 64 * 8 * CH) {
-    h8 x[CH];
+    h8 x[CH];   // 16-bit containers of either type
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int64_t e = ((int64_t)c * 64 + lane) * 8;
       if (e < kept) {
         x[c] = *reinterpret_cast<const h8*>(v + e);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) mx = fmaxf(mx, (float)x[c][t]);
+        for (int t = 0; t < 8; ++t) mx = fmaxf(mx, E::widen(f16_bits(x[c][t])));
       }
     }
 #pragma unroll
@@ -225,7 +236,7 @@ k_softmax_rows(uint16_t* __restrict__ vals, int64_t rows, int64_t kept, int64_t 
       const int64_t e = ((int64_t)c * 64 + lane) * 8;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        ex[c][t] = e < kept ? __expf((float)x[c][t] - mx) : 0.f;
+        ex[c][t] = e < kept ? __expf(E::widen(f16_bits(x[c][t])) - mx) : 0.f;
         sum += ex[c][t];
       }
     }
@@ -236,33 +247,33 @@ k_softmax_rows(uint16_t* __restrict__ vals, int64_t rows, int64_t kept, int64_t 
     for (int c = 0; c < CH; ++c) {
       const int64_t e = ((int64_t)c * 64 + lane) * 8;
       if (e < kept) {
-        h8 o;
+        u4 o;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) o[t] = to_f16(ex[c][t] * inv);
-        *reinterpret_cast<h8*>(v + e) = o;
+        for (int t = 0; t < 4; ++t) o[t] = E::pack2(f2{ex[c][2 * t] * inv, ex[c][2 * t + 1] * inv});
+        *reinterpret_cast<u4*>(v + e) = o;
       }
     }
     return;
   }
-  for (int64_t e = lane; e < kept; e += 64) mx = fmaxf(mx, (float)bits_f16(v[e]));
+  for (int64_t e = lane; e < kept; e += 64) mx = fmaxf(mx, E::widen(v[e]));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   float sum = 0.f;
-  for (int64_t e = lane; e < kept; e += 64) sum += __expf((float)bits_f16(v[e]) - mx);
+  for (int64_t e = lane; e < kept; e += 64) sum += __expf(E::widen(v[e]) - mx);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
   const float inv = 1.0f / sum;
-  for (int64_t e = lane; e < kept; e += 64) v[e] = f16_bits(to_f16(__expf((float)bits_f16(v[e]) - mx) * inv));
+  for (int64_t e = lane; e < kept; e += 64) v[e] = E::narrow(__expf(E::widen(v[e]) - mx) * inv);
 }
 
-template <int D, int QT, bool DENSE, bool RMAX>
+template <int D, int QT, bool DENSE, bool RMAX, bool BF>
 static hipError_t launch_sddmm_cfg1(const uint16_t* q, const uint16_t* k, int64_t batch, int64_t Lq,
                                    int64_t Lk, float scale, uint16_t* vv, uint16_t* mm, uint16_t* ss,
                                    float* rmax, hipStream_t stream) {
   using Cfg = SddmmCfg<D, QT>;
   const int64_t qblocks = (Lq + Cfg::kQueries - 1) / Cfg::kQueries;
   const dim3 grid((unsigned)qblocks, (unsigned)(batch < 65535 ? batch : 65535));
-  auto kern = k_sddmm_prune<D, QT, DENSE, RMAX>;
+  auto kern = k_sddmm_prune<D, QT, DENSE, RMAX, BF>;
   static bool attr_set = false;   // benign race: every caller sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLds);
@@ -272,38 +283,50 @@ static hipError_t launch_sddmm_cfg1(const uint16_t* q, const uint16_t* k, int64_
   hipLaunchKernelGGL(kern, grid, dim3(64 * Cfg::kWaves), Cfg::kLds, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax);
   return hipGetLastError();
 }
-template <int D, int QT>
+template <int D, int QT, bool BF>
 static hipError_t launch_sddmm_cfg(const uint16_t* q, const uint16_t* k, int64_t batch, int64_t Lq,
                                    int64_t Lk, float scale, uint16_t* vv, uint16_t* mm, uint16_t* ss,
                                    float* rmax, hipStream_t stream) {
-  if (ss && rmax) return launch_sddmm_cfg1<D, QT, true, true>(q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax, stream);
-  if (ss) return launch_sddmm_cfg1<D, QT, true, false>(q, k, batch, Lq, Lk, scale, vv, mm, ss, nullptr, stream);
-  if (rmax) return launch_sddmm_cfg1<D, QT, false, true>(q, k, batch, Lq, Lk, scale, vv, mm, nullptr, rmax, stream);
-  return launch_sddmm_cfg1<D, QT, false, false>(q, k, batch, Lq, Lk, scale, vv, mm, nullptr, nullptr, stream);
+  if (ss && rmax) return launch_sddmm_cfg1<D, QT, true, true, BF>(q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax, stream);
+  if (ss) return launch_sddmm_cfg1<D, QT, true, false, BF>(q, k, batch, Lq, Lk, scale, vv, mm, ss, nullptr, stream);
+  if (rmax) return launch_sddmm_cfg1<D, QT, false, true, BF>(q, k, batch, Lq, Lk, scale, vv, mm, nullptr, rmax, stream);
+  return launch_sddmm_cfg1<D, QT, false, false, BF>(q, k, batch, Lq, Lk, scale, vv, mm, nullptr, nullptr, stream);
+}
+
+template <bool BF>
+static hipError_t launch_sddmm_d(const uint16_t* q, const uint16_t* k, int64_t batch, int64_t Lq,
+                                 int64_t Lk, int64_t d, float scale, uint16_t* vv, uint16_t* mm,
+                                 uint16_t* ss, float* rmax, hipStream_t stream) {
+  switch (d) {
+    case 16: return launch_sddmm_cfg<16, 2, BF>(q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax, stream);
+    case 32: return launch_sddmm_cfg<32, 2, BF>(q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax, stream);
+    case 64: return launch_sddmm_cfg<64, 2, BF>(q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax, stream);
+    default: return launch_sddmm_cfg<128, 1, BF>(q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax, stream);
+  }
 }
 
 hipError_t launch_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
                                  int64_t Lk, int64_t d, float scale, void* values, void* meta,
-                                 void* S_dense, float* row_max, hipStream_t stream) {
+                                 void* S_dense, float* row_max, bool bf16, hipStream_t stream) {
   const uint16_t* q = (const uint16_t*)Q;
   const uint16_t* k = (const uint16_t*)Kmat;
   uint16_t* vv = (uint16_t*)values;
   uint16_t* mm = (uint16_t*)meta;
   uint16_t* ss = (uint16_t*)S_dense;
-  switch (d) {
-    case 16: return launch_sddmm_cfg<16, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, row_max, stream);
-    case 32: return launch_sddmm_cfg<32, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, row_max, stream);
-    case 64: return launch_sddmm_cfg<64, 2>(q, k, batch, Lq, Lk, scale, vv, mm, ss, row_max, stream);
-    default: return launch_sddmm_cfg<128, 1>(q, k, batch, Lq, Lk, scale, vv, mm, ss, row_max, stream);
-  }
+  if (bf16) return launch_sddmm_d<true>(q, k, batch, Lq, Lk, d, scale, vv, mm, ss, row_max, stream);
+  return launch_sddmm_d<false>(q, k, batch, Lq, Lk, d, scale, vv, mm, ss, row_max, stream);
 }
 
-hipError_t launch_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld,
+hipError_t launch_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, bool bf16,
                                   hipStream_t stream) {
   const int vec = (kept % 8 == 0) && (ld % 8 == 0);
   const int64_t blocks = (rows + 3) / 4;
-  hipLaunchKernelGGL((k_softmax_rows<8>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (uint16_t*)values, rows, kept, ld, vec);
+  if (bf16)
+    hipLaunchKernelGGL((k_softmax_rows<8, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (uint16_t*)values, rows, kept, ld, vec);
+  else
+    hipLaunchKernelGGL((k_softmax_rows<8, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (uint16_t*)values, rows, kept, ld, vec);
   return hipGetLastError();
 }
 

@@ -49,10 +49,15 @@ hipError_t launch_spmm_nm_softmax(const void* values, const void* meta, const fl
                                   int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb,
                                   void* Y, int64_t ldy, int64_t batch, int64_t stride_values,
                                   int64_t stride_meta, int64_t stride_row_max, int64_t stride_B,
-                                  int64_t stride_Y, hipStream_t stream);
+                                  int64_t stride_Y, bool bf16, hipStream_t stream);
+// 2:4 SpMM on bf16 values and B (wide kernel; its support set, row-major B).
+hipError_t launch_spmm_nm_bf16(const void* values, const void* meta, int64_t R, int64_t K,
+                               const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                               int64_t batch, int64_t stride_values, int64_t stride_meta,
+                               int64_t stride_B, int64_t stride_Y, hipStream_t stream);
 hipError_t launch_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
                                  int64_t Lk, int64_t d, float scale, void* values, void* meta,
-                                 void* S_dense, float* row_max, hipStream_t stream);
+                                 void* S_dense, float* row_max, bool bf16, hipStream_t stream);
 // Bitmap (Coruscant) format: encoder passes and the decode-shaped product (bitmap.hip).
 hipError_t launch_bitmap_count(const void* A, int64_t R, int64_t K, int64_t lda, uint64_t* bitmaps,
                                uint32_t* offsets, hipStream_t stream);
@@ -62,7 +67,7 @@ hipError_t launch_bitmap_values(const void* A, int64_t R, int64_t K, int64_t lda
 hipError_t launch_spmm_bitmap(const uint64_t* bitmaps, const uint32_t* offsets, const void* values,
                               int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb,
                               int b_layout, void* Y, int64_t ldy, hipStream_t stream);
-hipError_t launch_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld,
+hipError_t launch_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, bool bf16,
                                   hipStream_t stream);
 
 }  // namespace snm

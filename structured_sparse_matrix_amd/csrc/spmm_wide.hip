@@ -26,7 +26,7 @@
 //     and positions >= K' read valid memory whose products are never stored or are
 //     multiplied by zeroed operands), so no lane ever skips a DMA and every wave's
 //     vmcnt bookkeeping stays exact.
-#include "device_common.hpp"
+#include "elem.hpp"
 #include "launch.hpp"
 #include "wide_layout.hpp"
 
@@ -133,10 +133,6 @@ __device__ __forceinline__ h4 tr16_at(uint8_t* smem, uint32_t byte_off) {
   return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(p));
 }
 
-__device__ __forceinline__ f16v smfmac32(const h8& a, const h16& b, const f16v& c, uint32_t idx) {
-  return __builtin_amdgcn_smfmac_f32_32x32x32_f16(a, b, c, (int)idx, 0, 0);
-}
-
 template <int I>
 using cint = std::integral_constant<int, I>;
 template <int I, int N, typename F>
@@ -164,11 +160,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // PIPE: issue each step's products one step late (two operand buffers), so that the
 // operand reads of the next step -- across a stage barrier too -- overlap the matrix core;
 // off where the second buffer does not fit in the register file.
-template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER, bool SMAX, bool PIPE>
+// BF: bf16 values, B and Y (v_smfmac_f32_32x32x32_bf16; same lane layout) instead of fp16.
+template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER, bool SMAX, bool PIPE, bool BF>
 __global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
 k_spmm_wide(WideArgs a) {
   static_assert(!(SMAX && GATHER), "the softmax mode is defined for 2:4 scores only");
   using Cfg = WideCfg<WM, WN, TM, TN, KSTEPS, NST, GATHER>;
+  using E = Elem<BF>;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, KS = Cfg::KS;
   constexpr int nB = Cfg::nB, nA = Cfg::nA;
   constexpr int kRowsPerDma = 1024 / (2 * BN);   // B tile rows one DMA instruction fills
@@ -368,30 +366,27 @@ k_spmm_wide(WideArgs a) {
   };
   auto mma = [&](Frag& f) {
     if constexpr (SMAX) {
+      // scores -> 16-bit probabilities (packed pairs), and the fp32 sum of exactly the
+      // 16-bit numbers the matrix core multiplies
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
+      for (int tm = 0; tm < TM; ++tm) {
+        u4 w = __builtin_bit_cast(u4, f.af[tm]);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
+        for (int t = 0; t < 4; ++t) {
           f2 x;
-          x[0] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)f.af[tm][e], kLog2e, -mx2[tm]));
-          x[1] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)f.af[tm][e + 1], kLog2e, -mx2[tm]));
-          const hh2 p = __builtin_convertvector(x, hh2);
-          f.af[tm][e] = p[0];
-          f.af[tm][e + 1] = p[1];
+          x[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(E::lo(w[t]), kLog2e, -mx2[tm]));
+          x[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(E::hi(w[t]), kLog2e, -mx2[tm]));
+          w[t] = E::pack2(x);
         }
-    }
-    if constexpr (SMAX) {   // sum of the fp16 probabilities the matrix core multiplies
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          rsum[tm] = __builtin_amdgcn_fdot2(hh2{f.af[tm][e], f.af[tm][e + 1]}, hh2{(_Float16)1.f, (_Float16)1.f},
-                                            rsum[tm], false);
+        for (int t = 0; t < 4; ++t) rsum[tm] = E::sum2(w[t], rsum[tm]);
+        f.af[tm] = __builtin_bit_cast(h8, w);
+      }
     }
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = smfmac32(f.af[tm], f.bf[tn], acc[tm][tn], f.ix[tm]);
+      for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = E::smfmac32(f.af[tm], f.bf[tn], acc[tm][tn], f.ix[tm]);
   };
 
   // The last stage of a ragged K' (a multiple of 16 positions) holds clamped DMA sources
@@ -402,7 +397,7 @@ k_spmm_wide(WideArgs a) {
   auto clean_tail = [&](uint32_t sb) {
     constexpr int kChunks = KS / 16;
     const int c0 = krem / 16;
-    const uint32_t fill = SMAX ? 0xFC00FC00u : 0u;
+    const uint32_t fill = SMAX ? E::kNegInf2 : 0u;
     for (int e = tid; e < BM * kChunks; e += Cfg::kThreads) {
       const int R = e / kChunks;
       const int c = e - R * kChunks;
@@ -467,7 +462,7 @@ k_spmm_wide(WideArgs a) {
     else mma(fr[1]);
   }
 
-  // ---- epilogue: fp32 -> fp16 (RNE), staged through LDS so that output rows leave as
+  // ---- epilogue: fp32 -> fp16 or bf16 (RNE), staged through LDS so that output rows leave as
   // whole 128-byte lines of 16-byte stores ([VENOM] Sec. 4.2, Fig. 8: wide output stores)
   __syncthreads();   // every wave is done with the ring (and the column-loc bytes)
   uint8_t* const otile = smem;
@@ -489,7 +484,7 @@ k_spmm_wide(WideArgs a) {
       for (int i = 0; i < 16; ++i) {
         const int rt = (wm * TM + tm) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
         const float y = SMAX ? acc[tm][tn][i] * inv[i] : acc[tm][tn][i];
-        *reinterpret_cast<uint16_t*>(otile + rt * Cfg::kOutPitch + ct * 2) = f16_bits(to_f16(y));
+        *reinterpret_cast<uint16_t*>(otile + rt * Cfg::kOutPitch + ct * 2) = E::narrow(y);
       }
       // scheduling fence: convert and store tile by tile (hoisting every conversion above
       // the first store would need a second register copy of the accumulators)
@@ -521,7 +516,7 @@ k_spmm_wide(WideArgs a) {
 }
 
 template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER, bool SMAX = false,
-          bool PIPE = true>
+          bool PIPE = true, bool BF = false>
 hipError_t launch_wide(WideArgs a, hipStream_t stream) {
   using Cfg = WideCfg<WM, WN, TM, TN, KSTEPS, NST, GATHER>;
   a.n_row_tiles = (a.R + Cfg::BM - 1) / Cfg::BM;
@@ -534,7 +529,7 @@ hipError_t launch_wide(WideArgs a, hipStream_t stream) {
   const size_t ring = (size_t)Cfg::kRing + (GATHER ? (size_t)(a.Kc + 2 * Cfg::KS) : 0);
   const size_t lds = ring > (size_t)Cfg::kOut ? ring : (size_t)Cfg::kOut;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  auto kern = k_spmm_wide<WM, WN, TM, TN, KSTEPS, NST, GATHER, SMAX, PIPE>;
+  auto kern = k_spmm_wide<WM, WN, TM, TN, KSTEPS, NST, GATHER, SMAX, PIPE, BF>;
   static bool attr_set = false;   // benign race: every caller sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -560,7 +555,8 @@ bool spmm_wide_eligible(int64_t R, int64_t Kc, int V, int M, const void* B, int6
 
 bool spmm_wide_supported(int64_t R, int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb,
                          int64_t batch, int64_t stride_B) {
-  if (R <= 0 || Kc <= 0 || C <= 0 || C % 8 != 0 || ldb % 8 != 0) return false;
+  // Kc == 0 is an empty contraction: no stage runs and the epilogue writes zeros
+  if (R <= 0 || Kc < 0 || C <= 0 || C % 8 != 0 || ldb % 8 != 0) return false;
   if (((uintptr_t)B & 15) != 0) return false;
   if (batch > 1 && stride_B % 8 != 0) return false;
   if (V > 0 && (V % 32 != 0 || Kc > kMaxGatherKc)) return false;
@@ -604,6 +600,28 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
   return launch_wide<1, 4, 4, 2, 1, 3, false, false, false>(a, stream);     // 128 x 256
 }
 
+hipError_t launch_spmm_nm_bf16(const void* values, const void* meta, int64_t R, int64_t K,
+                               const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                               int64_t batch, int64_t stride_values, int64_t stride_meta,
+                               int64_t stride_B, int64_t stride_Y, hipStream_t stream) {
+  if (!spmm_wide_supported(R, K, 0, 4, B, C, ldb, batch, stride_B)) return hipErrorInvalidValue;
+  WideArgs a{};
+  a.values = (const uint16_t*)values;
+  a.meta = (const uint8_t*)meta;
+  a.B = (const uint16_t*)B;
+  a.Y = (uint16_t*)Y;
+  a.R = R; a.Kc = K; a.C = C; a.ldb = ldb; a.ldy = ldy;
+  a.batch = batch < 1 ? 1 : batch;
+  a.stride_values = stride_values; a.stride_meta = stride_meta;
+  a.stride_B = stride_B; a.stride_Y = stride_Y;
+  a.V = 0; a.M = 4;
+  a.y_vec = y_rows_aligned(Y, ldy, a.batch, stride_Y);
+  const bool wide_grid = a.batch * ((R + 127) / 128) * ((C + 255) / 256) >= 512;
+  if (C <= 64) return launch_wide<4, 1, 1, 2, 4, 2, false, false, true, true>(a, stream);
+  if (C <= 128 || !wide_grid) return launch_wide<1, 4, 4, 1, 2, 3, false, false, true, true>(a, stream);
+  return launch_wide<1, 4, 4, 2, 1, 3, false, false, false, true>(a, stream);
+}
+
 }  // namespace snm
 
 namespace snm {
@@ -612,7 +630,7 @@ hipError_t launch_spmm_nm_softmax(const void* values, const void* meta, const fl
                                   int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb,
                                   void* Y, int64_t ldy, int64_t batch, int64_t stride_values,
                                   int64_t stride_meta, int64_t stride_row_max, int64_t stride_B,
-                                  int64_t stride_Y, hipStream_t stream) {
+                                  int64_t stride_Y, bool bf16, hipStream_t stream) {
   if (!spmm_wide_supported(R, K, 0, 4, B, C, ldb, batch, stride_B)) return hipErrorInvalidValue;
   WideArgs a{};
   a.values = (const uint16_t*)values;
@@ -627,9 +645,12 @@ hipError_t launch_spmm_nm_softmax(const void* values, const void* meta, const fl
   a.V = 0; a.M = 4;
   a.y_vec = y_rows_aligned(Y, ldy, a.batch, stride_Y);
   // one wave column (WN = 1) so each score is exponentiated once per column tile
+  if (bf16) {
+    if (C <= 64) return launch_wide<4, 1, 1, 2, 4, 2, false, true, true, true>(a, stream);
+    return launch_wide<4, 1, 1, 4, 2, 3, false, true, true, true>(a, stream);
+  }
   if (C <= 64) return launch_wide<4, 1, 1, 2, 4, 2, false, true>(a, stream);    // 128 x 64
-  if (C <= 128) return launch_wide<4, 1, 1, 4, 2, 3, false, true>(a, stream);   // 128 x 128
-  return launch_wide<4, 1, 1, 4, 2, 3, false, true>(a, stream);                 // 128 x 128 strips
+  return launch_wide<4, 1, 1, 4, 2, 3, false, true>(a, stream);                 // 128 x 128 (strips)
 }
 
 }  // namespace snm

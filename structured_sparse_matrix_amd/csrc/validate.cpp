@@ -114,6 +114,17 @@ int check_sddmm_prune_nm_rowmax(const void* Q, const void* Kmat, int64_t batch, 
   return SNM_OK;
 }
 
+// Extra rules of the wide-output kernel (row-major B): 16-byte B rows and 32-bit per-lane
+// offsets (128 rows of values, 256 rows of B).
+static int check_wide_rules(int64_t K, const void* B, int64_t C, int64_t ldb, int64_t batch,
+                            int64_t stride_B) {
+  if (C % 8 != 0 || ldb % 8 != 0 || !aligned16(B) || (batch > 1 && stride_B % 8 != 0))
+    return SNM_E_ALIGN;
+  constexpr int64_t kLim = (int64_t)1 << 31;
+  if (128 * K >= kLim || (256 * ldb + C) * 2 >= kLim) return SNM_E_SHAPE;
+  return SNM_OK;
+}
+
 int check_spmm_nm_softmax(const void* values, const void* meta, const void* row_max, int64_t R,
                           int64_t K, const void* B, int64_t C, int64_t ldb, const void* Y,
                           int64_t ldy, int64_t batch, int64_t stride_values, int64_t stride_meta,
@@ -124,12 +135,26 @@ int check_spmm_nm_softmax(const void* values, const void* meta, const void* row_
   if (K == 0) return SNM_E_SHAPE;   // a softmax over no entries is undefined
   if (!row_max) return SNM_E_NULL;
   if (batch > 1 && (stride_row_max < R || !fits(batch, stride_row_max))) return SNM_E_SHAPE;
-  if (C % 8 != 0 || ldb % 8 != 0 || !aligned16(B) || (batch > 1 && stride_B % 8 != 0) ||
-      ((uintptr_t)row_max & 3u) != 0)
-    return SNM_E_ALIGN;
-  // the kernel's per-lane offsets are 32-bit: 128 rows of values, 256 rows of B
-  constexpr int64_t kLim = (int64_t)1 << 31;
-  if (128 * K >= kLim || (256 * ldb + C) * 2 >= kLim) return SNM_E_SHAPE;
+  if (((uintptr_t)row_max & 3u) != 0) return SNM_E_ALIGN;
+  return check_wide_rules(K, B, C, ldb, batch, stride_B);
+}
+
+int check_spmm_nm_bf16(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
+                       int64_t C, int64_t ldb, const void* Y, int64_t ldy, int64_t batch,
+                       int64_t stride_values, int64_t stride_meta, int64_t stride_B,
+                       int64_t stride_Y) {
+  int s = check_spmm_nm(values, meta, R, K, B, C, ldb, 0, Y, ldy, batch, stride_values,
+                        stride_meta, stride_B, stride_Y);
+  if (s != SNM_OK || R == 0 || C == 0 || batch == 0) return s;
+  return check_wide_rules(K, B, C, ldb, batch, stride_B);
+}
+
+int check_sddmm_prune_nm_bf16(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                              int64_t Lk, int64_t d, const void* values, const void* meta,
+                              const void* S_dense, const void* row_max) {
+  int s = check_sddmm_prune_nm(Q, Kmat, batch, Lq, Lk, d, values, meta, S_dense);
+  if (s != SNM_OK || batch == 0 || Lq == 0 || Lk == 0) return s;
+  if (((uintptr_t)row_max & 3u) != 0) return SNM_E_ALIGN;   // NULL: no row maxima
   return SNM_OK;
 }
 

@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     for n in ("snm_prune_encode_nm", "snm_prune_encode_vnm", "snm_spmm_nm", "snm_spmm_vnm",
               "snm_sddmm_prune_nm", "snm_softmax_nm_rows", "snm_sddmm_prune_nm_rowmax",
               "snm_spmm_nm_softmax", "snm_bitmap_sizes", "snm_bitmap_count", "snm_bitmap_encode",
-              "snm_spmm_bitmap"):
+              "snm_spmm_bitmap", "snm_sddmm_prune_nm_bf16", "snm_softmax_nm_rows_bf16",
+              "snm_spmm_nm_bf16", "snm_spmm_nm_softmax_bf16"):
         assert n in names
 
 
@@ -220,3 +221,42 @@ def test_binding_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
                 assert not re.search(r"import_module\(\s*['\"]oracle", text), f
+
+
+# Q, K, batch, Lq, Lk, d, scale, values, meta, S_dense, row_max, stream
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, 1, 16, 32, 48, ctypes.c_float(0.125), FAKE, FAKE, P(0), P(0), P(0)), 4),   # d unsupported
+    ((FAKE, FAKE, 1, 16, 40, 64, ctypes.c_float(0.125), FAKE, FAKE, P(0), P(0), P(0)), 2),   # Lk % 32
+    ((FAKE, P(0), 1, 16, 32, 64, ctypes.c_float(0.125), FAKE, FAKE, P(0), P(0), P(0)), 1),   # Kmat NULL
+    ((FAKE, FAKE, 1, 16, 32, 64, ctypes.c_float(0.125), FAKE, FAKE, MISALIGNED, P(0), P(0)), 3),
+    ((FAKE, FAKE, 1, 16, 32, 64, ctypes.c_float(0.125), FAKE, FAKE, P(0), P(0x1002), P(0)), 3),  # row_max % 4
+    ((P(0), P(0), 0, 16, 32, 64, ctypes.c_float(0.125), P(0), P(0), P(0), P(0), P(0)), 0),   # empty batch
+])
+def test_sddmm_bf16_validation(args, status):
+    assert _lib().snm_sddmm_prune_nm_bf16(*args) == status
+
+
+# values, meta, R, K, B, C, ldb, Y, ldy, batch, s_values, s_meta, s_B, s_Y, stream
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, 16, 24, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 2),       # K % 16
+    ((FAKE, P(0), 16, 32, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 1),       # meta NULL
+    ((FAKE, FAKE, 16, 32, FAKE, 12, 12, FAKE, 12, 1, 0, 0, 0, 0, P(0)), 3),    # C % 8
+    ((FAKE, FAKE, 16, 32, FAKE, 8, 12, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 3),      # ldb % 8
+    ((FAKE, FAKE, 16, 32, P(0x1008), 8, 8, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 3),  # B 16-byte alignment
+    ((FAKE, FAKE, 16, 1 << 24, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, P(0)), 2),  # 128*K >= 2^31
+    ((P(0), P(0), 0, 32, P(0), 8, 8, P(0), 8, 1, 0, 0, 0, 0, P(0)), 0),        # R == 0: ok
+])
+def test_spmm_bf16_validation(args, status):
+    assert _lib().snm_spmm_nm_bf16(*args) == status
+
+
+def test_bf16_softmax_and_fused_validation():
+    lib = _lib()
+    assert lib.snm_softmax_nm_rows_bf16(FAKE, 4, 16, 8, P(0)) == 2        # ld < kept
+    assert lib.snm_softmax_nm_rows_bf16(MISALIGNED, 4, 16, 16, P(0)) == 3
+    assert lib.snm_softmax_nm_rows_bf16(P(0), 0, 16, 16, P(0)) == 0
+    # values, meta, row_max, R, K, B, C, ldb, Y, ldy, batch, strides x 5, stream
+    assert lib.snm_spmm_nm_softmax_bf16(FAKE, FAKE, P(0), 16, 32, FAKE, 8, 8, FAKE, 8, 1,
+                                        0, 0, 0, 0, 0, P(0)) == 1       # row_max NULL
+    assert lib.snm_spmm_nm_softmax_bf16(FAKE, FAKE, FAKE, 16, 0, FAKE, 8, 8, FAKE, 8, 1,
+                                        0, 0, 0, 0, 0, P(0)) == 2       # K == 0

@@ -9,7 +9,8 @@ Every tensor is drawn as float64 ``standard_normal`` from
 ``numpy.random.default_rng(seed)``, multiplied by the workload's sigma and
 rounded once to float16 (round to nearest even). Tensors of one workload are
 drawn from one generator in the order listed. The same float16 bits feed the
-oracle and the GPU.
+oracle and the GPU. The bf16 and fp32 variants of the attention workload draw
+the same float64 numbers and round them to float32, then (bf16) to bf16.
 
 The pages measure on pruned BERT / GPT / OPT / Llama weights and on SQuAD
 attention; none of those is available, so these Gaussian tensors, at the
@@ -25,6 +26,19 @@ import numpy as np
 def normal_f16(rng: np.random.Generator, shape, sigma: float = 1.0) -> np.ndarray:
     """float64 standard normal x sigma, rounded once to float16 (RNE)."""
     return (rng.standard_normal(size=shape) * sigma).astype(np.float16)
+
+
+def normal_f32(rng: np.random.Generator, shape, sigma: float = 1.0) -> np.ndarray:
+    """float64 standard normal x sigma, rounded once to float32 (RNE)."""
+    return (rng.standard_normal(size=shape) * sigma).astype(np.float32)
+
+
+def normal_bf16(rng: np.random.Generator, shape, sigma: float = 1.0) -> np.ndarray:
+    """bf16 bit patterns (uint16): float64 standard normal x sigma, rounded to float32 and
+    then to bf16, both round to nearest even (the second step adds half an ulp minus one,
+    plus the kept lowest bit, and truncates)."""
+    b = normal_f32(rng, shape, sigma).view(np.uint32)
+    return ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
 
 
 @dataclass(frozen=True)
@@ -123,6 +137,14 @@ def attention_qkv(w: Workload):
     rng = np.random.default_rng(w.seed)
     shape = (w.batch * w.heads, w.seq, w.head_dim)
     return tuple(normal_f16(rng, shape, 1.0) for _ in range(3))
+
+
+def attention_qkv_typed(w: Workload, dtype: str):
+    """attention_qkv drawn in another element type: "bf16" (uint16 bit patterns) or "f32"."""
+    rng = np.random.default_rng(w.seed)
+    shape = (w.batch * w.heads, w.seq, w.head_dim)
+    draw = {"bf16": normal_bf16, "f32": normal_f32}[dtype]
+    return tuple(draw(rng, shape, 1.0) for _ in range(3))
 
 
 def small_matrix(seed: int, shape, sigma: float = 1.0) -> np.ndarray:
