@@ -263,6 +263,45 @@ int snm_spmm_nm_softmax_bf16(const void* values, const void* meta, const float* 
                              int64_t stride_meta, int64_t stride_row_max, int64_t stride_B,
                              int64_t stride_Y, void* stream);
 
+/* 1:2 dynamic attention on fp32 scores ("Dynamic N:M ... attention", Sec. 1 and Fig. 1-3:
+ * the mechanism at 1:2; Sec. 4.2: 32-bit data keeps one of every two 4-byte elements).
+ * Format of an R x K fp32 score matrix pruned 1:2 along K (K % 32 == 0):
+ *   values  fp32 [R, K/2]: the kept element of each pair (2p, 2p + 1), a bit copy;
+ *   meta    uint8 [R, K/4]: one 4-bit code per pair, 0x4 = the first element kept, 0xe = the
+ *           second (the codes of 2:4 over the pair's 16-bit halves); pair 2b in the low and
+ *           pair 2b + 1 in the high nibble of byte b.
+ * Selection: the element with the larger magnitude (fp32 bits without the sign) is kept; on
+ * a tie the first. The products run on the dense fp32 matrix core (full fp32 products,
+ * fp32 accumulation): this architecture has no 32-bit sparse matrix instruction.
+ *
+ * snm_sddmm_prune_1of2_f32: S = fp32((Q_b Kmat_b^T) * scale) for each batch entry, pruned
+ *   1:2 along the keys. Q fp32 [batch, Lq, d], Kmat fp32 [batch, Lk, d] contiguous;
+ *   values fp32 [batch, Lq, Lk/2]; meta [batch, Lq, Lk/4]; S_dense optional fp32
+ *   [batch, Lq, Lk] (pre-prune S); row_max optional fp32 [batch, Lq] (largest kept score).
+ *   Requires Lk % 32 == 0, d in {16, 32, 64, 128}, 16-byte aligned arrays (row_max 4). */
+int snm_sddmm_prune_1of2_f32(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                             int64_t Lk, int64_t d, float scale, void* values, void* meta,
+                             void* S_dense, float* row_max, void* stream);
+
+/* snm_softmax_nm_rows_f32: snm_softmax_nm_rows on fp32 rows (fp32 output, no rounding step
+ * beyond fp32 arithmetic). */
+int snm_softmax_nm_rows_f32(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream);
+
+/* snm_spmm_1of2_f32: Y = decode(values, meta) * B for 1:2 fp32 operands, per batch entry at
+ * values + b*stride_values, meta + b*stride_meta (bytes), B + b*stride_B, Y + b*stride_Y.
+ *   B  fp32 K x C row-major (ldb >= C);  Y  fp32 R x C (ldy >= C).
+ *   row_max  NULL: plain product. Otherwise values are scores and the row softmax over the
+ *            kept entries is applied inside the product (fused variant): p = exp(v - row_max)
+ *            in fp32, the output row divided by the fp32 sum of its p; row_max (R per batch
+ *            entry at row_max + b*stride_row_max) must be >= every kept score of its row.
+ * Requires K % 32 == 0 (K > 0 with row_max), C % 4 == 0, ldb % 4 == 0, values and B 16-byte,
+ * meta 8-byte, Y and row_max 4-byte aligned; with batch > 1, stride_values % 4 == 0,
+ * stride_meta % 8 == 0, stride_B % 4 == 0. K == 0 writes zeros. */
+int snm_spmm_1of2_f32(const void* values, const void* meta, const float* row_max, int64_t R,
+                      int64_t K, const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                      int64_t batch, int64_t stride_values, int64_t stride_meta,
+                      int64_t stride_row_max, int64_t stride_B, int64_t stride_Y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

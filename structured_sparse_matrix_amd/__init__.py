@@ -11,6 +11,8 @@ Layouts (canonical, see include/snm.h):
   bitmap  bitmaps [R, K/64] (64-bit words, held in int64), tile_offsets [R*K/64 + 1]
           (uint32 values, held in int32), values fp16 [tile_offsets[-1]]
 The ``*_bf16`` functions are the same operations on bf16 tensors (same layouts).
+  1:2 fp32  values fp32 [R, K/2], meta uint8 [R, K/4] (one code per pair: 0x4 first kept,
+            0xe second kept)
 """
 from __future__ import annotations
 
@@ -27,6 +29,8 @@ __all__ = [
     "bitmap_sizes", "bitmap_encode", "spmm_bitmap",
     "sddmm_prune_nm_bf16", "softmax_nm_rows_bf16", "spmm_nm_bf16", "spmm_nm_softmax_bf16",
     "attention_nm_bf16", "attention_nm_fused_bf16",
+    "sddmm_prune_1of2_f32", "softmax_nm_rows_f32", "spmm_1of2_f32", "attention_1of2_f32",
+    "attention_1of2_fused_f32",
     "LIB_PATH",
 ]
 
@@ -505,3 +509,92 @@ def attention_nm_fused_bf16(Q, Kmat, Vmat, scale=None):
     """attention_nm_fused on bf16: the SDDMM writes row maxima, the SpMM applies the softmax."""
     values, meta, row_max = sddmm_prune_nm_bf16(Q, Kmat, scale, return_rowmax=True)
     return spmm_nm_softmax_bf16(values, meta, row_max, Vmat)
+
+
+# ---------------------------------------------------------------------------------------
+# 1:2 on fp32 scores
+
+def sddmm_prune_1of2_f32(Q, Kmat, scale=None, return_dense=False, return_rowmax=False):
+    """fp32 scores S = (Q @ Kmat^T) * scale pruned 1:2 along the key axis.
+    Q [b, Lq, d], Kmat [b, Lk, d] fp32 -> values fp32 [b, Lq, Lk/2], meta uint8 [b, Lq, Lk/4],
+    plus S [b, Lq, Lk] if return_dense and row_max [b, Lq] if return_rowmax, in that order."""
+    torch = _torch()
+    nb, Lq, Lk, d, scale = _qk(Q, Kmat, torch.float32, scale)
+    values = torch.empty((nb, Lq, Lk // 2), dtype=torch.float32, device=Q.device)
+    meta = torch.empty((nb, Lq, Lk // 4), dtype=torch.uint8, device=Q.device)
+    S = torch.empty((nb, Lq, Lk), dtype=torch.float32, device=Q.device) if return_dense else None
+    rmax = torch.empty((nb, Lq), dtype=torch.float32, device=Q.device) if return_rowmax else None
+    check("snm_sddmm_prune_1of2_f32",
+          load().snm_sddmm_prune_1of2_f32(_ptr(Q), _ptr(Kmat), nb, Lq, Lk, d, scale, _ptr(values), _ptr(meta),
+                                          _ptr(S), _ptr(rmax), _stream(Q)))
+    return (values, meta) + ((S,) if return_dense else ()) + ((rmax,) if return_rowmax else ())
+
+
+def softmax_nm_rows_f32(values):
+    """In-place softmax over the last axis of compressed fp32 rows (kept entries only)."""
+    torch = _torch()
+    _need(values, "values", torch.float32)
+    if values.stride(-1) != 1:
+        raise ValueError("values must have unit stride along the last axis")
+    kept = values.shape[-1]
+    rows = values.numel() // kept if kept else 0
+    ld = values.stride(-2) if values.dim() >= 2 else kept
+    if values.dim() > 2 and not values.is_contiguous():
+        raise ValueError("batched values must be contiguous")
+    check("snm_softmax_nm_rows_f32", load().snm_softmax_nm_rows_f32(_ptr(values), rows, kept, ld,
+                                                                    _stream(values)))
+    return values
+
+
+def spmm_1of2_f32(values, meta, B, row_max=None, out=None):
+    """Y = decode(values, meta) @ B for 1:2 fp32 operands (row-major B). With row_max, the
+    row softmax over the kept scores is applied inside the product. 2-D: values [R, K/2],
+    meta [R, K/4], B [K, C] (row_max [R]) -> Y [R, C]; 3-D: one more leading batch axis."""
+    torch = _torch()
+    _need(values, "values", torch.float32, (2, 3))
+    _need(meta, "meta", torch.uint8, values.dim())
+    _need(B, "B", torch.float32, values.dim())
+    if row_max is not None:
+        _need(row_max, "row_max", torch.float32, values.dim() - 1)
+    batched = values.dim() == 3
+    if not batched:
+        values, meta, B = values[None], meta[None], B[None]
+        row_max = row_max[None] if row_max is not None else None
+        out = out[None] if out is not None else None
+    nb, R, half_k = values.shape
+    K = 2 * half_k
+    if B.shape[0] != nb or B.shape[1] != K or meta.shape != (nb, R, K // 4) or \
+            (row_max is not None and row_max.shape != (nb, R)):
+        raise ValueError(f"shape mismatch: values {tuple(values.shape)}, meta {tuple(meta.shape)}, "
+                         f"B {tuple(B.shape)}")
+    for t, n in ((values, "values"), (meta, "meta")):
+        if t.shape[2] and (t.stride(2) != 1 or t.stride(1) != t.shape[2]):
+            raise ValueError(f"{n} must be contiguous per batch entry")
+    if row_max is not None and row_max.stride(1) != 1:
+        raise ValueError("row_max must be contiguous per batch entry")
+    if B.stride(2) != 1:
+        raise ValueError("B must be row-major (unit stride along C)")
+    C = B.shape[2]
+    if out is None:
+        out = torch.empty((nb, R, C), dtype=torch.float32, device=B.device)
+    if out.stride(2) != 1:
+        raise ValueError("out must be row-major")
+    check("snm_spmm_1of2_f32",
+          load().snm_spmm_1of2_f32(_ptr(values), _ptr(meta), _ptr(row_max), R, K, _ptr(B), C, B.stride(1),
+                                   _ptr(out), out.stride(1), nb, values.stride(0), meta.stride(0),
+                                   row_max.stride(0) if row_max is not None else 0, B.stride(0),
+                                   out.stride(0), _stream(B)))
+    return out if batched else out[0]
+
+
+def attention_1of2_f32(Q, Kmat, Vmat, scale=None):
+    """1:2 dynamic attention on fp32: SDDMM-prune, softmax over kept entries, 1:2 product."""
+    values, meta = sddmm_prune_1of2_f32(Q, Kmat, scale)
+    softmax_nm_rows_f32(values)
+    return spmm_1of2_f32(values, meta, Vmat)
+
+
+def attention_1of2_fused_f32(Q, Kmat, Vmat, scale=None):
+    """1:2 fp32 attention with the softmax folded into the two kernels."""
+    values, meta, row_max = sddmm_prune_1of2_f32(Q, Kmat, scale, return_rowmax=True)
+    return spmm_1of2_f32(values, meta, Vmat, row_max=row_max)

@@ -40,6 +40,10 @@ SIGNATURES = {
     "snm_sddmm_prune_nm_bf16": [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp],
     "snm_softmax_nm_rows_bf16": [_vp, _i64, _i64, _i64, _vp],
     "snm_spmm_nm_bf16": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
+    "snm_sddmm_prune_1of2_f32": [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp],
+    "snm_softmax_nm_rows_f32": [_vp, _i64, _i64, _i64, _vp],
+    "snm_spmm_1of2_f32": [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
+                          _i64, _i64, _vp],
     "snm_spmm_nm_softmax_bf16": [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64,
                                  _i64, _i64, _i64, _vp],
 }

@@ -256,6 +256,36 @@ int snm_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, vo
   return launched(snm::launch_softmax_nm_rows(values, rows, kept, ld, false, (hipStream_t)stream));
 }
 
+int snm_sddmm_prune_1of2_f32(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                             int64_t Lk, int64_t d, float scale, void* values, void* meta,
+                             void* S_dense, float* row_max, void* stream) {
+  int s = snm::check_sddmm_prune_1of2_f32(Q, Kmat, batch, Lq, Lk, d, values, meta, S_dense, row_max);
+  if (s != SNM_OK || batch == 0 || Lq == 0 || Lk == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_sddmm_prune_1of2_f32(Q, Kmat, batch, Lq, Lk, d, scale, values, meta,
+                                                   S_dense, row_max, (hipStream_t)stream));
+}
+
+int snm_softmax_nm_rows_f32(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream) {
+  int s = snm::check_softmax_nm_rows(values, rows, kept, ld);
+  if (s != SNM_OK || rows == 0 || kept == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_softmax_rows_f32(values, rows, kept, ld, (hipStream_t)stream));
+}
+
+int snm_spmm_1of2_f32(const void* values, const void* meta, const float* row_max, int64_t R,
+                      int64_t K, const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                      int64_t batch, int64_t stride_values, int64_t stride_meta,
+                      int64_t stride_row_max, int64_t stride_B, int64_t stride_Y, void* stream) {
+  int s = snm::check_spmm_1of2_f32(values, meta, row_max, R, K, B, C, ldb, Y, ldy, batch,
+                                   stride_values, stride_meta, stride_row_max, stride_B, stride_Y);
+  if (s != SNM_OK || R == 0 || C == 0 || batch == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_spmm_1of2_f32(values, meta, row_max, R, K, B, C, ldb, Y, ldy, batch,
+                                            stride_values, stride_meta, stride_row_max, stride_B,
+                                            stride_Y, (hipStream_t)stream));
+}
+
 int snm_softmax_nm_rows_bf16(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream) {
   int s = snm::check_softmax_nm_rows(values, rows, kept, ld);
   if (s != SNM_OK || rows == 0 || kept == 0) return s;

@@ -69,5 +69,16 @@ hipError_t launch_spmm_bitmap(const uint64_t* bitmaps, const uint32_t* offsets, 
                               int b_layout, void* Y, int64_t ldy, hipStream_t stream);
 hipError_t launch_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, bool bf16,
                                   hipStream_t stream);
+// 1:2 attention on fp32 scores (attention_f32.hip).
+hipError_t launch_sddmm_prune_1of2_f32(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                                       int64_t Lk, int64_t d, float scale, void* values, void* meta,
+                                       void* S_dense, float* row_max, hipStream_t stream);
+hipError_t launch_softmax_rows_f32(void* values, int64_t rows, int64_t kept, int64_t ld,
+                                   hipStream_t stream);
+hipError_t launch_spmm_1of2_f32(const void* values, const void* meta, const float* row_max, int64_t R,
+                                int64_t K, const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                                int64_t batch, int64_t stride_values, int64_t stride_meta,
+                                int64_t stride_row_max, int64_t stride_B, int64_t stride_Y,
+                                hipStream_t stream);
 
 }  // namespace snm

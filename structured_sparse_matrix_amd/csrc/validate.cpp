@@ -158,6 +158,38 @@ int check_sddmm_prune_nm_bf16(const void* Q, const void* Kmat, int64_t batch, in
   return SNM_OK;
 }
 
+int check_sddmm_prune_1of2_f32(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                               int64_t Lk, int64_t d, const void* values, const void* meta,
+                               const void* S_dense, const void* row_max) {
+  // the same shape and alignment rules as the 16-bit SDDMM
+  return check_sddmm_prune_nm_bf16(Q, Kmat, batch, Lq, Lk, d, values, meta, S_dense, row_max);
+}
+
+int check_spmm_1of2_f32(const void* values, const void* meta, const void* row_max, int64_t R,
+                        int64_t K, const void* B, int64_t C, int64_t ldb, const void* Y,
+                        int64_t ldy, int64_t batch, int64_t stride_values, int64_t stride_meta,
+                        int64_t stride_row_max, int64_t stride_B, int64_t stride_Y) {
+  if (R < 0 || K < 0 || C < 0 || batch < 0 || K % 32 != 0 || !fits(R, K) || !fits(K, C) ||
+      !fits(R, C))
+    return SNM_E_SHAPE;
+  if (R == 0 || C == 0 || batch == 0) return SNM_OK;
+  if (row_max && K == 0) return SNM_E_SHAPE;   // a softmax over no entries is undefined
+  if (!Y || (K > 0 && (!values || !meta || !B))) return SNM_E_NULL;
+  if (ldy < C || ldb < C || !fits(K, ldb) || !fits(R, ldy)) return SNM_E_SHAPE;
+  if (batch > 1) {
+    if (stride_values < R * (K / 2) || stride_meta < R * (K / 4) || stride_B < K * ldb ||
+        stride_Y < R * ldy || (row_max && stride_row_max < R) || !fits(batch, stride_values) ||
+        !fits(batch, stride_meta) || !fits(batch, stride_B) || !fits(batch, stride_Y) ||
+        !fits(batch, stride_row_max))
+      return SNM_E_SHAPE;
+    if (stride_values % 4 != 0 || stride_meta % 8 != 0 || stride_B % 4 != 0) return SNM_E_ALIGN;
+  }
+  if (!aligned16(values) || ((uintptr_t)meta & 7u) != 0 || !aligned16(B) || C % 4 != 0 ||
+      ldb % 4 != 0 || ((uintptr_t)row_max & 3u) != 0 || ((uintptr_t)Y & 3u) != 0)
+    return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
 int check_bitmap_sizes(int64_t R, int64_t K) {
   if (R < 0 || K < 0 || K % 64 != 0 || !fits(R, K)) return SNM_E_SHAPE;
   if (R * K >= ((int64_t)1 << 31)) return SNM_E_SHAPE;   // 32-bit tile offsets

@@ -33,6 +33,13 @@ int check_spmm_nm_bf16(const void* values, const void* meta, int64_t R, int64_t 
 int check_sddmm_prune_nm_bf16(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
                               int64_t Lk, int64_t d, const void* values, const void* meta,
                               const void* S_dense, const void* row_max);
+int check_sddmm_prune_1of2_f32(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                               int64_t Lk, int64_t d, const void* values, const void* meta,
+                               const void* S_dense, const void* row_max);
+int check_spmm_1of2_f32(const void* values, const void* meta, const void* row_max, int64_t R,
+                        int64_t K, const void* B, int64_t C, int64_t ldb, const void* Y,
+                        int64_t ldy, int64_t batch, int64_t stride_values, int64_t stride_meta,
+                        int64_t stride_row_max, int64_t stride_B, int64_t stride_Y);
 int check_bitmap_sizes(int64_t R, int64_t K);
 int check_bitmap_encode(const void* A, int64_t R, int64_t K, int64_t lda, const void* bitmaps,
                         const void* offsets, const void* values, bool need_values);

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
               "snm_sddmm_prune_nm", "snm_softmax_nm_rows", "snm_sddmm_prune_nm_rowmax",
               "snm_spmm_nm_softmax", "snm_bitmap_sizes", "snm_bitmap_count", "snm_bitmap_encode",
               "snm_spmm_bitmap", "snm_sddmm_prune_nm_bf16", "snm_softmax_nm_rows_bf16",
-              "snm_spmm_nm_bf16", "snm_spmm_nm_softmax_bf16"):
+              "snm_spmm_nm_bf16", "snm_spmm_nm_softmax_bf16", "snm_sddmm_prune_1of2_f32",
+              "snm_softmax_nm_rows_f32", "snm_spmm_1of2_f32"):
         assert n in names
 
 
@@ -260,3 +261,26 @@ def test_bf16_softmax_and_fused_validation():
                                         0, 0, 0, 0, 0, P(0)) == 1       # row_max NULL
     assert lib.snm_spmm_nm_softmax_bf16(FAKE, FAKE, FAKE, 16, 0, FAKE, 8, 8, FAKE, 8, 1,
                                         0, 0, 0, 0, 0, P(0)) == 2       # K == 0
+
+
+def test_f32_1of2_validation():
+    lib = _lib()
+    f = ctypes.c_float(0.125)
+    # Q, K, batch, Lq, Lk, d, scale, values, meta, S_dense, row_max, stream
+    assert lib.snm_sddmm_prune_1of2_f32(FAKE, FAKE, 1, 16, 32, 48, f, FAKE, FAKE, P(0), P(0), P(0)) == 4
+    assert lib.snm_sddmm_prune_1of2_f32(FAKE, FAKE, 1, 16, 48, 64, f, FAKE, FAKE, P(0), P(0), P(0)) == 2
+    assert lib.snm_sddmm_prune_1of2_f32(FAKE, FAKE, 1, 16, 32, 64, f, P(0), FAKE, P(0), P(0), P(0)) == 1
+    assert lib.snm_sddmm_prune_1of2_f32(FAKE, FAKE, 1, 16, 32, 64, f, FAKE, FAKE, P(0), P(0x1002), P(0)) == 3
+    assert lib.snm_softmax_nm_rows_f32(FAKE, 4, 16, 8, P(0)) == 2
+    assert lib.snm_softmax_nm_rows_f32(MISALIGNED, 4, 16, 16, P(0)) == 3
+    # values, meta, row_max, R, K, B, C, ldb, Y, ldy, batch, s_values, s_meta, s_rowmax, s_B, s_Y, stream
+    def spmm(*a):
+        return lib.snm_spmm_1of2_f32(*a)
+    assert spmm(FAKE, FAKE, P(0), 16, 48, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)) == 2       # K % 32
+    assert spmm(FAKE, P(0), P(0), 16, 64, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)) == 1       # meta NULL
+    assert spmm(FAKE, FAKE, P(0), 16, 64, FAKE, 6, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)) == 3       # C % 4
+    assert spmm(FAKE, FAKE, P(0), 16, 64, FAKE, 8, 10, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)) == 3      # ldb % 4
+    assert spmm(FAKE, P(0x1004), P(0), 16, 64, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)) == 3  # meta % 8
+    assert spmm(FAKE, FAKE, FAKE, 16, 0, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)) == 2        # softmax, K == 0
+    assert spmm(FAKE, FAKE, P(0), 16, 64, FAKE, 8, 8, FAKE, 8, 2, 100, 256, 0, 512, 128, P(0)) == 2  # stride_values
+    assert spmm(P(0), P(0), P(0), 0, 64, P(0), 8, 8, P(0), 8, 1, 0, 0, 0, 0, 0, P(0)) == 0         # R == 0
