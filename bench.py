@@ -298,6 +298,85 @@ def bench_other(workload: str, steps: int, warmup: int) -> dict:
     return out
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def bench_attention_variant(variant: str, steps: int, warmup: int) -> dict:
+    """Per-kernel timings of the attention workload (batch 4 x 16 heads, seq 4096, head_dim 64)
+    in bf16 with 2:4, or in fp32 with 1:2: unfused (SDDMM-prune, softmax, P.V) and fused
+    (SDDMM with row maxima, P.V with the softmax inside). Each kernel: K back-to-back
+    launches between one HIP event pair."""
+    import numpy as np
+    import torch
+    import structured_sparse_matrix_amd as snm
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS["attention_2_4"]
+    bf = variant == "attention_2_4_bf16"
+    Q, Km, V = workloads.attention_qkv_typed(w, "bf16" if bf else "f32")
+    if bf:
+        Qd, Kd, Vd = (torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) for x in (Q, Km, V))
+    else:
+        Qd, Kd, Vd = (torch.from_numpy(x).to(dev) for x in (Q, Km, V))
+    nb, L, d = Q.shape
+    scale = 1.0 / np.sqrt(d)
+
+    def timed(launch):
+        for _ in range(warmup):
+            launch()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            launch()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps * 1e-3
+
+    esz = 2 if bf else 4
+    vbytes = nb * L * (L // 2) * esz
+    mbytes = nb * L * (L // 8 if bf else L // 4)
+    qkv = nb * L * d * esz
+    flops = 2 * nb * L * L * d
+    out = {"workload": variant, "shape": "batch 4 x 16 heads, seq 4096, head_dim 64",
+           "dtype": "bf16" if bf else "f32", "pattern": "2:4" if bf else "1:2", "kernels": {}}
+    O = torch.empty((nb, L, d), dtype=Qd.dtype, device=dev)
+    if bf:
+        sddmm = lambda: snm.sddmm_prune_nm_bf16(Qd, Kd, scale)
+        sddmm_r = lambda: snm.sddmm_prune_nm_bf16(Qd, Kd, scale, return_rowmax=True)
+        vals, meta = sddmm()
+        v2, m2, rmax = sddmm_r()
+        soft = lambda: snm.softmax_nm_rows_bf16(vals)
+        pv = lambda: snm.spmm_nm_bf16(vals, meta, Vd, out=O)
+        pvs = lambda: snm.spmm_nm_softmax_bf16(v2, m2, rmax, Vd, out=O)
+        peak, unit = 2500.0, "bf16 dense / sparse MFMA 2.5 / 5.0 PF/s"
+    else:
+        sddmm = lambda: snm.sddmm_prune_1of2_f32(Qd, Kd, scale)
+        sddmm_r = lambda: snm.sddmm_prune_1of2_f32(Qd, Kd, scale, return_rowmax=True)
+        vals, meta = sddmm()
+        v2, m2, rmax = sddmm_r()
+        soft = lambda: snm.softmax_nm_rows_f32(vals)
+        pv = lambda: snm.spmm_1of2_f32(vals, meta, Vd, out=O)
+        pvs = lambda: snm.spmm_1of2_f32(v2, m2, Vd, row_max=rmax, out=O)
+        peak, unit = FP32_MFMA_PEAK_TFLOPS, "fp32 MFMA 157.3 TF/s"
+    t = {"sddmm": timed(sddmm), "softmax": timed(soft), "pv": timed(pv),
+         "sddmm_rowmax": timed(sddmm_r), "pv_softmax": timed(pvs)}
+    io = vbytes + mbytes + 2 * qkv
+    for name, byt, fl in (("sddmm", io, flops), ("softmax", 2 * vbytes, 0), ("pv", io, flops),
+                          ("sddmm_rowmax", io + 4 * nb * L, flops), ("pv_softmax", io + 4 * nb * L, flops)):
+        k = {"avg_us": t[name] * 1e6, "GB/s": byt / t[name] / 1e9, "hbm_frac": byt / t[name] / 1e9 / HBM_PEAK_GBS}
+        if fl:
+            k["TFLOP/s"] = fl / t[name] / 1e12
+            k["mfma_frac"] = fl / t[name] / 1e12 / (peak if not bf else (2500.0 if "sddmm" in name else 5000.0))
+        out["kernels"][name] = k
+    out["mfma_peak"] = unit
+    out["attention_total_us"] = (t["sddmm"] + t["softmax"] + t["pv"]) * 1e6
+    out["attention_fused_total_us"] = (t["sddmm_rowmax"] + t["pv_softmax"]) * 1e6
+    return out
+
+
 def bench_sweep(steps: int, warmup: int, families=None) -> dict:
     """The general V:N:M sweep (VENOM, Sec. 4, Fig. 9 and Fig. 10 shapes, plus the GPT-3
     layer): per point, the V:2:M encode and the SpMM, each timed over K back-to-back
@@ -524,12 +603,20 @@ def main():
                     help="nm_decode (the headline line) or vnm_64_2_8 / vnm_128_2_16 / attention_2_4 "
                          "(per-kernel timings only) or vnm_sweep (the general V:N:M sweep) or energy "
                          "(energy of the GPU's V:2:M encodings) or bitmap (unstructured sparsity, "
-                         "bitmap format)")
+                         "bitmap format) or attention_2_4_bf16 / attention_1_2_f32 (the attention "
+                         "workload in bf16 with 2:4, in fp32 with 1:2)")
     ap.add_argument("--streams", type=int, default=2,
                     help="decode steps in flight (step i on stream i %% S); kernel timings use one")
     ap.add_argument("--families", default="",
                     help="with --workload vnm_sweep: comma-separated subset of fig9,fig10,gpt3")
     args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if args.workload in ("attention_2_4_bf16", "attention_1_2_f32"):
+        print(json.dumps(bench_attention_variant(args.workload, args.steps, args.warmup)))
+        return
     if args.workload == "bitmap":
         print(json.dumps(bench_bitmap(args.steps, args.warmup)))
         return
@@ -543,10 +630,6 @@ def main():
     if args.workload != "nm_decode":
         print(json.dumps(bench_other(args.workload, args.steps, args.warmup)))
         return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
     import numpy as np
 
     total_ms, wall, enc_ms, spmm_ms = run_gpu(args.steps, args.warmup, args.b_layout, args.a_layout,
