@@ -25,7 +25,9 @@ namespace snm {
 //   * values leave every 4 key tiles (128 keys = one 128-byte line per query row), and
 //     metadata every 32 key tiles (1024 keys = one 128-byte line per row): only whole
 //     lines are written, so the L2 never evicts partly written lines (measured: 16-byte
-//     metadata pieces cost as much as the 8x larger value stream).
+//     metadata pieces cost as much as the 8x larger value stream). The stores are
+//     non-temporal (streaming): the 1.1 GiB of output is not read back by this kernel,
+//     and keeping it out of the caches' normal replacement measured 12 % faster.
 //   * K tiles rotate through a 4-deep register ring loaded 3 tiles ahead. Vector loads and
 //     stores retire in issue order on this architecture, so a load issued after a flush
 //     cannot be waited for without waiting for the flush; the ring keeps every wait on a
@@ -163,7 +165,7 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
           const int64_t qi = q_wave + qt * 32 + row;
           if (ch < 2 * nk && qi < Lq) {
             const u4 v = *reinterpret_cast<const u4*>(sv + (qt * 32 + row) * VP + ch * 16);
-            *reinterpret_cast<u4*>(vals_b + qi * (Lk >> 1) + t0 * 16 + ch * 8) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<u4*>(vals_b + qi * (Lk >> 1) + t0 * 16 + ch * 8));
           }
         }
       }
@@ -183,7 +185,7 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
               const uint8_t* src = sm + (qt * 32 + row) * MP + ch * 16;
               uint8_t* dst = meta_b + qi * (Lk >> 3) + m0 * 4 + ch * 16;
               if (4 * ch + 4 <= nw && (Lk & 127) == 0) {
-                *reinterpret_cast<u4*>(dst) = *reinterpret_cast<const u4*>(src);
+                __builtin_nontemporal_store(*reinterpret_cast<const u4*>(src), reinterpret_cast<u4*>(dst));
               } else {
                 for (int w = 4 * ch; w < 4 * ch + 4 && w < nw; ++w)
                   reinterpret_cast<uint32_t*>(dst)[w - 4 * ch] = reinterpret_cast<const uint32_t*>(src)[w - 4 * ch];
@@ -222,7 +224,7 @@ k_softmax_rows(uint16_t* __restrict__ vals, int64_t rows, int64_t kept, int64_t 
     for (int c = 0; c < CH; ++c) {
       const int64_t e = ((int64_t)c * 64 + lane) * 8;
       if (e < kept) {
-        x[c] = *reinterpret_cast<const h8*>(v + e);
+        x[c] = __builtin_nontemporal_load(reinterpret_cast<const h8*>(v + e));
 #pragma unroll
         for (int t = 0; t < 8; ++t) mx = fmaxf(mx, E::widen(f16_bits(x[c][t])));
       }
@@ -250,7 +252,7 @@ k_softmax_rows(uint16_t* __restrict__ vals, int64_t rows, int64_t kept, int64_t 
         u4 o;
 #pragma unroll
         for (int t = 0; t < 4; ++t) o[t] = E::pack2(f2{ex[c][2 * t] * inv, ex[c][2 * t + 1] * inv});
-        *reinterpret_cast<u4*>(v + e) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u4*>(v + e));
       }
     }
     return;

@@ -39,7 +39,8 @@ __device__ __forceinline__ bool keep_second(float x0, float x1) {
 // two 1:2 pairs. The reduction index k of step j and lane half h is d = h D/2 + j, so a
 // lane reads its query's and key's halves of d as contiguous 16-byte pieces.
 //   * values leave every 2 key tiles (2 x 16 kept fp32 = one 128-byte line per query row),
-//     metadata every 16 key tiles (16 x 8 bytes = one line per row);
+//     metadata every 16 key tiles (16 x 8 bytes = one line per row), as non-temporal
+//     (streaming) stores;
 //   * the key tile t + 1 is loaded while tile t is multiplied (for D = 128, where two key
 //     tiles do not fit in the register file beside the queries, tile t is loaded just
 //     before use and the second wave of the SIMD covers the latency).
@@ -149,8 +150,8 @@ k_sddmm_1of2_f32(const float* __restrict__ Q, const float* __restrict__ Km, int6
         const int ch = lane & 7;   // 16-byte chunk = 4 kept values
         const int64_t q = q_wave + row;
         if (ch < 4 * nk && q < Lq)
-          *reinterpret_cast<u4*>(vals_b + q * (Lk >> 1) + t0 * 16 + ch * 4) =
-              *reinterpret_cast<const u4*>(sv + row * VP + ch * 16);
+          __builtin_nontemporal_store(*reinterpret_cast<const u4*>(sv + row * VP + ch * 16),
+                                      reinterpret_cast<u4*>(vals_b + q * (Lk >> 1) + t0 * 16 + ch * 4));
       }
       // ---- metadata: every MT tiles (or at the end)
       const int64_t tend = t0 + nk;
@@ -166,7 +167,7 @@ k_sddmm_1of2_f32(const float* __restrict__ Q, const float* __restrict__ Km, int6
             const uint8_t* src = sm + row * MP + ch * 16;
             uint8_t* dst = meta_b + q * (Lk >> 2) + m0 * 8 + ch * 16;
             if (2 * ch + 2 <= nw && (Lk & 63) == 0) {
-              *reinterpret_cast<u4*>(dst) = *reinterpret_cast<const u4*>(src);
+              __builtin_nontemporal_store(*reinterpret_cast<const u4*>(src), reinterpret_cast<u4*>(dst));
             } else {
               for (int w = 2 * ch; w < 2 * ch + 2 && w < nw; ++w)
                 reinterpret_cast<u2*>(dst)[w - 2 * ch] = reinterpret_cast<const u2*>(src)[w - 2 * ch];
@@ -199,7 +200,7 @@ k_softmax_rows_f32(float* __restrict__ vals, int64_t rows, int64_t kept, int64_t
     for (int c = 0; c < CH; ++c) {
       const int64_t e = ((int64_t)c * 64 + lane) * 4;
       if (e < kept) {
-        x[c] = *reinterpret_cast<const f4*>(v + e);
+        x[c] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(v + e));
         mx = fmaxf(mx, fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3])));
       }
     }
@@ -221,7 +222,7 @@ k_softmax_rows_f32(float* __restrict__ vals, int64_t rows, int64_t kept, int64_t
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int64_t e = ((int64_t)c * 64 + lane) * 4;
-      if (e < kept) *reinterpret_cast<f4*>(v + e) = x[c] * inv;
+      if (e < kept) __builtin_nontemporal_store(x[c] * inv, reinterpret_cast<f4*>(v + e));
     }
     return;
   }
