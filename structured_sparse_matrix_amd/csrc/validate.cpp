@@ -73,7 +73,8 @@ int check_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, co
         stride_Y < R * ldy || !fits(batch, stride_values) || !fits(batch, stride_B) ||
         !fits(batch, stride_Y) || !fits(batch, stride_meta))
       return SNM_E_SHAPE;
-    if (stride_values % 8 != 0 || stride_meta % 16 != 0) return SNM_E_ALIGN;
+    // an empty reduction (K == 0) reads no A entry: its strides carry no alignment rule
+    if (K > 0 && (stride_values % 8 != 0 || stride_meta % 16 != 0)) return SNM_E_ALIGN;
   }
   if (!all_aligned({values, meta}) || !aligned2(B) || !aligned2(Y)) return SNM_E_ALIGN;
   return SNM_OK;
@@ -182,7 +183,7 @@ int check_spmm_1of2_f32(const void* values, const void* meta, const void* row_ma
         !fits(batch, stride_meta) || !fits(batch, stride_B) || !fits(batch, stride_Y) ||
         !fits(batch, stride_row_max))
       return SNM_E_SHAPE;
-    if (stride_values % 4 != 0 || stride_meta % 8 != 0 || stride_B % 4 != 0) return SNM_E_ALIGN;
+    if (K > 0 && (stride_values % 4 != 0 || stride_meta % 8 != 0 || stride_B % 4 != 0)) return SNM_E_ALIGN;
   }
   if (!aligned16(values) || ((uintptr_t)meta & 7u) != 0 || !aligned16(B) || C % 4 != 0 ||
       ldb % 4 != 0 || ((uintptr_t)row_max & 3u) != 0 || ((uintptr_t)Y & 3u) != 0)

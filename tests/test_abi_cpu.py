@@ -284,3 +284,14 @@ def test_f32_1of2_validation():
     assert spmm(FAKE, FAKE, FAKE, 16, 0, FAKE, 8, 8, FAKE, 8, 1, 0, 0, 0, 0, 0, P(0)) == 2        # softmax, K == 0
     assert spmm(FAKE, FAKE, P(0), 16, 64, FAKE, 8, 8, FAKE, 8, 2, 100, 256, 0, 512, 128, P(0)) == 2  # stride_values
     assert spmm(P(0), P(0), P(0), 0, 64, P(0), 8, 8, P(0), 8, 1, 0, 0, 0, 0, 0, P(0)) == 0         # R == 0
+
+
+def test_empty_reduction_strides_carry_no_alignment_rule():
+    # values, meta, R, K, B, C, ldb, b_layout, Y, ldy, batch, s_values, s_meta, s_B, s_Y, stream
+    lib = _lib()
+    # K = 16: a metadata batch stride that is not a multiple of 16 bytes is rejected
+    assert lib.snm_spmm_nm(FAKE, FAKE, 40, 16, FAKE, 8, 8, 0, FAKE, 8, 2, 320, 88, 128, 320, P(0)) == 3
+    # K = 0 (nothing is read): the same strides pass validation; without a GPU the call then
+    # stops at the device check (SNM_E_DEVICE), with one it writes zeros (GPU test)
+    st = lib.snm_spmm_nm(FAKE, FAKE, 40, 0, FAKE, 8, 8, 0, FAKE, 8, 2, 40, 40, 0, 320, P(0))
+    assert st in (0, 5)

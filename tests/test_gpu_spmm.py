@@ -256,3 +256,19 @@ def test_spmm_vnm_wide_shapes(R, K, C, V, M):
     ov, omi, ocl, B = _vnm_case(R, K, C, V, M, R * 3 + K + C + V + M)
     Y = snm.spmm_vnm(to_dev(ov), to_dev(omi), to_dev(ocl), to_dev(B), V, M)
     assert_fp16_close(to_host(Y), oracle.spmm_vnm(ov, omi, ocl, V, M, B), f"wide vnm {R}x{K}x{C} V{V} M{M}")
+
+
+@pytest.mark.parametrize("C,colmajor", [(8, False), (8, True), (32, False), (48, False), (48, True)])
+def test_spmm_nm_empty_reduction_writes_zeros(C, colmajor):
+    # K = 0: every output is an empty sum; each kernel (decode C <= 32, wide row-major,
+    # column-major fallback) must write zeros without reading A or B
+    import torch
+    snm = _snm()
+    b, R = 2, 40
+    values = torch.empty((b, R, 0), dtype=torch.float16, device="cuda")
+    meta = torch.empty((b, R, 0), dtype=torch.uint8, device="cuda")
+    B = (torch.empty((b, C, 0), dtype=torch.float16, device="cuda").transpose(1, 2) if colmajor
+         else torch.empty((b, 0, C), dtype=torch.float16, device="cuda"))
+    out = torch.full((b, R, C), 7.0, dtype=torch.float16, device="cuda")
+    snm.spmm_nm(values, meta, B, out=out)
+    assert torch.count_nonzero(out).item() == 0
