@@ -217,9 +217,10 @@ int snm_bitmap_encode(const void* A, int64_t R, int64_t K, int64_t lda, const vo
 /* Y = decode(bitmaps, tile_offsets, values) * B for a decode-shaped B with C <= 32 columns
  * (Coruscant Sec. 3.2: the product of a bitmap-compressed weight with few activations).
  * B, b_layout, Y as in snm_spmm_nm; column-major B (b_layout 1) needs ldb % 8 == 0 and a
- * 16-byte aligned B (row-major B is supported, slower). values 16-byte aligned. fp32
- * accumulation, fp16 output (RNE). C > 32 returns SNM_E_UNSUPPORTED. values may be NULL when
- * the encoding holds no non-zeros. */
+ * 16-byte aligned B; row-major B (b_layout 0) is supported, slower, with ldb <= 2^25
+ * (larger strides return SNM_E_UNSUPPORTED). values 16-byte aligned. fp32 accumulation,
+ * fp16 output (RNE). C > 32 returns SNM_E_UNSUPPORTED. values may be NULL when the encoding
+ * holds no non-zeros. */
 int snm_spmm_bitmap(const void* bitmaps, const void* tile_offsets, const void* values, int64_t R,
                     int64_t K, const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                     int64_t ldy, void* stream);

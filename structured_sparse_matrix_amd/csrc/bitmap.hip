@@ -11,14 +11,19 @@
 //   * the encoder runs in three steps -- per-row bitmaps, padded counts and in-row
 //     offsets; one workgroup scanning the row totals; the final offsets -- then writes
 //     the values in a separate call, once the caller has allocated them.
-//   * the product: one workgroup per 16 rows, eight waves splitting K; each wave copies its
-//     rows' packed values for a phase of 4 tiles (16-byte aligned spans, because every
-//     tile starts at a multiple of 8 values) into its own LDS region with the
-//     global->LDS DMA, then expands each 8-position chunk through its bitmap byte with
-//     LDS reads at the computed ranks, and runs a dense MFMA on the expanded operand.
-//     Partial sums of the waves are added through LDS.
+//   * the product: one workgroup per 16 rows, eight waves splitting K. Each wave walks its
+//     tiles in phases of 2, software-pipelined: the tiles' bitmaps and offsets are copied
+//     into LDS (global->LDS DMA) two phases ahead, their packed values (16-byte aligned
+//     spans, because every tile starts at a multiple of 8 values) one phase ahead, into
+//     double-buffered per-wave regions whose 16-byte slots are XOR-swizzled by row so that
+//     the 16 rows' reads fall on different LDS banks. Each 8-position chunk is expanded
+//     through its bitmap byte with LDS reads at the computed ranks and fed to a dense
+//     MFMA. Partial sums of the waves are added through LDS.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "lds_dma.hpp"
+
+#include <type_traits>
 
 namespace snm {
 namespace {
@@ -171,28 +176,51 @@ __device__ __forceinline__ f4 mfma16x16x32(const h8& a, const h8& b, const f4& c
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// 4-byte global -> LDS DMA: lane l writes LDS bytes [lds_byte + 4 l, + 4) (lds_byte is
+// wave-uniform, through M0); completion is tracked with s_waitcnt vmcnt by the caller.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is set inside the statement
+__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds_byte) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "m0");
+}
+#pragma clang diagnostic pop
+
+template <int I>
+using cint = std::integral_constant<int, I>;
+
 // One workgroup (kBmWaves waves) per 16-row tile; wave w takes a contiguous 1/kBmWaves of
-// the row's tiles and walks it in phases of 4 tiles (256 positions). Eight waves and two
-// workgroups per CU keep sixteen phases' loads in flight per CU. Lane l = 16q + i works on row
-// i; in tile t it covers positions 32 blk + 8q + [0, 8), blk = 0, 1 (bitmap byte
-// 4 blk + q) -- the dense MFMA A operand of k-block (t, blk).
-// Per phase: (1) the packed values of the phase's 4 tiles of every row of the tile (a
-// contiguous, 16-byte aligned span of at most 256 values) are copied by DMA into the
-// wave's LDS region, row i at [512 i, 512 i + 512): DMA b covers rows 2b and 2b + 1, lane
-// l one 16-byte chunk (lanes past a row's span stay inactive); (2) the B operands are
-// loaded; (3) each chunk is expanded through its bitmap byte -- the e-th set bit takes
-// the next value of the span, at LDS byte 512 i + 2 (tile offset - span start + rank) --
-// and multiplied on the matrix core.
+// the row's tiles and walks it in phases of kPT tiles. Lane l = 16q + i works on row i; in
+// tile t it covers positions 32 blk + 8q + [0, 8), blk = 0, 1 (bitmap byte 4 blk + q) --
+// the dense MFMA A operand of k-block (t, blk).
+// A phase goes through three steps, each overlapped with the previous phase's work:
+//   (1) its metadata -- every row's bitmaps and tile offsets -- is copied by DMA into one of
+//       the wave's two metadata buffers (issued two phases ahead);
+//   (2) its packed values -- for each row the contiguous, 16-byte aligned span of its
+//       tiles' values -- are copied by DMA into one of two value buffers, row i at
+//       [256 i, 256 i + 256), with source addresses computed from (1) (one phase ahead),
+//       and its B operands are loaded (one phase ahead);
+//   (3) each chunk is expanded through its bitmap byte -- the e-th set bit takes the next
+//       value of the span -- and multiplied on the matrix core.
+// Each phase starts with one wait for everything issued during the previous phase, so the
+// latencies of (1) and (2) run under the expansion and products of the phase before. Lanes
+// with nothing to copy point their DMA at a readable dummy (B) and land in their own row's
+// region past its span, which the expansion never uses.
 constexpr int kBmWaves = 8;
-constexpr int kWaveBytes = 8192;                      // staged values of one wave
-constexpr int kLutOff = kBmWaves * kWaveBytes + 16;   // + a pad that over-reads may touch
+constexpr int kPT = 2;                                   // tiles per phase
+constexpr int kRowBytes = kPT * kTile * 2;               // staged values of a row per phase
+constexpr int kValBuf = 16 * kRowBytes;                  // one phase's values (4 KiB)
+constexpr int kMetaBuf = 512;                            // bitmaps 16 x 16 B, offsets 16 x 12 B
+constexpr int kMetaOffs = 256;                           // offsets within a metadata buffer
+constexpr int kWaveBytes = 2 * kValBuf + 2 * kMetaBuf;   // two phases in flight
+constexpr int kLutOff = kBmWaves * kWaveBytes + 16;      // + a pad that over-reads may touch
 constexpr int kLutBytes = 256 * 16 + 256 * 8;
 constexpr int kBitmapLds = kLutOff + kLutBytes;
 
 template <int CT, bool BCOL>
 __global__ void __launch_bounds__(64 * kBmWaves) __attribute__((amdgpu_waves_per_eu(4)))
 k_spmm_bitmap(BitmapArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];   // 8 KiB per wave, then the expansion table
+  extern __shared__ __align__(16) uint8_t smem[];   // per wave 9 KiB, then the expansion table
   // Expansion table, one entry per bitmap byte m: four dwords of 16-bit keep masks (0xFFFF
   // where bit e of m is set) and two dwords of eight byte offsets (2 rank_e, rank_e = set
   // bits of m below e). Expanding a chunk is then one address add and one read per
@@ -211,54 +239,78 @@ k_spmm_bitmap(BitmapArgs a) {
     *reinterpret_cast<u2*>(smem + kLutOff + 4096 + 8 * m) = u2{rk[0], rk[1]};
   }
   __syncthreads();
-  constexpr int kPhaseTiles = 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int q = lane >> 4;
   const int li = lane & 15;
   const int64_t row0 = (int64_t)blockIdx.x * 16;
-  const int64_t row = row0 + li;
-  const bool row_ok = row < a.R;
   const int64_t T = a.K / kTile;
+  const int64_t RT = a.R * T;                          // bitmaps; offsets hold RT + 1
   const int64_t tw = (T + kBmWaves - 1) / kBmWaves;     // tiles per wave
   const int64_t tbeg = (int64_t)w * tw;
   const int64_t tend = tbeg + tw < T ? tbeg + tw : T;
+  const int64_t nph = tend > tbeg ? (tend - tbeg + kPT - 1) / kPT : 0;
   uint8_t* const wl = smem + w * kWaveBytes;
   const uint32_t wl_lds = lds_addr(wl);
+  constexpr int kMetaBase = 2 * kValBuf;
 
-  f4 acc[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t kt0 = tbeg; kt0 < tend; kt0 += kPhaseTiles) {
-    const int nt = (int)(tend - kt0 < kPhaseTiles ? tend - kt0 : kPhaseTiles);
-    // (1) metadata of the lane's row and the DMA of every row's span
-    uint64_t bm[kPhaseTiles];
-    uint32_t off[kPhaseTiles];
-    uint32_t span0 = 0, span1 = 0;
-#pragma unroll
-    for (int t = 0; t < kPhaseTiles; ++t) { bm[t] = 0ull; off[t] = 0u; }
-    if (row_ok) {
-      const int64_t tb = row * T + kt0;
-#pragma unroll
-      for (int t = 0; t < kPhaseTiles; ++t)
-        if (t < nt) { bm[t] = a.bitmaps[tb + t]; off[t] = a.offsets[tb + t]; }
-      span0 = a.offsets[tb];
-      span1 = a.offsets[tb + nt];
+  // (1) metadata of phase p into metadata buffer mb: lane l copies bitmap word l % 2 of
+  // tile (l / 2) % 2 of row l / 4, and (l < 48) offset entry l % 3 of row l / 3; rows past
+  // R repeat row R - 1, tiles past the row's end repeat its last tile
+  auto issue_meta = [&](int64_t p, int mb) {
+    const int64_t kt0 = tbeg + p * kPT;
+    const uint32_t base = wl_lds + (uint32_t)(kMetaBase + mb * kMetaBuf);
+    {
+      int64_t r = row0 + (lane >> 2);
+      r = r < a.R ? r : a.R - 1;
+      int64_t t = kt0 + ((lane >> 1) & 1);
+      t = t < T ? t : T - 1;
+      lds_dma4(reinterpret_cast<const uint32_t*>(a.bitmaps + r * T + t) + (lane & 1), base);
     }
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int r = 2 * b + (lane >> 5);                        // row of the tile this lane copies
-      const uint32_t s0 = (uint32_t)__shfl((int)span0, r);
-      const uint32_t s1 = (uint32_t)__shfl((int)span1, r);
-      const uint32_t ch = (uint32_t)(lane & 31);
-      if (8u * ch < s1 - s0) lds_dma16(a.values + s0 + 8u * ch, wl_lds + (uint32_t)b * 1024u);
+    {
+      const int rr = lane < 48 ? lane / 3 : 0;
+      const int j = lane < 48 ? lane - 3 * rr : 0;
+      int64_t r = row0 + rr;
+      r = r < a.R ? r : a.R - 1;
+      int64_t idx = r * T + kt0 + j;
+      idx = idx < RT ? idx : RT;
+      lds_dma4(a.offsets + idx, base + (uint32_t)kMetaOffs);   // lanes >= 48 land in the pad
     }
-    // (2) B operands (column-major B: 16 contiguous bytes per lane)
-    h8 bop[kPhaseTiles][2][CT];
+  };
+  // (2) values of phase p (its metadata in buffer mb) into value buffer vb: DMA b fills rows
+  // 4b .. 4b + 3, lane l the 16-byte slot l % 16 of row r = 4b + l / 16, which holds the
+  // row's chunk (l % 16) ^ r. The swizzle spreads the rows over the LDS banks: unswizzled,
+  // rows 256 bytes apart start on the same bank, and the expansion's reads -- the same
+  // ranks in 16 rows -- would collide 16 ways.
+  auto issue_values = [&](int64_t p, int mb, int vb) {
+    const int64_t kt0 = tbeg + p * kPT;
+    const int nt = (int)(tend - kt0 < kPT ? tend - kt0 : kPT);
+    const uint8_t* offs = wl + kMetaBase + mb * kMetaBuf + kMetaOffs;
 #pragma unroll
-    for (int t = 0; t < kPhaseTiles; ++t)
+    for (int b = 0; b < 4; ++b) {
+      const int r = 4 * b + (lane >> 4);
+      const uint32_t ch = (uint32_t)((lane & 15) ^ r);
+      const uint32_t s0 = *reinterpret_cast<const uint32_t*>(offs + 12 * r);
+      const uint32_t s1 = *reinterpret_cast<const uint32_t*>(offs + 12 * r + 4 * nt);
+      const bool live = row0 + r < a.R && 8u * ch < s1 - s0;
+      const void* src = live ? static_cast<const void*>(a.values + s0 + 8u * ch) : static_cast<const void*>(a.B);
+      lds_dma16(src, wl_lds + (uint32_t)(vb * kValBuf + b * 1024));
+    }
+  };
+  // B operands of phase p. With one column tile and column-major B (16 contiguous bytes per
+  // lane) they are loaded one phase ahead into a second register set; otherwise (two column
+  // tiles, or row-major B's eight 2-byte loads per operand: too many registers to hold
+  // twice) at the start of their own phase.
+  constexpr bool kAheadB = BCOL && CT == 1;
+  constexpr int NB = kAheadB ? 2 : 1;
+  h8 bop[NB][kPT][2][CT];
+  auto load_b = [&](int64_t p, auto par_c) {
+    constexpr int P = decltype(par_c)::value;
+    const int64_t kt0 = tbeg + p * kPT;
+    const int nt = (int)(tend - kt0 < kPT ? tend - kt0 : kPT);
+#pragma unroll
+    for (int t = 0; t < kPT; ++t)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -270,47 +322,107 @@ k_spmm_bitmap(BitmapArgs a) {
             if constexpr (BCOL) {
               bv = *reinterpret_cast<const h8*>(a.B + col * a.ldb + k);
             } else {
+              // the tile's rows from a uniform base with 32-bit lane offsets (B's row
+              // stride is below 2^25 elements): one address register per load
+              const uint8_t* bt = reinterpret_cast<const uint8_t*>(a.B + (kt0 + t) * kTile * a.ldb);
+              const uint32_t o0 = (uint32_t)(((32 * blk + 8 * q) * a.ldb + col) * 2);
+              const uint32_t ostep = (uint32_t)(a.ldb * 2);
 #pragma unroll
-              for (int e = 0; e < 8; ++e) bv[e] = bits_f16(a.B[(k + e) * a.ldb + col]);
+              for (int e = 0; e < 8; ++e)
+                bv[e] = bits_f16(*reinterpret_cast<const uint16_t*>(bt + (o0 + (uint32_t)e * ostep)));
             }
           }
-          bop[t][blk][ct] = bv;
+          bop[P][t][blk][ct] = bv;
         }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the DMA has landed in LDS
-    // (3) expand and multiply
-    const uint32_t rbase = 512u * (uint32_t)li;
+  };
+
+  f4 acc[CT];
 #pragma unroll
-    for (int t = 0; t < kPhaseTiles; ++t) {
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+
+  auto phase = [&](int64_t p, auto par_c) {
+    constexpr int P = decltype(par_c)::value;   // p % 2: its value and metadata buffers
+    constexpr int PB = kAheadB ? P : 0;         // its B register set
+    wait_vmcnt<0>();   // this phase's values and B, the next phase's metadata
+    if constexpr (!kAheadB) {
+      load_b(p, cint<0>{});
+      wait_vmcnt<0>();
+    }
+    // the B operands have arrived: any wait the compiler adds for them goes here, where
+    // nothing is outstanding
+#pragma unroll
+    for (int t = 0; t < kPT; ++t)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) asm volatile("" : "+v"(bop[PB][t][blk][ct]));
+    const uint8_t* mbuf = wl + kMetaBase + P * kMetaBuf;
+    uint64_t bm[kPT];
+    uint32_t off[kPT];
+#pragma unroll
+    for (int t = 0; t < kPT; ++t) {
+      bm[t] = *reinterpret_cast<const uint64_t*>(mbuf + 16 * li + 8 * t);
+      off[t] = *reinterpret_cast<const uint32_t*>(mbuf + kMetaOffs + 12 * li + 4 * t);
+    }
+    if (p + 1 < nph) {
+      if constexpr (kAheadB) load_b(p + 1, cint<P ^ 1>{});
+      issue_values(p + 1, P ^ 1, P ^ 1);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // metadata reads done: refill buffer P
+    if (p + 2 < nph) issue_meta(p + 2, P);
+    // (3) expand and multiply
+    const int64_t kt0 = tbeg + p * kPT;
+    const int nt = (int)(tend - kt0 < kPT ? tend - kt0 : kPT);
+    const uint32_t rbase = (uint32_t)(P * kValBuf + kRowBytes * li);
+    const uint32_t swz = (uint32_t)li << 4;   // byte b of the row's span sits at rbase + (b ^ swz)
+    const uint32_t span0 = off[0];
+#pragma unroll
+    for (int t = 0; t < kPT; ++t) {
       if (t >= nt) break;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         const int byte = 4 * blk + q;
         const uint64_t below = byte == 0 ? 0ull : (bm[t] & ((1ull << (8 * byte)) - 1ull));
-        // first value of the chunk; a position past the last set bit reads at most one
-        // value beyond the row's span (inside the wave region, or the pad after the last)
-        const uint32_t a0 = rbase + 2u * ((off[t] - span0) + (uint32_t)__popcll(below));
+        // span byte of the chunk's first value; a position past the last set bit reads at
+        // most one value beyond the row's span (byte 256 at most: inside the wave region)
+        const uint32_t a0 = 2u * ((off[t] - span0) + (uint32_t)__popcll(below));
         const uint32_t m = (uint32_t)(bm[t] >> (8 * byte)) & 0xFFu;
         const u4 keep = *reinterpret_cast<const u4*>(smem + kLutOff + 16u * m);
         const u2 rk = *reinterpret_cast<const u2*>(smem + kLutOff + 4096u + 8u * m);
         u4 pk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t w = rk[i >> 1];
+          const uint32_t rw = rk[i >> 1];
           const int sh = 16 * (i & 1);
-          const uint32_t lo = *reinterpret_cast<const uint16_t*>(wl + a0 + ((w >> sh) & 0xFFu));
-          const uint32_t hi = *reinterpret_cast<const uint16_t*>(wl + a0 + ((w >> (sh + 8)) & 0xFFu));
+          const uint32_t blo = (a0 + ((rw >> sh) & 0xFFu)) ^ swz;
+          const uint32_t bhi = (a0 + ((rw >> (sh + 8)) & 0xFFu)) ^ swz;
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(wl + rbase + blo);
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(wl + rbase + bhi);
           pk[i] = (lo | (hi << 16)) & keep[i];
         }
         const h8 av = __builtin_bit_cast(h8, pk);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma16x16x32(av, bop[t][blk][ct], acc[ct]);
+        for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma16x16x32(av, bop[PB][t][blk][ct], acc[ct]);
         // scheduling fence: expand block by block (hoisting every block's LDS reads would
         // hold all their results in registers)
         asm volatile("" ::: "memory");
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // LDS reads done before the next DMA
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // value reads done: buffer P is free
+  };
+
+  if (nph > 0) {
+    issue_meta(0, 0);
+    if (nph > 1) issue_meta(1, 1);
+    wait_vmcnt<0>();
+    if constexpr (kAheadB) load_b(0, cint<0>{});
+    issue_values(0, 0, 0);
   }
+  for (int64_t p = 0; p < nph; p += 2) {
+    phase(p, cint<0>{});
+    if (p + 1 < nph) phase(p + 1, cint<1>{});
+  }
+  wait_vmcnt<0>();   // no copy in flight when the buffers are reused below
 
   // ---- sum the partial tiles of the waves and store Y -------------------------------------
   __syncthreads();
@@ -372,7 +484,7 @@ hipError_t launch_spmm_bitmap(const uint64_t* bitmaps, const uint32_t* offsets, 
   a.R = R; a.K = K; a.C = C; a.ldb = ldb; a.ldy = ldy;
   a.b_col = b_layout == 1;
   const unsigned g = (unsigned)((R + 15) / 16);
-  const size_t lds = (size_t)kBitmapLds;   // 69 KiB: two workgroups per CU
+  const size_t lds = (size_t)kBitmapLds;   // 78 KiB: two workgroups per CU
   const dim3 blk(64 * kBmWaves);
   auto go = [&](auto kern) -> hipError_t {
     static bool set[2][2] = {};

@@ -220,6 +220,8 @@ int check_spmm_bitmap(const void* bitmaps, const void* offsets, const void* valu
   if (b_layout != 0 && b_layout != 1) return SNM_E_UNSUPPORTED;
   if (C < 0 || !fits(K, C) || !fits(R, C)) return SNM_E_SHAPE;
   if (C > 32) return SNM_E_UNSUPPORTED;
+  // row-major B is read with 32-bit byte offsets from each 64-row tile's start
+  if (b_layout == 0 && ldb > (int64_t(1) << 25)) return SNM_E_UNSUPPORTED;
   if (R == 0 || C == 0) return SNM_OK;
   if (!Y || (K > 0 && (!bitmaps || !offsets || !B))) return SNM_E_NULL;   // values may be NULL (no non-zeros)
   const int64_t b_lines = b_layout == 0 ? K : C;

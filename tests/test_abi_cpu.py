@@ -191,6 +191,7 @@ def test_bitmap_sizes_and_validation():
     # spmm: bitmaps, offsets, values, R, K, B, C, ldb, b_layout, Y, ldy, stream
     assert lib.snm_spmm_bitmap(FAKE, FAKE, FAKE, 16, 64, FAKE, 40, 64, 1, FAKE, 40, P(0)) == 4   # C > 32
     assert lib.snm_spmm_bitmap(FAKE, FAKE, FAKE, 16, 64, FAKE, 8, 64, 2, FAKE, 8, P(0)) == 4     # layout
+    assert lib.snm_spmm_bitmap(FAKE, FAKE, FAKE, 16, 64, FAKE, 8, (1 << 25) + 1, 0, FAKE, 8, P(0)) == 4  # row stride
     assert lib.snm_spmm_bitmap(FAKE, FAKE, MISALIGNED, 16, 64, FAKE, 8, 64, 1, FAKE, 8, P(0)) == 3
     assert lib.snm_spmm_bitmap(FAKE, FAKE, FAKE, 16, 64, FAKE, 8, 68, 1, FAKE, 8, P(0)) == 3     # ldb % 8
     assert lib.snm_spmm_bitmap(FAKE, FAKE, FAKE, 16, 64, FAKE, 8, 32, 1, FAKE, 8, P(0)) == 2     # ldb < K
