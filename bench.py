@@ -261,12 +261,19 @@ def bench_other(workload: str, steps: int, warmup: int) -> dict:
             + w.K * C * 2 + w.R * C * 2
         bytes_enc = w.R * w.K * 2 + w.R * (2 * w.K // w.M) * 2 + w.R * (w.K // w.M) // 2 + (w.R // w.V) * (w.K // w.M) * 4
         out["kernels"]["prune_encode_vnm"] = {"avg_us": t_enc * 1e6, "GB/s": bytes_enc / t_enc / 1e9}
-        out["kernels"]["spmm_vnm"] = {
-            "avg_us": t_mm * 1e6, "GB/s": bytes_mm / t_mm / 1e9,
-            "dense_equiv_TFLOP/s": 2 * w.R * w.K * C / t_mm / 1e12,
-            "smfmac_TFLOP/s": 2 * w.R * Kp * C / t_mm / 1e12,
-            "sparse_mfma_frac": 2 * w.R * Kp * C / t_mm / 1e12 / 5000.0,
-            "hbm_frac": bytes_mm / t_mm / 1e9 / HBM_PEAK_GBS}
+        def mm_stats(t):
+            return {"avg_us": t * 1e6, "GB/s": bytes_mm / t / 1e9,
+                    "dense_equiv_TFLOP/s": 2 * w.R * w.K * C / t / 1e12,
+                    "smfmac_TFLOP/s": 2 * w.R * Kp * C / t / 1e12,
+                    "sparse_mfma_frac": 2 * w.R * Kp * C / t / 1e12 / 5000.0,
+                    "hbm_frac": bytes_mm / t / 1e9 / HBM_PEAK_GBS}
+        out["kernels"]["spmm_vnm"] = mm_stats(t_mm)
+        # the same arrays in the row-group interleaved storage (whole-line copies of A)
+        enc_t = [snm.prune_encode_vnm_tiled(a, w.V, w.M) for a in Ad]
+        t_enc_t = timed(lambda j: snm.prune_encode_vnm_tiled(Ad[j], w.V, w.M))
+        t_mm_t = timed(lambda j: snm.spmm_vnm_tiled(*enc_t[j], Bd[j], w.V, w.M, out=Ys[j]))
+        out["kernels"]["prune_encode_vnm_tiled"] = {"avg_us": t_enc_t * 1e6, "GB/s": bytes_enc / t_enc_t / 1e9}
+        out["kernels"]["spmm_vnm_tiled"] = mm_stats(t_mm_t)
     elif w.kind == "attention":
         Q, Km, V = workloads.attention_qkv(w)
         Qd, Kd, Vd = (torch.from_numpy(x).to(dev) for x in (Q, Km, V))

@@ -146,6 +146,29 @@ int snm_spmm_vnm(const void* values, const void* midx, const void* colloc, int64
                  int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
                  int64_t ldy, void* stream);
 
+/* V:2:M prune and compress (as snm_prune_encode_vnm) into the row-group interleaved
+ * storage of values and m-indices: the same arrays permuted so that the product's copies
+ * read whole cache lines (the MI355X counterpart of VENOM Sec. 4.1.2 and Fig. 7, which
+ * store the format in the order the kernel's fragments load it). With W = K/(4M) 16-byte
+ * value chunks per row (chunk c = the 8 values of groups 4c .. 4c+3, whose m-indices form
+ * the 16-bit word c of the canonical midx row):
+ *   values_t  chunk c of row r at fp16 element ((r/32)*W + c)*256 + (r%32)*8;
+ *   midx_t    word c of row r at 16-bit word ((r/32)*W + c)*32 + (r%32);
+ *   colloc    canonical (unchanged).
+ * Sizes as snm_vnm_sizes. Requires its shape rules and V % 32 == 0 (else
+ * SNM_E_UNSUPPORTED); values_t, midx_t 16-byte aligned. */
+int snm_prune_encode_vnm_tiled(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
+                               void* values_t, void* midx_t, void* colloc, void* stream);
+
+/* Y = decode_vnm(values_t, midx_t, colloc) * B with values and m-indices in the row-group
+ * interleaved storage of snm_prune_encode_vnm_tiled; B, Y as in snm_spmm_vnm. fp32
+ * accumulation, fp16 output (RNE). Runs the wide-tile kernel only: requires V % 32 == 0,
+ * C % 8 == 0, ldb % 8 == 0, 4K/M <= 16384 and 32-bit copy offsets (128*4K/M < 2^31,
+ * (32*M*ldb + C)*2 < 2^31), else SNM_E_UNSUPPORTED; B 16-byte aligned (else SNM_E_ALIGN). */
+int snm_spmm_vnm_tiled(const void* values_t, const void* midx_t, const void* colloc, int64_t R,
+                       int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
+                       int64_t ldy, void* stream);
+
 /* Dynamic 2:4 SDDMM ("Dynamic N:M ... attention", Sec. 3.2 and Listing 1; Sec. 4.2-4.3):
  * for each batch entry b, S = fp16_RNE((Q_b Kmat_b^T) * scale), then 2:4 prune and
  * compress each row of S along the key axis, fused in one kernel.

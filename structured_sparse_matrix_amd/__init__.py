@@ -25,6 +25,7 @@ __all__ = [
     "prune_encode_nm", "prune_encode_vnm", "spmm_nm", "spmm_vnm", "sddmm_prune_nm",
     "softmax_nm_rows", "attention_nm", "nm_sizes", "vnm_sizes", "abi_version", "SnmError",
     "nm_tiled_sizes", "prune_encode_nm_tiled", "spmm_nm_tiled",
+    "prune_encode_vnm_tiled", "spmm_vnm_tiled",
     "sddmm_prune_nm_rowmax", "spmm_nm_softmax", "attention_nm_fused",
     "bitmap_sizes", "bitmap_encode", "spmm_bitmap",
     "sddmm_prune_nm_bf16", "softmax_nm_rows_bf16", "spmm_nm_bf16", "spmm_nm_softmax_bf16",
@@ -143,6 +144,17 @@ def spmm_nm_tiled(values_t, meta_t, R: int, B, out=None):
 
 def prune_encode_vnm(A, V: int, M: int):
     """V:2:M prune of fp16 A [R, K] -> (values [R, 2K/M], midx [R, K/(2M)], colloc [R/V, K/M, 4])."""
+    return _prune_encode_vnm(A, V, M, "snm_prune_encode_vnm")
+
+
+def prune_encode_vnm_tiled(A, V: int, M: int):
+    """V:2:M prune of fp16 A [R, K] into the row-group interleaved storage (V % 32 == 0):
+    (values_t [R, 2K/M], midx_t [R, K/(2M)], colloc [R/V, K/M, 4]). values_t and midx_t
+    hold the canonical arrays permuted as snm.h describes; they feed spmm_vnm_tiled."""
+    return _prune_encode_vnm(A, V, M, "snm_prune_encode_vnm_tiled")
+
+
+def _prune_encode_vnm(A, V: int, M: int, entry: str):
     torch = _torch()
     _need(A, "A", torch.float16, 2)
     if A.stride(1) != 1:
@@ -152,9 +164,8 @@ def prune_encode_vnm(A, V: int, M: int):
     values = torch.empty((R, 2 * G), dtype=torch.float16, device=A.device)
     midx = torch.empty((R, G // 2), dtype=torch.uint8, device=A.device)
     colloc = torch.empty((R // V if V > 0 else 0, G, 4), dtype=torch.uint8, device=A.device)
-    check("snm_prune_encode_vnm",
-          load().snm_prune_encode_vnm(_ptr(A), R, K, A.stride(0), V, M, _ptr(values), _ptr(midx),
-                                      _ptr(colloc), _stream(A)))
+    check(entry, getattr(load(), entry)(_ptr(A), R, K, A.stride(0), V, M, _ptr(values), _ptr(midx),
+                                        _ptr(colloc), _stream(A)))
     return values, midx, colloc
 
 
@@ -204,6 +215,16 @@ def spmm_nm(values, meta, B, out=None):
 
 def spmm_vnm(values, midx, colloc, B, V: int, M: int, out=None):
     """Y = decode_vnm(values, midx, colloc) @ B with B [K, C] -> Y [R, C]."""
+    return _spmm_vnm(values, midx, colloc, B, V, M, out, "snm_spmm_vnm")
+
+
+def spmm_vnm_tiled(values_t, midx_t, colloc, B, V: int, M: int, out=None):
+    """spmm_vnm on the row-group interleaved storage of prune_encode_vnm_tiled (wide-tile
+    kernel: V % 32 == 0, C % 8 == 0, B rows 16-byte aligned)."""
+    return _spmm_vnm(values_t, midx_t, colloc, B, V, M, out, "snm_spmm_vnm_tiled")
+
+
+def _spmm_vnm(values, midx, colloc, B, V: int, M: int, out, entry: str):
     torch = _torch()
     _need(values, "values", torch.float16, 2)
     _need(midx, "midx", torch.uint8, 2)
@@ -219,9 +240,8 @@ def spmm_vnm(values, midx, colloc, B, V: int, M: int, out=None):
         raise ValueError("shape mismatch between the V:2:M arrays and B")
     if out is None:
         out = torch.empty((R, C), dtype=torch.float16, device=B.device)
-    check("snm_spmm_vnm",
-          load().snm_spmm_vnm(_ptr(values), _ptr(midx), _ptr(colloc), R, K, V, M, _ptr(B), C,
-                              B.stride(0), _ptr(out), out.stride(0), _stream(B)))
+    check(entry, getattr(load(), entry)(_ptr(values), _ptr(midx), _ptr(colloc), R, K, V, M, _ptr(B), C,
+                                        B.stride(0), _ptr(out), out.stride(0), _stream(B)))
     return out
 
 

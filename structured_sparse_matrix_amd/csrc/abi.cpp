@@ -109,7 +109,16 @@ int snm_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V
   int s = snm::check_prune_encode_vnm(A, R, K, lda, V, M, values, midx, colloc);
   if (s != SNM_OK || R == 0 || K == 0) return s;
   if ((s = check_device()) != SNM_OK) return s;
-  return launched(snm::launch_prune_encode_vnm(A, R, K, lda, V, M, values, midx, colloc,
+  return launched(snm::launch_prune_encode_vnm(A, R, K, lda, V, M, values, midx, colloc, false,
+                                               (hipStream_t)stream));
+}
+
+int snm_prune_encode_vnm_tiled(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
+                               void* values_t, void* midx_t, void* colloc, void* stream) {
+  int s = snm::check_prune_encode_vnm_tiled(A, R, K, lda, V, M, values_t, midx_t, colloc);
+  if (s != SNM_OK || R == 0 || K == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_prune_encode_vnm(A, R, K, lda, V, M, values_t, midx_t, colloc, true,
                                                (hipStream_t)stream));
 }
 
@@ -134,6 +143,16 @@ int snm_spmm_vnm(const void* values, const void* midx, const void* colloc, int64
   if ((s = check_device()) != SNM_OK) return s;
   return launched(snm::launch_spmm_vnm(values, midx, colloc, R, K, V, M, B, C, ldb, Y, ldy,
                                        (hipStream_t)stream));
+}
+
+int snm_spmm_vnm_tiled(const void* values_t, const void* midx_t, const void* colloc, int64_t R,
+                       int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
+                       int64_t ldy, void* stream) {
+  int s = snm::check_spmm_vnm_tiled(values_t, midx_t, colloc, R, K, V, M, B, C, ldb, Y, ldy);
+  if (s != SNM_OK || R == 0 || C == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_spmm_vnm_tiled(values_t, midx_t, colloc, R, K, V, M, B, C, ldb, Y,
+                                             ldy, (hipStream_t)stream));
 }
 
 int snm_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq, int64_t Lk,

@@ -120,10 +120,24 @@ k_prune_encode_nm_tiled(const uint16_t* __restrict__ A, int64_t R, int64_t K, in
 constexpr int kVnmThreads = 256;
 constexpr int kVnmMaxCols = 1024;
 
+// Where the V:2:M encoders put a row's value pair of group g (element index) and the index
+// word of groups 4w .. 4w + 3 (word index). Canonical: row-major arrays. Row-group
+// interleaved ("tiled", R % 32 == 0): per group of 32 rows, 16-byte chunk c (the 8 values
+// of groups 4c .. 4c + 3) of the 32 rows is stored together, row after row, and likewise
+// their 2-byte index words, so that a copy of any run of chunks of 32 consecutive rows
+// reads whole cache lines.
+__device__ __forceinline__ int64_t vnm_value_at(int64_t row, int64_t g, int64_t G, int tiled) {
+  return tiled ? (((row >> 5) * (G >> 2) + (g >> 2)) << 8) + ((row & 31) << 3) + ((g & 3) << 1)
+               : row * 2 * G + 2 * g;
+}
+__device__ __forceinline__ int64_t vnm_word_at(int64_t row, int64_t w, int64_t G, int tiled) {
+  return tiled ? (((row >> 5) * (G >> 2) + w) << 5) + (row & 31) : row * (G >> 2) + w;
+}
+
 __global__ void __launch_bounds__(kVnmThreads)
 k_prune_encode_vnm(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t lda, int V, int M,
                    int GC, uint16_t* __restrict__ values, uint16_t* __restrict__ midx,
-                   uint8_t* __restrict__ colloc) {
+                   uint8_t* __restrict__ colloc, int tiled) {
   __shared__ double score[kVnmMaxCols];
   __shared__ uint8_t keep[kVnmMaxCols];
   __shared__ uint8_t sel[kVnmMaxCols / 4 * 4];   // [group in chunk][4]
@@ -180,8 +194,6 @@ k_prune_encode_vnm(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t
   }
   __syncthreads();
   const int words = ng >> 2;
-  const int64_t vals_per_row = 2 * G;
-  const int64_t midx_words_per_row = G >> 2;
   for (int it = threadIdx.x; it < V * words; it += kVnmThreads) {
     const int r = it / words;
     const int w = it - r * words;
@@ -200,8 +212,8 @@ k_prune_encode_vnm(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t
     }
     const int64_t row = vb * V + r;
     u4 o = {out[0], out[1], out[2], out[3]};
-    *reinterpret_cast<u4*>(values + row * vals_per_row + 2 * (g0 + 4 * w)) = o;
-    midx[row * midx_words_per_row + (g0 >> 2) + w] = (uint16_t)word;
+    *reinterpret_cast<u4*>(values + vnm_value_at(row, g0 + 4 * w, G, tiled)) = o;
+    midx[vnm_word_at(row, (g0 >> 2) + w, G, tiled)] = (uint16_t)word;
   }
 }
 
@@ -217,7 +229,7 @@ static int vnm_tile_bytes(int V) { return V >= 128 ? kVnmTileBytes : kVnmTileByt
 __global__ void __launch_bounds__(kVnmThreads)
 k_prune_encode_vnm_lds(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t lda, int V,
                        int M, int GC, uint16_t* __restrict__ values, uint16_t* __restrict__ midx,
-                       uint8_t* __restrict__ colloc) {
+                       uint8_t* __restrict__ colloc, int tiled) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int64_t G = K / M;
   const int64_t nchunks = (G + GC - 1) / GC;
@@ -338,8 +350,6 @@ k_prune_encode_vnm_lds(const uint16_t* __restrict__ A, int64_t R, int64_t K, int
   // in flight per thread. Consecutive threads take consecutive groups of a row (ng is a
   // multiple of 4), so the four groups of a metadata word sit in one lane quad and their
   // codes are combined with two quad permutes.
-  const int64_t vals_per_row = 2 * G;
-  const int64_t midx_words_per_row = G >> 2;
   const int nitems = V * ng;
   const int lane = threadIdx.x & 63;
   for (int i0 = threadIdx.x; i0 < nitems + 3 * kVnmThreads; i0 += 4 * kVnmThreads) {
@@ -367,8 +377,8 @@ k_prune_encode_vnm_lds(const uint16_t* __restrict__ A, int64_t R, int64_t K, int
       w |= (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
       if (it < nitems) {
         const int64_t row = vb * V + rr[t];
-        *reinterpret_cast<uint32_t*>(values + row * vals_per_row + 2 * (g0 + gg[t])) = kept;
-        if ((lane & 3) == 0) midx[row * midx_words_per_row + ((g0 + gg[t]) >> 2)] = (uint16_t)w;
+        *reinterpret_cast<uint32_t*>(values + vnm_value_at(row, g0 + gg[t], G, tiled)) = kept;
+        if ((lane & 3) == 0) midx[vnm_word_at(row, (g0 + gg[t]) >> 2, G, tiled)] = (uint16_t)w;
       }
     }
   }
@@ -414,7 +424,8 @@ static int vnm_lds_groups(int V, int M) {
 }
 
 hipError_t launch_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
-                                   void* values, void* midx, void* colloc, hipStream_t stream) {
+                                   void* values, void* midx, void* colloc, bool tiled,
+                                   hipStream_t stream) {
   if (R == 0 || K == 0) return hipSuccess;
   const int GL = vnm_lds_groups(V, M);
   if (GL > 0) {
@@ -431,7 +442,7 @@ hipError_t launch_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t 
     }
     hipLaunchKernelGGL(k_prune_encode_vnm_lds, dim3((unsigned)blocks), dim3(kVnmThreads), lds, stream,
                        (const uint16_t*)A, R, K, lda, V, M, GL, (uint16_t*)values, (uint16_t*)midx,
-                       (uint8_t*)colloc);
+                       (uint8_t*)colloc, (int)tiled);
     return hipGetLastError();
   }
   const int GC = vnm_chunk_groups(M);
@@ -440,7 +451,7 @@ hipError_t launch_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t 
   const int64_t blocks = (R / V) * nchunks;
   hipLaunchKernelGGL(k_prune_encode_vnm, dim3((unsigned)blocks), dim3(kVnmThreads), 0, stream,
                      (const uint16_t*)A, R, K, lda, V, M, GC, (uint16_t*)values, (uint16_t*)midx,
-                     (uint8_t*)colloc);
+                     (uint8_t*)colloc, (int)tiled);
   return hipGetLastError();
 }
 

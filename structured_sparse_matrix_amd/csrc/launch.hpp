@@ -17,8 +17,10 @@ hipError_t launch_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_
 hipError_t launch_spmm_nm_tiled_skinny(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                                        const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                                        int64_t ldy, hipStream_t stream);
+// tiled: the row-group interleaved storage of values and m-indices (R % 32 == 0)
 hipError_t launch_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
-                                   void* values, void* midx, void* colloc, hipStream_t stream);
+                                   void* values, void* midx, void* colloc, bool tiled,
+                                   hipStream_t stream);
 hipError_t launch_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
                           int64_t C, int64_t ldb, int b_layout, void* Y, int64_t ldy, int64_t batch,
                           int64_t stride_values, int64_t stride_meta, int64_t stride_B,
@@ -43,7 +45,12 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
                             int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb,
                             void* Y, int64_t ldy, int64_t batch, int64_t stride_values,
                             int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
-                            hipStream_t stream);
+                            hipStream_t stream, bool a_tiled = false);
+// V:2:M product with values and m-indices in the row-group interleaved storage (wide
+// kernel only: V % 32 == 0 and the shape rules of spmm_wide_supported)
+hipError_t launch_spmm_vnm_tiled(const void* values_t, const void* midx_t, const void* colloc,
+                                 int64_t R, int64_t K, int V, int M, const void* B, int64_t C,
+                                 int64_t ldb, void* Y, int64_t ldy, hipStream_t stream);
 // 2:4 SpMM that applies the softmax over each row's kept scores (wide kernel, softmax mode).
 hipError_t launch_spmm_nm_softmax(const void* values, const void* meta, const float* row_max,
                                   int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb,

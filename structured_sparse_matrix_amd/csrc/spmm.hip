@@ -433,4 +433,13 @@ hipError_t launch_spmm_vnm(const void* values, const void* midx, const void* col
   return launch_cfg<1, 4, 1, 1, 2, 2, true>(a, stream);                    // BM = 16, BN = 128
 }
 
+hipError_t launch_spmm_vnm_tiled(const void* values_t, const void* midx_t, const void* colloc,
+                                 int64_t R, int64_t K, int V, int M, const void* B, int64_t C,
+                                 int64_t ldb, void* Y, int64_t ldy, hipStream_t stream) {
+  const int64_t Kc = 4 * (K / M);
+  if (V % 32 != 0 || !spmm_wide_supported(R, Kc, V, M, B, C, ldb, 1, 0)) return hipErrorInvalidValue;
+  return launch_spmm_wide(values_t, midx_t, colloc, R, Kc, V, M, B, C, ldb, Y, ldy, 1, 0, 0, 0, 0,
+                          stream, true);
+}
+
 }  // namespace snm

@@ -51,6 +51,9 @@ struct WideArgs {
   int V, M;
   int xcd_remap;                  // total workgroups are a multiple of 8
   int y_vec;                      // Y rows start 16-byte aligned (16-byte output stores)
+  int a_tiled;                    // V:2:M values and m-indices in the row-group interleaved
+                                  // storage (per 32 rows: 16-byte chunk c of every row, then
+                                  // chunk c + 1; 2-byte words likewise)
 };
 
 template <int WM, int WN, int TM, int TN, int KSTEPS, int NST, bool GATHER>
@@ -174,17 +177,26 @@ k_spmm_wide(WideArgs a) {
     c = c < a.C ? c : 0;
     boff[j] = GATHER ? (uint32_t)(((int64_t)(x >> 2) * a.M * a.ldb + c) * 2) : (uint32_t)(((int64_t)x * a.ldb + c) * 2);
   }
-  uint32_t aoff[nA], moff[nA];   // A chunk (16 bytes = 16 positions) and index word sources
+  // A chunk (16 bytes = 16 positions) and index word sources. Canonical storage: row r's
+  // chunk c at r Kc + 16 c, word w at r mrow + 2 w. Row-group interleaved storage (row0 is
+  // a multiple of 32): chunk c of row r at 32 Kc (r / 32) + 512 c + 16 (r % 32), word w at
+  // 32 mrow (r / 32) + 64 w + 2 (r % 32), so a stage's copies read whole lines.
+  uint32_t aoff[nA], moff[nA];
 #pragma unroll
   for (int j = 0; j < nA; ++j) {
     const int bi = wave * nA + j;
     int64_t r = wide::a_dma_row<KS>(bi, lane);
     r = row0 + r < a.R ? r : a.R - 1 - row0;
-    aoff[j] = (uint32_t)(r * Kc + wide::a_dma_chunk<KS>(bi, lane) * 16);
+    const int64_t ch = wide::a_dma_chunk<KS>(bi, lane);
+    aoff[j] = a.a_tiled ? (uint32_t)((r >> 5) * 32 * Kc + ch * 512 + (r & 31) * 16) : (uint32_t)(r * Kc + ch * 16);
     int64_t rm = wide::m_dma_row<KS>(bi, lane);
     rm = row0 + rm < a.R ? rm : a.R - 1 - row0;
-    moff[j] = (uint32_t)(rm * mrow + wide::m_dma_word<KS>(lane) * 2);
+    const int64_t wd = wide::m_dma_word<KS>(lane);
+    moff[j] = a.a_tiled ? (uint32_t)((rm >> 5) * 32 * mrow + wd * 64 + (rm & 31) * 2) : (uint32_t)(rm * mrow + wd * 2);
   }
+  // bytes between consecutive stages' A chunks and index words (the same run of rows)
+  const int64_t a_stage = a.a_tiled ? (int64_t)KS * 32 : (int64_t)KS;
+  const int64_t m_stage = a.a_tiled ? (int64_t)KS * 4 : (int64_t)(KS / 8);
 
   // column-loc bytes of the B rows a stage gathers: read from LDS one stage ahead of the
   // DMA that needs them, so the issue path never waits on LDS
@@ -205,8 +217,8 @@ k_spmm_wide(WideArgs a) {
         const uint32_t v = GATHER ? boff[j] + (uint32_t)gcl[j] * (uint32_t)ldb2 : boff[j];
         dma_s<16>(bs, v, sb + (uint32_t)((wave * nB + j) * 1024));
       }
-      const uint8_t* vs = vals + row0 * Kc + s * KS;
-      const uint8_t* ms = meta + row0 * mrow + s * (KS / 8);
+      const uint8_t* vs = vals + row0 * Kc + s * a_stage;
+      const uint8_t* ms = meta + row0 * mrow + s * m_stage;
 #pragma unroll
       for (int j = 0; j < nA; ++j) {
         dma_s<16>(vs, aoff[j], sb + (uint32_t)(Cfg::kAOff + (wave * nA + j) * 1024));
@@ -235,12 +247,14 @@ k_spmm_wide(WideArgs a) {
         r = r < a.R ? r : a.R - 1;
         int64_t p = s * KS + wide::a_dma_chunk<KS>(bi, lane) * 16;   // first position of the chunk
         p = p < Kc ? p : Kc - 16;
-        dma_v<16>(vals + r * Kc + p, sb + (uint32_t)(Cfg::kAOff + bi * 1024));
+        const int64_t va = a.a_tiled ? (r >> 5) * 32 * Kc + (p >> 4) * 512 + (r & 31) * 16 : r * Kc + p;
+        dma_v<16>(vals + va, sb + (uint32_t)(Cfg::kAOff + bi * 1024));
         int64_t rm = row0 + wide::m_dma_row<KS>(bi, lane);
         rm = rm < a.R ? rm : a.R - 1;
         int64_t wd = s * (KS / 16) + wide::m_dma_word<KS>(lane);   // index word of the row
         wd = wd < Kc / 16 ? wd : Kc / 16 - 1;
-        dma_v<2>(meta + rm * mrow + wd * 2, sb + (uint32_t)(Cfg::kMOff + bi * 256));
+        const int64_t ma = a.a_tiled ? (rm >> 5) * 32 * mrow + wd * 64 + (rm & 31) * 2 : rm * mrow + wd * 2;
+        dma_v<2>(meta + ma, sb + (uint32_t)(Cfg::kMOff + bi * 256));
       }
     }
   };
@@ -528,8 +542,10 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
                             int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb,
                             void* Y, int64_t ldy, int64_t batch, int64_t stride_values,
                             int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
-                            hipStream_t stream) {
+                            hipStream_t stream, bool a_tiled) {
+  if (a_tiled && (V <= 0 || V % 32 != 0 || batch > 1)) return hipErrorInvalidValue;
   WideArgs a{};
+  a.a_tiled = a_tiled ? 1 : 0;
   a.values = (const uint16_t*)values;
   a.meta = (const uint8_t*)meta;
   a.B = (const uint16_t*)B;

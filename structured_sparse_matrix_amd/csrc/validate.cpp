@@ -93,6 +93,32 @@ int check_spmm_vnm(const void* values, const void* midx, const void* colloc, int
   return SNM_OK;
 }
 
+int check_prune_encode_vnm_tiled(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
+                                 const void* values_t, const void* midx_t, const void* colloc) {
+  int s = check_vnm_sizes(R, K, V, M);
+  if (s != SNM_OK) return s;
+  if (V % 32 != 0) return SNM_E_UNSUPPORTED;   // whole groups of 32 rows
+  return check_prune_encode_vnm(A, R, K, lda, V, M, values_t, midx_t, colloc);
+}
+
+int check_spmm_vnm_tiled(const void* values_t, const void* midx_t, const void* colloc, int64_t R,
+                         int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb,
+                         const void* Y, int64_t ldy) {
+  int s = check_vnm_sizes(R, K, V, M);
+  if (s != SNM_OK) return s;
+  if (V % 32 != 0) return SNM_E_UNSUPPORTED;
+  if ((s = check_spmm_vnm(values_t, midx_t, colloc, R, K, V, M, B, C, ldb, Y, ldy)) != SNM_OK) return s;
+  if (R == 0 || C == 0) return SNM_OK;
+  // the wide-tile kernel: 16-byte B rows, column-loc of a V-block staged in LDS, 32-bit
+  // per-lane copy offsets (one tile's A rows, one stage's gathered B rows)
+  const int64_t Kc = 4 * (K / M);
+  if (C % 8 != 0 || ldb % 8 != 0 || Kc > 16384) return SNM_E_UNSUPPORTED;
+  constexpr int64_t kLim = (int64_t)1 << 31;
+  if (128 * Kc >= kLim || (32 * (int64_t)M * ldb + C) * 2 >= kLim) return SNM_E_UNSUPPORTED;
+  if (K > 0 && !aligned16(B)) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
 int check_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq, int64_t Lk,
                          int64_t d, const void* values, const void* meta, const void* S_dense) {
   if (d != 16 && d != 32 && d != 64 && d != 128) return SNM_E_UNSUPPORTED;

@@ -17,6 +17,11 @@ int check_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, co
                   int64_t stride_values, int64_t stride_meta, int64_t stride_B, int64_t stride_Y);
 int check_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R, int64_t K,
                    int V, int M, const void* B, int64_t C, int64_t ldb, const void* Y, int64_t ldy);
+int check_prune_encode_vnm_tiled(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
+                                 const void* values_t, const void* midx_t, const void* colloc);
+int check_spmm_vnm_tiled(const void* values_t, const void* midx_t, const void* colloc, int64_t R,
+                         int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb,
+                         const void* Y, int64_t ldy);
 int check_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq, int64_t Lk,
                          int64_t d, const void* values, const void* meta, const void* S_dense);
 int check_sddmm_prune_nm_rowmax(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,

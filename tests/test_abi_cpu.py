@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
               "snm_spmm_nm_softmax", "snm_bitmap_sizes", "snm_bitmap_count", "snm_bitmap_encode",
               "snm_spmm_bitmap", "snm_sddmm_prune_nm_bf16", "snm_softmax_nm_rows_bf16",
               "snm_spmm_nm_bf16", "snm_spmm_nm_softmax_bf16", "snm_sddmm_prune_1of2_f32",
-              "snm_softmax_nm_rows_f32", "snm_spmm_1of2_f32"):
+              "snm_softmax_nm_rows_f32", "snm_spmm_1of2_f32", "snm_prune_encode_vnm_tiled",
+              "snm_spmm_vnm_tiled"):
         assert n in names
 
 
@@ -130,6 +131,29 @@ def test_spmm_nm_validation(args, status):
 ])
 def test_spmm_vnm_validation(args, status):
     assert _lib().snm_spmm_vnm(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 128, 64, 64, 16, 8, FAKE, FAKE, FAKE, P(0)), 4),     # V % 32
+    ((FAKE, 128, 48, 48, 64, 8, FAKE, FAKE, FAKE, P(0)), 2),     # (K/M) % 4
+    ((FAKE, 128, 64, 64, 64, 8, FAKE, P(0), FAKE, P(0)), 1),     # midx NULL
+    ((FAKE, 128, 64, 60, 64, 8, FAKE, FAKE, FAKE, P(0)), 2),     # lda < K
+])
+def test_prune_encode_vnm_tiled_validation(args, status):
+    assert _lib().snm_prune_encode_vnm_tiled(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, FAKE, 64, 64, 16, 8, FAKE, 64, 64, FAKE, 64, P(0)), 4),         # V % 32
+    ((FAKE, FAKE, FAKE, 64, 64, 64, 8, FAKE, 60, 64, FAKE, 64, P(0)), 4),         # C % 8
+    ((FAKE, FAKE, FAKE, 64, 64, 64, 8, FAKE, 64, 68, FAKE, 64, P(0)), 4),         # ldb % 8
+    ((FAKE, FAKE, FAKE, 64, 64, 64, 8, P(0x1008), 64, 64, FAKE, 64, P(0)), 3),    # B not 16-byte aligned
+    ((FAKE, FAKE, FAKE, 64, 8 * 4100 * 4, 64, 8, FAKE, 64, 64, FAKE, 64, P(0)), 4),  # 4K/M > 16384
+    ((FAKE, FAKE, P(0), 64, 64, 64, 8, FAKE, 64, 64, FAKE, 64, P(0)), 1),         # colloc NULL
+    ((P(0), P(0), P(0), 64, 64, 64, 8, P(0), 0, 0, P(0), 0, P(0)), 0),            # C == 0: ok
+])
+def test_spmm_vnm_tiled_validation(args, status):
+    assert _lib().snm_spmm_vnm_tiled(*args) == status
 
 
 @pytest.mark.parametrize("args,status", [
