@@ -1,8 +1,11 @@
 """Summaries of rocprofv3 output for the profiles/ folder.
 
   python -m structured_sparse_matrix_amd.profiling kernels TRACE_CSV [--match snm] [--skip N]
+         [--groups G]
       Markdown table of kernel dispatch durations (calls, mean, median, min, max) from a
-      `rocprofv3 --kernel-trace -f csv` run.
+      `rocprofv3 --kernel-trace -f csv` run. --groups G splits each kernel's dispatches, in
+      dispatch order, into G equal consecutive groups reported as separate rows (a program
+      that times the same kernel on G inputs one after the other).
 
   python -m structured_sparse_matrix_amd.profiling traffic --fetch FETCH_CSV --write WRITE_CSV
          --match NAME --calibration-bytes N [--command CMD]
@@ -44,12 +47,16 @@ def _durations(path, match, skip):
     return {k: v[skip:] if len(v) > skip else v for k, v in by.items()}
 
 
-def kernels_table(path, match, skip):
+def kernels_table(path, match, skip, groups=1):
     rows = ["| kernel | calls | mean us | median us | min us | max us |", "|---|---|---|---|---|---|"]
     for name, ds in sorted(_durations(path, match, skip).items(), key=lambda kv: -sum(kv[1])):
         short = name if len(name) < 110 else name[:107] + "..."
-        rows.append(f"| `{short}` | {len(ds)} | {statistics.mean(ds) / 1e3:.2f} | "
-                    f"{statistics.median(ds) / 1e3:.2f} | {min(ds) / 1e3:.2f} | {max(ds) / 1e3:.2f} |")
+        n = len(ds) // groups if groups > 1 and len(ds) % groups == 0 else len(ds)
+        parts = [ds[i:i + n] for i in range(0, len(ds), n)]
+        for g, part in enumerate(parts):
+            label = f"`{short}`" + (f" ({g + 1} of {len(parts)})" if len(parts) > 1 else "")
+            rows.append(f"| {label} | {len(part)} | {statistics.mean(part) / 1e3:.2f} | "
+                        f"{statistics.median(part) / 1e3:.2f} | {min(part) / 1e3:.2f} | {max(part) / 1e3:.2f} |")
     return "\n".join(rows)
 
 
@@ -93,6 +100,7 @@ def main(argv=None):
     k.add_argument("trace")
     k.add_argument("--match", default="")
     k.add_argument("--skip", type=int, default=0)
+    k.add_argument("--groups", type=int, default=1)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -101,7 +109,7 @@ def main(argv=None):
     t.add_argument("--command", default="")
     a = ap.parse_args(argv)
     if a.cmd == "kernels":
-        print(kernels_table(a.trace, a.match, a.skip))
+        print(kernels_table(a.trace, a.match, a.skip, a.groups))
     else:
         out = traffic(a.fetch, a.write, a.match, a.calibration_bytes)
         out["kernel_source_hash"] = kernel_source_hash()
