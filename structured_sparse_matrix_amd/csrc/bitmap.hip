@@ -176,15 +176,6 @@ __device__ __forceinline__ f4 mfma16x16x32(const h8& a, const h8& b, const f4& c
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// 4-byte global -> LDS DMA: lane l writes LDS bytes [lds_byte + 4 l, + 4) (lds_byte is
-// wave-uniform, through M0); completion is tracked with s_waitcnt vmcnt by the caller.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"   // m0 is set inside the statement
-__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds_byte) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_byte);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "m0");
-}
-#pragma clang diagnostic pop
 
 template <int I>
 using cint = std::integral_constant<int, I>;
@@ -255,28 +246,32 @@ k_spmm_bitmap(BitmapArgs a) {
   const uint32_t wl_lds = lds_addr(wl);
   constexpr int kMetaBase = 2 * kValBuf;
 
+  // Copy sources are the arrays themselves (wave-uniform bases) plus 32-bit lane byte
+  // offsets: R K < 2^31, so every offset into the three arrays fits. The lane parts that do
+  // not depend on the phase are computed once here.
+  const uint32_t T32 = (uint32_t)T, RT32 = (uint32_t)RT;
+  const int64_t rbm = row0 + (lane >> 2) < a.R ? row0 + (lane >> 2) : a.R - 1;
+  const uint32_t bm_lane = (uint32_t)(rbm * T) * 8u + (uint32_t)(lane & 1) * 4u;
+  const uint32_t bm_t = (uint32_t)((lane >> 1) & 1);
+  const int orr = lane < 48 ? lane / 3 : 0;
+  const int64_t rof = row0 + orr < a.R ? row0 + orr : a.R - 1;
+  const uint32_t of_lane = (uint32_t)(rof * T) + (uint32_t)(lane < 48 ? lane - 3 * orr : 0);
+  // a matrix without non-zeros has no values to copy (and its values pointer may be NULL);
+  // otherwise the first 16 bytes of values are a readable target for idle lanes
+  const bool any_values = a.offsets[RT] != 0u;
+
   // (1) metadata of phase p into metadata buffer mb: lane l copies bitmap word l % 2 of
   // tile (l / 2) % 2 of row l / 4, and (l < 48) offset entry l % 3 of row l / 3; rows past
   // R repeat row R - 1, tiles past the row's end repeat its last tile
   auto issue_meta = [&](int64_t p, int mb) {
-    const int64_t kt0 = tbeg + p * kPT;
+    const uint32_t kt0 = (uint32_t)(tbeg + p * kPT);
     const uint32_t base = wl_lds + (uint32_t)(kMetaBase + mb * kMetaBuf);
-    {
-      int64_t r = row0 + (lane >> 2);
-      r = r < a.R ? r : a.R - 1;
-      int64_t t = kt0 + ((lane >> 1) & 1);
-      t = t < T ? t : T - 1;
-      lds_dma4(reinterpret_cast<const uint32_t*>(a.bitmaps + r * T + t) + (lane & 1), base);
-    }
-    {
-      const int rr = lane < 48 ? lane / 3 : 0;
-      const int j = lane < 48 ? lane - 3 * rr : 0;
-      int64_t r = row0 + rr;
-      r = r < a.R ? r : a.R - 1;
-      int64_t idx = r * T + kt0 + j;
-      idx = idx < RT ? idx : RT;
-      lds_dma4(a.offsets + idx, base + (uint32_t)kMetaOffs);   // lanes >= 48 land in the pad
-    }
+    uint32_t t = kt0 + bm_t;
+    t = t < T32 ? t : T32 - 1;
+    dma_s<4>(a.bitmaps, bm_lane + 8u * t, base);
+    uint32_t idx = of_lane + kt0;
+    idx = idx < RT32 ? idx : RT32;
+    dma_s<4>(a.offsets, 4u * idx, base + (uint32_t)kMetaOffs);   // lanes >= 48 land in the pad
   };
   // (2) values of phase p (its metadata in buffer mb) into value buffer vb: DMA b fills rows
   // 4b .. 4b + 3, lane l the 16-byte slot l % 16 of row r = 4b + l / 16, which holds the
@@ -284,6 +279,7 @@ k_spmm_bitmap(BitmapArgs a) {
   // rows 256 bytes apart start on the same bank, and the expansion's reads -- the same
   // ranks in 16 rows -- would collide 16 ways.
   auto issue_values = [&](int64_t p, int mb, int vb) {
+    if (!any_values) return;
     const int64_t kt0 = tbeg + p * kPT;
     const int nt = (int)(tend - kt0 < kPT ? tend - kt0 : kPT);
     const uint8_t* offs = wl + kMetaBase + mb * kMetaBuf + kMetaOffs;
@@ -294,8 +290,7 @@ k_spmm_bitmap(BitmapArgs a) {
       const uint32_t s0 = *reinterpret_cast<const uint32_t*>(offs + 12 * r);
       const uint32_t s1 = *reinterpret_cast<const uint32_t*>(offs + 12 * r + 4 * nt);
       const bool live = row0 + r < a.R && 8u * ch < s1 - s0;
-      const void* src = live ? static_cast<const void*>(a.values + s0 + 8u * ch) : static_cast<const void*>(a.B);
-      lds_dma16(src, wl_lds + (uint32_t)(vb * kValBuf + b * 1024));
+      dma_s<16>(a.values, live ? 2u * (s0 + 8u * ch) : 0u, wl_lds + (uint32_t)(vb * kValBuf + b * 1024));
     }
   };
   // B operands of phase p. With one column tile and column-major B (16 contiguous bytes per
@@ -305,6 +300,14 @@ k_spmm_bitmap(BitmapArgs a) {
   constexpr bool kAheadB = BCOL && CT == 1;
   constexpr int NB = kAheadB ? 2 : 1;
   h8 bop[NB][kPT][2][CT];
+  // column-major B: each lane's first operand of the wave's first tile; a phase, a tile and a
+  // 32-position block are then uniform or constant steps from it
+  const uint16_t* bcol_base[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int64_t col = 16 * ct + li < a.C ? 16 * ct + li : a.C - 1;
+    bcol_base[ct] = a.B + col * a.ldb + tbeg * kTile + 8 * q;
+  }
   auto load_b = [&](int64_t p, auto par_c) {
     constexpr int P = decltype(par_c)::value;
     const int64_t kt0 = tbeg + p * kPT;
@@ -320,7 +323,7 @@ k_spmm_bitmap(BitmapArgs a) {
           const int64_t col = 16 * ct + li;
           if (t < nt && col < a.C) {
             if constexpr (BCOL) {
-              bv = *reinterpret_cast<const h8*>(a.B + col * a.ldb + k);
+              bv = *reinterpret_cast<const h8*>(bcol_base[ct] + p * (kPT * kTile) + t * kTile + 32 * blk);
             } else {
               // the tile's rows from a uniform base with 32-bit lane offsets (B's row
               // stride is below 2^25 elements): one address register per load

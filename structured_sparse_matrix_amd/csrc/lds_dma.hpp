@@ -18,8 +18,8 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Global -> LDS DMA of 16 bytes (or 2 bytes, zero-extended to a dword) per lane: lane l
-// writes LDS bytes [lds_byte + 16 l, +16) (or [lds_byte + 4 l, +4)); lds_byte is
+// Global -> LDS DMA of 16 bytes (or 4 bytes, or 2 bytes zero-extended to a dword) per lane:
+// lane l writes LDS bytes [lds_byte + 16 l, +16) (or [lds_byte + 4 l, +4)); lds_byte is
 // wave-uniform and goes through M0. dma_s addresses a wave-uniform base (SGPR pair) plus a
 // per-lane 32-bit byte offset, dma_v a per-lane 64-bit address. Issued from inline assembly
 // on purpose: the compiler's waitcnt pass would otherwise make every later LDS read it
@@ -42,6 +42,8 @@ __device__ __forceinline__ void dma_s(const void* sbase_in, uint32_t voff, uint3
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_byte);
   if constexpr (SIZE == 16)
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0) : "m0");
+  else if constexpr (SIZE == 4)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0) : "m0");
   else
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff), "s"(sbase), "s"(m0) : "m0");
 }
