@@ -189,45 +189,57 @@ using cint = std::integral_constant<int, I>;
 //       the wave's two metadata buffers (issued two phases ahead);
 //   (2) its packed values -- for each row the contiguous, 16-byte aligned span of its
 //       tiles' values -- are copied by DMA into one of two value buffers, row i at
-//       [256 i, 256 i + 256), with source addresses computed from (1) (one phase ahead),
+//       [272 i, 272 i + 256), with source addresses computed from (1) (one phase ahead),
 //       and its B operands are loaded (one phase ahead);
 //   (3) each chunk is expanded through its bitmap byte -- the e-th set bit takes the next
 //       value of the span -- and multiplied on the matrix core.
 // Each phase starts with one wait for everything issued during the previous phase, so the
-// latencies of (1) and (2) run under the expansion and products of the phase before. Lanes
-// with nothing to copy point their DMA at a readable dummy (B) and land in their own row's
-// region past its span, which the expansion never uses.
+// latencies of (1) and (2) run under the expansion and products of the phase before.
+// The 16-byte pad after each staged row puts row i on banks 4i.. onwards: the expansion
+// reads the same ranks in all 16 rows at once, which rows 256 bytes apart would send to one
+// bank. Lanes with nothing to copy point their DMA at the first 16 bytes of the values (or
+// are masked off past the last row) and land in their row's pad or past its span, which the
+// expansion never uses.
 constexpr int kBmWaves = 8;
 constexpr int kPT = 2;                                   // tiles per phase
-constexpr int kRowBytes = kPT * kTile * 2;               // staged values of a row per phase
-constexpr int kValBuf = 16 * kRowBytes;                  // one phase's values (4 KiB)
-constexpr int kMetaBuf = 512;                            // bitmaps 16 x 16 B, offsets 16 x 12 B
+constexpr int kRowPitch = kPT * kTile * 2 + 16;          // a row's staged values + pad: 17 slots
+constexpr int kSlots = 16 * (kRowPitch / 16);            // 16-byte slots of a value buffer (272)
+constexpr int kValBuf = 16 * kRowPitch;                  // one phase's values (4352 bytes)
+constexpr int kMetaBuf = 448;                            // bitmaps 16 x 16 B, offsets 16 x 12 B
 constexpr int kMetaOffs = 256;                           // offsets within a metadata buffer
-constexpr int kWaveBytes = 2 * kValBuf + 2 * kMetaBuf;   // two phases in flight
-constexpr int kLutOff = kBmWaves * kWaveBytes + 16;      // + a pad that over-reads may touch
-constexpr int kLutBytes = 256 * 16 + 256 * 8;
-constexpr int kBitmapLds = kLutOff + kLutBytes;
+constexpr int kValBase = 2 * kMetaBuf;                   // metadata first: a pair read one value
+                                                         // before a row stays inside the region
+constexpr int kWaveBytes = kValBase + 2 * kValBuf;       // two phases in flight (9600 bytes)
+constexpr int kLutOff = kBmWaves * kWaveBytes;
+constexpr int kLutBytes = 256 * 8 + 16 * 8;              // ranks per byte, keep masks per nibble
+constexpr int kBitmapLds = kLutOff + kLutBytes;          // 77 KiB: two workgroups per CU
+// two workgroups of exactly 80 KiB (the CU's whole 160 KiB) measured at one per CU
+static_assert(kBitmapLds <= 78 * 1024, "two workgroups per CU");
 
 template <int CT, bool BCOL>
-__global__ void __launch_bounds__(64 * kBmWaves) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ void __launch_bounds__(64 * kBmWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
 k_spmm_bitmap(BitmapArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];   // per wave 9 KiB, then the expansion table
-  // Expansion table, one entry per bitmap byte m: four dwords of 16-bit keep masks (0xFFFF
-  // where bit e of m is set) and two dwords of eight byte offsets (2 rank_e, rank_e = set
-  // bits of m below e). Expanding a chunk is then one address add and one read per
-  // position, and one AND per pair of positions.
+  extern __shared__ __align__(16) uint8_t smem[];   // per wave 9600 bytes, then the table
+  // Expansion tables: per bitmap byte m, eight byte offsets 2 rank_e (rank_e = set bits of
+  // m below e); per bitmap nibble, two dwords of 16-bit keep masks (0xFFFF where the bit is
+  // set). Expanding a chunk is then one add and one 2-byte read per position and one AND
+  // per pair of positions. (4-byte reads of value pairs would halve the reads, but at
+  // 2-byte alignment they stall the LDS: measured twice as slow.)
   for (int m = threadIdx.x; m < 256; m += 64 * kBmWaves) {
-    uint32_t mk[4], rk[2] = {0u, 0u}, r = 0;
+    uint32_t rk[2] = {0u, 0u}, r = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       rk[e >> 2] |= (2u * r) << (8 * (e & 3));
       r += (m >> e) & 1;
     }
+    *reinterpret_cast<u2*>(smem + kLutOff + 8 * m) = u2{rk[0], rk[1]};
+    if (m < 16) {
+      uint32_t mk[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      mk[i] = (((m >> (2 * i)) & 1) ? 0xFFFFu : 0u) | (((m >> (2 * i + 1)) & 1) ? 0xFFFF0000u : 0u);
-    *reinterpret_cast<u4*>(smem + kLutOff + 16 * m) = u4{mk[0], mk[1], mk[2], mk[3]};
-    *reinterpret_cast<u2*>(smem + kLutOff + 4096 + 8 * m) = u2{rk[0], rk[1]};
+      for (int i = 0; i < 2; ++i)
+        mk[i] = (((m >> (2 * i)) & 1) ? 0xFFFFu : 0u) | (((m >> (2 * i + 1)) & 1) ? 0xFFFF0000u : 0u);
+      *reinterpret_cast<u2*>(smem + kLutOff + 2048 + 8 * m) = u2{mk[0], mk[1]};
+    }
   }
   __syncthreads();
   const int tid = threadIdx.x;
@@ -244,7 +256,7 @@ k_spmm_bitmap(BitmapArgs a) {
   const int64_t nph = tend > tbeg ? (tend - tbeg + kPT - 1) / kPT : 0;
   uint8_t* const wl = smem + w * kWaveBytes;
   const uint32_t wl_lds = lds_addr(wl);
-  constexpr int kMetaBase = 2 * kValBuf;
+  constexpr int kMetaBase = 0;
 
   // Copy sources are the arrays themselves (wave-uniform bases) plus 32-bit lane byte
   // offsets: R K < 2^31, so every offset into the three arrays fits. The lane parts that do
@@ -271,26 +283,27 @@ k_spmm_bitmap(BitmapArgs a) {
     dma_s<4>(a.bitmaps, bm_lane + 8u * t, base);
     uint32_t idx = of_lane + kt0;
     idx = idx < RT32 ? idx : RT32;
-    dma_s<4>(a.offsets, 4u * idx, base + (uint32_t)kMetaOffs);   // lanes >= 48 land in the pad
+    if (lane < 48) dma_s<4>(a.offsets, 4u * idx, base + (uint32_t)kMetaOffs);
   };
-  // (2) values of phase p (its metadata in buffer mb) into value buffer vb: DMA b fills rows
-  // 4b .. 4b + 3, lane l the 16-byte slot l % 16 of row r = 4b + l / 16, which holds the
-  // row's chunk (l % 16) ^ r. The swizzle spreads the rows over the LDS banks: unswizzled,
-  // rows 256 bytes apart start on the same bank, and the expansion's reads -- the same
-  // ranks in 16 rows -- would collide 16 ways.
+  // (2) values of phase p (its metadata in buffer mb) into value buffer vb: DMA b fills the
+  // 16-byte slots 64 b .. 64 b + 63 of the buffer, slot = 17 r + c being chunk c of row r
+  // (c = 16: the row's pad); the last DMA covers slots 256 .. 271 with lanes 0 .. 15
   auto issue_values = [&](int64_t p, int mb, int vb) {
     if (!any_values) return;
     const int64_t kt0 = tbeg + p * kPT;
     const int nt = (int)(tend - kt0 < kPT ? tend - kt0 : kPT);
     const uint8_t* offs = wl + kMetaBase + mb * kMetaBuf + kMetaOffs;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int r = 4 * b + (lane >> 4);
-      const uint32_t ch = (uint32_t)((lane & 15) ^ r);
-      const uint32_t s0 = *reinterpret_cast<const uint32_t*>(offs + 12 * r);
-      const uint32_t s1 = *reinterpret_cast<const uint32_t*>(offs + 12 * r + 4 * nt);
-      const bool live = row0 + r < a.R && 8u * ch < s1 - s0;
-      dma_s<16>(a.values, live ? 2u * (s0 + 8u * ch) : 0u, wl_lds + (uint32_t)(vb * kValBuf + b * 1024));
+    for (int b = 0; b < (kSlots + 63) / 64; ++b) {
+      const int slot = 64 * b + lane;
+      const int r = slot / 17;
+      const uint32_t ch = (uint32_t)(slot - 17 * r);
+      const int rc = r < 16 ? r : 15;
+      const uint32_t s0 = *reinterpret_cast<const uint32_t*>(offs + 12 * rc);
+      const uint32_t s1 = *reinterpret_cast<const uint32_t*>(offs + 12 * rc + 4 * nt);
+      const bool live = r < 16 && row0 + r < a.R && 8u * ch < s1 - s0;   // ch = 16 is never live
+      const uint32_t dst = wl_lds + (uint32_t)(kValBase + vb * kValBuf + b * 1024);
+      if (64 * b + 64 <= kSlots || slot < kSlots) dma_s<16>(a.values, live ? 2u * (s0 + 8u * ch) : 0u, dst);
     }
   };
   // B operands of phase p. With one column tile and column-major B (16 contiguous bytes per
@@ -305,6 +318,7 @@ k_spmm_bitmap(BitmapArgs a) {
   const uint16_t* bcol_base[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
+    // columns past C are clamped to C - 1: they feed only output columns that are not stored
     const int64_t col = 16 * ct + li < a.C ? 16 * ct + li : a.C - 1;
     bcol_base[ct] = a.B + col * a.ldb + tbeg * kTile + 8 * q;
   }
@@ -319,9 +333,8 @@ k_spmm_bitmap(BitmapArgs a) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           h8 bv = {};
-          const int64_t k = (kt0 + t) * kTile + 32 * blk + 8 * q;
-          const int64_t col = 16 * ct + li;
-          if (t < nt && col < a.C) {
+          const int64_t col = 16 * ct + li < a.C ? 16 * ct + li : a.C - 1;
+          if (t < nt) {   // uniform: every lane loads (past C from column C - 1)
             if constexpr (BCOL) {
               bv = *reinterpret_cast<const h8*>(bcol_base[ct] + p * (kPT * kTile) + t * kTile + 32 * blk);
             } else {
@@ -376,8 +389,7 @@ k_spmm_bitmap(BitmapArgs a) {
     // (3) expand and multiply
     const int64_t kt0 = tbeg + p * kPT;
     const int nt = (int)(tend - kt0 < kPT ? tend - kt0 : kPT);
-    const uint32_t rbase = (uint32_t)(P * kValBuf + kRowBytes * li);
-    const uint32_t swz = (uint32_t)li << 4;   // byte b of the row's span sits at rbase + (b ^ swz)
+    const uint8_t* rowp = wl + kValBase + P * kValBuf + kRowPitch * li;   // staged row li
     const uint32_t span0 = off[0];
 #pragma unroll
     for (int t = 0; t < kPT; ++t) {
@@ -386,21 +398,21 @@ k_spmm_bitmap(BitmapArgs a) {
       for (int blk = 0; blk < 2; ++blk) {
         const int byte = 4 * blk + q;
         const uint64_t below = byte == 0 ? 0ull : (bm[t] & ((1ull << (8 * byte)) - 1ull));
-        // span byte of the chunk's first value; a position past the last set bit reads at
-        // most one value beyond the row's span (byte 256 at most: inside the wave region)
-        const uint32_t a0 = 2u * ((off[t] - span0) + (uint32_t)__popcll(below));
+        // the chunk's first value in the staged row; a position past the last set bit reads
+        // at most one value beyond the row's span (byte 256: the row's pad)
+        const uint8_t* cb = rowp + 2u * ((off[t] - span0) + (uint32_t)__popcll(below));
         const uint32_t m = (uint32_t)(bm[t] >> (8 * byte)) & 0xFFu;
-        const u4 keep = *reinterpret_cast<const u4*>(smem + kLutOff + 16u * m);
-        const u2 rk = *reinterpret_cast<const u2*>(smem + kLutOff + 4096u + 8u * m);
+        const u2 klo = *reinterpret_cast<const u2*>(smem + kLutOff + 2048u + 8u * (m & 15u));
+        const u2 khi = *reinterpret_cast<const u2*>(smem + kLutOff + 2048u + 8u * (m >> 4));
+        const u4 keep = {klo[0], klo[1], khi[0], khi[1]};
+        const u2 rk = *reinterpret_cast<const u2*>(smem + kLutOff + 8u * m);
         u4 pk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t rw = rk[i >> 1];
           const int sh = 16 * (i & 1);
-          const uint32_t blo = (a0 + ((rw >> sh) & 0xFFu)) ^ swz;
-          const uint32_t bhi = (a0 + ((rw >> (sh + 8)) & 0xFFu)) ^ swz;
-          const uint32_t lo = *reinterpret_cast<const uint16_t*>(wl + rbase + blo);
-          const uint32_t hi = *reinterpret_cast<const uint16_t*>(wl + rbase + bhi);
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(cb + ((rw >> sh) & 0xFFu));
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(cb + ((rw >> (sh + 8)) & 0xFFu));
           pk[i] = (lo | (hi << 16)) & keep[i];
         }
         const h8 av = __builtin_bit_cast(h8, pk);
@@ -487,7 +499,7 @@ hipError_t launch_spmm_bitmap(const uint64_t* bitmaps, const uint32_t* offsets, 
   a.R = R; a.K = K; a.C = C; a.ldb = ldb; a.ldy = ldy;
   a.b_col = b_layout == 1;
   const unsigned g = (unsigned)((R + 15) / 16);
-  const size_t lds = (size_t)kBitmapLds;   // 78 KiB: two workgroups per CU
+  const size_t lds = (size_t)kBitmapLds;   // 77 KiB: two workgroups per CU
   const dim3 blk(64 * kBmWaves);
   auto go = [&](auto kern) -> hipError_t {
     static bool set[2][2] = {};
