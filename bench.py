@@ -97,7 +97,7 @@ def cpu_baseline(min_seconds: float = 10.0) -> dict:
 
 
 def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_copy: bool,
-            nstreams: int = 2):
+            nstreams: int = 2, submit: str = "eager"):
     import torch
     import structured_sparse_matrix_amd as snm
     import workloads
@@ -149,33 +149,38 @@ def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_c
         check(name, fn(*args))
         return lambda: fn(*args)
 
-    enc_calls, mm_calls = [], []
-    for j in range(NROT):
-        stream = streams[j % nstreams].cuda_stream
-        if a_layout == "tiled":
-            enc_calls.append(bind("snm_prune_encode_nm_tiled", As[j].data_ptr(), R, K, K,
-                                  vals[j].data_ptr(), metas[j].data_ptr(), stream))
-        else:
-            enc_calls.append(bind("snm_prune_encode_nm", As[j].data_ptr(), R, K, K,
-                                  vals[j].data_ptr(), metas[j].data_ptr(), stream))
-        row = []
-        for t in range(len(NS)):
-            B, Y = Bsel[j][t], Ys[j][t]
-            lay = 1 if b_layout == "col" else 0
-            ldb = B.stride(1) if lay == 1 else B.stride(0)
+    def bind_steps(strms):
+        """The step's calls for every rotating copy j, bound to stream j % nstreams of strms."""
+        enc_calls, mm_calls = [], []
+        for j in range(NROT):
+            stream = strms[j % nstreams].cuda_stream
             if a_layout == "tiled":
-                row.append(bind("snm_spmm_nm_tiled", vals[j].data_ptr(), metas[j].data_ptr(), R, K,
-                                B.data_ptr(), NS[t], ldb, lay, Y.data_ptr(), NS[t], stream))
+                enc_calls.append(bind("snm_prune_encode_nm_tiled", As[j].data_ptr(), R, K, K,
+                                      vals[j].data_ptr(), metas[j].data_ptr(), stream))
             else:
-                row.append(bind("snm_spmm_nm", vals[j].data_ptr(), metas[j].data_ptr(), R, K,
-                                B.data_ptr(), NS[t], ldb, lay, Y.data_ptr(), NS[t], 1, 0, 0, 0, 0, stream))
-        mm_calls.append(row)
+                enc_calls.append(bind("snm_prune_encode_nm", As[j].data_ptr(), R, K, K,
+                                      vals[j].data_ptr(), metas[j].data_ptr(), stream))
+            row = []
+            for t in range(len(NS)):
+                B, Y = Bsel[j][t], Ys[j][t]
+                lay = 1 if b_layout == "col" else 0
+                ldb = B.stride(1) if lay == 1 else B.stride(0)
+                if a_layout == "tiled":
+                    row.append(bind("snm_spmm_nm_tiled", vals[j].data_ptr(), metas[j].data_ptr(), R, K,
+                                    B.data_ptr(), NS[t], ldb, lay, Y.data_ptr(), NS[t], stream))
+                else:
+                    row.append(bind("snm_spmm_nm", vals[j].data_ptr(), metas[j].data_ptr(), R, K,
+                                    B.data_ptr(), NS[t], ldb, lay, Y.data_ptr(), NS[t], 1, 0, 0, 0, 0, stream))
+            mm_calls.append(row)
 
-    def step(i):
-        j = i % NROT
-        enc_calls[j]()
-        for t in range(len(NS)):
-            mm_calls[j][t]()
+        def step(i):
+            j = i % NROT
+            enc_calls[j]()
+            for t in range(len(NS)):
+                mm_calls[j][t]()
+        return enc_calls, mm_calls, step
+
+    enc_calls, mm_calls, step = bind_steps(streams)
 
     def timed_steps():
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -213,12 +218,43 @@ def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_c
             mm_calls[j][t]()
         return launch
 
+    def timed_graph():
+        """The K steps captured once into a HIP graph (the same streams, fork and join) and
+        replayed: the timed region then holds no host launch cost, which otherwise (four
+        launches of a few microseconds each per step of about 30 us) can leave the GPU
+        waiting on a slow host. The graph holds only our kernels and stream waits."""
+        cap = torch.cuda.Stream()
+        gstreams = [cap] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
+        _, _, gstep = bind_steps(gstreams)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for st in gstreams[1:]:
+                st.wait_stream(cap)
+            for i in range(steps):
+                gstep(warmup + i)
+            for st in gstreams[1:]:
+                cap.wait_stream(st)
+        g.replay()   # untimed first replay
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(main_stream)
+        g.replay()
+        stop.record(main_stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop), time.perf_counter() - t0
+
     for i in range(warmup):
         step(i)
-    total_ms, wall = timed_steps()
+    eager_ms, eager_wall = timed_steps()
+    if submit == "graph":
+        total_ms, wall = timed_graph()
+    else:
+        total_ms, wall = eager_ms, eager_wall
     enc_ms = timed_kernel(encode)
     spmm_ms = [timed_kernel(spmm(t)) for t in range(len(NS))]
-    return total_ms, wall, enc_ms, spmm_ms
+    return total_ms, wall, enc_ms, spmm_ms, eager_ms
 
 
 def bench_other(workload: str, steps: int, warmup: int) -> dict:
@@ -614,6 +650,9 @@ def main():
                          "workload in bf16 with 2:4, in fp32 with 1:2)")
     ap.add_argument("--streams", type=int, default=2,
                     help="decode steps in flight (step i on stream i %% S); kernel timings use one")
+    ap.add_argument("--submit", choices=("eager", "graph"), default="eager",
+                    help="timed decode steps launched one by one from the host (default) or "
+                         "replayed from one captured HIP graph")
     ap.add_argument("--families", default="",
                     help="with --workload vnm_sweep: comma-separated subset of fig9,fig10,gpt3")
     args = ap.parse_args()
@@ -639,8 +678,9 @@ def main():
         return
     import numpy as np
 
-    total_ms, wall, enc_ms, spmm_ms = run_gpu(args.steps, args.warmup, args.b_layout, args.a_layout,
-                                              args.calibration_copy, args.streams)
+    total_ms, wall, enc_ms, spmm_ms, eager_ms = run_gpu(args.steps, args.warmup, args.b_layout,
+                                                        args.a_layout, args.calibration_copy,
+                                                        args.streams, args.submit)
     ms_per_step = total_ms / args.steps
     flops_step = sum(2 * R * K * n for n in NS)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
@@ -680,6 +720,8 @@ def main():
                                "32 rotating input copies",
                    "R": R, "K": K, "N": list(NS), "rotating_copies": NROT,
                    "streams": args.streams,
+                   "submission": "one HIP graph of the K steps" if args.submit == "graph"
+                                 else "eager launches",
                    "B_storage": "column-major (X[N][K])" if args.b_layout == "col" else "row-major (K x N)",
                    "A_storage": "operand-major (tiled)" if args.a_layout == "tiled" else "canonical"},
         "roofline": {"bound": "hbm", "kernel": spmm_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -688,6 +730,7 @@ def main():
                               "durations (HIP events around K back-to-back launches of each)"},
         "kernels": kernels,
         "wall_s_timed_region": wall,
+        "eager_ms_per_step": eager_ms / args.steps,   # equals ms_per_step unless --submit graph
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
