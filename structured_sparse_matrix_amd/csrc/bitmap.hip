@@ -96,8 +96,16 @@ __global__ void __launch_bounds__(1024) k_bitmap_scan_rows(uint32_t* __restrict_
   const int64_t per = (R + 1023) / 1024;
   const int64_t r0 = tid * per;
   const int64_t r1 = r0 + per < R ? r0 + per : R;
+  // row totals eight at a time, the eight loads independent (one round trip per batch)
+  constexpr int U = 8;
   uint32_t s = 0;
-  for (int64_t r = r0; r < r1; ++r) s += offsets[r * T];
+  for (int64_t r = r0; r < r1; r += U) {
+    uint32_t x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = r + u < r1 ? offsets[(r + u) * T] : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += x[u];
+  }
   part[tid] = s;
   __syncthreads();
   for (int d = 1; d < 1024; d <<= 1) {   // inclusive Hillis-Steele scan of the 1024 parts
@@ -107,10 +115,15 @@ __global__ void __launch_bounds__(1024) k_bitmap_scan_rows(uint32_t* __restrict_
     __syncthreads();
   }
   uint32_t base = tid > 0 ? part[tid - 1] : 0u;
-  for (int64_t r = r0; r < r1; ++r) {
-    const uint32_t x = offsets[r * T];
-    offsets[r * T] = base;
-    base += x;
+  for (int64_t r = r0; r < r1; r += U) {
+    uint32_t x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = r + u < r1 ? offsets[(r + u) * T] : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (r + u < r1) offsets[(r + u) * T] = base;
+      base += x[u];
+    }
   }
   if (tid == 1023) offsets[R * T] = part[1023];
 }
