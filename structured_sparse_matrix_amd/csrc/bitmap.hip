@@ -15,7 +15,7 @@
 //     tiles in phases of 2, software-pipelined: the tiles' bitmaps and offsets are copied
 //     into LDS (global->LDS DMA) two phases ahead, their packed values (16-byte aligned
 //     spans, because every tile starts at a multiple of 8 values) one phase ahead, into
-//     double-buffered per-wave regions whose 16-byte slots are XOR-swizzled by row so that
+//     double-buffered per-wave regions whose rows are padded to a 272-byte pitch so that
 //     the 16 rows' reads fall on different LDS banks. Each 8-position chunk is expanded
 //     through its bitmap byte with LDS reads at the computed ranks and fed to a dense
 //     MFMA. Partial sums of the waves are added through LDS.
