@@ -8,6 +8,7 @@
 // streaming stores measured slower, and keep ordinary stores.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "lds_dma.hpp"
 
 namespace snm {
 
@@ -245,7 +246,24 @@ k_prune_encode_vnm_lds(const uint16_t* __restrict__ A, int64_t R, int64_t K, int
   const uint16_t* Ablk = A + vb * V * lda + g0 * M;
 
   // ---- stage the tile
-  if ((((uintptr_t)Ablk) & 15) == 0 && (ncols & 7) == 0 && (lda & 7) == 0) {
+  if (ncols == pitch && (((uintptr_t)Ablk) & 15) == 0 && (lda & 7) == 0) {
+    // a full tile is dense in LDS (row pitch = row length): 16-byte chunk ci = row-major
+    // chunk index, so each wave's DMA instruction fills 1 KiB of consecutive chunks and every
+    // copy of the workgroup is in flight at once
+    const int c8 = ncols >> 3;
+    const int n = V * c8;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t tile_lds = lds_addr(smem);
+    for (int b0 = 64 * wave; b0 < n; b0 += kVnmThreads) {
+      const int ci = b0 + lane;
+      if (ci < n) {   // the last instruction may be partial: its idle lanes write nothing
+        const int r = ci / c8;
+        const int c = (ci - r * c8) * 8;
+        dma_v<16>(Ablk + (int64_t)r * lda + c, tile_lds + (uint32_t)b0 * 16u);
+      }
+    }
+    wait_vmcnt<0>();
+  } else if ((((uintptr_t)Ablk) & 15) == 0 && (ncols & 7) == 0 && (lda & 7) == 0) {
     // eight 16-byte loads in flight per thread before their LDS writes
     const int c8 = ncols >> 3;
     const int n = V * c8;
