@@ -52,6 +52,25 @@ def spmm_bytes(n: int) -> int:
 ENCODE_BYTES = R * K * 2 + R * (K // 2) * 2 + R * (K // 8)
 
 
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_spmm_vnm_128_2_16_8192x8192x4096.json")
+
+
+def measured_mfma():
+    """Matrix-core counters of the V:2:16 product from the committed rocprofv3 summary, or
+    None if it is missing or was taken on a different kernel source."""
+    try:
+        with open(MFMA_SUMMARY) as f:
+            s = json.load(f)
+    except (OSError, ValueError):
+        return None
+    from structured_sparse_matrix_amd.profiling import kernel_source_hash, WIDE_KERNEL_SOURCES
+    if s.get("kernel_source_hash") != kernel_source_hash(WIDE_KERNEL_SOURCES):
+        return None
+    return {g.get("label", str(i)): {"mfma_busy_frac": g["mfma_busy_frac"],
+                                     "fp16_matrix_ops": g["fp16_matrix_ops"]}
+            for i, g in enumerate(s["groups"])}
+
+
 def measured_traffic():
     """HBM bytes per SpMM launch from the committed rocprofv3 counter summary, or None if
     the summary is missing or was taken on a different kernel source."""
@@ -310,6 +329,9 @@ def bench_other(workload: str, steps: int, warmup: int) -> dict:
         t_mm_t = timed(lambda j: snm.spmm_vnm_tiled(*enc_t[j], Bd[j], w.V, w.M, out=Ys[j]))
         out["kernels"]["prune_encode_vnm_tiled"] = {"avg_us": t_enc_t * 1e6, "GB/s": bytes_enc / t_enc_t / 1e9}
         out["kernels"]["spmm_vnm_tiled"] = mm_stats(t_mm_t)
+        if workload == "vnm_128_2_16":
+            # rocprofv3 counters of the same kernels (profiles/), None if the source changed
+            out["counters"] = measured_mfma()
     elif w.kind == "attention":
         Q, Km, V = workloads.attention_qkv(w)
         Qd, Kd, Vd = (torch.from_numpy(x).to(dev) for x in (Q, Km, V))

@@ -14,6 +14,15 @@
       counter is scaled by what it reads for the largest plain copy kernel (N bytes read
       and N bytes written) dispatched before the first matching kernel. Prints JSON with
       the kernel-source hash that bench.py compares against.
+
+  python -m structured_sparse_matrix_amd.profiling mfma COUNTER_CSV --match NAME [--groups G]
+         [--cus 256] [--command CMD]
+      Matrix-core use of the kernels whose name contains NAME, from one `rocprofv3 --pmc
+      SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_BUSY_CU_CYCLES`
+      run: per dispatch (split in order into G groups) the busy fraction of the matrix cores
+      (MFMA busy cycles, summed over SIMDs, over the per-XCD GUI-active cycles x CUs x 4
+      SIMDs; GRBM_GUI_ACTIVE is summed over the XCDs) and the fp16 matrix operations
+      (MOPS x 512). Prints JSON with the wide-kernel source hash.
 """
 from __future__ import annotations
 
@@ -26,6 +35,7 @@ import statistics
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 DECODE_KERNEL_SOURCES = ("spmm_skinny.hip", "device_common.hpp")
+WIDE_KERNEL_SOURCES = ("spmm_wide.hip", "lds_dma.hpp", "wide_layout.hpp", "elem.hpp", "device_common.hpp")
 
 
 def kernel_source_hash(files=DECODE_KERNEL_SOURCES) -> str:
@@ -93,6 +103,29 @@ def traffic(fetch_csv, write_csv, match, calibration_bytes):
     }
 
 
+def mfma(csv_path, match, groups=1, cus=256, xcds=8):
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if match not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)
+    n = len(ids) // groups if groups > 1 and len(ids) % groups == 0 else len(ids)
+    out = []
+    for g in range(0, len(ids), n):
+        rows = [per[i] for i in ids[g:g + n]]
+        busy = statistics.mean(r["SQ_VALU_MFMA_BUSY_CYCLES"] for r in rows)
+        gui = statistics.mean(r["GRBM_GUI_ACTIVE"] for r in rows)
+        mops = statistics.mean(r["SQ_INSTS_VALU_MFMA_MOPS_F16"] for r in rows)
+        out.append({"dispatches": len(rows), "mfma_busy_cycles": busy,
+                    "gui_active_cycles_per_xcd": gui / xcds,
+                    "mfma_busy_frac": busy / (gui / xcds * cus * 4),
+                    "fp16_matrix_ops": mops * 512.0,
+                    "busy_cu_cycles": statistics.mean(r["SQ_BUSY_CU_CYCLES"] for r in rows)})
+    return {"kernel_match": match, "groups": out, "cus": cus, "xcds": xcds}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -107,9 +140,26 @@ def main(argv=None):
     t.add_argument("--match", required=True)
     t.add_argument("--calibration-bytes", type=int, required=True)
     t.add_argument("--command", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("counters")
+    m.add_argument("--match", required=True)
+    m.add_argument("--groups", type=int, default=1)
+    m.add_argument("--cus", type=int, default=256)
+    m.add_argument("--xcds", type=int, default=8)
+    m.add_argument("--labels", default="", help="comma-separated names of the groups")
+    m.add_argument("--workload", default="")
+    m.add_argument("--command", default="")
     a = ap.parse_args(argv)
     if a.cmd == "kernels":
         print(kernels_table(a.trace, a.match, a.skip, a.groups))
+    elif a.cmd == "mfma":
+        out = mfma(a.counters, a.match, a.groups, a.cus, a.xcds)
+        for g, lab in zip(out["groups"], [x for x in a.labels.split(",") if x]):
+            g["label"] = lab
+        out["workload"] = a.workload
+        out["kernel_source_hash"] = kernel_source_hash(WIDE_KERNEL_SOURCES)
+        out["command"] = a.command
+        print(json.dumps(out, indent=1))
     else:
         out = traffic(a.fetch, a.write, a.match, a.calibration_bytes)
         out["kernel_source_hash"] = kernel_source_hash()
