@@ -281,8 +281,9 @@ k_spmm_bitmap(BitmapArgs a) {
   const int64_t rof = row0 + orr < a.R ? row0 + orr : a.R - 1;
   const uint32_t of_lane = (uint32_t)(rof * T) + (uint32_t)(lane < 48 ? lane - 3 * orr : 0);
   // a matrix without non-zeros has no values to copy (and its values pointer may be NULL);
-  // otherwise the first 16 bytes of values are a readable target for idle lanes
-  const bool any_values = a.offsets[RT] != 0u;
+  // otherwise the first 16 bytes of values are a readable target for idle lanes. A wave
+  // without tiles reads nothing (with K = 0 the arrays may all be NULL).
+  const bool any_values = nph > 0 && a.offsets[RT] != 0u;
 
   // (1) metadata of phase p into metadata buffer mb: lane l copies bitmap word l % 2 of
   // tile (l / 2) % 2 of row l / 4, and (l < 48) offset entry l % 3 of row l / 3; rows past

@@ -108,3 +108,21 @@ def test_bitmap_decode_shapes_sampled(n, s):
     ref = A[rows].astype(np.float64) @ B.astype(np.float64)
     assert_fp16_close(Y[rows], ref, f"bitmap {n}x{n} s={s} N=8 sampled rows")
     assert int(offh[-1]) == int(np.sum((np.count_nonzero(A.reshape(n * T, 64), axis=1) + 7) // 8 * 8))
+
+
+def test_bitmap_spmm_empty_reduction_writes_zeros():
+    """K = 0 through the C entry point with the (empty) bitmap arrays passed as NULL, as the
+    header allows: every output is 0, both B layouts, one and two column tiles."""
+    import torch
+    from structured_sparse_matrix_amd._lib import load, check
+    lib = load()
+    stream = torch.cuda.current_stream().cuda_stream
+    for C, layout in ((8, 1), (32, 1), (8, 0), (24, 0)):
+        R = 40
+        B = torch.zeros((max(C, 8), 8), dtype=torch.float16, device="cuda")   # a readable pointer, never read
+        Y = torch.full((R, C), 7.0, dtype=torch.float16, device="cuda")
+        ldb = 8 if layout == 1 else C   # column-major B needs ldb >= K (0) and ldb % 8 == 0
+        check("snm_spmm_bitmap", lib.snm_spmm_bitmap(None, None, None, R, 0, B.data_ptr(), C, ldb, layout,
+                                                     Y.data_ptr(), C, stream))
+        torch.cuda.synchronize()
+        assert not to_host(Y).view(np.uint16).any(), f"C={C} layout={layout}"
