@@ -373,10 +373,6 @@ k_spmm_bitmap(BitmapArgs a) {
     constexpr int P = decltype(par_c)::value;   // p % 2: its value and metadata buffers
     constexpr int PB = kAheadB ? P : 0;         // its B register set
     wait_vmcnt<0>();   // this phase's values and B, the next phase's metadata
-    if constexpr (!kAheadB) {
-      load_b(p, cint<0>{});
-      wait_vmcnt<0>();
-    }
     // the B operands have arrived: any wait the compiler adds for them goes here, where
     // nothing is outstanding
 #pragma unroll
@@ -436,6 +432,10 @@ k_spmm_bitmap(BitmapArgs a) {
         asm volatile("" ::: "memory");
       }
     }
+    // one register set (kAheadB off): the next phase's B operands are requested once this
+    // phase's products have been issued, and arrive under the wait that opens the next phase
+    if constexpr (!kAheadB)
+      if (p + 1 < nph) load_b(p + 1, cint<0>{});
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // value reads done: buffer P is free
   };
 
@@ -443,7 +443,7 @@ k_spmm_bitmap(BitmapArgs a) {
     issue_meta(0, 0);
     if (nph > 1) issue_meta(1, 1);
     wait_vmcnt<0>();
-    if constexpr (kAheadB) load_b(0, cint<0>{});
+    load_b(0, cint<0>{});
     issue_values(0, 0, 0);
   }
   for (int64_t p = 0; p < nph; p += 2) {
