@@ -138,39 +138,56 @@ __global__ void __launch_bounds__(256) k_bitmap_fix_offsets(uint32_t* __restrict
   }
 }
 
-// Values: lane l (positions base + 8l .. + 7) writes its non-zeros at the tile's offset
-// plus their rank in the tile; lane 7 of a tile writes the zero padding.
+// Values: per 512-position chunk of a row (8 tiles, whose packed values are contiguous in
+// the output), lane l (positions base + 8l .. + 7) writes its non-zeros into the wave's LDS
+// copy of the chunk at the tile's offset plus their rank in the tile; the copy starts zeroed,
+// so each tile's padding is +0; then the chunk leaves as whole 16-byte pieces (2-byte stores
+// if the values array is not 16-byte aligned).
 __global__ void __launch_bounds__(256) k_bitmap_values(const uint16_t* __restrict__ A, int64_t R,
                                                        int64_t K, int64_t lda,
                                                        const uint64_t* __restrict__ bitmaps,
                                                        const uint32_t* __restrict__ offsets,
-                                                       uint16_t* __restrict__ values) {
+                                                       uint16_t* __restrict__ values, int vec) {
+  __shared__ __align__(16) uint16_t stage[4][512];
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= R) return;   // no barriers in this kernel
+  const int w = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + w;
+  if (r >= R) return;   // no barriers in this kernel: each wave works alone
   const int64_t T = K / kTile;
   const int tin = lane >> 3, c = lane & 7;
+  uint16_t* const st = stage[w];
   for (int64_t base = 0; base < K; base += 512) {
-    const int64_t kt = base / kTile + tin;
-    if (kt >= T) continue;
-    const u4 v = *reinterpret_cast<const u4*>(A + r * lda + base + 8 * lane);
-    const uint64_t bm = bitmaps[r * T + kt];
-    const uint64_t below = c == 0 ? 0ull : (bm & ((1ull << (8 * c)) - 1ull));
-    uint32_t pos = offsets[r * T + kt] + (uint32_t)__popcll(below);
-    const uint32_t m = (uint32_t)(bm >> (8 * c)) & 0xFFu;
+    const int64_t kt0 = base / kTile;
+    const int ntile = (int)(T - kt0 < 8 ? T - kt0 : 8);
+    const uint32_t cbase = offsets[r * T + kt0];           // the chunk's first value
+    const uint32_t n = offsets[r * T + kt0 + ntile] - cbase;   // its values, padding included (<= 512)
+    *reinterpret_cast<u4*>(st + 8 * lane) = u4{0u, 0u, 0u, 0u};
+    asm volatile("" ::: "memory");   // the wave's LDS operations stay in program order
+    if (tin < ntile) {
+      const int64_t kt = kt0 + tin;
+      const u4 v = *reinterpret_cast<const u4*>(A + r * lda + base + 8 * lane);
+      const uint64_t bm = bitmaps[r * T + kt];
+      const uint64_t below = c == 0 ? 0ull : (bm & ((1ull << (8 * c)) - 1ull));
+      uint32_t pos = offsets[r * T + kt] - cbase + (uint32_t)__popcll(below);
+      const uint32_t m = (uint32_t)(bm >> (8 * c)) & 0xFFu;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (m & (1u << e)) {
-        const uint32_t word = v[e >> 1];
-        values[pos] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-        ++pos;
+      for (int e = 0; e < 8; ++e) {
+        if (m & (1u << e)) {
+          const uint32_t word = v[e >> 1];
+          st[pos] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xFFFFu));
+          ++pos;
+        }
       }
     }
-    if (c == 7) {
-      const uint32_t cnt = (uint32_t)__popcll(bm);
-      const uint32_t start = offsets[r * T + kt];
-      for (uint32_t p = cnt; p < ((cnt + 7u) & ~7u); ++p) values[start + p] = 0;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (vec) {
+      if ((uint32_t)lane < n / 8)
+        __builtin_nontemporal_store(*reinterpret_cast<const u4*>(st + 8 * lane),
+                                    reinterpret_cast<u4*>(values + cbase + 8 * lane));
+    } else {
+      for (uint32_t i = (uint32_t)lane; i < n; i += 64) values[cbase + i] = st[i];
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next zeroing
   }
 }
 
@@ -495,8 +512,9 @@ hipError_t launch_bitmap_values(const void* A, int64_t R, int64_t K, int64_t lda
                                 const uint64_t* bitmaps, const uint32_t* offsets, void* values,
                                 hipStream_t stream) {
   const unsigned g = (unsigned)((R + 3) / 4);
+  const int vec = ((uintptr_t)values & 15u) == 0;
   hipLaunchKernelGGL(k_bitmap_values, dim3(g), dim3(256), 0, stream, (const uint16_t*)A, R, K, lda,
-                     bitmaps, offsets, (uint16_t*)values);
+                     bitmaps, offsets, (uint16_t*)values, vec);
   return hipGetLastError();
 }
 
