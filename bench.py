@@ -554,6 +554,79 @@ def bench_sweep(steps: int, warmup: int, families=None) -> dict:
     return {"workload": "vnm_sweep", "points": points}
 
 
+def bench_decode_ws(steps: int, warmup: int) -> dict:
+    """The decode product with the split reduction (snm_spmm_nm_tiled_ws) beside the unsplit
+    one (snm_spmm_nm_tiled) on 4096 x 4096 and on 4096 x 14336 (a feed-forward down
+    projection), N = 8 / 16 / 32, B as X[N][K]. Each entry point is timed over K
+    back-to-back launches with one event pair, twice in alternating order (the first heavy
+    loop of a process runs slower); the minimum is reported. The compressed A rotates over
+    copies of > 512 MiB so that the last-level cache cannot hold it."""
+    import torch
+    import structured_sparse_matrix_amd as snm
+    from structured_sparse_matrix_amd._lib import load as load_lib, check
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = load_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(launch, nrot):
+        for i in range(warmup):
+            launch(i % nrot)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            launch(i % nrot)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps * 1e-3
+
+    gen = torch.Generator(device=dev)
+    points = []
+    for (r, k) in ((4096, 4096), (4096, 14336)):
+        gen.manual_seed(r + k)
+        A = (torch.randn((r, k), generator=gen, device=dev) * 0.02).half()
+        vt0, mt0 = snm.prune_encode_nm_tiled(A)
+        del A
+        nrot = max(2, -(-(512 << 20) // (vt0.numel() * 2 + mt0.numel())))
+        vts = [vt0.clone() for _ in range(nrot)]
+        mts = [mt0.clone() for _ in range(nrot)]
+        for n in NS:
+            X = torch.randn((n, k), generator=gen, device=dev).half()
+            Y = torch.empty((r, n), dtype=torch.float16, device=dev)
+            nb = snm.spmm_nm_tiled_ws_bytes(r, k, n)
+            ws = torch.zeros((max(nb, 16),), dtype=torch.uint8, device=dev)
+
+            def unsplit(i):
+                check("snm_spmm_nm_tiled", lib.snm_spmm_nm_tiled(vts[i].data_ptr(), mts[i].data_ptr(), r, k,
+                                                                 X.data_ptr(), n, k, 1, Y.data_ptr(), n, stream))
+
+            def split(i):
+                check("snm_spmm_nm_tiled_ws", lib.snm_spmm_nm_tiled_ws(
+                    vts[i].data_ptr(), mts[i].data_ptr(), r, k, X.data_ptr(), n, k, Y.data_ptr(), n,
+                    ws.data_ptr(), nb, stream))
+
+            t = {"unsplit": [], "ws": []}
+            for order in (("unsplit", "ws"), ("ws", "unsplit")):
+                for name in order:
+                    t[name].append(timed(unsplit if name == "unsplit" else split, nrot))
+            by = r * (k // 2) * 2 + r * (k // 8) + k * n * 2 + r * n * 2
+            pt = {"R": r, "K": k, "N": n, "workspace_bytes": nb, "split": nb > 0, "algorithmic_bytes": by}
+            for name, ts in t.items():
+                sec = min(ts)
+                pt[name] = {"avg_us": sec * 1e6, "GB/s": by / sec / 1e9, "hbm_frac": by / sec / 1e9 / HBM_PEAK_GBS,
+                            "dense_equiv_TFLOP/s": 2 * r * k * n / sec / 1e12}
+            pt["speedup_ws_vs_unsplit"] = min(t["unsplit"]) / min(t["ws"])
+            points.append(pt)
+        del vts, mts
+        torch.cuda.empty_cache()
+    return {"workload": "nm_decode_long_k", "dtype": "fp16", "data": "synthetic",
+            "config": {"workload": "2:4 decode SpMM, A R x K fp16 N(0,0.02) in the operand-major "
+                                   "layout, X[N][K] fp16 N(0,1); split reduction vs unsplit"},
+            "steps": steps, "warmup": warmup, "points": points}
+
+
 def bench_bitmap(steps: int, warmup: int) -> dict:
     """Unstructured sparsity in the bitmap format (Coruscant, Sec. 3 and 5.2): OPT-30B /
     OPT-66B weight shapes (7168 and 9216 square) at 30 / 50 / 70 % sparsity, activations
@@ -703,7 +776,8 @@ def main():
                          "(per-kernel timings only) or vnm_sweep (the general V:N:M sweep) or energy "
                          "(energy of the GPU's V:2:M encodings) or bitmap (unstructured sparsity, "
                          "bitmap format) or attention_2_4_bf16 / attention_1_2_f32 (the attention "
-                         "workload in bf16 with 2:4, in fp32 with 1:2)")
+                         "workload in bf16 with 2:4, in fp32 with 1:2) or nm_decode_long_k (the decode "
+                         "product with and without the split reduction, 4096 x 4096 and 4096 x 14336)")
     ap.add_argument("--streams", type=int, default=2,
                     help="decode steps in flight (step i on stream i %% S); kernel timings use one")
     ap.add_argument("--submit", choices=("eager", "graph"), default="eager",
@@ -718,6 +792,9 @@ def main():
         sys.exit(2)
     if args.workload in ("attention_2_4_bf16", "attention_1_2_f32"):
         print(json.dumps(bench_attention_variant(args.workload, args.steps, args.warmup)))
+        return
+    if args.workload == "nm_decode_long_k":
+        print(json.dumps(bench_decode_ws(args.steps, args.warmup)))
         return
     if args.workload == "bitmap":
         print(json.dumps(bench_bitmap(args.steps, args.warmup)))

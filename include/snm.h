@@ -136,6 +136,31 @@ int snm_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_t R, int64
                       const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                       int64_t ldy, void* stream);
 
+/* Bytes of workspace that snm_spmm_nm_tiled_ws needs for an R x K matrix and C columns
+ * (0 when it runs without a split reduction). K % 16 == 0; C <= 32 (else
+ * SNM_E_UNSUPPORTED). Host only. */
+int snm_spmm_nm_tiled_ws_bytes(int64_t R, int64_t K, int64_t C, int64_t* workspace_bytes);
+
+/* Y = decode(values_t, meta_t) * B for the decode regime, the same product as
+ * snm_spmm_nm_tiled with B column-major (element (k, c) at B[c*ldb + k], ldb >= K, as
+ * decode activations X[C][K] are stored) and C <= 32 (else SNM_E_UNSUPPORTED). The
+ * reduction over K is split across workgroups where that pays (the lecture notes on 2:4
+ * sparse tensor cores: small products are bound by memory traffic and fixed costs): each
+ * dense operand load then serves 32 or 64 rows instead of 16. Chosen when K*C >= 163840
+ * or ceil(R/16) < 256 (with K >= 2048); elsewhere the call runs the kernel of
+ * snm_spmm_nm_tiled and the workspace size is 0.
+ *   workspace  device memory of at least snm_spmm_nm_tiled_ws_bytes(R, K, C) bytes,
+ *              16-byte aligned, owned by the caller. It holds fp32 partial sums and
+ *              arrival counters. It must be zero-filled before its first use; every
+ *              call leaves the counters at zero again, so it needs no clearing between
+ *              calls. Calls that may run at the same time (other streams) need separate
+ *              workspaces. May be NULL when the size is 0.
+ * fp32 accumulation; the split partial sums are added in a fixed order, so the result
+ * does not depend on scheduling. fp16 output (RNE). */
+int snm_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                         const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Y = decode_vnm(values, midx, colloc) * B (VENOM Sec. 4 and Fig. 4: per block of V rows
  * the K/M*4 rows of B named by colloc are gathered, then 2:4 is applied with midx).
  *   values, midx, colloc  V:2:M arrays of an R x K matrix (canonical layout).

@@ -25,6 +25,7 @@ __all__ = [
     "prune_encode_nm", "prune_encode_vnm", "spmm_nm", "spmm_vnm", "sddmm_prune_nm",
     "softmax_nm_rows", "attention_nm", "nm_sizes", "vnm_sizes", "abi_version", "SnmError",
     "nm_tiled_sizes", "prune_encode_nm_tiled", "spmm_nm_tiled",
+    "spmm_nm_tiled_ws_bytes", "spmm_nm_tiled_ws",
     "prune_encode_vnm_tiled", "spmm_vnm_tiled",
     "sddmm_prune_nm_rowmax", "spmm_nm_softmax", "attention_nm_fused",
     "bitmap_sizes", "bitmap_encode", "spmm_bitmap",
@@ -139,6 +140,45 @@ def spmm_nm_tiled(values_t, meta_t, R: int, B, out=None):
     check("snm_spmm_nm_tiled",
           load().snm_spmm_nm_tiled(_ptr(values_t), _ptr(meta_t), R, K, _ptr(B), C, ldb, layout,
                                    _ptr(out), out.stride(0), _stream(B)))
+    return out
+
+
+def spmm_nm_tiled_ws_bytes(R: int, K: int, C: int) -> int:
+    """Workspace bytes of spmm_nm_tiled_ws for an R x K matrix and C <= 32 columns."""
+    n = ctypes.c_int64()
+    check("snm_spmm_nm_tiled_ws_bytes", load().snm_spmm_nm_tiled_ws_bytes(R, K, C, ctypes.byref(n)))
+    return n.value
+
+
+def spmm_nm_tiled_ws(values_t, meta_t, R: int, X, workspace, out=None):
+    """Y = decode(values_t, meta_t) @ X.T for decode activations X [C, K] (C <= 32),
+    with the reduction split across workgroups. workspace: a zero-filled uint8 device
+    tensor of at least spmm_nm_tiled_ws_bytes(R, K, C) bytes (calls leave it zeroed);
+    separate workspaces for calls that may overlap."""
+    torch = _torch()
+    _need(values_t, "values_t", torch.float16)
+    _need(meta_t, "meta_t", torch.uint8)
+    _need(X, "X", torch.float16, 2)
+    if X.stride(1) != 1:
+        raise ValueError("X must have unit stride along K (rows of X are the columns of B)")
+    C, K = X.shape
+    nv, nm = nm_tiled_sizes(R, K)
+    if values_t.numel() < nv or meta_t.numel() < nm or not values_t.is_contiguous() or not meta_t.is_contiguous():
+        raise ValueError("operand-major arrays do not match R x K")
+    need = spmm_nm_tiled_ws_bytes(R, K, C)
+    if need > 0:
+        _need(workspace, "workspace", torch.uint8)
+        if workspace.numel() < need or not workspace.is_contiguous():
+            raise ValueError(f"workspace needs {need} contiguous bytes")
+    if out is None:
+        out = torch.empty((R, C), dtype=torch.float16, device=X.device)
+    if out.stride(1) != 1:
+        raise ValueError("out must be row-major")
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_len = workspace.numel() if workspace is not None else 0
+    check("snm_spmm_nm_tiled_ws",
+          load().snm_spmm_nm_tiled_ws(_ptr(values_t), _ptr(meta_t), R, K, _ptr(X), C, X.stride(0),
+                                      _ptr(out), out.stride(0), ws_ptr, ws_len, _stream(X)))
     return out
 
 

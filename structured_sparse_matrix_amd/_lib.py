@@ -28,6 +28,8 @@ SIGNATURES = {
     "snm_nm_tiled_sizes": [_i64, _i64, _p64, _p64],
     "snm_prune_encode_nm_tiled": [_vp, _i64, _i64, _i64, _vp, _vp, _vp],
     "snm_spmm_nm_tiled": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _vp, _i64, _vp],
+    "snm_spmm_nm_tiled_ws_bytes": [_i64, _i64, _i64, _vp],
+    "snm_spmm_nm_tiled_ws": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp],
     "snm_spmm_vnm": [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
     "snm_spmm_vnm_tiled": [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
     "snm_sddmm_prune_nm": [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp],

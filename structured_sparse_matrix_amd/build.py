@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsnm.so")
 
-SOURCES = ["encode.hip", "spmm.hip", "spmm_skinny.hip", "spmm_wide.hip", "attention.hip", "attention_f32.hip", "bitmap.hip", "validate.cpp", "abi.cpp"]
+SOURCES = ["encode.hip", "spmm.hip", "spmm_skinny.hip", "spmm_splitk.hip", "spmm_wide.hip", "attention.hip", "attention_f32.hip", "bitmap.hip", "validate.cpp", "abi.cpp"]
 
 HIP_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

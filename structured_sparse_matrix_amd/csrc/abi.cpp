@@ -104,6 +104,27 @@ int snm_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_t R, int64
                                             (hipStream_t)stream));
 }
 
+int snm_spmm_nm_tiled_ws_bytes(int64_t R, int64_t K, int64_t C, int64_t* workspace_bytes) {
+  int s = snm::check_nm_sizes(R, K);
+  if (s != SNM_OK) return s;
+  if (C < 0) return SNM_E_SHAPE;
+  if (C > 32) return SNM_E_UNSUPPORTED;
+  if (!workspace_bytes) return SNM_E_NULL;
+  *workspace_bytes = (R == 0 || C == 0) ? 0 : snm::splitk_plan(R, K, C).workspace_bytes;
+  return SNM_OK;
+}
+
+int snm_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, int64_t K, const void* B,
+                         int64_t C, int64_t ldb, void* Y, int64_t ldy, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  int s = snm::check_spmm_nm_tiled_ws(values_t, meta_t, R, K, B, C, ldb, Y, ldy, workspace,
+                                      workspace_bytes);
+  if (s != SNM_OK || R == 0 || C == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_spmm_nm_tiled_splitk(values_t, meta_t, R, K, B, C, ldb, Y, ldy,
+                                                   workspace, (hipStream_t)stream));
+}
+
 int snm_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
                          void* values, void* midx, void* colloc, void* stream) {
   int s = snm::check_prune_encode_vnm(A, R, K, lda, V, M, values, midx, colloc);

@@ -14,6 +14,10 @@ hipError_t launch_prune_encode_nm_tiled(const void* A, int64_t R, int64_t K, int
 hipError_t launch_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                                 const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                                 int64_t ldy, hipStream_t stream);
+// split reduction (plan from splitk_plan); B column-major; workspace as the plan sizes it
+hipError_t launch_spmm_nm_tiled_splitk(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                                       const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                                       void* workspace, hipStream_t stream);
 hipError_t launch_spmm_nm_tiled_skinny(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                                        const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                                        int64_t ldy, hipStream_t stream);

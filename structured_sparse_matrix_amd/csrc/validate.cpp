@@ -268,4 +268,49 @@ int check_softmax_nm_rows(const void* values, int64_t rows, int64_t kept, int64_
   return SNM_OK;
 }
 
+SplitPlan splitk_plan(int64_t R, int64_t K, int64_t C) {
+  constexpr int64_t kWaves = 16;          // waves per workgroup of the split kernel
+  constexpr int64_t kTargetGroups = 256;  // about one workgroup per CU
+  SplitPlan p{};
+  p.cp = C <= 16 ? 16 : 32;
+  p.rt = C <= 16 ? 2 : 4;
+  const int64_t rt16 = (R + 15) / 16;
+  p.groups = (rt16 + p.rt - 1) / p.rt;
+  const int64_t kc = (K + 63) / 64;
+  // The split pays where the unsplit kernel (one workgroup per 16-row tile, all of K) would
+  // stream a large dense operand per workgroup (K*C >= 163840: 320 KiB) or leave CUs idle
+  // (fewer than 256 row tiles); elsewhere its extra round trips (partial stores, fence,
+  // counter, re-read) cost more than they save (measured on MI355X at 4096 x 4096).
+  const bool worth = K * C >= 163840 || rt16 < kTargetGroups;
+  // enough splits for about one workgroup per CU, and at least one chunk per wave
+  int64_t s = !worth ? 1 : p.groups > 0 ? (kTargetGroups + p.groups - 1) / p.groups : 1;
+  if (s > kc / kWaves) s = kc / kWaves;
+  if (s < 1) s = 1;
+  p.splits = (int)s;
+  p.chunks_per_split = (int)((kc + s - 1) / s);
+  const int64_t tile = 16 * p.rt * p.cp;
+  p.count_bytes = p.splits > 1 ? ((p.groups * 4 + 255) / 256) * 256 : 0;
+  p.workspace_bytes = p.splits > 1 ? p.count_bytes + (int64_t)p.splits * p.groups * tile * 4 : 0;
+  return p;
+}
+
+int check_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                           const void* B, int64_t C, int64_t ldb, const void* Y, int64_t ldy,
+                           const void* workspace, int64_t workspace_bytes) {
+  int s = check_spmm_nm(values_t, meta_t, R, K, B, C, ldb, 1, Y, ldy, 1, 0, 0, 0, 0);
+  if (s != SNM_OK) return s;
+  if (C > 32) return SNM_E_UNSUPPORTED;
+  if (workspace_bytes < 0) return SNM_E_SHAPE;
+  if (R == 0 || C == 0) return SNM_OK;
+  // grid: groups workgroups along x (< 2^31)
+  if ((R + 15) / 16 > ((int64_t)1 << 31)) return SNM_E_SHAPE;
+  const SplitPlan p = splitk_plan(R, K, C);
+  if (p.workspace_bytes > 0) {
+    if (workspace_bytes < p.workspace_bytes) return SNM_E_SHAPE;
+    if (!workspace) return SNM_E_NULL;
+    if (((uintptr_t)workspace & 15u) != 0) return SNM_E_ALIGN;
+  }
+  return SNM_OK;
+}
+
 }  // namespace snm

@@ -53,4 +53,18 @@ int check_spmm_bitmap(const void* bitmaps, const void* offsets, const void* valu
                       int64_t ldy);
 int check_softmax_nm_rows(const void* values, int64_t rows, int64_t kept, int64_t ld);
 
+// Split-reduction plan of the operand-major 2:4 decode product (snm_spmm_nm_tiled_ws):
+// row groups of 16*rt rows, `splits` workgroups per group along K, each covering
+// chunks_per_split 64-position chunks; workspace = count_bytes of arrival counters, then
+// splits x groups x (16*rt*cp) fp32 partial tiles. splits == 1: the product runs the
+// unsplit decode kernel and needs no workspace.
+struct SplitPlan {
+  int cp, rt, splits, chunks_per_split;
+  int64_t groups, count_bytes, workspace_bytes;
+};
+SplitPlan splitk_plan(int64_t R, int64_t K, int64_t C);
+int check_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                           const void* B, int64_t C, int64_t ldb, const void* Y, int64_t ldy,
+                           const void* workspace, int64_t workspace_bytes);
+
 }  // namespace snm

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
               "snm_spmm_bitmap", "snm_sddmm_prune_nm_bf16", "snm_softmax_nm_rows_bf16",
               "snm_spmm_nm_bf16", "snm_spmm_nm_softmax_bf16", "snm_sddmm_prune_1of2_f32",
               "snm_softmax_nm_rows_f32", "snm_spmm_1of2_f32", "snm_prune_encode_vnm_tiled",
-              "snm_spmm_vnm_tiled"):
+              "snm_spmm_vnm_tiled", "snm_spmm_nm_tiled_ws_bytes", "snm_spmm_nm_tiled_ws"):
         assert n in names
 
 
@@ -220,6 +220,34 @@ def test_bitmap_sizes_and_validation():
     assert lib.snm_spmm_bitmap(FAKE, FAKE, FAKE, 16, 64, FAKE, 8, 68, 1, FAKE, 8, P(0)) == 3     # ldb % 8
     assert lib.snm_spmm_bitmap(FAKE, FAKE, FAKE, 16, 64, FAKE, 8, 32, 1, FAKE, 8, P(0)) == 2     # ldb < K
     assert lib.snm_spmm_bitmap(P(0), P(0), P(0), 0, 64, P(0), 8, 64, 1, P(0), 8, P(0)) == 0      # R == 0
+
+
+def test_spmm_ws_plan_and_validation():
+    from structured_sparse_matrix_amd import spmm_nm_tiled_ws_bytes, SnmError
+    # 4096 x 14336: C = 32 -> 64 groups of 4 row tiles x 4 splits; C = 16 -> 128 groups of
+    # 2 x 2; counters (256-byte rounded) then fp32 tiles of 16*rt rows x 32 or 16 columns
+    assert spmm_nm_tiled_ws_bytes(4096, 14336, 32) == 256 + 4 * 64 * (64 * 32) * 4
+    assert spmm_nm_tiled_ws_bytes(4096, 14336, 16) == 512 + 2 * 128 * (32 * 16) * 4
+    assert spmm_nm_tiled_ws_bytes(4096, 14336, 8) == 0     # K*C < 163840 with 256 row tiles
+    assert spmm_nm_tiled_ws_bytes(4096, 4096, 32) == 0     # the unsplit kernel is faster there
+    assert spmm_nm_tiled_ws_bytes(2048, 8192, 8) == 256 + 4 * 64 * (32 * 16) * 4   # 128 row tiles: 64 groups x 4
+    assert spmm_nm_tiled_ws_bytes(64, 512, 32) == 0        # 8 chunks: fewer than one per wave
+    assert spmm_nm_tiled_ws_bytes(0, 4096, 32) == 0
+    with pytest.raises(SnmError):
+        spmm_nm_tiled_ws_bytes(16, 64, 33)                  # C > 32
+    with pytest.raises(SnmError):
+        spmm_nm_tiled_ws_bytes(16, 72, 8)                   # K % 16
+    lib = _lib()
+    need = spmm_nm_tiled_ws_bytes(64, 2048, 32)
+    assert need > 0
+    # values_t, meta_t, R, K, B, C, ldb, Y, ldy, workspace, workspace_bytes, stream
+    assert lib.snm_spmm_nm_tiled_ws(FAKE, FAKE, 64, 2048, FAKE, 32, 2048, FAKE, 32, FAKE, need - 1, P(0)) == 2
+    assert lib.snm_spmm_nm_tiled_ws(FAKE, FAKE, 64, 2048, FAKE, 32, 2048, FAKE, 32, P(0), need, P(0)) == 1
+    assert lib.snm_spmm_nm_tiled_ws(FAKE, FAKE, 64, 2048, FAKE, 32, 2048, FAKE, 32, MISALIGNED, need, P(0)) == 3
+    assert lib.snm_spmm_nm_tiled_ws(FAKE, FAKE, 64, 2048, FAKE, 40, 2048, FAKE, 40, FAKE, need, P(0)) == 4
+    assert lib.snm_spmm_nm_tiled_ws(FAKE, FAKE, 64, 2048, FAKE, 32, 2040, FAKE, 32, FAKE, need, P(0)) == 2  # ldb < K
+    assert lib.snm_spmm_nm_tiled_ws(FAKE, FAKE, 64, 2048, FAKE, 32, 2048, FAKE, 32, FAKE, -1, P(0)) == 2
+    assert lib.snm_spmm_nm_tiled_ws(P(0), P(0), 0, 2048, P(0), 32, 2048, P(0), 32, P(0), 0, P(0)) == 0    # R == 0
 
 
 def test_softmax_validation():

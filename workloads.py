@@ -59,7 +59,7 @@ class Workload:
     extra: dict = field(default_factory=dict)
 
 
-# The five workloads. Seeds of the last four are this library's choice.
+# The workloads. Seeds of all but the first are this library's choice.
 WORKLOADS = {
     "nm_tiny": Workload("nm_tiny", "nm", seed=0, R=256, K=256, Cs=(64,), sigma_a=1.0),
     "nm_decode": Workload("nm_decode", "nm", seed=1, R=4096, K=4096, Cs=(8, 16, 32), sigma_a=0.02),
@@ -69,6 +69,10 @@ WORKLOADS = {
                               head_dim=64),
     "vnm_128_2_16": Workload("vnm_128_2_16", "vnm", seed=4, R=8192, K=8192, Cs=(4096,), sigma_a=0.02,
                              V=128, M=16),
+    # decode with a long reduction (a feed-forward down projection, 4096 x 14336): the
+    # shape on which the split reduction of the decode product is measured
+    "nm_decode_long_k": Workload("nm_decode_long_k", "nm", seed=5, R=4096, K=14336, Cs=(8, 16, 32),
+                                 sigma_a=0.02),
 }
 
 
