@@ -786,6 +786,8 @@ def main():
     ap.add_argument("--families", default="",
                     help="with --workload vnm_sweep: comma-separated subset of fig9,fig10,gpt3")
     args = ap.parse_args()
+    if args.streams < 1 or NROT % args.streams != 0:
+        ap.error(f"--streams must divide the {NROT} rotating input copies")
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
