@@ -5,7 +5,8 @@
 // Why a split: with one workgroup per 16-row tile and all of K, every workgroup reads the
 // whole dense operand (256 KiB at K = 4096, C = 32) from L2 to use it once, 3.5x the bytes
 // of its share of the compressed weights. Here each wave applies every B operand it loads
-// to RT row tiles (RT = 4 for C > 16), which divides the B bytes per row by RT; the K range
+// to RT = 4 row tiles (2 when fewer than 256 row tiles exist), which divides the B bytes per
+// row by RT; the K range
 // is cut into S splits so that the grid still holds one workgroup per CU or more.
 //
 //   * workgroup (g, s): rows [16 RT g, +16 RT), 64-position chunks [s Q, min(KC, (s+1) Q))
@@ -44,9 +45,10 @@ struct SplitArgs {
 };
 
 // U chunks per wave and round: every load of a round is in flight before its first MFMA
-// (U = 1 with four row tiles keeps the operands within the 128 VGPRs of 16-wave groups).
-template <int CP, int RT, int U, bool BVEC>
-__global__ void __launch_bounds__(64 * kSplitWaves)
+// (U = 1 with four row tiles keeps the operands within the 128 VGPRs of 16-wave groups;
+// 8-wave groups with U = 2 or 4 measured slower on MI355X).
+template <int CP, int RT, int U, int NWAVES, bool BVEC>
+__global__ void __launch_bounds__(64 * NWAVES)
 k_spmm_nm_splitk(SplitArgs a) {
   constexpr int CT = CP / 16;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -54,7 +56,7 @@ k_spmm_nm_splitk(SplitArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int NW = blockDim.x >> 6;
+  constexpr int NW = NWAVES;
   const int q = lane >> 4;
   const int li = lane & 15;
   const int64_t g = blockIdx.x;
@@ -129,12 +131,12 @@ k_spmm_nm_splitk(SplitArgs a) {
     for (int ct = 0; ct < CT; ++ct) red[((w * RT + i) * CT + ct) * 64 + lane] = acc[i][ct];
   __syncthreads();
   constexpr int kTile = 16 * RT * CP;                 // fp32 elements of the workgroup tile
-  constexpr int kPer = (kTile + 64 * kSplitWaves - 1) / (64 * kSplitWaves);
+  constexpr int kPer = (kTile + 64 * NWAVES - 1) / (64 * NWAVES);
   const float* rp = reinterpret_cast<const float*>(red);
   float v[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int e = tid + j * blockDim.x;
+    const int e = tid + j * 64 * NW;
     float sum = 0.f;
     if (e < kTile) {
       const int r = e / CP;                            // row within the group
@@ -151,7 +153,7 @@ k_spmm_nm_splitk(SplitArgs a) {
     float* mine = a.part + ((int64_t)s * a.G + g) * kTile;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int e = tid + j * blockDim.x;
+      const int e = tid + j * 64 * NW;
       if (e < kTile) mine[e] = v[j];
     }
     // Every wave's stores have reached L2 before the barrier; one thread then publishes the
@@ -169,7 +171,7 @@ k_spmm_nm_splitk(SplitArgs a) {
     if (last_flag == 0u) return;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int e = tid + j * blockDim.x;
+      const int e = tid + j * 64 * NW;
       if (e >= kTile) continue;
       float t = 0.f;
       for (int ss = 0; ss < a.S; ++ss)
@@ -180,7 +182,7 @@ k_spmm_nm_splitk(SplitArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int e = tid + j * blockDim.x;
+    const int e = tid + j * 64 * NW;
     if (e >= kTile) continue;
     const int r = e / CP;
     const int c = e - r * CP;
@@ -193,9 +195,9 @@ k_spmm_nm_splitk(SplitArgs a) {
 
 template <int CP, int RT, int U, bool BVEC>
 static hipError_t launch_splitk(const SplitArgs& a, hipStream_t stream) {
-  const int nw = kSplitWaves;
+  constexpr int nw = kSplitWaves;
   const size_t lds = (size_t)nw * RT * (CP / 16) * 64 * 16;
-  auto kern = k_spmm_nm_splitk<CP, RT, U, BVEC>;
+  auto kern = k_spmm_nm_splitk<CP, RT, U, nw, BVEC>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -227,9 +229,14 @@ hipError_t launch_spmm_nm_tiled_splitk(const void* values_t, const void* meta_t,
   a.S = p.splits;
   a.Q = p.chunks_per_split;
   a.b_vec = (ldb % 8 == 0) && (((uintptr_t)B & 15) == 0);
+  if (p.rt == 4) {
+    if (p.cp == 16)
+      return a.b_vec ? launch_splitk<16, 4, 1, true>(a, stream) : launch_splitk<16, 4, 1, false>(a, stream);
+    return a.b_vec ? launch_splitk<32, 4, 1, true>(a, stream) : launch_splitk<32, 4, 1, false>(a, stream);
+  }
   if (p.cp == 16)
     return a.b_vec ? launch_splitk<16, 2, 2, true>(a, stream) : launch_splitk<16, 2, 2, false>(a, stream);
-  return a.b_vec ? launch_splitk<32, 4, 1, true>(a, stream) : launch_splitk<32, 4, 1, false>(a, stream);
+  return a.b_vec ? launch_splitk<32, 2, 2, true>(a, stream) : launch_splitk<32, 2, 2, false>(a, stream);
 }
 
 }  // namespace snm

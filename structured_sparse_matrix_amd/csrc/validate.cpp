@@ -273,8 +273,11 @@ SplitPlan splitk_plan(int64_t R, int64_t K, int64_t C) {
   constexpr int64_t kTargetGroups = 256;  // about one workgroup per CU
   SplitPlan p{};
   p.cp = C <= 16 ? 16 : 32;
-  p.rt = C <= 16 ? 2 : 4;
   const int64_t rt16 = (R + 15) / 16;
+  // 64 rows per dense-operand load where 64 groups or more fill the grid with at most 4
+  // splits; else 32. More than 4 splits, or two workgroups per CU, measured slower: the
+  // end chain of every split workgroup (stores, fence, counter) contends.
+  p.rt = rt16 >= 256 ? 4 : 2;
   p.groups = (rt16 + p.rt - 1) / p.rt;
   const int64_t kc = (K + 63) / 64;
   // The split pays where the unsplit kernel (one workgroup per 16-row tile, all of K) would
@@ -284,6 +287,7 @@ SplitPlan splitk_plan(int64_t R, int64_t K, int64_t C) {
   const bool worth = K * C >= 163840 || rt16 < kTargetGroups;
   // enough splits for about one workgroup per CU, and at least one chunk per wave
   int64_t s = !worth ? 1 : p.groups > 0 ? (kTargetGroups + p.groups - 1) / p.groups : 1;
+  if (s > 4) s = 4;
   if (s > kc / kWaves) s = kc / kWaves;
   if (s < 1) s = 1;
   p.splits = (int)s;

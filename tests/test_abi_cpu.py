@@ -224,13 +224,14 @@ def test_bitmap_sizes_and_validation():
 
 def test_spmm_ws_plan_and_validation():
     from structured_sparse_matrix_amd import spmm_nm_tiled_ws_bytes, SnmError
-    # 4096 x 14336: C = 32 -> 64 groups of 4 row tiles x 4 splits; C = 16 -> 128 groups of
-    # 2 x 2; counters (256-byte rounded) then fp32 tiles of 16*rt rows x 32 or 16 columns
+    # 4096 x 14336: 64 groups of 4 row tiles x 4 splits; counters (256-byte rounded) then
+    # fp32 tiles of 64 rows x 32 (C > 16) or 16 columns
     assert spmm_nm_tiled_ws_bytes(4096, 14336, 32) == 256 + 4 * 64 * (64 * 32) * 4
-    assert spmm_nm_tiled_ws_bytes(4096, 14336, 16) == 512 + 2 * 128 * (32 * 16) * 4
+    assert spmm_nm_tiled_ws_bytes(4096, 14336, 16) == 256 + 4 * 64 * (64 * 16) * 4
     assert spmm_nm_tiled_ws_bytes(4096, 14336, 8) == 0     # K*C < 163840 with 256 row tiles
     assert spmm_nm_tiled_ws_bytes(4096, 4096, 32) == 0     # the unsplit kernel is faster there
-    assert spmm_nm_tiled_ws_bytes(2048, 8192, 8) == 256 + 4 * 64 * (32 * 16) * 4   # 128 row tiles: 64 groups x 4
+    assert spmm_nm_tiled_ws_bytes(2048, 8192, 8) == 256 + 4 * 64 * (32 * 16) * 4   # 128 row tiles: 64 groups of 2, 4 splits
+    assert spmm_nm_tiled_ws_bytes(1024, 16384, 32) == 256 + 4 * 32 * (32 * 32) * 4  # at most 4 splits
     assert spmm_nm_tiled_ws_bytes(64, 512, 32) == 0        # 8 chunks: fewer than one per wave
     assert spmm_nm_tiled_ws_bytes(0, 4096, 32) == 0
     with pytest.raises(SnmError):

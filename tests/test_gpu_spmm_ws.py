@@ -47,9 +47,10 @@ def _run(A, X, ws=None, ldb_pad=0):
 @pytest.mark.parametrize("R,K,C", [
     (16, 64, 16),      # unsplit kernel
     (33, 1040, 5),     # unsplit kernel, ragged rows and columns
-    (100, 4096, 8),    # 2 row tiles per group, 4 splits, ragged rows
-    (64, 2048, 32),    # 4 row tiles per group, 2 splits
-    (200, 4096, 24),   # 4 row tiles, 4 splits, 24 of 32 columns
+    (100, 4096, 8),    # 4 groups of 2 row tiles (the last partial), 4 splits, ragged rows
+    (64, 2048, 32),    # 2 groups of 2 row tiles, 2 splits
+    (4100, 8192, 24),  # 65 groups of 4 row tiles (the last partial), 4 splits
+    (200, 4096, 24),   # 2 row tiles, 4 splits, 24 of 32 columns
     (1000, 8192, 32),  # 8 splits
     (17, 3072, 12),    # one partial row group
 ])
