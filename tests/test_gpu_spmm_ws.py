@@ -118,3 +118,27 @@ def test_spmm_ws_reuse_with_smaller_input():
         Y = snm.spmm_nm_tiled_ws(vt, mt, R, to_dev(X), ws, out=out)
         ov, om = oracle.prune_encode_nm(A)
         assert_fp16_close(to_host(Y), oracle.spmm_nm(ov, om, np.ascontiguousarray(X.T)), f"reuse R={R} K={K}")
+
+
+def test_spmm_ws_two_streams_separate_workspaces():
+    # calls that overlap on two streams, each with its own workspace, both give the
+    # single-stream result bit for bit
+    import torch
+    snm = _snm()
+    R, K = 1024, 8192
+    A = workloads.small_matrix(91, (R, K), 0.02)
+    vt, mt = snm.prune_encode_nm_tiled(to_dev(A))
+    Xs = [to_dev(workloads.small_matrix(92 + i, (32, K))) for i in range(2)]
+    wss = [_ws(R, K, 32)[0] for _ in range(2)]
+    assert _snm().spmm_nm_tiled_ws_bytes(R, K, 32) > 0
+    ref = [to_host(snm.spmm_nm_tiled_ws(vt, mt, R, X, wss[0])).view(np.uint16).copy() for X in Xs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty((R, 32), dtype=torch.float16, device="cuda") for _ in range(2)]
+    for rep in range(8):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                snm.spmm_nm_tiled_ws(vt, mt, R, Xs[i], wss[i], out=outs[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert np.array_equal(to_host(outs[i]).view(np.uint16), ref[i]), f"rep {rep}, stream {i}"
