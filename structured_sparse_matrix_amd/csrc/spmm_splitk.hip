@@ -5,9 +5,9 @@
 // Why a split: with one workgroup per 16-row tile and all of K, every workgroup reads the
 // whole dense operand (256 KiB at K = 4096, C = 32) from L2 to use it once, 3.5x the bytes
 // of its share of the compressed weights. Here each wave applies every B operand it loads
-// to RT = 4 row tiles (2 when fewer than 256 row tiles exist), which divides the B bytes per
-// row by RT; the K range
-// is cut into S splits so that the grid still holds one workgroup per CU or more.
+// to RT = 4 row tiles (2 when fewer than 256 row tiles exist), which divides the B bytes
+// per row by RT; the K range is cut into S <= 4 splits so that the grid still holds about
+// one workgroup per CU.
 //
 //   * workgroup (g, s): rows [16 RT g, +16 RT), 64-position chunks [s Q, min(KC, (s+1) Q))
 //     with Q = ceil(KC / S); its NW waves take the chunks round-robin.
@@ -16,10 +16,10 @@
 //   * B column-major: each lane loads its operand half (eight consecutive k of one
 //     column); the four lanes of a column read whole 128-byte lines.
 //   * the NW wave partials are summed through LDS; the workgroup (S >= 2) stores its fp32
-//     tile in the workspace, publishes it with one agent-scope
-//     release fence and counts itself in on the row group's counter; the workgroup that arrives
-//     last reads the S tiles back, adds them in split order (so the result does not depend
-//     on the arrival order), writes Y and sets the counter back to zero.
+//     tile in the workspace, publishes it with one agent-scope release fence and counts
+//     itself in on the row group's counter; the workgroup that arrives last reads the S
+//     tiles back, adds them in split order (so the result does not depend on the arrival
+//     order), writes Y and sets the counter back to zero.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "validate.hpp"
@@ -149,37 +149,36 @@ k_spmm_nm_splitk(SplitArgs a) {
   }
   const int64_t row0 = g * 16 * RT;
 
-  {
-    float* mine = a.part + ((int64_t)s * a.G + g) * kTile;
+  float* mine = a.part + ((int64_t)s * a.G + g) * kTile;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = tid + j * 64 * NW;
-      if (e < kTile) mine[e] = v[j];
-    }
-    // Every wave's stores have reached L2 before the barrier; one thread then publishes the
-    // tile at agent scope and counts in. Agent-scope fences write back and invalidate the
-    // XCD's L2, so they are issued once per workgroup, not once per thread.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      const bool last = atomicAdd(a.count + g, 1u) == (uint32_t)(a.S - 1);
-      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other splits' tiles
-      last_flag = last ? 1u : 0u;
-    }
-    __syncthreads();
-    if (last_flag == 0u) return;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = tid + j * 64 * NW;
-      if (e >= kTile) continue;
-      float t = 0.f;
-      for (int ss = 0; ss < a.S; ++ss)
-        t += ss == s ? v[j] : a.part[((int64_t)ss * a.G + g) * kTile + e];
-      v[j] = t;
-    }
-    if (tid == 0) __hip_atomic_store(a.count + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + j * 64 * NW;
+    if (e < kTile) mine[e] = v[j];
   }
+  // Every wave's stores have reached L2 before the barrier; one thread then publishes the
+  // tile at agent scope and counts in. An agent-scope release writes back the XCD's L2 and
+  // an acquire invalidates it, so each is issued once per workgroup, not once per thread
+  // (once per thread measured 94 us per launch).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const bool last = atomicAdd(a.count + g, 1u) == (uint32_t)(a.S - 1);
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other splits' tiles
+    last_flag = last ? 1u : 0u;
+  }
+  __syncthreads();
+  if (last_flag == 0u) return;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + j * 64 * NW;
+    if (e >= kTile) continue;
+    float t = 0.f;
+    for (int ss = 0; ss < a.S; ++ss)
+      t += ss == s ? v[j] : a.part[((int64_t)ss * a.G + g) * kTile + e];
+    v[j] = t;
+  }
+  if (tid == 0) __hip_atomic_store(a.count + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int e = tid + j * 64 * NW;
