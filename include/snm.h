@@ -146,15 +146,17 @@ int snm_spmm_nm_tiled_ws_bytes(int64_t R, int64_t K, int64_t C, int64_t* workspa
  * decode activations X[C][K] are stored) and C <= 32 (else SNM_E_UNSUPPORTED). The
  * reduction over K is split across workgroups where that pays (the lecture notes on 2:4
  * sparse tensor cores: small products are bound by memory traffic and fixed costs): each
- * dense operand load then serves 32 or 64 rows instead of 16. Chosen when K*C >= 163840
- * or ceil(R/16) < 256 (with K >= 2048); elsewhere the call runs the kernel of
- * snm_spmm_nm_tiled and the workspace size is 0.
+ * dense operand load then serves 32 or 64 rows instead of 16. The split is chosen when
+ * (K*C >= 163840 or ceil(R/16) < 256) and ceil(K/64) >= 32, with at most 4 splits;
+ * elsewhere the call runs the kernel of snm_spmm_nm_tiled and the workspace size is 0.
+ * The workspace never exceeds 4 MiB + 1 KiB, whatever the shape.
  *   workspace  device memory of at least snm_spmm_nm_tiled_ws_bytes(R, K, C) bytes,
  *              16-byte aligned, owned by the caller. It holds fp32 partial sums and
  *              arrival counters. It must be zero-filled before its first use; every
- *              call leaves the counters at zero again, so it needs no clearing between
- *              calls. Calls that may run at the same time (other streams) need separate
- *              workspaces. May be NULL when the size is 0.
+ *              call leaves every byte it wrote zero again, so one workspace serves any
+ *              sequence of calls and shapes with no clearing in between. Calls that may
+ *              run at the same time (other streams) need separate workspaces. May be NULL
+ *              when the size is 0.
  * fp32 accumulation; the split partial sums are added in a fixed order, so the result
  * does not depend on scheduling. fp16 output (RNE). */
 int snm_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, int64_t K,

@@ -153,8 +153,9 @@ def spmm_nm_tiled_ws_bytes(R: int, K: int, C: int) -> int:
 def spmm_nm_tiled_ws(values_t, meta_t, R: int, X, workspace, out=None):
     """Y = decode(values_t, meta_t) @ X.T for decode activations X [C, K] (C <= 32),
     with the reduction split across workgroups. workspace: a zero-filled uint8 device
-    tensor of at least spmm_nm_tiled_ws_bytes(R, K, C) bytes (calls leave it zeroed);
-    separate workspaces for calls that may overlap."""
+    tensor of at least spmm_nm_tiled_ws_bytes(R, K, C) bytes. Every call leaves the whole
+    workspace zero again, so one workspace serves calls of any shape in turn; calls that
+    may overlap need separate workspaces."""
     torch = _torch()
     _need(values_t, "values_t", torch.float16)
     _need(meta_t, "meta_t", torch.uint8)

@@ -278,12 +278,8 @@ static hipError_t launch_sddmm_cfg1(const uint16_t* q, const uint16_t* k, int64_
   const int64_t qblocks = (Lq + Cfg::kQueries - 1) / Cfg::kQueries;
   const dim3 grid((unsigned)qblocks, (unsigned)(batch < 65535 ? batch : 65535));
   auto kern = k_sddmm_prune<D, QT, DENSE, RMAX, BF>;
-  static bool attr_set = false;   // benign race: every caller sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit(lds_set, (const void*)kern, Cfg::kLds)) return e;
   hipLaunchKernelGGL(kern, grid, dim3(64 * Cfg::kWaves), Cfg::kLds, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax);
   return hipGetLastError();
 }

@@ -533,13 +533,8 @@ hipError_t launch_spmm_bitmap(const uint64_t* bitmaps, const uint32_t* offsets, 
   const size_t lds = (size_t)kBitmapLds;   // 77 KiB: two workgroups per CU
   const dim3 blk(64 * kBmWaves);
   auto go = [&](auto kern) -> hipError_t {
-    static bool set[2][2] = {};
-    bool& done = set[C > 16][b_layout == 1];
-    if (!done) {
-      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      done = true;
-    }
+    static std::atomic<uint64_t> lds_set[2][2] = {};
+    if (hipError_t e = ensure_lds_limit(lds_set[C > 16][b_layout == 1], (const void*)kern, (int)lds)) return e;
     hipLaunchKernelGGL(kern, dim3(g), blk, lds, stream, a);
     return hipGetLastError();
   };

@@ -451,13 +451,8 @@ hipError_t launch_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t 
     const int64_t nchunks = (G + GL - 1) / GL;
     const int64_t blocks = (R / V) * nchunks;
     const size_t lds = (size_t)V * GL * M * 2 + (size_t)GL * M * (8 + 1) + (size_t)GL * 4;   // tile, score, sel, keep
-    static bool attr_set = false;   // benign race: every caller sets the same value
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)k_prune_encode_vnm_lds,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = ensure_lds_limit(lds_set, (const void*)k_prune_encode_vnm_lds, 96 * 1024)) return e;
     hipLaunchKernelGGL(k_prune_encode_vnm_lds, dim3((unsigned)blocks), dim3(kVnmThreads), lds, stream,
                        (const uint16_t*)A, R, K, lda, V, M, GL, (uint16_t*)values, (uint16_t*)midx,
                        (uint8_t*)colloc, (int)tiled);

@@ -5,7 +5,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace snm {
+
+// Raises a kernel's dynamic-LDS limit on the current device, once per device: `done` is the
+// launch site's record, bit d for device d (the entry points accept devices 0..63 only).
+// hipFuncSetAttribute acts on the current device, so every device a kernel runs on gets its
+// own call. Two threads that reach a device's first launch together both set the same
+// value, which is harmless; the bit is published only after the call succeeded.
+inline hipError_t ensure_lds_limit(std::atomic<uint64_t>& done, const void* kern, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const uint64_t bit = (uint64_t)1 << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  done.fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
 
 hipError_t launch_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda, void* values,
                                   void* meta, hipStream_t stream);

@@ -345,12 +345,8 @@ static hipError_t launch_cfg(SpmmArgs a, hipStream_t stream) {
   if (tiles == 0 || a.batch == 0) return hipSuccess;
   const unsigned gy = (unsigned)(a.batch < 65535 ? a.batch : 65535);
   auto kern = k_spmm<WM, WN, WK, TM, TN, KSUB, GATHER, BCOL, ATILED>;
-  static bool attr_set = false;   // benign race: every thread sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit(lds_set, (const void*)kern, Cfg::kLds)) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles, gy), dim3(Cfg::kThreads), Cfg::kLds, stream, a);
   return hipGetLastError();
 }

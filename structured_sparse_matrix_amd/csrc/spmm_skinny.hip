@@ -293,13 +293,8 @@ static hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
   const size_t red = (size_t)nw * Cfg::CT * 64 * 16;
   const size_t lds = btile + mtile > red ? btile + mtile : red;
   auto kern = k_spmm_skinny<CP, KSUB, ATILED, BCOL, BVEC>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit(lds_set, (const void*)kern, 160 * 1024)) return e;
   const unsigned gx = (unsigned)((a.R + 15) / 16);
   const unsigned gy = (unsigned)(a.batch < 65535 ? a.batch : 65535);
   hipLaunchKernelGGL(kern, dim3(gx, gy), dim3(64 * nw), lds, stream, a);

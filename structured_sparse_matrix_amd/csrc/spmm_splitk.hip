@@ -20,6 +20,10 @@
 //     itself in on the row group's counter; the workgroup that arrives last reads the S
 //     tiles back, adds them in split order (so the result does not depend on the arrival
 //     order), writes Y and sets the counter back to zero.
+//   * the last workgroup also zeroes the S partial tiles it consumed, so a call leaves the
+//     whole workspace zero. Where the counters end and the partial tiles begin depends on
+//     the shape; without this, a later call of another shape on the same workspace would
+//     take stale partial sums for its counters.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "validate.hpp"
@@ -174,8 +178,11 @@ k_spmm_nm_splitk(SplitArgs a) {
     const int e = tid + j * 64 * NW;
     if (e >= kTile) continue;
     float t = 0.f;
-    for (int ss = 0; ss < a.S; ++ss)
-      t += ss == s ? v[j] : a.part[((int64_t)ss * a.G + g) * kTile + e];
+    for (int ss = 0; ss < a.S; ++ss) {
+      float* p = a.part + ((int64_t)ss * a.G + g) * kTile + e;
+      t += ss == s ? v[j] : *p;
+      *p = 0.f;   // every byte a call writes is zero again when it ends (see below)
+    }
     v[j] = t;
   }
   if (tid == 0) __hip_atomic_store(a.count + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -197,13 +204,8 @@ static hipError_t launch_splitk(const SplitArgs& a, hipStream_t stream) {
   constexpr int nw = kSplitWaves;
   const size_t lds = (size_t)nw * RT * (CP / 16) * 64 * 16;
   auto kern = k_spmm_nm_splitk<CP, RT, U, nw, BVEC>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit(lds_set, (const void*)kern, (int)lds)) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)a.G, (unsigned)a.S), dim3(64 * nw), lds, stream, a);
   return hipGetLastError();
 }

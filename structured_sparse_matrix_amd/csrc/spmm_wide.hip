@@ -500,12 +500,8 @@ hipError_t launch_wide(WideArgs a, hipStream_t stream) {
   const size_t lds = ring > (size_t)Cfg::kOut ? ring : (size_t)Cfg::kOut;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = k_spmm_wide<WM, WN, TM, TN, KSTEPS, NST, GATHER, SMAX, PIPE, BF>;
-  static bool attr_set = false;   // benign race: every caller sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit(lds_set, (const void*)kern, 160 * 1024)) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(Cfg::kThreads), lds, stream, a);
   return hipGetLastError();
 }

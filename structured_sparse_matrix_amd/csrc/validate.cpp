@@ -3,6 +3,8 @@
 
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "snm.h"
 
 namespace snm {

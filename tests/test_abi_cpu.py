@@ -349,3 +349,30 @@ def test_empty_reduction_strides_carry_no_alignment_rule():
     # stops at the device check (SNM_E_DEVICE), with one it writes zeros (GPU test)
     st = lib.snm_spmm_nm(FAKE, FAKE, 40, 0, FAKE, 8, 8, 0, FAKE, 8, 2, 40, 40, 0, 320, P(0))
     assert st in (0, 5)
+
+
+def test_validation_unit_builds_with_the_host_compiler(tmp_path):
+    # validate.cpp is HIP-free: it must compile with a plain host compiler (where it can be
+    # built with host sanitizers), warnings treated as errors
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    src = os.path.join(ROOT, "structured_sparse_matrix_amd", "csrc", "validate.cpp")
+    out = subprocess.run([gxx, "-std=c++17", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                          "-c", src, "-o", str(tmp_path / "validate.o")], capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr
+
+
+def test_split_workspace_is_bounded():
+    # the split reduction keeps about 256 workgroups with at most 4 splits, so S * groups
+    # < 512 tiles of at most 8 KiB, plus 1 KiB of counters, whatever the shape
+    from structured_sparse_matrix_amd import spmm_nm_tiled_ws_bytes
+    _lib()
+    worst = 0
+    for R in [16 * t for t in (1, 63, 64, 255, 256, 257, 1020, 1021, 4096)] + [12288, 16320, 16384, 1 << 20]:
+        for K in (1984, 2048, 4096, 14336, 1 << 20):
+            for C in (1, 16, 17, 32):
+                worst = max(worst, spmm_nm_tiled_ws_bytes(R, K, C))
+    assert 0 < worst <= (4 << 20) + 1024

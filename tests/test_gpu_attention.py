@@ -60,13 +60,33 @@ def _layered_sddmm_checks(Q, K, scale, values, meta, S_gpu, what):
 
 
 @pytest.mark.parametrize("b,lq,lk,d", [(1, 32, 32, 64), (2, 100, 64, 64), (3, 257, 96, 16),
-                                       (2, 64, 128, 32), (1, 40, 64, 128), (2, 512, 512, 64)])
+                                       (2, 64, 128, 32), (1, 40, 64, 128), (2, 512, 512, 64),
+                                       # full key length (128 key tiles: four metadata lines
+                                       # of 32 tiles per row) and a ragged one (33 tiles)
+                                       (1, 64, 4096, 64), (1, 48, 1056, 64)])
 def test_sddmm_prune_layered(b, lq, lk, d):
     snm = _snm()
     Q, K, _ = _qkv(b * 1000 + lq + lk + d, b, lq, lk, d)
     scale = 1.0 / np.sqrt(d)
     v, m, S = snm.sddmm_prune_nm(to_dev(Q), to_dev(K), scale, return_dense=True)
     _layered_sddmm_checks(Q, K, scale, to_host(v), to_host(m), to_host(S), f"{b}x{lq}x{lk}x{d}")
+
+
+def test_sddmm_prune_workload_layered_full_length():
+    # The attention workload itself (batch 4 x 16 heads, seq 4096, head_dim 64, fp16): the
+    # SDDMM runs over all 64 slices with the pre-prune scores kept; two slices get every
+    # layered check (legal codes, bit-exact 2:4 of the GPU's own scores, scores within the
+    # fp16 bars, selection valid for the oracle's float64 scores) and the count of groups
+    # whose selection differs from the oracle's is reported.
+    snm = _snm()
+    w = workloads.WORKLOADS["attention_2_4"]
+    Q, K, _ = workloads.attention_qkv(w)
+    scale = 0.125
+    v, m, S = snm.sddmm_prune_nm(to_dev(Q), to_dev(K), scale, return_dense=True)
+    for h in (0, 37):
+        differ = _layered_sddmm_checks(Q[h:h + 1], K[h:h + 1], scale, to_host(v[h:h + 1]),
+                                       to_host(m[h:h + 1]), to_host(S[h:h + 1]), f"slice {h}")
+        print(f"slice {h}: {differ} of {4096 * 1024} groups select differently from the oracle", flush=True)
 
 
 def test_sddmm_identity_keys_exact():

@@ -1,8 +1,8 @@
 """GPU parity of the split-reduction decode product (snm_spmm_nm_tiled_ws) against the
 float64 oracle: shapes with and without a split, ragged rows and columns, unaligned B
 columns, the empty reduction, the full 4096 x 4096 decode workload, and reuse of one
-workspace across calls (the counters must come back to zero, the result must not depend
-on which split arrives last)."""
+workspace across calls of different shapes (every call must leave the whole workspace
+zero, the result must not depend on which split arrives last).""" 
 import ctypes
 
 import numpy as np
@@ -51,7 +51,7 @@ def _run(A, X, ws=None, ldb_pad=0):
     (64, 2048, 32),    # 2 groups of 2 row tiles, 2 splits
     (4100, 8192, 24),  # 65 groups of 4 row tiles (the last partial), 4 splits
     (200, 4096, 24),   # 2 row tiles, 4 splits, 24 of 32 columns
-    (1000, 8192, 32),  # 8 splits
+    (1000, 8192, 32),  # 32 groups of 2 row tiles; 8 splits would fill the grid, the plan caps them at 4
     (17, 3072, 12),    # one partial row group
 ])
 def test_spmm_ws_matches_oracle(R, K, C):
@@ -142,3 +142,25 @@ def test_spmm_ws_two_streams_separate_workspaces():
         torch.cuda.synchronize()
         for i in range(2):
             assert np.array_equal(to_host(outs[i]).view(np.uint16), ref[i]), f"rep {rep}, stream {i}"
+
+
+def test_spmm_ws_reuse_across_plans_leaves_workspace_zero():
+    # Regression: where the counters end and the partial tiles begin depends on the plan
+    # (4096 x 14336, N = 32: counters in bytes [0, 256), partials from 256; 3072 x 4096,
+    # N = 8: counters in [0, 512)). One workspace serves both shapes in turn; Y starts
+    # filled with a marker, and after every call the whole workspace must be zero again.
+    import torch
+    snm = _snm()
+    shapes = ((4096, 14336, 32), (3072, 4096, 8), (4096, 14336, 32), (1000, 8192, 32))
+    nbytes = max(snm.spmm_nm_tiled_ws_bytes(r, k, c) for r, k, c in shapes)
+    assert snm.spmm_nm_tiled_ws_bytes(3072, 4096, 8) > 0 and snm.spmm_nm_tiled_ws_bytes(4096, 14336, 32) > 0
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
+    for i, (R, K, C) in enumerate(shapes):
+        A = workloads.small_matrix(300 + i, (R, K), 0.02)
+        X = workloads.small_matrix(400 + i, (C, K))
+        vt, mt = snm.prune_encode_nm_tiled(to_dev(A))
+        out = torch.full((R, C), 7.0, dtype=torch.float16, device="cuda")
+        Y = snm.spmm_nm_tiled_ws(vt, mt, R, to_dev(X), ws, out=out)
+        ov, om = oracle.prune_encode_nm(A)
+        assert_fp16_close(to_host(Y), oracle.spmm_nm(ov, om, np.ascontiguousarray(X.T)), f"call {i}: {R}x{K}x{C}")
+        assert not to_host(ws).any(), f"call {i} ({R}x{K}x{C}) left non-zero bytes in the workspace"

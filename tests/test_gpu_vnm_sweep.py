@@ -84,3 +84,35 @@ def test_sweep_full_size(family, V, M):
     rows = np.unique(np.concatenate([np.sort(rng.choice(R, 96, replace=False)), [0, V - 1, V, R - 1]]))
     dense = oracle.decode_vnm(ov, omi, ocl, V, M, K)[rows].astype(np.float64)
     assert_fp16_close(Y[rows], dense @ B.astype(np.float64), f"{family} {R}x{K}x{C} V{V} M{M} sampled rows")
+
+
+def test_sweep_gpt3_layer_m8():
+    # The larger problem the pages repeat the ablation on (36864 x 12288 x 4096, V = 128,
+    # 2:8; column-loc of a V-block is 6144 bytes, the largest any test stages): the whole
+    # encoding bit for bit (compared 32 V-blocks at a time), then 96 sampled output rows
+    # and the first/last rows of V-blocks (every column) against the oracle's product, on
+    # both storages (canonical and row-group interleaved).
+    snm = _snm()
+    (_, R, K, C, V, M), = [p for p in workloads.vnm_sweep() if p[0] == "gpt3" and p[5] == 8]
+    rng = np.random.default_rng(7777)
+    A = workloads.normal_f16(rng, (R, K), 0.02)
+    B = workloads.normal_f16(rng, (K, C), 1.0)
+    Ad, Bd = to_dev(A), to_dev(B)
+    v, mi, cl = snm.prune_encode_vnm(Ad, V, M)
+    Y = to_host(snm.spmm_vnm(v, mi, cl, Bd, V, M))
+    vt, mit, clt = snm.prune_encode_vnm_tiled(Ad, V, M)
+    Yt = to_host(snm.spmm_vnm_tiled(vt, mit, clt, Bd, V, M))
+    del Ad
+    v, mi, cl = to_host(v), to_host(mi), to_host(cl)
+    assert_bits_equal(to_host(clt), cl, "colloc of the interleaved encode")
+    step = 32 * V
+    for r0 in range(0, R, step):
+        ov, omi, ocl = oracle.prune_encode_vnm(A[r0:r0 + step], V, M)
+        assert_bits_equal(cl[r0 // V:(r0 + step) // V], ocl, f"colloc rows {r0}+")
+        assert_bits_equal(mi[r0:r0 + step], omi, f"midx rows {r0}+")
+        assert_bits_equal(v[r0:r0 + step], ov, f"values rows {r0}+")
+    rows = np.unique(np.concatenate([np.sort(rng.choice(R, 96, replace=False)), [0, V - 1, V, R - V, R - 1]]))
+    dense = oracle.decode_vnm(v[rows], mi[rows], np.repeat(cl, V, axis=0)[rows], 1, M, K).astype(np.float64)
+    ref = dense @ B.astype(np.float64)
+    assert_fp16_close(Y[rows], ref, f"gpt3 {R}x{K}x{C} V{V} M{M} sampled rows")
+    assert_fp16_close(Yt[rows], ref, f"gpt3 {R}x{K}x{C} V{V} M{M} sampled rows, interleaved storage")
