@@ -163,6 +163,23 @@ int snm_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, in
                          const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
                          void* workspace, int64_t workspace_bytes, void* stream);
 
+/* snm_spmm_nm_tiled_ws for callers that cannot allocate device memory: code recorded
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * product, kernels and result bits as snm_spmm_nm_tiled_ws, with no workspace argument:
+ * the split reduction's partial sums and counters live in a scratch array the library
+ * holds on each device (4 MiB + 4 KiB, a static device array of the library, kept until
+ * the process ends; every split plan fits it, a larger one would return
+ * SNM_E_UNSUPPORTED). The call allocates and frees nothing. On its first use on a device
+ * it looks the array up and enqueues one kernel on `stream` that zeroes it; every call
+ * leaves the array zero again.
+ * Concurrency: every call on one device shares that device's array, so calls that may
+ * overlap on one device (other streams, other host threads) race and give wrong results;
+ * serialise them, or use snm_spmm_nm_tiled_ws with a workspace per stream.
+ * Arguments, layouts and requirements as snm_spmm_nm_tiled_ws without the workspace. */
+int snm_spmm_nm_tiled_noalloc(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                              const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                              void* stream);
+
 /* Y = decode_vnm(values, midx, colloc) * B (VENOM Sec. 4 and Fig. 4: per block of V rows
  * the K/M*4 rows of B named by colloc are gathered, then 2:4 is applied with midx).
  *   values, midx, colloc  V:2:M arrays of an R x K matrix (canonical layout).

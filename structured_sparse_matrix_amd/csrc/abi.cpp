@@ -125,6 +125,16 @@ int snm_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, in
                                                    workspace, (hipStream_t)stream));
 }
 
+int snm_spmm_nm_tiled_noalloc(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                              const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
+                              void* stream) {
+  int s = snm::check_spmm_nm_tiled_noalloc(values_t, meta_t, R, K, B, C, ldb, Y, ldy);
+  if (s != SNM_OK || R == 0 || C == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_spmm_nm_tiled_splitk_noalloc(values_t, meta_t, R, K, B, C, ldb, Y, ldy,
+                                                           (hipStream_t)stream));
+}
+
 int snm_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
                          void* values, void* midx, void* colloc, void* stream) {
   int s = snm::check_prune_encode_vnm(A, R, K, lda, V, M, values, midx, colloc);

@@ -38,6 +38,10 @@ hipError_t launch_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_
 hipError_t launch_spmm_nm_tiled_splitk(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                                        const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
                                        void* workspace, hipStream_t stream);
+// the same product with the library's own per-device scratch as the workspace
+hipError_t launch_spmm_nm_tiled_splitk_noalloc(const void* values_t, const void* meta_t, int64_t R,
+                                               int64_t K, const void* B, int64_t C, int64_t ldb,
+                                               void* Y, int64_t ldy, hipStream_t stream);
 hipError_t launch_spmm_nm_tiled_skinny(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                                        const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                                        int64_t ldy, hipStream_t stream);

@@ -28,6 +28,9 @@
 #include "launch.hpp"
 #include "validate.hpp"
 
+#include <atomic>
+#include <mutex>
+
 namespace snm {
 
 namespace {
@@ -197,6 +200,51 @@ k_spmm_nm_splitk(SplitArgs a) {
   }
 }
 
+// ---- the no-allocation variant's scratch ----------------------------------------------
+// One array per device for the split reduction's counters and partial tiles, used by
+// snm_spmm_nm_tiled_noalloc instead of a caller's workspace. In host code `scratch` names
+// a host-side stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kSplitScratchBytes];
+
+__global__ void __launch_bounds__(256) k_zero_scratch(u4* p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = u4{0u, 0u, 0u, 0u};
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+std::atomic<uint64_t> g_scratch_ready{0};   // bit d: device d's address is known and its
+                                            // zero fill has been enqueued
+
+// Device address of the current device's scratch. The first call on a device looks the
+// array up and enqueues a fill kernel on `stream` (a kernel, not a memset, so that it can
+// also be recorded into a graph) ahead of the caller's work; split calls then leave every
+// byte they write zero, so the array stays zero between calls.
+hipError_t scratch_of_current_device(void** out, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const uint64_t bit = (uint64_t)1 << dev;
+  if (!(g_scratch_ready.load(std::memory_order_acquire) & bit)) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!(g_scratch_ready.load(std::memory_order_relaxed) & bit)) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr || ((uintptr_t)p & 255u) != 0) return hipErrorInvalidSymbol;
+      hipLaunchKernelGGL(k_zero_scratch, dim3(256), dim3(256), 0, stream, (u4*)p,
+                         (int64_t)(kSplitScratchBytes / 16));
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      g_scratch_ptr[dev] = p;
+      g_scratch_ready.fetch_or(bit, std::memory_order_release);
+    }
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 template <int CP, int RT, int U, bool BVEC>
@@ -238,6 +286,19 @@ hipError_t launch_spmm_nm_tiled_splitk(const void* values_t, const void* meta_t,
   if (p.cp == 16)
     return a.b_vec ? launch_splitk<16, 2, 2, true>(a, stream) : launch_splitk<16, 2, 2, false>(a, stream);
   return a.b_vec ? launch_splitk<32, 2, 2, true>(a, stream) : launch_splitk<32, 2, 2, false>(a, stream);
+}
+
+hipError_t launch_spmm_nm_tiled_splitk_noalloc(const void* values_t, const void* meta_t, int64_t R,
+                                               int64_t K, const void* B, int64_t C, int64_t ldb,
+                                               void* Y, int64_t ldy, hipStream_t stream) {
+  const SplitPlan p = splitk_plan(R, K, C);
+  void* ws = nullptr;
+  if (p.splits >= 2) {   // the unsplit kernel needs no scratch
+    if (p.workspace_bytes > kSplitScratchBytes) return hipErrorInvalidValue;
+    hipError_t e = scratch_of_current_device(&ws, stream);
+    if (e != hipSuccess) return e;
+  }
+  return launch_spmm_nm_tiled_splitk(values_t, meta_t, R, K, B, C, ldb, Y, ldy, ws, stream);
 }
 
 }  // namespace snm

@@ -319,4 +319,17 @@ int check_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, 
   return SNM_OK;
 }
 
+int check_spmm_nm_tiled_noalloc(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                                const void* B, int64_t C, int64_t ldb, const void* Y, int64_t ldy) {
+  int s = check_spmm_nm(values_t, meta_t, R, K, B, C, ldb, 1, Y, ldy, 1, 0, 0, 0, 0);
+  if (s != SNM_OK) return s;
+  if (C > 32) return SNM_E_UNSUPPORTED;
+  if (R == 0 || C == 0) return SNM_OK;
+  if ((R + 15) / 16 > ((int64_t)1 << 31)) return SNM_E_SHAPE;
+  // never taken for a plan of splitk_plan; kept so that a change of the plan cannot
+  // overrun the fixed scratch
+  if (splitk_plan(R, K, C).workspace_bytes > kSplitScratchBytes) return SNM_E_UNSUPPORTED;
+  return SNM_OK;
+}
+
 }  // namespace snm

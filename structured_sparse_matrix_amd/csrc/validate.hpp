@@ -66,5 +66,11 @@ SplitPlan splitk_plan(int64_t R, int64_t K, int64_t C);
 int check_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                            const void* B, int64_t C, int64_t ldb, const void* Y, int64_t ldy,
                            const void* workspace, int64_t workspace_bytes);
+// Size of the device-resident scratch of snm_spmm_nm_tiled_noalloc. A split plan keeps
+// about 256 workgroups with at most 4 splits, so splits x groups < 512 partial tiles of at
+// most 8 KiB, plus at most 1 KiB of counters: every plan fits.
+constexpr int64_t kSplitScratchBytes = ((int64_t)4 << 20) + 4096;
+int check_spmm_nm_tiled_noalloc(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+                                const void* B, int64_t C, int64_t ldb, const void* Y, int64_t ldy);
 
 }  // namespace snm

@@ -249,6 +249,11 @@ def test_spmm_ws_plan_and_validation():
     assert lib.snm_spmm_nm_tiled_ws(FAKE, FAKE, 64, 2048, FAKE, 32, 2040, FAKE, 32, FAKE, need, P(0)) == 2  # ldb < K
     assert lib.snm_spmm_nm_tiled_ws(FAKE, FAKE, 64, 2048, FAKE, 32, 2048, FAKE, 32, FAKE, -1, P(0)) == 2
     assert lib.snm_spmm_nm_tiled_ws(P(0), P(0), 0, 2048, P(0), 32, 2048, P(0), 32, P(0), 0, P(0)) == 0    # R == 0
+    # the no-allocation variant: the same checks without the workspace
+    assert lib.snm_spmm_nm_tiled_noalloc(FAKE, FAKE, 64, 2048, FAKE, 40, 2048, FAKE, 40, P(0)) == 4
+    assert lib.snm_spmm_nm_tiled_noalloc(FAKE, FAKE, 64, 2048, FAKE, 32, 2040, FAKE, 32, P(0)) == 2  # ldb < K
+    assert lib.snm_spmm_nm_tiled_noalloc(P(0), FAKE, 64, 2048, FAKE, 32, 2048, FAKE, 32, P(0)) == 1
+    assert lib.snm_spmm_nm_tiled_noalloc(P(0), P(0), 0, 2048, P(0), 32, 2048, P(0), 32, P(0)) == 0    # R == 0
 
 
 def test_softmax_validation():
