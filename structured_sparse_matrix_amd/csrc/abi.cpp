@@ -7,6 +7,7 @@
 
 #include "launch.hpp"
 #include "snm.h"
+#include "snm_ceilings.h"
 #include "validate.hpp"
 
 namespace {
@@ -341,6 +342,27 @@ int snm_softmax_nm_rows_bf16(void* values, int64_t rows, int64_t kept, int64_t l
   if (s != SNM_OK || rows == 0 || kept == 0) return s;
   if ((s = check_device()) != SNM_OK) return s;
   return launched(snm::launch_softmax_nm_rows(values, rows, kept, ld, true, (hipStream_t)stream));
+}
+
+int snm_ceiling_read(const void* src, int64_t bytes, void* sink, void* stream) {
+  int s = snm::check_ceiling_stream(src, sink, bytes);
+  if (s != SNM_OK || bytes == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_ceiling_read(src, bytes, sink, (hipStream_t)stream));
+}
+
+int snm_ceiling_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  int s = snm::check_ceiling_stream(src, dst, bytes);
+  if (s != SNM_OK || bytes == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_ceiling_copy(src, dst, bytes, (hipStream_t)stream));
+}
+
+int snm_ceiling_matrix(int kind, int64_t workgroups, int64_t iters, float* out, void* stream) {
+  int s = snm::check_ceiling_matrix(kind, workgroups, iters, out);
+  if (s != SNM_OK || workgroups == 0) return s;
+  if ((s = check_device()) != SNM_OK) return s;
+  return launched(snm::launch_ceiling_matrix(kind, workgroups, iters, out, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,124 @@
+// Measured ceilings of the device: the rates that bound this library's kernels with no
+// algorithm around them, so that each kernel's achieved rate can be reported against what
+// the same chip sustains, beside the published peaks.
+//
+//   * k_ceiling_read / k_ceiling_copy: STREAM-style streams of 16-byte coalesced accesses,
+//     four independent loads in flight per lane per iteration, grid-stride. A read over a
+//     working set as large as one decode product shows what a kernel of that size can
+//     reach (launch ramp, loaded latency and tail included); a read over 1 GiB shows the
+//     sustained HBM rate.
+//   * k_ceiling_matrix<SPARSE>: each wave issues independent chains of one matrix
+//     instruction on register-resident operands, no memory traffic: the issue rate of
+//     v_smfmac_f32_32x32x32_f16 (SPARSE; counted as 2*32*32*32 flops, the dense equivalent
+//     of the 2:4 product, as the sparse peak counts it) or of v_mfma_f32_32x32x16_f16
+//     (2*32*32*16 flops).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace snm {
+namespace {
+
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 4;
+
+__global__ void __launch_bounds__(kStreamThreads) k_ceiling_read(const u4* __restrict__ src, int64_t n16,
+                                                                 u4* __restrict__ sink) {
+  u4 acc = {0u, 0u, 0u, 0u};
+  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+  for (; i + (kStreamUnroll - 1) * stride < n16; i += kStreamUnroll * stride) {
+    u4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u];
+  }
+  for (; i < n16; i += stride) acc ^= src[i];
+  // a store no input can trigger in practice keeps the loads alive
+  if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u && acc.z == 0xF39CC060u && acc.w == 0x5CEDC834u)
+    sink[0] = acc;
+}
+
+__global__ void __launch_bounds__(kStreamThreads) k_ceiling_copy(const u4* __restrict__ src, u4* __restrict__ dst,
+                                                                 int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+  for (; i + (kStreamUnroll - 1) * stride < n16; i += kStreamUnroll * stride) {
+    u4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) dst[i + u * stride] = v[u];
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+constexpr int kChains = 4;   // independent accumulator chains per wave
+
+template <bool SPARSE>
+__global__ void __launch_bounds__(256) k_ceiling_matrix(int64_t iters, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  // operands that depend on the lane, so nothing folds; finite small values
+  h8 a;
+  h16 b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = (_Float16)((float)((lane + e) & 7) * 0.125f);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) b[e] = (_Float16)((float)((lane * 3 + e) & 7) * 0.0625f);
+  const uint32_t idx = 0x4E4E4E4Eu;   // legal 2:4 codes 0xe and 0x4 in every group
+  f16v acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+      if constexpr (SPARSE)
+        acc[c] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(a, b, acc[c], (int)idx, 0, 0);
+      else
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_shufflevector(b, b, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                        acc[c], 0, 0, 0);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[c][e];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+unsigned stream_grid(int64_t n16) {
+  // enough workgroups for every CU to hold several (256 CUs), capped so that each lane
+  // runs a few unrolled iterations
+  int64_t g = (n16 + kStreamThreads * kStreamUnroll - 1) / (kStreamThreads * kStreamUnroll);
+  if (g > 4096) g = 4096;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_ceiling_read(const void* src, int64_t bytes, void* sink, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  hipLaunchKernelGGL(k_ceiling_read, dim3(stream_grid(n16)), dim3(kStreamThreads), 0, stream,
+                     (const u4*)src, n16, (u4*)sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  hipLaunchKernelGGL(k_ceiling_copy, dim3(stream_grid(n16)), dim3(kStreamThreads), 0, stream,
+                     (const u4*)src, (u4*)dst, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_ceiling_matrix(int sparse, int64_t workgroups, int64_t iters, float* out, hipStream_t stream) {
+  if (sparse)
+    hipLaunchKernelGGL(k_ceiling_matrix<true>, dim3((unsigned)workgroups), dim3(256), 0, stream, iters, out);
+  else
+    hipLaunchKernelGGL(k_ceiling_matrix<false>, dim3((unsigned)workgroups), dim3(256), 0, stream, iters, out);
+  return hipGetLastError();
+}
+
+}  // namespace snm

@@ -102,6 +102,10 @@ hipError_t launch_bitmap_values(const void* A, int64_t R, int64_t K, int64_t lda
 hipError_t launch_spmm_bitmap(const uint64_t* bitmaps, const uint32_t* offsets, const void* values,
                               int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb,
                               int b_layout, void* Y, int64_t ldy, hipStream_t stream);
+// Measured ceilings (ceilings.hip): plain streams and matrix-instruction issue loops.
+hipError_t launch_ceiling_read(const void* src, int64_t bytes, void* sink, hipStream_t stream);
+hipError_t launch_ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+hipError_t launch_ceiling_matrix(int sparse, int64_t workgroups, int64_t iters, float* out, hipStream_t stream);
 hipError_t launch_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, bool bf16,
                                   hipStream_t stream);
 // 1:2 attention on fp32 scores (attention_f32.hip).

@@ -332,4 +332,21 @@ int check_spmm_nm_tiled_noalloc(const void* values_t, const void* meta_t, int64_
   return SNM_OK;
 }
 
+int check_ceiling_stream(const void* src, const void* dst, int64_t bytes) {
+  if (bytes < 0 || bytes % 16 != 0) return SNM_E_SHAPE;
+  if (bytes == 0) return SNM_OK;
+  if (!src || !dst) return SNM_E_NULL;
+  if (((uintptr_t)src & 15u) != 0 || ((uintptr_t)dst & 15u) != 0) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
+int check_ceiling_matrix(int kind, int64_t workgroups, int64_t iters, const void* out) {
+  if (kind != 0 && kind != 1) return SNM_E_UNSUPPORTED;
+  if (workgroups < 0 || workgroups > 0x7FFFFFFF || iters < 0) return SNM_E_SHAPE;
+  if (workgroups == 0) return SNM_OK;
+  if (!out) return SNM_E_NULL;
+  if (((uintptr_t)out & 3u) != 0) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
 }  // namespace snm

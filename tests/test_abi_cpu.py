@@ -7,7 +7,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "snm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _lib():
@@ -18,7 +19,7 @@ def _lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(snm_[a-z0-9_]+)\s*\(", text)))
 
@@ -381,3 +382,19 @@ def test_split_workspace_is_bounded():
             for C in (1, 16, 17, 32):
                 worst = max(worst, spmm_nm_tiled_ws_bytes(R, K, C))
     assert 0 < worst <= (4 << 20) + 1024
+
+
+def test_ceiling_validation():
+    lib = _lib()
+    # src, bytes, sink, stream
+    assert lib.snm_ceiling_read(FAKE, 100, FAKE, P(0)) == 2            # bytes % 16
+    assert lib.snm_ceiling_read(P(0), 1024, FAKE, P(0)) == 1
+    assert lib.snm_ceiling_read(MISALIGNED, 1024, FAKE, P(0)) == 3
+    assert lib.snm_ceiling_read(P(0), 0, P(0), P(0)) == 0
+    assert lib.snm_ceiling_copy(FAKE, MISALIGNED, 1024, P(0)) == 3
+    assert lib.snm_ceiling_copy(FAKE, FAKE, -16, P(0)) == 2
+    # kind, workgroups, iters, out, stream
+    assert lib.snm_ceiling_matrix(2, 8, 8, FAKE, P(0)) == 4
+    assert lib.snm_ceiling_matrix(1, -1, 8, FAKE, P(0)) == 2
+    assert lib.snm_ceiling_matrix(0, 8, 8, P(0), P(0)) == 1
+    assert lib.snm_ceiling_matrix(1, 0, 8, P(0), P(0)) == 0
