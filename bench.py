@@ -1475,7 +1475,7 @@ def main():
                    "rotating_copies": HEADLINE_ROT, "streams": args.streams, "windows": args.windows,
                    "value_basis": "dense-equivalent flops 2*R*K*C of the product per step / median window "
                                   "time per step (encode + product)"},
-        "roofline": {"bound": "mfma", "kernel": "snm_spmm_vnm_tiled (k_spmm_wide, V:2:16 gather)",
+        "roofline": {"bound": "mfma", "kernel": "snm_spmm_vnm_tiled (k_spmm_vnm_big8, V:2:16 gather, 128x512 tiles)",
                      "achieved": mmk["smfmac_TFLOP/s"], "peak": SPARSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": mmk["sparse_mfma_frac"], "traffic": measured_vnm_traffic(),
                      "frac_of_measured_smfmac": mmk.get("frac_of_measured_smfmac"),

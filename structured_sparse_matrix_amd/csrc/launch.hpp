@@ -74,6 +74,12 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
                             void* Y, int64_t ldy, int64_t batch, int64_t stride_values,
                             int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
                             hipStream_t stream, bool a_tiled = false);
+// Large V:2:M products (spmm_vnm_big.hip): V % 128 == 0, K' = 4K/M a multiple of 128 in
+// [256, 12224], C >= 256, C % 8 == 0, 16-byte B rows. One workgroup per CU, 128 x 512 tiles.
+bool spmm_vnm_big_eligible(int64_t R, int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb);
+hipError_t launch_spmm_vnm_big(const void* values, const void* meta, const void* colloc, int64_t R,
+                               int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
+                               int64_t ldy, bool a_tiled, hipStream_t stream);
 // V:2:M product with values and m-indices in the row-group interleaved storage (wide
 // kernel only: V % 32 == 0 and the shape rules of spmm_wide_supported)
 hipError_t launch_spmm_vnm_tiled(const void* values_t, const void* midx_t, const void* colloc,

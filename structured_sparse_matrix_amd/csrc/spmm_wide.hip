@@ -556,6 +556,9 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
   // 128 x 256 tiles where they still give every CU two workgroups; 128 x 128 otherwise
   const bool wide_grid = a.batch * ((R + 127) / 128) * ((C + 255) / 256) >= 512;
   if (V > 0) {
+    // the large-tile kernel runs one workgroup per CU: only where its grid fills the chip
+    if (a.batch == 1 && spmm_vnm_big_eligible(R, Kc, V, M, B, C, ldb) && (R / 128) * ((C + 511) / 512) >= 256)
+      return launch_spmm_vnm_big(values, meta, colloc, R, Kc, V, M, B, C, ldb, Y, ldy, a_tiled, stream);
     if (V % 128 == 0) {
       if (C > 128 && wide_grid) return launch_wide<1, 4, 4, 2, 1, 3, true, false, false>(a, stream);   // 128 x 256
       return launch_wide<1, 4, 4, 1, 2, 3, true>(a, stream);                // 128 x 128

@@ -8,7 +8,7 @@
       that times the same kernel on G inputs one after the other).
 
   python -m structured_sparse_matrix_amd.profiling traffic --fetch FETCH_CSV --write WRITE_CSV
-         --match NAME --calibration-bytes N [--command CMD]
+         --match NAME --calibration-bytes N [--sources decode|wide] [--workload W] [--command CMD]
       HBM traffic per launch of the kernels whose name contains NAME, from two
       `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of the same program. Each
       counter is scaled by what it reads for the largest plain copy kernel (N bytes read
@@ -35,7 +35,8 @@ import statistics
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 DECODE_KERNEL_SOURCES = ("spmm_skinny.hip", "device_common.hpp")
-WIDE_KERNEL_SOURCES = ("spmm_wide.hip", "lds_dma.hpp", "wide_layout.hpp", "elem.hpp", "device_common.hpp")
+WIDE_KERNEL_SOURCES = ("spmm_wide.hip", "spmm_vnm_big.hip", "lds_dma.hpp", "wide_layout.hpp", "elem.hpp",
+                       "device_common.hpp")
 
 
 def kernel_source_hash(files=DECODE_KERNEL_SOURCES) -> str:
@@ -140,6 +141,9 @@ def main(argv=None):
     t.add_argument("--match", required=True)
     t.add_argument("--calibration-bytes", type=int, required=True)
     t.add_argument("--command", default="")
+    t.add_argument("--sources", choices=("decode", "wide"), default="decode",
+                   help="kernel sources whose hash is recorded: the decode or the wide products")
+    t.add_argument("--workload", default="")
     m = sub.add_parser("mfma")
     m.add_argument("counters")
     m.add_argument("--match", required=True)
@@ -162,7 +166,10 @@ def main(argv=None):
         print(json.dumps(out, indent=1))
     else:
         out = traffic(a.fetch, a.write, a.match, a.calibration_bytes)
-        out["kernel_source_hash"] = kernel_source_hash()
+        if a.workload:
+            out["workload"] = a.workload
+        out["kernel_source_hash"] = kernel_source_hash(
+            WIDE_KERNEL_SOURCES if a.sources == "wide" else DECODE_KERNEL_SOURCES)
         out["command"] = a.command
         print(json.dumps(out, indent=1))
 
