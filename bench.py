@@ -117,6 +117,17 @@ def cpu_baseline(min_seconds: float = 10.0) -> dict:
                       f"products with N=8,16,32 over the decoded matrix), {dt:.2f} s per step"}
 
 
+def _calibration_copy(dev):
+    """A plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(CALIBRATION_BYTES // 2, dtype=torch.float16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_copy: bool,
             nstreams: int = 2, submit: str = "eager"):
     import torch
@@ -126,13 +137,7 @@ def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_c
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if calibration_copy:
-        # a plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
-        src = torch.empty(CALIBRATION_BYTES // 2, dtype=torch.float16, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        _calibration_copy(dev)
     A0, Bs0 = workloads.weight_and_activations(workloads.WORKLOADS["nm_decode"])
     A0d = torch.from_numpy(A0).to(dev)
     B0d = [torch.from_numpy(b).to(dev) for b in Bs0]
@@ -324,7 +329,7 @@ def nm_decode_line(args) -> dict:
     return out
 
 
-def bench_other(workload: str, steps: int, warmup: int) -> dict:
+def bench_other(workload: str, steps: int, warmup: int, calibration_copy: bool = False) -> dict:
     """Per-kernel timings of the other workloads (not the headline line): each kernel is
     timed over K back-to-back launches with one HIP event pair."""
     import numpy as np
@@ -334,6 +339,8 @@ def bench_other(workload: str, steps: int, warmup: int) -> dict:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if calibration_copy:
+        _calibration_copy(dev)
     w = workloads.WORKLOADS[workload]
     nrot = 4
 
@@ -846,6 +853,9 @@ def measured_vnm_traffic():
     from structured_sparse_matrix_amd.profiling import kernel_source_hash, WIDE_KERNEL_SOURCES
     if s.get("kernel_source_hash") != kernel_source_hash(WIDE_KERNEL_SOURCES):
         return None
+    for g in s.get("groups", []):
+        if g.get("label") == "interleaved":
+            return g["bytes_per_launch_avg"]
     return s.get("bytes_per_launch_avg")
 
 
@@ -1445,7 +1455,7 @@ def main():
         print(json.dumps(nm_decode_line(args)))
         return
     if args.workload != "headline":
-        print(json.dumps(bench_other(args.workload, args.steps, args.warmup)))
+        print(json.dumps(bench_other(args.workload, args.steps, args.warmup, args.calibration_copy)))
         return
 
     res = run_headline(args)

@@ -285,10 +285,6 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
       copy(sx, cint<NX>{}, cint<0>{});
       copy(sx, cint<NX>{}, cint<1>{});
     }
-    if constexpr (ISSUE) {
-      copy(sx, cint<NX>{}, cint<0>{});
-      copy(sx, cint<NX>{}, cint<1>{});
-    }
     static_for<0, kPairs>([&](auto q) {
       constexpr int Q = decltype(q)::value;   // product pair: row tile Q / (TN / 2)
       constexpr int kRd = kPairs / 4;         // pairs per read part

@@ -1,14 +1,17 @@
 """Summaries of rocprofv3 output for the profiles/ folder.
 
   python -m structured_sparse_matrix_amd.profiling kernels TRACE_CSV [--match snm] [--skip N]
-         [--groups G]
+         [--groups G] [--alone]
       Markdown table of kernel dispatch durations (calls, mean, median, min, max) from a
       `rocprofv3 --kernel-trace -f csv` run. --groups G splits each kernel's dispatches, in
       dispatch order, into G equal consecutive groups reported as separate rows (a program
-      that times the same kernel on G inputs one after the other).
+      that times the same kernel on G inputs one after the other). --alone keeps only the
+      dispatches that overlapped no other dispatch (a program that also runs kernels
+      concurrently on several streams).
 
   python -m structured_sparse_matrix_amd.profiling traffic --fetch FETCH_CSV --write WRITE_CSV
-         --match NAME --calibration-bytes N [--sources decode|wide] [--workload W] [--command CMD]
+         --match NAME --calibration-bytes N [--sources decode|wide] [--groups G --labels L,..]
+         [--workload W] [--command CMD]
       HBM traffic per launch of the kernels whose name contains NAME, from two
       `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of the same program. Each
       counter is scaled by what it reads for the largest plain copy kernel (N bytes read
@@ -48,19 +51,37 @@ def kernel_source_hash(files=DECODE_KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def _durations(path, match, skip):
+def _alone(spans):
+    """Flags, per (start, end) span in dispatch order, whether no other span overlaps it."""
+    order = sorted(range(len(spans)), key=lambda i: spans[i][0])
+    flags = [True] * len(spans)
+    reach = None   # latest end among the spans that start earlier
+    for pos, i in enumerate(order):
+        b, e = spans[i]
+        if reach is not None and reach > b:
+            flags[i] = False
+        if pos + 1 < len(order) and spans[order[pos + 1]][0] < e:
+            flags[i] = False
+        reach = e if reach is None else max(reach, e)
+    return flags
+
+
+def _durations(path, match, skip, alone=False):
+    rows = list(csv.DictReader(open(path)))
+    spans = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    keep = _alone(spans) if alone else [True] * len(rows)
     by = {}
-    for r in csv.DictReader(open(path)):
+    for r, (b, e), k in zip(rows, spans, keep):
         name = r["Kernel_Name"]
-        if match and match not in name:
+        if not k or (match and match not in name):
             continue
-        by.setdefault(name, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        by.setdefault(name, []).append(e - b)
     return {k: v[skip:] if len(v) > skip else v for k, v in by.items()}
 
 
-def kernels_table(path, match, skip, groups=1):
+def kernels_table(path, match, skip, groups=1, alone=False):
     rows = ["| kernel | calls | mean us | median us | min us | max us |", "|---|---|---|---|---|---|"]
-    for name, ds in sorted(_durations(path, match, skip).items(), key=lambda kv: -sum(kv[1])):
+    for name, ds in sorted(_durations(path, match, skip, alone).items(), key=lambda kv: -sum(kv[1])):
         short = name if len(name) < 110 else name[:107] + "..."
         n = len(ds) // groups if groups > 1 and len(ds) % groups == 0 else len(ds)
         parts = [ds[i:i + n] for i in range(0, len(ds), n)]
@@ -80,7 +101,7 @@ def _counter_rows(path, counter):
     return out
 
 
-def traffic(fetch_csv, write_csv, match, calibration_bytes):
+def traffic(fetch_csv, write_csv, match, calibration_bytes, groups=1):
     fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
     write = _counter_rows(write_csv, "WRITE_SIZE")
     first = next(i for i, (_, n, _) in enumerate(fetch) if match in n)
@@ -93,7 +114,7 @@ def traffic(fetch_csv, write_csv, match, calibration_bytes):
     kw = [b / fw for _, n, b in write if match in n]
     n = min(len(kf), len(kw))
     per = [kf[i] + kw[i] for i in range(n)]
-    return {
+    out = {
         "kernel_match": match,
         "launches": n,
         "fetch_bytes_per_launch_avg": statistics.mean(kf[:n]),
@@ -102,6 +123,14 @@ def traffic(fetch_csv, write_csv, match, calibration_bytes):
         "calibration": {"bytes": calibration_bytes, "fetch_factor": ff, "write_factor": fw,
                         "fetch_kernel": calib_f[1][:80], "write_kernel": calib_w[1][:80]},
     }
+    if groups > 1 and n % groups == 0:
+        g = n // groups
+        out["groups"] = [{"launches": g,
+                          "fetch_bytes_per_launch_avg": statistics.mean(kf[i:i + g]),
+                          "write_bytes_per_launch_avg": statistics.mean(kw[i:i + g]),
+                          "bytes_per_launch_avg": statistics.mean(per[i:i + g])}
+                         for i in range(0, n, g)]
+    return out
 
 
 def mfma(csv_path, match, groups=1, cus=256, xcds=8):
@@ -135,6 +164,8 @@ def main(argv=None):
     k.add_argument("--match", default="")
     k.add_argument("--skip", type=int, default=0)
     k.add_argument("--groups", type=int, default=1)
+    k.add_argument("--alone", action="store_true",
+                   help="only dispatches that overlapped no other dispatch in time")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -144,6 +175,9 @@ def main(argv=None):
     t.add_argument("--sources", choices=("decode", "wide"), default="decode",
                    help="kernel sources whose hash is recorded: the decode or the wide products")
     t.add_argument("--workload", default="")
+    t.add_argument("--groups", type=int, default=1,
+                   help="split the matching dispatches, in order, into G equal groups")
+    t.add_argument("--labels", default="", help="comma-separated names of the groups")
     m = sub.add_parser("mfma")
     m.add_argument("counters")
     m.add_argument("--match", required=True)
@@ -155,7 +189,7 @@ def main(argv=None):
     m.add_argument("--command", default="")
     a = ap.parse_args(argv)
     if a.cmd == "kernels":
-        print(kernels_table(a.trace, a.match, a.skip, a.groups))
+        print(kernels_table(a.trace, a.match, a.skip, a.groups, a.alone))
     elif a.cmd == "mfma":
         out = mfma(a.counters, a.match, a.groups, a.cus, a.xcds)
         for g, lab in zip(out["groups"], [x for x in a.labels.split(",") if x]):
@@ -165,7 +199,9 @@ def main(argv=None):
         out["command"] = a.command
         print(json.dumps(out, indent=1))
     else:
-        out = traffic(a.fetch, a.write, a.match, a.calibration_bytes)
+        out = traffic(a.fetch, a.write, a.match, a.calibration_bytes, a.groups)
+        for g, lab in zip(out.get("groups", []), [x for x in a.labels.split(",") if x]):
+            g["label"] = lab
         if a.workload:
             out["workload"] = a.workload
         out["kernel_source_hash"] = kernel_source_hash(
