@@ -121,7 +121,7 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
   const uint32_t lds0 = lds_addr(smem);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
 
   // ---- tile (XCD-aware: the workgroups resident on one XCD share a column strip of B) ----
   int64_t L = blockIdx.x;
@@ -172,10 +172,20 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
   const uint8_t* meta = a.meta + row0 * mrow;
   const uint32_t ldb2 = (uint32_t)(a.ldb * 2);
 
-  int gcl[nB];   // column-loc bytes of the rows the next issue gathers
+  // column-loc bytes of the nB rows this wave gathers for the next stage it copies, four
+  // to a word (xrow0 is a multiple of 4). The word is read late in a stage and only used
+  // after the next barrier, which waits for every LDS read anyway: unpacking it earlier
+  // would make the wave wait for all of its operand reads in flight (LDS reads complete in
+  // order) in the middle of a stage.
+  static_assert(nB % 4 == 0, "whole words of column-loc");
+  uint32_t gw[nB / 4];
   auto fetch_colloc = [&](int64_t s) {
 #pragma unroll
-    for (int j = 0; j < nB; ++j) gcl[j] = smem[kRing + s * KS + xrow0 + j];
+    for (int w = 0; w < nB / 4; ++w) gw[w] = *reinterpret_cast<const uint32_t*>(smem + kRing + s * KS + xrow0 + 4 * w);
+  };
+  auto pin_colloc = [&]() {
+#pragma unroll
+    for (int w = 0; w < nB / 4; ++w) asm volatile("" : "+v"(gw[w]));
   };
   // copy J of stage s into ring slot SLOT: J < nB is gathered B row xrow0 + J of the stage,
   // then this wave's values and/or index block. One instruction each, so that a stage's
@@ -186,7 +196,8 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
     const uint32_t sb = lds0 + (uint32_t)(slot * kStage);
     if constexpr (j < nB) {
       const uint16_t* bs = a.B + s * (KS / 4) * a.M * a.ldb;
-      dma_s<16>(bs, boff[j] + (uint32_t)gcl[j] * ldb2, sb + (uint32_t)((xrow0 + j) * 1024));
+      const uint32_t g = (gw[j / 4] >> (8 * (j % 4))) & 0xFFu;
+      dma_s<16>(bs, boff[j] + g * ldb2, sb + (uint32_t)((xrow0 + j) * 1024));
     } else if constexpr (WAVES == 4) {
       if constexpr (j == nB) dma_s<16>(vals + s * a_stage, aoff, sb + (uint32_t)(kAOff + ablk * 1024));
       else dma_s<2>(meta + s * m_stage, moff, sb + (uint32_t)(kMOff + ablk * 256));
@@ -282,6 +293,7 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
     const Frag& prev = fr[(U + 1) % 2];
     const int64_t sx = s + NST - 1;
     if constexpr (ISSUE) {
+      pin_colloc();   // after this stage's barrier: the read has completed
       copy(sx, cint<NX>{}, cint<0>{});
       copy(sx, cint<NX>{}, cint<1>{});
     }
@@ -290,11 +302,10 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
       constexpr int kRd = kPairs / 4;         // pairs per read part
       if constexpr (MMA) mma_pair(prev, cint<Q / (TN / 2)>{}, cint<2 * (Q % (TN / 2))>{});
       if constexpr (Q % kRd == 0) read_part(cur, sb, cint<Q / kRd>{});
-      // the next stage's column-loc bytes replace this one's only after its last B-row copy
-      // (copy nB - 1 goes out after pair nB - 3)
-      if constexpr (Q == nB - 2 && ISSUE) fetch_colloc(s + NST);
       if constexpr (ISSUE && Q + 2 < kDma) copy(sx, cint<NX>{}, cint<Q + 2>{});
     });
+    // the column-loc of the stage the next stage copies, after this stage's last copy
+    if constexpr (ISSUE) fetch_colloc(s + NST);
   };
 
   // ---- the ring: stage s in slot s % NST, operands of stage s in fr[s % 2] ---------------
@@ -333,7 +344,10 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
     constexpr int kAfter = (NST - 2) < (NST - 1 - U) ? (NST - 2) : (NST - 1 - U);
     wait_vmcnt<kDma * kAfter>();
     lds_barrier();
-    if constexpr (U == 0) copy_all(s + NST - 1, cint<(U + NST - 1) % NST>{});
+    if constexpr (U == 0) {
+      pin_colloc();
+      copy_all(s + NST - 1, cint<(U + NST - 1) % NST>{});
+    }
     stage(s, cint<U>{}, cint<0>{}, cint<1>{});
   });
   static_for<0, kPairs>([&](auto q) {   // products of the last stage
