@@ -184,7 +184,7 @@ def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_c
                 enc_calls.append(bind("snm_prune_encode_nm_tiled", As[j].data_ptr(), R, K, K,
                                       vals[j].data_ptr(), metas[j].data_ptr(), stream))
             else:
-                enc_calls.append(bind("snm_prune_encode_nm", As[j].data_ptr(), R, K, K,
+                enc_calls.append(bind("snm_prune_encode_nm", As[j].data_ptr(), R, K, K, 2, 4,
                                       vals[j].data_ptr(), metas[j].data_ptr(), stream))
             row = []
             for t in range(len(NS)):
@@ -195,7 +195,7 @@ def run_gpu(steps: int, warmup: int, b_layout: str, a_layout: str, calibration_c
                     row.append(bind("snm_spmm_nm_tiled", vals[j].data_ptr(), metas[j].data_ptr(), R, K,
                                     B.data_ptr(), NS[t], ldb, lay, Y.data_ptr(), NS[t], stream))
                 else:
-                    row.append(bind("snm_spmm_nm", vals[j].data_ptr(), metas[j].data_ptr(), R, K,
+                    row.append(bind("snm_spmm_nm", vals[j].data_ptr(), metas[j].data_ptr(), R, K, 2, 4,
                                     B.data_ptr(), NS[t], ldb, lay, Y.data_ptr(), NS[t], 1, 0, 0, 0, 0, stream))
             mm_calls.append(row)
 
@@ -370,7 +370,7 @@ def bench_other(workload: str, steps: int, warmup: int, calibration_copy: bool =
         stream = torch.cuda.current_stream().cuda_stream
 
         def enc_args(j, e):
-            return (Ad[j].data_ptr(), w.R, w.K, w.K, w.V, w.M, e[0].data_ptr(), e[1].data_ptr(),
+            return (Ad[j].data_ptr(), w.R, w.K, w.K, w.V, 2, w.M, e[0].data_ptr(), e[1].data_ptr(),
                     e[2].data_ptr(), stream)
         for j in range(nrot):
             check("snm_prune_encode_vnm", lib.snm_prune_encode_vnm(*enc_args(j, enc[j])))
@@ -410,7 +410,7 @@ def bench_other(workload: str, steps: int, warmup: int, calibration_copy: bool =
         from structured_sparse_matrix_amd._lib import load as load_lib, check
         lib = load_lib()
         stream = torch.cuda.current_stream().cuda_stream
-        sd_args = (Qd.data_ptr(), Kd.data_ptr(), nb, L, L, d, float(1.0 / np.sqrt(d)), vals.data_ptr(),
+        sd_args = (Qd.data_ptr(), Kd.data_ptr(), nb, L, L, d, float(1.0 / np.sqrt(d)), 2, 4, vals.data_ptr(),
                    meta.data_ptr(), None, stream)
         check("snm_sddmm_prune_nm", lib.snm_sddmm_prune_nm(*sd_args))
         t_sd = timed(lambda j: lib.snm_sddmm_prune_nm(*sd_args))
@@ -581,9 +581,9 @@ def bench_sweep(steps: int, warmup: int, families=None) -> dict:
         midx = torch.empty((nmi,), dtype=torch.uint8, device=dev)
         colloc = torch.empty((ncl,), dtype=torch.uint8, device=dev)
         Y = torch.empty((R, C), dtype=torch.float16, device=dev)
-        enc = bind("snm_prune_encode_vnm", Abuf.data_ptr(), R, K, lda, V, M, values.data_ptr(),
+        enc = bind("snm_prune_encode_vnm", Abuf.data_ptr(), R, K, lda, V, 2, M, values.data_ptr(),
                    midx.data_ptr(), colloc.data_ptr(), stream)
-        mm = bind("snm_spmm_vnm", values.data_ptr(), midx.data_ptr(), colloc.data_ptr(), R, K, V, M,
+        mm = bind("snm_spmm_vnm", values.data_ptr(), midx.data_ptr(), colloc.data_ptr(), R, K, V, 2, M,
                   B.data_ptr(), C, C, Y.data_ptr(), C, stream)
         t_enc = timed(enc)
         t_mm = timed(mm)
@@ -804,7 +804,7 @@ def bench_energy(steps: int, warmup: int) -> dict:
             values = torch.empty((nv,), dtype=torch.float16, device=dev)
             midx = torch.empty((nmi,), dtype=torch.uint8, device=dev)
             colloc = torch.empty((ncl,), dtype=torch.uint8, device=dev)
-            args = (buf.data_ptr(), 768, K, lda, V, M, values.data_ptr(), midx.data_ptr(),
+            args = (buf.data_ptr(), 768, K, lda, V, 2, M, values.data_ptr(), midx.data_ptr(),
                     colloc.data_ptr(), stream)
             check("snm_prune_encode_vnm", lib.snm_prune_encode_vnm(*args))
             for _ in range(warmup):
@@ -1066,9 +1066,9 @@ def run_headline(args) -> dict:
 
     def step_calls(j, stream):
         e = encs[j]
-        enc = _bind(lib, "snm_prune_encode_vnm_tiled", As[j].data_ptr(), R, K, K, V, M, e[0].data_ptr(),
+        enc = _bind(lib, "snm_prune_encode_vnm_tiled", As[j].data_ptr(), R, K, K, V, 2, M, e[0].data_ptr(),
                     e[1].data_ptr(), e[2].data_ptr(), stream)
-        mm = _bind(lib, "snm_spmm_vnm_tiled", e[0].data_ptr(), e[1].data_ptr(), e[2].data_ptr(), R, K, V, M,
+        mm = _bind(lib, "snm_spmm_vnm_tiled", e[0].data_ptr(), e[1].data_ptr(), e[2].data_ptr(), R, K, V, 2, M,
                    Bs[j].data_ptr(), C, C, Ys[j].data_ptr(), C, stream)
         return enc, mm
     # copy j always runs on stream j % nstreams, so reuse of a copy stays in order
@@ -1124,7 +1124,7 @@ def run_headline(args) -> dict:
                                                           smfmac_flops=smf, ceil=ceil, read_ceiling_key="read_1GiB")
     # the canonical storage through snm_spmm_vnm (the boundary's plain call)
     ce = snm.prune_encode_vnm(As[0], V, M)
-    canon = _bind(lib, "snm_spmm_vnm", ce[0].data_ptr(), ce[1].data_ptr(), ce[2].data_ptr(), R, K, V, M,
+    canon = _bind(lib, "snm_spmm_vnm", ce[0].data_ptr(), ce[1].data_ptr(), ce[2].data_ptr(), R, K, V, 2, M,
                   Bs[0].data_ptr(), C, C, Ys[1].data_ptr(), C, ms_)
     warm(lambda i: canon(), 2)
     t_canon = _windows(lambda i: canon(), K_, NW, main)
@@ -1175,8 +1175,8 @@ def _other_configs(args, lib, main, ceil, res):
     v = torch.empty((256, 128), dtype=torch.float16, device=dev)
     m = torch.empty((256, 32), dtype=torch.uint8, device=dev)
     Y = torch.empty((256, 64), dtype=torch.float16, device=dev)
-    enc = _bind(lib, "snm_prune_encode_nm", Ad.data_ptr(), 256, 256, 256, v.data_ptr(), m.data_ptr(), ms_)
-    mm = _bind(lib, "snm_spmm_nm", v.data_ptr(), m.data_ptr(), 256, 256, Bd.data_ptr(), 64, 64, 0, Y.data_ptr(), 64,
+    enc = _bind(lib, "snm_prune_encode_nm", Ad.data_ptr(), 256, 256, 256, 2, 4, v.data_ptr(), m.data_ptr(), ms_)
+    mm = _bind(lib, "snm_spmm_nm", v.data_ptr(), m.data_ptr(), 256, 256, 2, 4, Bd.data_ptr(), 64, 64, 0, Y.data_ptr(), 64,
                1, 0, 0, 0, 0, ms_)
     warm(lambda i: (enc(), mm()))
     res["kernels"]["cfg1_prune_encode_nm"] = _kernel_entry(_windows(lambda i: enc(), K_, NW, main), nbytes=256 * 256 * 2 + 256 * 128 * 2 + 256 * 32)
@@ -1240,7 +1240,7 @@ def _other_configs(args, lib, main, ceil, res):
     es = [e0] + [tuple(x.clone() for x in e0) for _ in range(nrot - 1)]
     Bs_ = [B0] + [B0.clone() for _ in range(nrot - 1)]
     Ys = [torch.empty((R, C), dtype=torch.float16, device=dev) for _ in range(nrot)]
-    mms = [_bind(lib, "snm_spmm_vnm_tiled", es[j][0].data_ptr(), es[j][1].data_ptr(), es[j][2].data_ptr(), R, K, V, M,
+    mms = [_bind(lib, "snm_spmm_vnm_tiled", es[j][0].data_ptr(), es[j][1].data_ptr(), es[j][2].data_ptr(), R, K, V, 2, M,
                  Bs_[j].data_ptr(), C, C, Ys[j].data_ptr(), C, ms_) for j in range(nrot)]
     warm(lambda i: mms[i % nrot]())
     tw = _windows(lambda i: mms[i % nrot](), K_, NW, main)
@@ -1249,7 +1249,7 @@ def _other_configs(args, lib, main, ceil, res):
                                                           read_ceiling_key="read_19MB")
     nrot_a = max(2, -(-COLD_BYTES // (R * K * 2)))
     Acopies = [A0] + [A0.clone() for _ in range(nrot_a - 1)]
-    encs = [_bind(lib, "snm_prune_encode_vnm_tiled", Acopies[j].data_ptr(), R, K, K, V, M, es[j % nrot][0].data_ptr(),
+    encs = [_bind(lib, "snm_prune_encode_vnm_tiled", Acopies[j].data_ptr(), R, K, K, V, 2, M, es[j % nrot][0].data_ptr(),
                   es[j % nrot][1].data_ptr(), es[j % nrot][2].data_ptr(), ms_) for j in range(nrot_a)]
     warm(lambda i: encs[i % nrot_a]())
     tw = _windows(lambda i: encs[i % nrot_a](), K_, NW, main)
@@ -1271,10 +1271,10 @@ def _other_configs(args, lib, main, ceil, res):
     vals = torch.empty((nb, L, L // 2), dtype=torch.float16, device=dev)
     meta = torch.empty((nb, L, L // 8), dtype=torch.uint8, device=dev)
     O = torch.empty((nb, L, d), dtype=torch.float16, device=dev)
-    sd = _bind(lib, "snm_sddmm_prune_nm", Qd.data_ptr(), Kd.data_ptr(), nb, L, L, d, float(scale), vals.data_ptr(),
+    sd = _bind(lib, "snm_sddmm_prune_nm", Qd.data_ptr(), Kd.data_ptr(), nb, L, L, d, float(scale), 2, 4, vals.data_ptr(),
                meta.data_ptr(), None, ms_)
     sm = _bind(lib, "snm_softmax_nm_rows", vals.data_ptr(), nb * L, L // 2, L // 2, ms_)
-    pv = _bind(lib, "snm_spmm_nm", vals.data_ptr(), meta.data_ptr(), L, L, Vd.data_ptr(), d, d, 0, O.data_ptr(), d,
+    pv = _bind(lib, "snm_spmm_nm", vals.data_ptr(), meta.data_ptr(), L, L, 2, 4, Vd.data_ptr(), d, d, 0, O.data_ptr(), d,
                nb, L * (L // 2), L * (L // 8), L * d, L * d, ms_)
     n4 = max(3, min(K_, 20))   # each launch moves 1-2 GiB: fewer per window
     warm(lambda i: (sd(), sm(), pv()), 2)

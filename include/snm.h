@@ -69,31 +69,38 @@ typedef enum {
 int snm_abi_version(void);
 
 /* Static, human-readable name of a status code. Never NULL. */
-const char* snm_status_string(int status);
+const char* snm_status_string(snm_status status);
+
+/* Pattern arguments. The calls named after a pattern take its parameters, as the pages
+ * write them: (n, m) for N:M, (v, n, m) for V:N:M. This library implements n = 2 of m = 4
+ * (N:M) and n = 2 of m in [4, 256] (V:N:M, the sparse matrix core's 2:4 after the column
+ * selection); any other (n, m) returns SNM_E_UNSUPPORTED before anything else is checked.
+ * Size queries report element counts of the values arrays (fp16) and byte counts of the
+ * metadata arrays, as int64_t like every other size here. */
 
 /* Sizes of the compressed 2:4 arrays of an R x K matrix: values elements (R*K/2) and
  * meta bytes (R*K/8). Requires R >= 0, K >= 0, K % 16 == 0. Host only. */
-int snm_nm_sizes(int64_t R, int64_t K, int64_t* values_elems, int64_t* meta_bytes);
+snm_status snm_nm_sizes(int64_t R, int64_t K, int n, int m, int64_t* values_elems, int64_t* meta_bytes);
 
 /* Sizes of the V:2:M arrays of an R x K matrix. Requires R % V == 0, K % M == 0,
  * (K/M) % 4 == 0, V in {1,...,256}, 4 <= M <= 256. Host only. */
-int snm_vnm_sizes(int64_t R, int64_t K, int V, int M, int64_t* values_elems,
-                  int64_t* midx_bytes, int64_t* colloc_bytes);
+snm_status snm_vnm_sizes(int64_t R, int64_t K, int V, int N, int M, int64_t* values_elems,
+                         int64_t* midx_bytes, int64_t* colloc_bytes);
 
 /* 2:4 magnitude prune along K and compress (lecture notes, "The definition" and
  * "The compressed format"; worked 2 x 8 example).
  *   A       fp16 R x K, leading dimension lda >= K.
  *   values  fp16 R x K/2 (contiguous), meta uint8 R x K/8 (contiguous): written.
  * Requires K % 16 == 0. Output is bit-exactly the canonical layout above. */
-int snm_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda,
-                        void* values, void* meta, void* stream);
+snm_status snm_prune_encode_nm(const void* A, int64_t R, int64_t K, int64_t lda, int n, int m,
+                               void* values, void* meta, void* stream);
 
 /* V:2:M prune and compress (VENOM Sec. 3, Fig. 2 and Fig. 3).
  *   A       fp16 R x K, leading dimension lda >= K.
  *   values  fp16 R x 2K/M, midx uint8 R x K/(2M), colloc uint8 (R/V) x (K/M) x 4.
  * Requires the shape rules of snm_vnm_sizes. */
-int snm_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
-                         void* values, void* midx, void* colloc, void* stream);
+snm_status snm_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V, int N, int M,
+                                void* values, void* midx, void* colloc, void* stream);
 
 /* Y = decode(values, meta) * B, batched (lecture notes, "How the tensor core uses it";
  * the metadata selects, per kept value, the row of B it multiplies).
@@ -105,7 +112,7 @@ int snm_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t lda, int V
  *   Y             fp16 R x C, row-major, leading dimension ldy >= C, entry b at Y + b*stride_Y.
  * Products accumulate in fp32; Y is rounded to fp16 (round to nearest even). Requires
  * K % 16 == 0, batch >= 1 (0 enqueues nothing). Strides are ignored when batch == 1. */
-int snm_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K,
+snm_status snm_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K, int n, int m,
                 const void* B, int64_t C, int64_t ldb, int b_layout, void* Y, int64_t ldy,
                 int64_t batch, int64_t stride_values, int64_t stride_meta,
                 int64_t stride_B, int64_t stride_Y, void* stream);
@@ -123,23 +130,23 @@ int snm_spmm_nm(const void* values, const void* meta, int64_t R, int64_t K,
 
 /* Sizes of the operand-major arrays: values elements and meta bytes for an R x K matrix
  * (ceil(R/16)*ceil(K/64) blocks of 512 elements and 128 bytes). K % 16 == 0. Host only. */
-int snm_nm_tiled_sizes(int64_t R, int64_t K, int64_t* values_elems, int64_t* meta_bytes);
+snm_status snm_nm_tiled_sizes(int64_t R, int64_t K, int64_t* values_elems, int64_t* meta_bytes);
 
 /* 2:4 prune and compress straight into the operand-major layout. Same selection as
  * snm_prune_encode_nm; A fp16 R x K (lda >= K, lda % 8 == 0); K % 16 == 0. */
-int snm_prune_encode_nm_tiled(const void* A, int64_t R, int64_t K, int64_t lda,
+snm_status snm_prune_encode_nm_tiled(const void* A, int64_t R, int64_t K, int64_t lda,
                               void* values_t, void* meta_t, void* stream);
 
 /* Y = decode(values_t, meta_t) * B with A in the operand-major layout; B, b_layout, Y as
  * in snm_spmm_nm (no batching). fp32 accumulation, fp16 output (RNE). */
-int snm_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+snm_status snm_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                       const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                       int64_t ldy, void* stream);
 
 /* Bytes of workspace that snm_spmm_nm_tiled_ws needs for an R x K matrix and C columns
  * (0 when it runs without a split reduction). K % 16 == 0; C <= 32 (else
  * SNM_E_UNSUPPORTED). Host only. */
-int snm_spmm_nm_tiled_ws_bytes(int64_t R, int64_t K, int64_t C, int64_t* workspace_bytes);
+snm_status snm_spmm_nm_tiled_ws_bytes(int64_t R, int64_t K, int64_t C, int64_t* workspace_bytes);
 
 /* Y = decode(values_t, meta_t) * B for the decode regime, the same product as
  * snm_spmm_nm_tiled with B column-major (element (k, c) at B[c*ldb + k], ldb >= K, as
@@ -159,7 +166,7 @@ int snm_spmm_nm_tiled_ws_bytes(int64_t R, int64_t K, int64_t C, int64_t* workspa
  *              when the size is 0.
  * fp32 accumulation; the split partial sums are added in a fixed order, so the result
  * does not depend on scheduling. fp16 output (RNE). */
-int snm_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+snm_status snm_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                          const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
                          void* workspace, int64_t workspace_bytes, void* stream);
 
@@ -176,7 +183,7 @@ int snm_spmm_nm_tiled_ws(const void* values_t, const void* meta_t, int64_t R, in
  * overlap on one device (other streams, other host threads) race and give wrong results;
  * serialise them, or use snm_spmm_nm_tiled_ws with a workspace per stream.
  * Arguments, layouts and requirements as snm_spmm_nm_tiled_ws without the workspace. */
-int snm_spmm_nm_tiled_noalloc(const void* values_t, const void* meta_t, int64_t R, int64_t K,
+snm_status snm_spmm_nm_tiled_noalloc(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                               const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
                               void* stream);
 
@@ -186,8 +193,8 @@ int snm_spmm_nm_tiled_noalloc(const void* values_t, const void* meta_t, int64_t 
  *   B  fp16 K x C (ldb >= C);  Y  fp16 R x C (ldy >= C).
  * fp32 accumulation, fp16 output (RNE). Requires the shape rules of snm_vnm_sizes and
  * V a multiple of 16. */
-int snm_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R,
-                 int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
+snm_status snm_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R,
+                 int64_t K, int V, int N, int M, const void* B, int64_t C, int64_t ldb, void* Y,
                  int64_t ldy, void* stream);
 
 /* V:2:M prune and compress (as snm_prune_encode_vnm) into the row-group interleaved
@@ -201,16 +208,16 @@ int snm_spmm_vnm(const void* values, const void* midx, const void* colloc, int64
  *   colloc    canonical (unchanged).
  * Sizes as snm_vnm_sizes. Requires its shape rules and V % 32 == 0 (else
  * SNM_E_UNSUPPORTED); values_t, midx_t 16-byte aligned. */
-int snm_prune_encode_vnm_tiled(const void* A, int64_t R, int64_t K, int64_t lda, int V, int M,
-                               void* values_t, void* midx_t, void* colloc, void* stream);
+snm_status snm_prune_encode_vnm_tiled(const void* A, int64_t R, int64_t K, int64_t lda, int V, int N,
+                                      int M, void* values_t, void* midx_t, void* colloc, void* stream);
 
 /* Y = decode_vnm(values_t, midx_t, colloc) * B with values and m-indices in the row-group
  * interleaved storage of snm_prune_encode_vnm_tiled; B, Y as in snm_spmm_vnm. fp32
  * accumulation, fp16 output (RNE). Runs the wide-tile kernel only: requires V % 32 == 0,
  * C % 8 == 0, ldb % 8 == 0, 4K/M <= 16384 and 32-bit copy offsets (128*4K/M < 2^31,
  * (32*M*ldb + C)*2 < 2^31), else SNM_E_UNSUPPORTED; B 16-byte aligned (else SNM_E_ALIGN). */
-int snm_spmm_vnm_tiled(const void* values_t, const void* midx_t, const void* colloc, int64_t R,
-                       int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
+snm_status snm_spmm_vnm_tiled(const void* values_t, const void* midx_t, const void* colloc, int64_t R,
+                       int64_t K, int V, int N, int M, const void* B, int64_t C, int64_t ldb, void* Y,
                        int64_t ldy, void* stream);
 
 /* Dynamic 2:4 SDDMM ("Dynamic N:M ... attention", Sec. 3.2 and Listing 1; Sec. 4.2-4.3):
@@ -221,8 +228,8 @@ int snm_spmm_vnm_tiled(const void* values_t, const void* midx_t, const void* col
  *   S_dense optional fp16 [batch, Lq, Lk]: if not NULL it receives S before pruning.
  * The product accumulates in fp32 and is scaled in fp32 before the single rounding to
  * fp16. Requires Lk % 32 == 0 and d in {16, 32, 64, 128}. */
-int snm_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
-                       int64_t Lk, int64_t d, float scale, void* values, void* meta,
+snm_status snm_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+                       int64_t Lk, int64_t d, float scale, int n, int m, void* values, void* meta,
                        void* S_dense, void* stream);
 
 /* Fused-softmax variant of dynamic 2:4 attention ("Dynamic N:M ... attention", Sec. 3.2:
@@ -234,7 +241,7 @@ int snm_sddmm_prune_nm(const void* Q, const void* Kmat, int64_t batch, int64_t L
  * snm_sddmm_prune_nm_rowmax: exactly snm_sddmm_prune_nm (no S_dense) and, in addition,
  *   row_max  fp32 [batch, Lq]: the largest kept (fp16) score of each row, widened exactly.
  * Requires what snm_sddmm_prune_nm requires; row_max 4-byte aligned. */
-int snm_sddmm_prune_nm_rowmax(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+snm_status snm_sddmm_prune_nm_rowmax(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
                               int64_t Lk, int64_t d, float scale, void* values, void* meta,
                               float* row_max, void* stream);
 
@@ -250,7 +257,7 @@ int snm_sddmm_prune_nm_rowmax(const void* Q, const void* Kmat, int64_t batch, in
  *   B, Y          as in snm_spmm_nm with b_layout 0 (row-major B).
  * Requires K % 16 == 0 and K > 0, C % 8 == 0, ldb % 8 == 0, B 16-byte aligned (and
  * stride_B % 8 == 0 when batch > 1), 128*K < 2^31 and (256*ldb + C)*2 < 2^31. */
-int snm_spmm_nm_softmax(const void* values, const void* meta, const float* row_max, int64_t R,
+snm_status snm_spmm_nm_softmax(const void* values, const void* meta, const float* row_max, int64_t R,
                         int64_t K, const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
                         int64_t batch, int64_t stride_values, int64_t stride_meta,
                         int64_t stride_row_max, int64_t stride_B, int64_t stride_Y, void* stream);
@@ -268,17 +275,17 @@ int snm_spmm_nm_softmax(const void* values, const void* meta, const float* row_m
  *                 order, padded with +0 to a multiple of 8 (every tile starts 16-byte
  *                 aligned).
  * Sizes of the fixed arrays (host only). */
-int snm_bitmap_sizes(int64_t R, int64_t K, int64_t* n_tiles, int64_t* n_offsets);
+snm_status snm_bitmap_sizes(int64_t R, int64_t K, int64_t* n_tiles, int64_t* n_offsets);
 
 /* Encoder, pass 1: bitmaps and tile_offsets of A (fp16 R x K row-major, lda >= K,
  * lda % 8 == 0, A 16-byte aligned; bitmaps 8-byte and tile_offsets 4-byte aligned). After
  * the stream reaches this call, tile_offsets[R*K/64] is the number of values to allocate. */
-int snm_bitmap_count(const void* A, int64_t R, int64_t K, int64_t lda, void* bitmaps,
+snm_status snm_bitmap_count(const void* A, int64_t R, int64_t K, int64_t lda, void* bitmaps,
                      void* tile_offsets, void* stream);
 
 /* Encoder, pass 2: the packed values (fp16 [tile_offsets[R*K/64]]) from A and the arrays of
  * pass 1. values may be NULL when that count is 0 (it is then never touched). */
-int snm_bitmap_encode(const void* A, int64_t R, int64_t K, int64_t lda, const void* bitmaps,
+snm_status snm_bitmap_encode(const void* A, int64_t R, int64_t K, int64_t lda, const void* bitmaps,
                       const void* tile_offsets, void* values, void* stream);
 
 /* Y = decode(bitmaps, tile_offsets, values) * B for a decode-shaped B with C <= 32 columns
@@ -288,7 +295,7 @@ int snm_bitmap_encode(const void* A, int64_t R, int64_t K, int64_t lda, const vo
  * (larger strides return SNM_E_UNSUPPORTED). values 16-byte aligned. fp32 accumulation,
  * fp16 output (RNE). C > 32 returns SNM_E_UNSUPPORTED. values may be NULL when the encoding
  * holds no non-zeros. */
-int snm_spmm_bitmap(const void* bitmaps, const void* tile_offsets, const void* values, int64_t R,
+snm_status snm_spmm_bitmap(const void* bitmaps, const void* tile_offsets, const void* values, int64_t R,
                     int64_t K, const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                     int64_t ldy, void* stream);
 
@@ -296,7 +303,7 @@ int snm_spmm_bitmap(const void* bitmaps, const void* tile_offsets, const void* v
  * attention", Sec. 3.2: softmax runs only on each row's kept entries; dropped
  * entries count as -inf). values: fp16 rows x kept, leading dimension ld >= kept.
  * p = exp(v - max) / sum exp(v - max) per row, in fp32, rounded to fp16 (RNE). */
-int snm_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream);
+snm_status snm_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream);
 
 /* bf16 variant of dynamic 2:4 attention ("Dynamic N:M ... attention", Sec. 4.2: 16-bit
  * scores of either fp16 or bf16 are pruned 2 of 4 in every 8 bytes). Every element buffer
@@ -307,25 +314,25 @@ int snm_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, vo
  *
  * snm_sddmm_prune_nm_bf16: snm_sddmm_prune_nm on bf16 Q, Kmat, values (and S_dense);
  *   row_max optional (NULL: not written): as in snm_sddmm_prune_nm_rowmax. */
-int snm_sddmm_prune_nm_bf16(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+snm_status snm_sddmm_prune_nm_bf16(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
                             int64_t Lk, int64_t d, float scale, void* values, void* meta,
                             void* S_dense, float* row_max, void* stream);
 
 /* snm_softmax_nm_rows_bf16: snm_softmax_nm_rows on bf16 rows. */
-int snm_softmax_nm_rows_bf16(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream);
+snm_status snm_softmax_nm_rows_bf16(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream);
 
 /* snm_spmm_nm_bf16: snm_spmm_nm with b_layout 0 on bf16 values, B and Y, batched the same
  * way. Requires, beyond the rules of snm_spmm_nm: C % 8 == 0, ldb % 8 == 0, B 16-byte
  * aligned (and stride_B % 8 == 0 when batch > 1), 128*K < 2^31 and (256*ldb + C)*2 < 2^31;
  * otherwise SNM_E_ALIGN or SNM_E_SHAPE. K == 0 writes zeros. */
-int snm_spmm_nm_bf16(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
+snm_status snm_spmm_nm_bf16(const void* values, const void* meta, int64_t R, int64_t K, const void* B,
                      int64_t C, int64_t ldb, void* Y, int64_t ldy, int64_t batch,
                      int64_t stride_values, int64_t stride_meta, int64_t stride_B,
                      int64_t stride_Y, void* stream);
 
 /* snm_spmm_nm_softmax_bf16: snm_spmm_nm_softmax on bf16 values, B and Y; the probabilities
  * are p = bf16_RNE(exp(v - row_max)). */
-int snm_spmm_nm_softmax_bf16(const void* values, const void* meta, const float* row_max,
+snm_status snm_spmm_nm_softmax_bf16(const void* values, const void* meta, const float* row_max,
                              int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb, void* Y,
                              int64_t ldy, int64_t batch, int64_t stride_values,
                              int64_t stride_meta, int64_t stride_row_max, int64_t stride_B,
@@ -347,13 +354,13 @@ int snm_spmm_nm_softmax_bf16(const void* values, const void* meta, const float* 
  *   values fp32 [batch, Lq, Lk/2]; meta [batch, Lq, Lk/4]; S_dense optional fp32
  *   [batch, Lq, Lk] (pre-prune S); row_max optional fp32 [batch, Lq] (largest kept score).
  *   Requires Lk % 32 == 0, d in {16, 32, 64, 128}, 16-byte aligned arrays (row_max 4). */
-int snm_sddmm_prune_1of2_f32(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
+snm_status snm_sddmm_prune_1of2_f32(const void* Q, const void* Kmat, int64_t batch, int64_t Lq,
                              int64_t Lk, int64_t d, float scale, void* values, void* meta,
                              void* S_dense, float* row_max, void* stream);
 
 /* snm_softmax_nm_rows_f32: snm_softmax_nm_rows on fp32 rows (fp32 output, no rounding step
  * beyond fp32 arithmetic). */
-int snm_softmax_nm_rows_f32(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream);
+snm_status snm_softmax_nm_rows_f32(void* values, int64_t rows, int64_t kept, int64_t ld, void* stream);
 
 /* snm_spmm_1of2_f32: Y = decode(values, meta) * B for 1:2 fp32 operands, per batch entry at
  * values + b*stride_values, meta + b*stride_meta (bytes), B + b*stride_B, Y + b*stride_Y.
@@ -365,7 +372,7 @@ int snm_softmax_nm_rows_f32(void* values, int64_t rows, int64_t kept, int64_t ld
  * Requires K % 32 == 0 (K > 0 with row_max), C % 4 == 0, ldb % 4 == 0, values and B 16-byte,
  * meta 8-byte, Y and row_max 4-byte aligned; with batch > 1, stride_values % 4 == 0,
  * stride_meta % 8 == 0, stride_B % 4 == 0. K == 0 writes zeros. */
-int snm_spmm_1of2_f32(const void* values, const void* meta, const float* row_max, int64_t R,
+snm_status snm_spmm_1of2_f32(const void* values, const void* meta, const float* row_max, int64_t R,
                       int64_t K, const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
                       int64_t batch, int64_t stride_values, int64_t stride_meta,
                       int64_t stride_row_max, int64_t stride_B, int64_t stride_Y, void* stream);

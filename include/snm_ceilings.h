@@ -18,6 +18,8 @@
 
 #include <stdint.h>
 
+#include "snm.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -25,11 +27,11 @@ extern "C" {
 /* Reads `bytes` bytes of src (16-byte aligned, bytes % 16 == 0) with 16-byte coalesced
  * loads, four in flight per lane. sink: 16 bytes of device memory, written only if the
  * XOR of the data equals a fixed 128-bit constant (it keeps the loads alive). */
-int snm_ceiling_read(const void* src, int64_t bytes, void* sink, void* stream);
+snm_status snm_ceiling_read(const void* src, int64_t bytes, void* sink, void* stream);
 
 /* Copies `bytes` bytes from src to dst (both 16-byte aligned, bytes % 16 == 0, not
  * overlapping) with 16-byte coalesced loads and stores. */
-int snm_ceiling_copy(const void* src, void* dst, int64_t bytes, void* stream);
+snm_status snm_ceiling_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 /* Matrix-instruction issue loop: `workgroups` workgroups of 4 waves; every wave runs
  * `iters` iterations of 4 independent accumulator chains of one instruction on register
@@ -39,7 +41,7 @@ int snm_ceiling_copy(const void* src, void* dst, int64_t bytes, void* stream);
  *   kind 1: v_smfmac_f32_32x32x32_f16, 2*32*32*32 = 65536 flops per instruction (the
  *           dense equivalent of the 2:4 product, which is how the sparse peak counts).
  * Flops per launch = workgroups * 4 * iters * 4 * (flops per instruction). */
-int snm_ceiling_matrix(int kind, int64_t workgroups, int64_t iters, float* out, void* stream);
+snm_status snm_ceiling_matrix(int kind, int64_t workgroups, int64_t iters, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -67,19 +67,19 @@ def abi_version() -> int:
     return load().snm_abi_version()
 
 
-def nm_sizes(R: int, K: int):
-    v, m = ctypes.c_int64(), ctypes.c_int64()
-    check("snm_nm_sizes", load().snm_nm_sizes(R, K, ctypes.byref(v), ctypes.byref(m)))
-    return v.value, m.value
+def nm_sizes(R: int, K: int, n: int = 2, m: int = 4):
+    v, mb = ctypes.c_int64(), ctypes.c_int64()
+    check("snm_nm_sizes", load().snm_nm_sizes(R, K, n, m, ctypes.byref(v), ctypes.byref(mb)))
+    return v.value, mb.value
 
 
-def vnm_sizes(R: int, K: int, V: int, M: int):
+def vnm_sizes(R: int, K: int, V: int, M: int, N: int = 2):
     v, m, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
-    check("snm_vnm_sizes", load().snm_vnm_sizes(R, K, V, M, ctypes.byref(v), ctypes.byref(m), ctypes.byref(c)))
+    check("snm_vnm_sizes", load().snm_vnm_sizes(R, K, V, N, M, ctypes.byref(v), ctypes.byref(m), ctypes.byref(c)))
     return v.value, m.value, c.value
 
 
-def prune_encode_nm(A, values=None, meta=None):
+def prune_encode_nm(A, values=None, meta=None, n: int = 2, m: int = 4):
     """2:4 magnitude prune of fp16 A [R, K] along K -> (values [R, K/2], meta [R, K/8])."""
     torch = _torch()
     _need(A, "A", torch.float16, 2)
@@ -91,7 +91,7 @@ def prune_encode_nm(A, values=None, meta=None):
     if meta is None:
         meta = torch.empty((R, K // 8), dtype=torch.uint8, device=A.device)
     check("snm_prune_encode_nm",
-          load().snm_prune_encode_nm(_ptr(A), R, K, A.stride(0), _ptr(values), _ptr(meta), _stream(A)))
+          load().snm_prune_encode_nm(_ptr(A), R, K, A.stride(0), n, m, _ptr(values), _ptr(meta), _stream(A)))
     return values, meta
 
 
@@ -205,7 +205,7 @@ def _prune_encode_vnm(A, V: int, M: int, entry: str):
     values = torch.empty((R, 2 * G), dtype=torch.float16, device=A.device)
     midx = torch.empty((R, G // 2), dtype=torch.uint8, device=A.device)
     colloc = torch.empty((R // V if V > 0 else 0, G, 4), dtype=torch.uint8, device=A.device)
-    check(entry, getattr(load(), entry)(_ptr(A), R, K, A.stride(0), V, M, _ptr(values), _ptr(midx),
+    check(entry, getattr(load(), entry)(_ptr(A), R, K, A.stride(0), V, 2, M, _ptr(values), _ptr(midx),
                                         _ptr(colloc), _stream(A)))
     return values, midx, colloc
 
@@ -248,7 +248,7 @@ def spmm_nm(values, meta, B, out=None):
     if out.stride(2) != 1:
         raise ValueError("out must be row-major")
     check("snm_spmm_nm",
-          load().snm_spmm_nm(_ptr(values), _ptr(meta), R, K, _ptr(B), C, ldb, layout, _ptr(out),
+          load().snm_spmm_nm(_ptr(values), _ptr(meta), R, K, 2, 4, _ptr(B), C, ldb, layout, _ptr(out),
                              out.stride(1), nb, values.stride(0), meta.stride(0), B.stride(0),
                              out.stride(0), _stream(B)))
     return out if batched else out[0]
@@ -281,7 +281,7 @@ def _spmm_vnm(values, midx, colloc, B, V: int, M: int, out, entry: str):
         raise ValueError("shape mismatch between the V:2:M arrays and B")
     if out is None:
         out = torch.empty((R, C), dtype=torch.float16, device=B.device)
-    check(entry, getattr(load(), entry)(_ptr(values), _ptr(midx), _ptr(colloc), R, K, V, M, _ptr(B), C,
+    check(entry, getattr(load(), entry)(_ptr(values), _ptr(midx), _ptr(colloc), R, K, V, 2, M, _ptr(B), C,
                                         B.stride(0), _ptr(out), out.stride(0), _stream(B)))
     return out
 
@@ -304,7 +304,7 @@ def sddmm_prune_nm(Q, Kmat, scale=None, return_dense=False):
     meta = torch.empty((nb, Lq, Lk // 8), dtype=torch.uint8, device=Q.device)
     S = torch.empty((nb, Lq, Lk), dtype=torch.float16, device=Q.device) if return_dense else None
     check("snm_sddmm_prune_nm",
-          load().snm_sddmm_prune_nm(_ptr(Q), _ptr(Kmat), nb, Lq, Lk, d, float(scale), _ptr(values),
+          load().snm_sddmm_prune_nm(_ptr(Q), _ptr(Kmat), nb, Lq, Lk, d, float(scale), 2, 4, _ptr(values),
                                     _ptr(meta), _ptr(S), _stream(Q)))
     return (values, meta, S) if return_dense else (values, meta)
 

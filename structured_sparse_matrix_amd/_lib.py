@@ -15,16 +15,16 @@ _vp = ctypes.c_void_p
 _f32 = ctypes.c_float
 _p64 = ctypes.POINTER(ctypes.c_int64)
 
-# name -> argument types (every entry point returns int status)
+# name -> argument types (every entry point returns its snm_status as a C int)
 SIGNATURES = {
     "snm_abi_version": [],
     "snm_status_string": [_int],
-    "snm_nm_sizes": [_i64, _i64, _p64, _p64],
-    "snm_vnm_sizes": [_i64, _i64, _int, _int, _p64, _p64, _p64],
-    "snm_prune_encode_nm": [_vp, _i64, _i64, _i64, _vp, _vp, _vp],
-    "snm_prune_encode_vnm": [_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp],
-    "snm_prune_encode_vnm_tiled": [_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp],
-    "snm_spmm_nm": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
+    "snm_nm_sizes": [_i64, _i64, _int, _int, _p64, _p64],
+    "snm_vnm_sizes": [_i64, _i64, _int, _int, _int, _p64, _p64, _p64],
+    "snm_prune_encode_nm": [_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp],
+    "snm_prune_encode_vnm": [_vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp],
+    "snm_prune_encode_vnm_tiled": [_vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp],
+    "snm_spmm_nm": [_vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _int, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp],
     "snm_nm_tiled_sizes": [_i64, _i64, _p64, _p64],
     "snm_prune_encode_nm_tiled": [_vp, _i64, _i64, _i64, _vp, _vp, _vp],
     "snm_spmm_nm_tiled": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _vp, _i64, _vp],
@@ -34,9 +34,9 @@ SIGNATURES = {
     "snm_ceiling_read": [_vp, _i64, _vp, _vp],
     "snm_ceiling_copy": [_vp, _vp, _i64, _vp],
     "snm_ceiling_matrix": [_int, _i64, _i64, _vp, _vp],
-    "snm_spmm_vnm": [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
-    "snm_spmm_vnm_tiled": [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
-    "snm_sddmm_prune_nm": [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp],
+    "snm_spmm_vnm": [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
+    "snm_spmm_vnm_tiled": [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
+    "snm_sddmm_prune_nm": [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _int, _vp, _vp, _vp, _vp],
     "snm_softmax_nm_rows": [_vp, _i64, _i64, _i64, _vp],
     "snm_bitmap_sizes": [_i64, _i64, _p64, _p64],
     "snm_bitmap_count": [_vp, _i64, _i64, _i64, _vp, _vp, _vp],

@@ -26,6 +26,7 @@
 //                   registers while the current one is multiplied.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "variant.hpp"
 
 namespace snm {
 
@@ -355,12 +356,18 @@ hipError_t launch_spmm_nm(const void* values, const void* meta, int64_t R, int64
                           int64_t C, int64_t ldb, int b_layout, void* Y, int64_t ldy, int64_t batch,
                           int64_t stride_values, int64_t stride_meta, int64_t stride_B,
                           int64_t stride_Y, hipStream_t stream) {
-  if (C <= 32)   // decode regime: weight streaming, see spmm_skinny.hip
+  const bool generic = forced_variant() == Variant::kGeneric;
+  if (C <= 32 && !generic) {   // decode regime: weight streaming, see spmm_skinny.hip
+    log_variant("spmm_nm", R, K, C, "skinny");
     return launch_spmm_nm_skinny(values, meta, R, K, B, C, ldb, b_layout, Y, ldy, batch,
                                  stride_values, stride_meta, stride_B, stride_Y, stream);
-  if (b_layout == 0 && spmm_wide_eligible(R, K, 0, 4, B, C, ldb, batch, stride_B))
+  }
+  if (b_layout == 0 && !generic && spmm_wide_eligible(R, K, 0, 4, B, C, ldb, batch, stride_B)) {
+    log_variant("spmm_nm", R, K, C, "wide");
     return launch_spmm_wide(values, meta, nullptr, R, K, 0, 4, B, C, ldb, Y, ldy, batch,
                             stride_values, stride_meta, stride_B, stride_Y, stream);
+  }
+  log_variant("spmm_nm", R, K, C, "generic");
   SpmmArgs a{};
   a.values = (const uint16_t*)values;
   a.meta = (const uint8_t*)meta;
@@ -384,8 +391,11 @@ hipError_t launch_spmm_nm(const void* values, const void* meta, int64_t R, int64
 hipError_t launch_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                                 const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                                 int64_t ldy, hipStream_t stream) {
-  if (C <= 32)
+  if (C <= 32 && forced_variant() != Variant::kGeneric) {
+    log_variant("spmm_nm_tiled", R, K, C, "skinny");
     return launch_spmm_nm_tiled_skinny(values_t, meta_t, R, K, B, C, ldb, b_layout, Y, ldy, stream);
+  }
+  log_variant("spmm_nm_tiled", R, K, C, "generic");
   SpmmArgs a{};
   a.values = (const uint16_t*)values_t;
   a.meta = (const uint8_t*)meta_t;
@@ -409,9 +419,10 @@ hipError_t launch_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_
 hipError_t launch_spmm_vnm(const void* values, const void* midx, const void* colloc, int64_t R,
                            int64_t K, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
                            int64_t ldy, hipStream_t stream) {
-  if (spmm_wide_eligible(R, 4 * (K / M), V, M, B, C, ldb, 1, 0))
+  if (forced_variant() != Variant::kGeneric && spmm_wide_eligible(R, 4 * (K / M), V, M, B, C, ldb, 1, 0))
     return launch_spmm_wide(values, midx, colloc, R, 4 * (K / M), V, M, B, C, ldb, Y, ldy, 1, 0, 0,
-                            0, 0, stream);
+                            0, 0, stream);   // logs the tile it picks
+  log_variant("spmm_vnm", R, K, C, "generic");
   SpmmArgs a{};
   a.values = (const uint16_t*)values;
   a.meta = (const uint8_t*)midx;

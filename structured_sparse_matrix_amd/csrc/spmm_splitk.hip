@@ -26,6 +26,7 @@
 //     take stale partial sums for its counters.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "variant.hpp"
 #include "validate.hpp"
 
 #include <atomic>
@@ -262,8 +263,12 @@ hipError_t launch_spmm_nm_tiled_splitk(const void* values_t, const void* meta_t,
                                        const void* B, int64_t C, int64_t ldb, void* Y, int64_t ldy,
                                        void* workspace, hipStream_t stream) {
   const SplitPlan p = splitk_plan(R, K, C);
-  if (p.splits < 2)   // the split does not pay here: one workgroup per row tile, all of K
+  if (p.splits < 2 || forced_variant() == Variant::kUnsplit) {
+    // the split does not pay here: one workgroup per row tile, all of K
+    log_variant("spmm_nm_tiled_ws", R, K, C, "skinny");
     return launch_spmm_nm_tiled_skinny(values_t, meta_t, R, K, B, C, ldb, 1, Y, ldy, stream);
+  }
+  log_variant("spmm_nm_tiled_ws", R, K, C, p.splits == 2 ? "split 2" : p.splits == 3 ? "split 3" : "split 4");
   SplitArgs a{};
   a.values = (const uint16_t*)values_t;
   a.meta = (const uint8_t*)meta_t;
@@ -293,7 +298,7 @@ hipError_t launch_spmm_nm_tiled_splitk_noalloc(const void* values_t, const void*
                                                void* Y, int64_t ldy, hipStream_t stream) {
   const SplitPlan p = splitk_plan(R, K, C);
   void* ws = nullptr;
-  if (p.splits >= 2) {   // the unsplit kernel needs no scratch
+  if (p.splits >= 2 && forced_variant() != Variant::kUnsplit) {   // the unsplit kernel needs no scratch
     if (p.workspace_bytes > kSplitScratchBytes) return hipErrorInvalidValue;
     hipError_t e = scratch_of_current_device(&ws, stream);
     if (e != hipSuccess) return e;

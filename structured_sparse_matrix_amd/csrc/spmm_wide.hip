@@ -29,6 +29,7 @@
 #include "elem.hpp"
 #include "lds_dma.hpp"
 #include "launch.hpp"
+#include "variant.hpp"
 #include "wide_layout.hpp"
 
 #include <type_traits>
@@ -555,20 +556,41 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
   a.y_vec = y_rows_aligned(Y, ldy, a.batch, stride_Y);
   // 128 x 256 tiles where they still give every CU two workgroups; 128 x 128 otherwise
   const bool wide_grid = a.batch * ((R + 127) / 128) * ((C + 255) / 256) >= 512;
+  const char* op = V > 0 ? (a_tiled ? "spmm_vnm_tiled" : "spmm_vnm") : "spmm_nm";
+  const int64_t K = V > 0 ? Kc / 4 * M : Kc;
   if (V > 0) {
     // the large-tile kernel runs one workgroup per CU: only where its grid fills the chip
-    if (a.batch == 1 && spmm_vnm_big_eligible(R, Kc, V, M, B, C, ldb) && (R / 128) * ((C + 511) / 512) >= 256)
+    const Variant f = forced_variant();
+    if (a.batch == 1 && f != Variant::kWide && spmm_vnm_big_eligible(R, Kc, V, M, B, C, ldb) &&
+        (f == Variant::kLarge || (R / 128) * ((C + 511) / 512) >= 256)) {
+      log_variant(op, R, K, C, "large 128x512");
       return launch_spmm_vnm_big(values, meta, colloc, R, Kc, V, M, B, C, ldb, Y, ldy, a_tiled, stream);
-    if (V % 128 == 0) {
-      if (C > 128 && wide_grid) return launch_wide<1, 4, 4, 2, 1, 3, true, false, false>(a, stream);   // 128 x 256
-      return launch_wide<1, 4, 4, 1, 2, 3, true>(a, stream);                // 128 x 128
     }
-    if (V % 64 == 0) return launch_wide<1, 4, 2, 1, 2, 3, true>(a, stream);  // 64 x 128
-    return launch_wide<1, 4, 1, 1, 4, 2, true>(a, stream);                  // 32 x 128, 128-position stages
+    if (V % 128 == 0) {
+      if (C > 128 && wide_grid) {
+        log_variant(op, R, K, C, "wide 128x256");
+        return launch_wide<1, 4, 4, 2, 1, 3, true, false, false>(a, stream);
+      }
+      log_variant(op, R, K, C, "wide 128x128");
+      return launch_wide<1, 4, 4, 1, 2, 3, true>(a, stream);
+    }
+    if (V % 64 == 0) {
+      log_variant(op, R, K, C, "wide 64x128");
+      return launch_wide<1, 4, 2, 1, 2, 3, true>(a, stream);
+    }
+    log_variant(op, R, K, C, "wide 32x128");   // 128-position stages
+    return launch_wide<1, 4, 1, 1, 4, 2, true>(a, stream);
   }
-  if (C <= 64) return launch_wide<4, 1, 1, 2, 4, 2, false>(a, stream);      // 128 x 64, 128-position stages
-  if (C <= 128 || !wide_grid) return launch_wide<1, 4, 4, 1, 2, 3, false>(a, stream);   // 128 x 128
-  return launch_wide<1, 4, 4, 2, 1, 3, false, false, false>(a, stream);     // 128 x 256
+  if (C <= 64) {
+    log_variant(op, R, K, C, "wide 128x64");   // 128-position stages
+    return launch_wide<4, 1, 1, 2, 4, 2, false>(a, stream);
+  }
+  if (C <= 128 || !wide_grid) {
+    log_variant(op, R, K, C, "wide 128x128");
+    return launch_wide<1, 4, 4, 1, 2, 3, false>(a, stream);
+  }
+  log_variant(op, R, K, C, "wide 128x256");
+  return launch_wide<1, 4, 4, 2, 1, 3, false, false, false>(a, stream);
 }
 
 hipError_t launch_spmm_nm_bf16(const void* values, const void* meta, int64_t R, int64_t K,

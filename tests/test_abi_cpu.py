@@ -86,6 +86,45 @@ FAKE = P(0x1000)          # never dereferenced: every call below fails validatio
 MISALIGNED = P(0x1008)
 
 
+def _nm(args, at, n=2, m=4):
+    """The argument tuple with the N:M pattern (n, m) inserted at position `at`."""
+    return tuple(args[:at]) + (n, m) + tuple(args[at:])
+
+
+def _vnm(args, at, n=2):
+    """The argument tuple with the V:N:M n inserted at position `at` (between V and M)."""
+    return tuple(args[:at]) + (n,) + tuple(args[at:])
+
+
+# The pattern arguments are checked first: anything but 2:4 (N:M) or n = 2 (V:N:M) is
+# SNM_E_UNSUPPORTED even where every other argument is valid, and nothing is enqueued.
+@pytest.mark.parametrize("n,m", [(1, 2), (2, 8), (4, 8), (1, 4), (2, 2), (0, 0)])
+def test_nm_pattern_arguments_rejected(n, m):
+    lib = _lib()
+    v, mb = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.snm_nm_sizes(64, 64, n, m, ctypes.byref(v), ctypes.byref(mb)) == 4
+    assert lib.snm_prune_encode_nm(FAKE, 4, 16, 16, n, m, FAKE, FAKE, P(0)) == 4
+    assert lib.snm_spmm_nm(FAKE, FAKE, 16, 32, n, m, FAKE, 8, 8, 0, FAKE, 8, 1, 0, 0, 0, 0, P(0)) == 4
+    assert lib.snm_sddmm_prune_nm(FAKE, FAKE, 1, 16, 32, 64, ctypes.c_float(0.125), n, m, FAKE, FAKE,
+                                  P(0), P(0)) == 4
+    # the same calls with (2, 4) get past the pattern check (to the size query's result, or
+    # to the empty-problem early return with nothing enqueued)
+    assert lib.snm_nm_sizes(64, 64, 2, 4, ctypes.byref(v), ctypes.byref(mb)) == 0 and v.value == 64 * 32
+    assert lib.snm_prune_encode_nm(P(0), 0, 16, 16, 2, 4, P(0), P(0), P(0)) == 0
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 0])
+def test_vnm_pattern_argument_rejected(n):
+    lib = _lib()
+    v, mi, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    assert lib.snm_vnm_sizes(128, 64, 64, n, 8, ctypes.byref(v), ctypes.byref(mi), ctypes.byref(c)) == 4
+    assert lib.snm_prune_encode_vnm(FAKE, 128, 64, 64, 64, n, 8, FAKE, FAKE, FAKE, P(0)) == 4
+    assert lib.snm_prune_encode_vnm_tiled(FAKE, 128, 64, 64, 64, n, 8, FAKE, FAKE, FAKE, P(0)) == 4
+    assert lib.snm_spmm_vnm(FAKE, FAKE, FAKE, 64, 64, 64, n, 8, FAKE, 8, 8, FAKE, 8, P(0)) == 4
+    assert lib.snm_spmm_vnm_tiled(FAKE, FAKE, FAKE, 64, 64, 64, n, 8, FAKE, 64, 64, FAKE, 64, P(0)) == 4
+    assert lib.snm_vnm_sizes(128, 64, 64, 2, 8, ctypes.byref(v), ctypes.byref(mi), ctypes.byref(c)) == 0
+
+
 @pytest.mark.parametrize("args,status", [
     ((P(0), 4, 16, 16, FAKE, FAKE, P(0)), 1),           # A NULL
     ((FAKE, 4, 12, 16, FAKE, FAKE, P(0)), 2),           # K % 16
@@ -96,7 +135,7 @@ MISALIGNED = P(0x1008)
     ((P(0), 0, 16, 16, P(0), P(0), P(0)), 0),           # empty: ok, nothing enqueued
 ])
 def test_prune_encode_nm_validation(args, status):
-    assert _lib().snm_prune_encode_nm(*args) == status
+    assert _lib().snm_prune_encode_nm(*_nm(args, 4)) == status
 
 
 @pytest.mark.parametrize("args,status", [
@@ -107,7 +146,7 @@ def test_prune_encode_nm_validation(args, status):
     ((FAKE, 128, 64, 64, 64, 8, P(0), FAKE, FAKE, P(0)), 1),     # values NULL
 ])
 def test_prune_encode_vnm_validation(args, status):
-    assert _lib().snm_prune_encode_vnm(*args) == status
+    assert _lib().snm_prune_encode_vnm(*_vnm(args, 5)) == status
 
 
 @pytest.mark.parametrize("args,status", [
@@ -122,7 +161,7 @@ def test_prune_encode_vnm_validation(args, status):
     ((P(0), P(0), 16, 32, P(0), 0, 0, 0, P(0), 0, 1, 0, 0, 0, 0, P(0)), 0),      # C == 0: ok
 ])
 def test_spmm_nm_validation(args, status):
-    assert _lib().snm_spmm_nm(*args) == status
+    assert _lib().snm_spmm_nm(*_nm(args, 4)) == status
 
 
 @pytest.mark.parametrize("args,status", [
@@ -131,7 +170,7 @@ def test_spmm_nm_validation(args, status):
     ((FAKE, FAKE, P(0), 64, 64, 64, 8, FAKE, 8, 8, FAKE, 8, P(0)), 1),   # colloc NULL
 ])
 def test_spmm_vnm_validation(args, status):
-    assert _lib().snm_spmm_vnm(*args) == status
+    assert _lib().snm_spmm_vnm(*_vnm(args, 6)) == status
 
 
 @pytest.mark.parametrize("args,status", [
@@ -141,7 +180,7 @@ def test_spmm_vnm_validation(args, status):
     ((FAKE, 128, 64, 60, 64, 8, FAKE, FAKE, FAKE, P(0)), 2),     # lda < K
 ])
 def test_prune_encode_vnm_tiled_validation(args, status):
-    assert _lib().snm_prune_encode_vnm_tiled(*args) == status
+    assert _lib().snm_prune_encode_vnm_tiled(*_vnm(args, 5)) == status
 
 
 @pytest.mark.parametrize("args,status", [
@@ -154,7 +193,7 @@ def test_prune_encode_vnm_tiled_validation(args, status):
     ((P(0), P(0), P(0), 64, 64, 64, 8, P(0), 0, 0, P(0), 0, P(0)), 0),            # C == 0: ok
 ])
 def test_spmm_vnm_tiled_validation(args, status):
-    assert _lib().snm_spmm_vnm_tiled(*args) == status
+    assert _lib().snm_spmm_vnm_tiled(*_vnm(args, 6)) == status
 
 
 @pytest.mark.parametrize("args,status", [
@@ -164,7 +203,7 @@ def test_spmm_vnm_tiled_validation(args, status):
     ((FAKE, FAKE, 1, 16, 32, 64, ctypes.c_float(0.125), FAKE, FAKE, MISALIGNED, P(0)), 3),
 ])
 def test_sddmm_validation(args, status):
-    assert _lib().snm_sddmm_prune_nm(*args) == status
+    assert _lib().snm_sddmm_prune_nm(*_nm(args, 7)) == status
 
 
 @pytest.mark.parametrize("args,status", [
@@ -350,10 +389,10 @@ def test_empty_reduction_strides_carry_no_alignment_rule():
     # values, meta, R, K, B, C, ldb, b_layout, Y, ldy, batch, s_values, s_meta, s_B, s_Y, stream
     lib = _lib()
     # K = 16: a metadata batch stride that is not a multiple of 16 bytes is rejected
-    assert lib.snm_spmm_nm(FAKE, FAKE, 40, 16, FAKE, 8, 8, 0, FAKE, 8, 2, 320, 88, 128, 320, P(0)) == 3
+    assert lib.snm_spmm_nm(FAKE, FAKE, 40, 16, 2, 4, FAKE, 8, 8, 0, FAKE, 8, 2, 320, 88, 128, 320, P(0)) == 3
     # K = 0 (nothing is read): the same strides pass validation; without a GPU the call then
     # stops at the device check (SNM_E_DEVICE), with one it writes zeros (GPU test)
-    st = lib.snm_spmm_nm(FAKE, FAKE, 40, 0, FAKE, 8, 8, 0, FAKE, 8, 2, 40, 40, 0, 320, P(0))
+    st = lib.snm_spmm_nm(FAKE, FAKE, 40, 0, 2, 4, FAKE, 8, 8, 0, FAKE, 8, 2, 40, 40, 0, 320, P(0))
     assert st in (0, 5)
 
 
