@@ -838,6 +838,14 @@ def vnm_bytes(R, K, C, V, M):
     return R * (2 * K // M) * 2 + R * (K // M) // 2 + (R // V) * (K // M) * 4 + K * C * 2 + R * C * 2
 
 
+def big_lds_bytes(R, K, C, V, M):
+    """Bytes the large-tile V:2:M product copies global -> LDS per launch: for every 128 x 512
+    tile and every 32 positions of K' = 4K/M, 32 gathered B rows of 512 columns, the tile's
+    values and its index words zero-extended to dwords (37 KiB)."""
+    tiles = (R // 128) * -(-C // 512)
+    return tiles * (4 * K // M // 32) * (32768 + 4096 + 1024)
+
+
 def vnm_encode_bytes(R, K, V, M):
     return R * K * 2 + R * (2 * K // M) * 2 + R * (K // M) // 2 + (R // V) * (K // M) * 4
 
@@ -985,6 +993,17 @@ def measure_ceilings(lib, stream, windows=5) -> dict:
     out["copy_1GiB"] = {"GB/s": 2 * (1 << 30) / (ms * 1e-3) / 1e9, "avg_us": ms * 1e3,
                         "bytes": 2 * (1 << 30), "note": "read + write bytes"}
     del src, dst
+    # global -> LDS copies from a 2 MiB window (L2-resident), one workgroup of 8 waves per CU
+    win = torch.ones((2 << 20,), dtype=torch.uint8, device=dev)
+    fo = torch.empty((256,), dtype=torch.float32, device=dev)
+    fill_iters = 2048
+    fill = _bind(lib, "snm_ceiling_lds_fill", win.data_ptr(), 2 << 20, 256, fill_iters, fo.data_ptr(), s)
+    ms = _med(_windows(lambda i: fill(), 3, windows, stream))
+    nb = 256 * 8 * fill_iters * 1024
+    out["lds_fill_L2"] = {"GB/s": nb / (ms * 1e-3) / 1e9, "avg_us": ms * 1e3, "bytes": nb,
+                          "B_per_clk_per_CU_at_2.4GHz": nb / (ms * 1e-3) / 256 / 2.4e9,
+                          "note": "global->LDS DMA from a 2 MiB window, 256 workgroups x 8 waves"}
+    del win, fo
     wg, iters = 2048, 2048
     res = torch.empty((wg * 256,), dtype=torch.float32, device=dev)
     for kind, label, per in ((1, "smfmac_f32_32x32x32_f16", 65536), (0, "mfma_f32_32x32x16_f16", 32768)):
@@ -1044,7 +1063,8 @@ def run_headline(args) -> dict:
     ceil = measure_ceilings(lib, main, NW)
     res["ceilings"] = ceil
     print(f"ceilings: read 19MB {ceil['read_19MB']['GB/s']:.0f} GB/s, read 1GiB {ceil['read_1GiB']['GB/s']:.0f}, "
-          f"copy {ceil['copy_1GiB']['GB/s']:.0f}, smfmac {ceil['smfmac_f32_32x32x32_f16']['TFLOP/s']:.0f} TF/s, "
+          f"copy {ceil['copy_1GiB']['GB/s']:.0f}, LDS fill {ceil['lds_fill_L2']['GB/s']:.0f} "
+          f"({ceil['lds_fill_L2']['B_per_clk_per_CU_at_2.4GHz']:.1f} B/clk/CU), smfmac {ceil['smfmac_f32_32x32x32_f16']['TFLOP/s']:.0f} TF/s, "
           f"mfma {ceil['mfma_f32_32x32x16_f16']['TFLOP/s']:.0f} TF/s", file=sys.stderr, flush=True)
 
     # ---- the headline: V:2:16, V = 128, 8192x8192 . 8192x4096 ---------------------------
@@ -1415,7 +1435,7 @@ def main():
     ap.add_argument("--calibration-copy", action="store_true",
                     help=f"copy {CALIBRATION_BYTES >> 20} MiB once before timing (counter calibration)")
     ap.add_argument("--workload", default="headline",
-                    help="headline (default: the V:2:16 line with every configuration's kernels) or "
+                    help="headline (default: the V:2:16 line with every configuration's kernels) or ceilings or "
                          "nm_decode or vnm_64_2_8 / vnm_128_2_16 / attention_2_4 (per-kernel timings "
                          "only) or vnm_sweep or energy or bitmap or attention_2_4_bf16 / "
                          "attention_1_2_f32 or nm_decode_long_k")
@@ -1450,6 +1470,13 @@ def main():
     if args.workload == "vnm_sweep":
         fams = args.families.split(",") if args.families else None
         print(json.dumps(bench_sweep(args.steps, args.warmup, fams)))
+        return
+    if args.workload == "ceilings":
+        import torch
+        from structured_sparse_matrix_amd._lib import load as load_lib
+        torch.cuda.set_device(0)
+        print(json.dumps({"workload": "ceilings", "ceilings": measure_ceilings(load_lib(), torch.cuda.current_stream(),
+                                                                               args.windows)}))
         return
     if args.workload == "nm_decode":
         print(json.dumps(nm_decode_line(args)))
@@ -1491,6 +1518,9 @@ def main():
                      "frac_of_measured_smfmac": mmk.get("frac_of_measured_smfmac"),
                      "flops_per_launch": h["smfmac_flops"],
                      "algorithmic_bytes": vnm_bytes(h["R"], h["K"], h["C"], h["V"], h["M"]),
+                     "lds_fill_bytes": big_lds_bytes(h["R"], h["K"], h["C"], h["V"], h["M"]),
+                     "frac_of_measured_lds_fill": big_lds_bytes(h["R"], h["K"], h["C"], h["V"], h["M"])
+                     / (mmk["avg_us"] * 1e-6) / 1e9 / res["ceilings"]["lds_fill_L2"]["GB/s"],
                      "mfma_busy_frac": (mfma or {}).get("interleaved", {}).get("mfma_busy_frac"),
                      "basis": "smfmac flops 2*R*K'*C (K' = 4K/M) per launch / median per-launch duration "
                               "(HIP events around K back-to-back launches on the launch stream)"},

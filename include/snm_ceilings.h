@@ -33,6 +33,16 @@ snm_status snm_ceiling_read(const void* src, int64_t bytes, void* sink, void* st
  * overlapping) with 16-byte coalesced loads and stores. */
 snm_status snm_ceiling_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/* Global -> LDS copy loop (the DMA path through which the products stage their operands):
+ * `workgroups` workgroups of 8 waves, one per CU, each wave copying 1 KiB per iteration
+ * (16 bytes per lane, at most 16 copies in flight) for `iters` iterations from the first
+ * window_bytes bytes of src into its own LDS ring. window_bytes: a power of two, at least
+ * 1024 (a window of a few MiB stays in L2, so this measures how fast a CU fills its LDS from
+ * L2); src holds window_bytes bytes, 16-byte aligned. out: one float per workgroup, 4-byte
+ * aligned. Bytes moved per launch = workgroups * 8 * iters * 1024. */
+snm_status snm_ceiling_lds_fill(const void* src, int64_t window_bytes, int64_t workgroups, int64_t iters,
+                                float* out, void* stream);
+
 /* Matrix-instruction issue loop: `workgroups` workgroups of 4 waves; every wave runs
  * `iters` iterations of 4 independent accumulator chains of one instruction on register
  * operands (no memory traffic), then writes one float per lane to out (workgroups * 256

@@ -33,6 +33,7 @@ SIGNATURES = {
     "snm_spmm_nm_tiled_noalloc": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "snm_ceiling_read": [_vp, _i64, _vp, _vp],
     "snm_ceiling_copy": [_vp, _vp, _i64, _vp],
+    "snm_ceiling_lds_fill": [_vp, _i64, _i64, _i64, _vp, _vp],
     "snm_ceiling_matrix": [_int, _i64, _i64, _vp, _vp],
     "snm_spmm_vnm": [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
     "snm_spmm_vnm_tiled": [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],

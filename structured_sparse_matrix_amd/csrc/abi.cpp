@@ -373,6 +373,14 @@ snm_status snm_ceiling_copy(const void* src, void* dst, int64_t bytes, void* str
   return st(launched(snm::launch_ceiling_copy(src, dst, bytes, (hipStream_t)stream)));
 }
 
+snm_status snm_ceiling_lds_fill(const void* src, int64_t window_bytes, int64_t workgroups, int64_t iters,
+                                float* out, void* stream) {
+  int s = snm::check_ceiling_lds_fill(src, window_bytes, workgroups, iters, out);
+  if (s != SNM_OK || workgroups == 0) return st(s);
+  if ((s = check_device()) != SNM_OK) return st(s);
+  return st(launched(snm::launch_ceiling_lds_fill(src, window_bytes, workgroups, iters, out, (hipStream_t)stream)));
+}
+
 snm_status snm_ceiling_matrix(int kind, int64_t workgroups, int64_t iters, float* out, void* stream) {
   int s = snm::check_ceiling_matrix(kind, workgroups, iters, out);
   if (s != SNM_OK || workgroups == 0) return st(s);

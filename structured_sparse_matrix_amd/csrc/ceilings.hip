@@ -7,6 +7,10 @@
 //     working set as large as one decode product shows what a kernel of that size can
 //     reach (launch ramp, loaded latency and tail included); a read over 1 GiB shows the
 //     sustained HBM rate.
+//   * k_ceiling_lds_fill: global -> LDS copies (the DMA path the V:N:M products stage their
+//     operands through) from a window small enough to stay in L2, one workgroup of eight
+//     waves per CU: the rate at which a CU can fill its LDS, which bounds a product whose
+//     gathered operand rows are read from L2 once per workgroup.
 //   * k_ceiling_matrix<SPARSE>: each wave issues independent chains of one matrix
 //     instruction on register-resident operands, no memory traffic: the issue rate of
 //     v_smfmac_f32_32x32x32_f16 (SPARSE; counted as 2*32*32*32 flops, the dense equivalent
@@ -14,6 +18,7 @@
 //     (2*32*32*16 flops).
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "lds_dma.hpp"
 
 namespace snm {
 namespace {
@@ -51,6 +56,31 @@ __global__ void __launch_bounds__(kStreamThreads) k_ceiling_copy(const u4* __res
     for (int u = 0; u < kStreamUnroll; ++u) dst[i + u * stride] = v[u];
   }
   for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+constexpr int kFillWaves = 8;                 // waves per workgroup of the LDS-fill loop
+constexpr int kFillSlot = 8 * 1024;           // LDS ring per wave: 8 copies of 1 KiB
+constexpr int kFillLds = 96 * 1024;           // requested LDS: one workgroup per CU
+
+// Wave w of workgroup g copies 1 KiB per iteration (16 bytes per lane) from the window into
+// its own 8 KiB LDS ring, at most 16 copies in flight. Source offsets stay inside the window
+// (masked), LDS offsets inside the wave's ring.
+__global__ void __launch_bounds__(64 * kFillWaves) k_ceiling_lds_fill(const uint8_t* __restrict__ src,
+                                                                      uint64_t window_mask, int64_t iters,
+                                                                      float* __restrict__ out) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t ring = lds_addr(lds) + (uint32_t)(wave * kFillSlot);
+  const uint64_t base = ((uint64_t)blockIdx.x * kFillWaves + wave) * (uint64_t)iters * 1024u;
+  for (int64_t i = 0; i < iters; ++i) {
+    const uint64_t off = (base + (uint64_t)i * 1024u + (uint64_t)lane * 16u) & window_mask;
+    dma_v<16>(src + off, ring + (uint32_t)((i & 7) * 1024));
+    wait_vmcnt<16>();
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = (float)lds[wave * kFillSlot];
 }
 
 constexpr int kChains = 4;   // independent accumulator chains per wave
@@ -110,6 +140,15 @@ hipError_t launch_ceiling_copy(const void* src, void* dst, int64_t bytes, hipStr
   const int64_t n16 = bytes / 16;
   hipLaunchKernelGGL(k_ceiling_copy, dim3(stream_grid(n16)), dim3(kStreamThreads), 0, stream,
                      (const u4*)src, (u4*)dst, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_ceiling_lds_fill(const void* src, int64_t window_bytes, int64_t workgroups, int64_t iters,
+                                   float* out, hipStream_t stream) {
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit(lds_set, (const void*)k_ceiling_lds_fill, kFillLds)) return e;
+  hipLaunchKernelGGL(k_ceiling_lds_fill, dim3((unsigned)workgroups), dim3(64 * kFillWaves), kFillLds, stream,
+                     (const uint8_t*)src, (uint64_t)(window_bytes - 1), iters, out);
   return hipGetLastError();
 }
 

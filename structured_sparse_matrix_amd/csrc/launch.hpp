@@ -111,6 +111,8 @@ hipError_t launch_spmm_bitmap(const uint64_t* bitmaps, const uint32_t* offsets, 
 // Measured ceilings (ceilings.hip): plain streams and matrix-instruction issue loops.
 hipError_t launch_ceiling_read(const void* src, int64_t bytes, void* sink, hipStream_t stream);
 hipError_t launch_ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+hipError_t launch_ceiling_lds_fill(const void* src, int64_t window_bytes, int64_t workgroups, int64_t iters,
+                                   float* out, hipStream_t stream);
 hipError_t launch_ceiling_matrix(int sparse, int64_t workgroups, int64_t iters, float* out, hipStream_t stream);
 hipError_t launch_softmax_nm_rows(void* values, int64_t rows, int64_t kept, int64_t ld, bool bf16,
                                   hipStream_t stream);

@@ -340,6 +340,17 @@ int check_ceiling_stream(const void* src, const void* dst, int64_t bytes) {
   return SNM_OK;
 }
 
+int check_ceiling_lds_fill(const void* src, int64_t window_bytes, int64_t workgroups, int64_t iters,
+                           const void* out) {
+  if (window_bytes < 1024 || window_bytes > ((int64_t)1 << 40) || (window_bytes & (window_bytes - 1)) != 0)
+    return SNM_E_SHAPE;
+  if (workgroups < 0 || workgroups > 0x7FFFFFFF || iters < 0) return SNM_E_SHAPE;
+  if (workgroups == 0) return SNM_OK;
+  if (!src || !out) return SNM_E_NULL;
+  if (((uintptr_t)src & 15u) != 0 || ((uintptr_t)out & 3u) != 0) return SNM_E_ALIGN;
+  return SNM_OK;
+}
+
 int check_ceiling_matrix(int kind, int64_t workgroups, int64_t iters, const void* out) {
   if (kind != 0 && kind != 1) return SNM_E_UNSUPPORTED;
   if (workgroups < 0 || workgroups > 0x7FFFFFFF || iters < 0) return SNM_E_SHAPE;

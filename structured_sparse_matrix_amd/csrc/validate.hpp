@@ -53,6 +53,8 @@ int check_spmm_bitmap(const void* bitmaps, const void* offsets, const void* valu
                       int64_t ldy);
 int check_softmax_nm_rows(const void* values, int64_t rows, int64_t kept, int64_t ld);
 int check_ceiling_stream(const void* src, const void* dst, int64_t bytes);
+int check_ceiling_lds_fill(const void* src, int64_t window_bytes, int64_t workgroups, int64_t iters,
+                           const void* out);
 int check_ceiling_matrix(int kind, int64_t workgroups, int64_t iters, const void* out);
 
 // Split-reduction plan of the operand-major 2:4 decode product (snm_spmm_nm_tiled_ws):

@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 output for the profiles/ folder.
 
   python -m structured_sparse_matrix_amd.profiling kernels TRACE_CSV [--match snm] [--skip N]
-         [--groups G] [--alone]
+         [--groups G] [--alone] [--dispatch A:B]
       Markdown table of kernel dispatch durations (calls, mean, median, min, max) from a
       `rocprofv3 --kernel-trace -f csv` run. --groups G splits each kernel's dispatches, in
       dispatch order, into G equal consecutive groups reported as separate rows (a program
@@ -66,7 +66,7 @@ def _alone(spans):
     return flags
 
 
-def _durations(path, match, skip, alone=False):
+def _durations(path, match, skip, alone=False, dispatch=None):
     rows = list(csv.DictReader(open(path)))
     spans = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
     keep = _alone(spans) if alone else [True] * len(rows)
@@ -75,13 +75,15 @@ def _durations(path, match, skip, alone=False):
         name = r["Kernel_Name"]
         if not k or (match and match not in name):
             continue
+        if dispatch and not dispatch[0] <= int(r["Dispatch_Id"]) <= dispatch[1]:
+            continue
         by.setdefault(name, []).append(e - b)
     return {k: v[skip:] if len(v) > skip else v for k, v in by.items()}
 
 
-def kernels_table(path, match, skip, groups=1, alone=False):
+def kernels_table(path, match, skip, groups=1, alone=False, dispatch=None):
     rows = ["| kernel | calls | mean us | median us | min us | max us |", "|---|---|---|---|---|---|"]
-    for name, ds in sorted(_durations(path, match, skip, alone).items(), key=lambda kv: -sum(kv[1])):
+    for name, ds in sorted(_durations(path, match, skip, alone, dispatch).items(), key=lambda kv: -sum(kv[1])):
         short = name if len(name) < 110 else name[:107] + "..."
         n = len(ds) // groups if groups > 1 and len(ds) % groups == 0 else len(ds)
         parts = [ds[i:i + n] for i in range(0, len(ds), n)]
@@ -166,6 +168,7 @@ def main(argv=None):
     k.add_argument("--groups", type=int, default=1)
     k.add_argument("--alone", action="store_true",
                    help="only dispatches that overlapped no other dispatch in time")
+    k.add_argument("--dispatch", default="", help="A:B -- only dispatch ids A..B (inclusive)")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -189,7 +192,8 @@ def main(argv=None):
     m.add_argument("--command", default="")
     a = ap.parse_args(argv)
     if a.cmd == "kernels":
-        print(kernels_table(a.trace, a.match, a.skip, a.groups, a.alone))
+        rng = tuple(int(x) for x in a.dispatch.split(":")) if a.dispatch else None
+        print(kernels_table(a.trace, a.match, a.skip, a.groups, a.alone, rng))
     elif a.cmd == "mfma":
         out = mfma(a.counters, a.match, a.groups, a.cus, a.xcds)
         for g, lab in zip(out["groups"], [x for x in a.labels.split(",") if x]):

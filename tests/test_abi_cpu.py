@@ -436,4 +436,10 @@ def test_ceiling_validation():
     assert lib.snm_ceiling_matrix(2, 8, 8, FAKE, P(0)) == 4
     assert lib.snm_ceiling_matrix(1, -1, 8, FAKE, P(0)) == 2
     assert lib.snm_ceiling_matrix(0, 8, 8, P(0), P(0)) == 1
+    assert lib.snm_ceiling_lds_fill(FAKE, 3 << 20, 8, 8, FAKE, P(0)) == 2   # window not a power of two
+    assert lib.snm_ceiling_lds_fill(FAKE, 512, 8, 8, FAKE, P(0)) == 2       # window < one copy
+    assert lib.snm_ceiling_lds_fill(FAKE, 1 << 21, -1, 8, FAKE, P(0)) == 2
+    assert lib.snm_ceiling_lds_fill(P(0), 1 << 21, 8, 8, FAKE, P(0)) == 1
+    assert lib.snm_ceiling_lds_fill(MISALIGNED, 1 << 21, 8, 8, FAKE, P(0)) == 3
+    assert lib.snm_ceiling_lds_fill(P(0), 1 << 21, 0, 8, P(0), P(0)) == 0   # empty: nothing enqueued
     assert lib.snm_ceiling_matrix(1, 0, 8, P(0), P(0)) == 0
