@@ -128,3 +128,35 @@ def test_encode_is_deterministic():
     a2 = [to_host(x) for x in snm.prune_encode_nm(A)]
     for x, y in zip(a1, a2):
         assert_bits_equal(x, y, "repeat")
+
+
+def _permuted_columns(seed, V, M, G, big):
+    """Every group's M columns hold row permutations of one column of values, so the exact
+    column sums of squares are equal within a group. small: |a| <= 1/16, every float64 sum
+    of the squares is exact in any order (the scores tie; the lower column wins). big: each
+    column mixes values near 8 with values near 2^-18, so the float64 row-order sum rounds
+    and permuted columns get scores that differ in their last bits."""
+    rng = np.random.default_rng(seed)
+    A = np.empty((V, G * M), dtype=np.float16)
+    for g in range(G):
+        if big:
+            x = np.where(rng.random(V) < 0.5, rng.uniform(4, 12, V), rng.uniform(1, 2, V) * 2.0 ** -18)
+        else:
+            x = rng.uniform(-1, 1, V) / 16
+        x = (x * np.where(rng.random(V) < 0.5, -1, 1)).astype(np.float16)
+        for j in range(M):
+            A[:, g * M + j] = x[rng.permutation(V)]
+    return A
+
+
+@pytest.mark.parametrize("big", [False, True])
+def test_vnm_scores_order_of_summation(big):
+    """The encoder sums column scores in any order where float64 is exact and in row order
+    where it is not; both must give the oracle's column selection bit for bit."""
+    V, M, G = 128, 16, 32
+    A = _permuted_columns(41 + big, V, M, G, big)
+    A = np.concatenate([A, A[::-1]], axis=0)   # two V-blocks
+    _check_vnm(A, V, M, f"permuted columns, {'rounded' if big else 'exact'} sums")
+    if not big:   # every group's scores tie: the lowest four columns
+        ov, omi, ocl = oracle.prune_encode_vnm(A, V, M)
+        assert np.all(ocl.reshape(-1, 4) == np.arange(4, dtype=np.uint8))
