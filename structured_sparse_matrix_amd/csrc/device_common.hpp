@@ -78,30 +78,37 @@ __device__ __forceinline__ _Float16 bits_f16(uint16_t x) { return __builtin_bit_
 // fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default rounding mode).
 __device__ __forceinline__ _Float16 to_f16(float x) { return (_Float16)x; }
 
-// 2 of 4 by magnitude on composite keys: key_i = |h_i| << 2 | (3 - i), where |h| is the
-// fp16 pattern without its sign (orders like the magnitude; NaN > Inf > finite), so a
+// 2 of 4 by magnitude on composite keys: key_i = |h_i| << 16 | t_i, where |h| is the fp16
+// pattern without its sign (orders like the magnitude; NaN > Inf > finite) and the tie
+// field t = 0xFFFF, 0xFF00, 0x00FF, 0x0000 for slots 0..3 decreases with the slot, so a
 // larger key means a larger magnitude or, on equal magnitudes, a lower slot -- the
-// lower-slot-wins tie rule. The two largest keys are the kept slots (a 6-operation
-// max/min network instead of pairwise ranks). Inputs are the group's four fp16 patterns
-// packed in pairs (p01 = h0 | h1 << 16, p23 = h2 | h3 << 16); the kept pair, ascending
-// slot order, comes back packed the same way, gathered with one byte permute.
+// lower-slot-wins tie rule. Every key is one byte permute of the sign-cleared pair (the
+// tie bytes are the permute's constant 0x00 / 0xFF bytes), and bits 8..7 of a key are
+// 3 - slot. The two largest keys are the kept slots (a 6-operation max/min network instead
+// of pairwise ranks). Inputs are the group's four fp16 patterns packed in pairs
+// (p01 = h0 | h1 << 16, p23 = h2 | h3 << 16); the kept pair, ascending slot order, comes
+// back packed the same way, gathered with one byte permute. Returns the group's code
+// s0 | s1 << 2 (s0 < s1, the kept slots).
 __device__ __forceinline__ uint32_t select_2of4_keys(uint32_t p01, uint32_t p23, uint32_t& kept) {
-  const uint32_t c0 = ((p01 & 0x7FFFu) << 2) | 3u;
-  const uint32_t c1 = ((p01 >> 14) & 0x1FFFCu) | 2u;
-  const uint32_t c2 = ((p23 & 0x7FFFu) << 2) | 1u;
-  const uint32_t c3 = (p23 >> 14) & 0x1FFFCu;
+  const uint32_t a01 = p01 & 0x7FFF7FFFu, a23 = p23 & 0x7FFF7FFFu;
+  // permute selectors: byte i of the result is byte sel_i of the pair (0..3), or 0x00
+  // (0x0C) or 0xFF (0x0D)
+  const uint32_t c0 = __builtin_amdgcn_perm(a01, a01, 0x01000D0Du);   // |h0| : FF FF
+  const uint32_t c1 = __builtin_amdgcn_perm(a01, a01, 0x03020D0Cu);   // |h1| : FF 00
+  const uint32_t c2 = __builtin_amdgcn_perm(a23, a23, 0x01000C0Du);   // |h2| : 00 FF
+  const uint32_t c3 = a23 & 0xFFFF0000u;                              // |h3| : 00 00
   const uint32_t m01 = c0 > c1 ? c0 : c1, n01 = c0 > c1 ? c1 : c0;
   const uint32_t m23 = c2 > c3 ? c2 : c3, n23 = c2 > c3 ? c3 : c2;
   const uint32_t t1 = m01 > m23 ? m01 : m23;
   const uint32_t lo_m = m01 > m23 ? m23 : m01;
   const uint32_t hi_n = n01 > n23 ? n01 : n23;
   const uint32_t t2 = lo_m > hi_n ? lo_m : hi_n;
-  const uint32_t x = t1 & 3u, y = t2 & 3u;   // 3 - slot of the two kept entries
-  const uint32_t s0 = 3u - (x > y ? x : y);
-  const uint32_t s1 = 3u - (x > y ? y : x);
-  // bytes 2 s0, 2 s0 + 1, 2 s1, 2 s1 + 1 of {p23 : p01}
-  kept = __builtin_amdgcn_perm(p23, p01, (s0 | (s1 << 16)) * 0x0202u + 0x01000100u);
-  return s0 | (s1 << 2);
+  const uint32_t x = (t1 >> 7) & 3u, y = (t2 >> 7) & 3u;   // 3 - slot of the two kept entries
+  const uint32_t hi = x > y ? x : y, lo = x > y ? y : x;   // 3 - s0, 3 - s1
+  // selector bytes 2 s0, 2 s0 + 1, 2 s1, 2 s1 + 1 of {p23 : p01}:
+  // (s0 | s1 << 16) * 0x0202 + 0x01000100 with s = 3 - (3 - s)
+  kept = __builtin_amdgcn_perm(p23, p01, 0x07060706u - (hi | (lo << 16)) * 0x0202u);
+  return 15u - (hi | (lo << 2));
 }
 
 }  // namespace snm
