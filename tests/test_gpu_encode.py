@@ -160,3 +160,31 @@ def test_vnm_scores_order_of_summation(big):
     if not big:   # every group's scores tie: the lowest four columns
         ov, omi, ocl = oracle.prune_encode_vnm(A, V, M)
         assert np.all(ocl.reshape(-1, 4) == np.arange(4, dtype=np.uint8))
+
+
+@pytest.mark.parametrize("R,K,V,M,pad", [
+    (8192, 3104, 32, 8, 0),     # 388 groups per row: the last workgroup chunk is ragged
+    (8192, 2048, 128, 16, 8),   # rows 8 elements longer than K (a view of a wider array)
+    (4096, 4096, 64, 4, 0),     # M = 4: every column kept
+])
+def test_vnm_encoder_large_shapes(R, K, V, M, pad):
+    """Large encodes, canonical and row-group interleaved: many workgroup chunks with a
+    ragged last one, rows of a wider array, M = 4."""
+    import torch
+    snm = _snm()
+    A = workloads.small_matrix(R + K + V + M + pad, (R, K), 0.02)
+    buf = torch.zeros((R, K + pad), dtype=torch.float16, device="cuda")
+    buf[:, :K] = to_dev(A)
+    v, mi, cl = snm.prune_encode_vnm(buf[:, :K], V, M)
+    vt, mit, clt = snm.prune_encode_vnm_tiled(buf[:, :K], V, M) if V % 32 == 0 else (None, None, None)
+    ov, omi, ocl = oracle.prune_encode_vnm(A, V, M)
+    what = f"{R}x{K} V{V} M{M} pad {pad}"
+    assert_bits_equal(to_host(cl), ocl, what + " colloc")
+    assert_bits_equal(to_host(mi), omi, what + " midx")
+    assert_bits_equal(to_host(v), ov, what + " values")
+    if vt is not None:
+        from _vnm_tiled import untile
+        uv, umi = untile(to_host(vt), to_host(mit), M)
+        assert_bits_equal(to_host(clt), ocl, what + " colloc (interleaved)")
+        assert_bits_equal(umi, omi, what + " midx (interleaved)")
+        assert_bits_equal(uv, ov, what + " values (interleaved)")
