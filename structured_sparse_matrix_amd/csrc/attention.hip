@@ -90,18 +90,22 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
       }
     }
 
-    // K ring: slot t % 4 holds key tile t; tile t + 3 is requested while tile t is used
+    // K ring: slot t % 4 holds key tile t; tile t + 3 is requested while tile t is used.
+    // Requests past the last tile load the last tile again (nkt >= 1 where this runs), so
+    // every path through a block issues the same loads and the waits the compiler derives
+    // for each slot are exact instead of the worst case over skipped loads.
     h8 kr[4][KSTEPS];
     auto load_k = [&](int64_t t, h8 (&kf)[KSTEPS]) {
-      if (t < nkt) {
+      const int64_t tc = t < nkt ? t : nkt - 1;
 #pragma unroll
-        for (int j = 0; j < KSTEPS; ++j)
-          kf[j] = *reinterpret_cast<const h8*>(Kb + (t * 32 + l32) * D + 16 * j + 8 * half);
-      }
+      for (int j = 0; j < KSTEPS; ++j)
+        kf[j] = *reinterpret_cast<const h8*>(Kb + (tc * 32 + l32) * D + 16 * j + 8 * half);
     };
-    load_k(0, kr[0]);
-    load_k(1, kr[1]);
-    load_k(2, kr[2]);
+    if (nkt > 0) {
+      load_k(0, kr[0]);
+      load_k(1, kr[1]);
+      load_k(2, kr[2]);
+    }
     hh2 rmx[QT];     // running max of the kept scores of each query tile's row (RMAX, fp16)
     float rmf[QT];   // the same for bf16
 #pragma unroll
@@ -110,6 +114,9 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
       rmf[qt] = -__builtin_inff();
     }
 
+    // the first K tiles and Q are in registers before the loop: the loop head then has no
+    // load to wait for on either path into it
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     for (int64_t t0 = 0; t0 < nkt; t0 += KT) {
       const int nk = (int)(nkt - t0 < KT ? nkt - t0 : KT);
 #pragma unroll
@@ -155,17 +162,30 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
           if (!half) *reinterpret_cast<uint32_t*>(sm + (qt * 32 + l32) * MP + mcol * 4) = mword;
         }
       }
-      // ---- values: the 4 staged tiles of every row as one 128-byte line
+      // Every K tile requested so far (up to 3 tiles ahead) has arrived before the flush is
+      // issued: waiting for a load issued after a store must wait for the store too (loads
+      // and stores share one counter and may complete out of order), so a wait after the
+      // flush would drain it. Waiting here instead leaves the next tiles nothing to wait for
+      // until the flush is old. (vmcnt(0), other counters untouched)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      // ---- values: the 4 staged tiles of every row as one 128-byte line. Every staged
+      // chunk is read first (the reads stay inside the wave's buffer) and then stored, so
+      // the LDS latency is paid once per flush, not once per store.
+      {
+        u4 vv[QT][4];
+        const int ch = lane & 7;               // 16-byte chunk = 8 kept values
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
+        for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 8 * i + (lane >> 3);
-          const int ch = lane & 7;             // 16-byte chunk = 8 kept values
-          const int64_t qi = q_wave + qt * 32 + row;
-          if (ch < 2 * nk && qi < Lq) {
-            const u4 v = *reinterpret_cast<const u4*>(sv + (qt * 32 + row) * VP + ch * 16);
-            __builtin_nontemporal_store(v, reinterpret_cast<u4*>(vals_b + qi * (Lk >> 1) + t0 * 16 + ch * 8));
+          for (int i = 0; i < 4; ++i)
+            vv[qt][i] = *reinterpret_cast<const u4*>(sv + (qt * 32 + 8 * i + (lane >> 3)) * VP + ch * 16);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t qi = q_wave + qt * 32 + 8 * i + (lane >> 3);
+            if (ch < 2 * nk && qi < Lq)
+              __builtin_nontemporal_store(vv[qt][i], reinterpret_cast<u4*>(vals_b + qi * (Lk >> 1) + t0 * 16 + ch * 8));
           }
         }
       }
@@ -174,21 +194,26 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
       if (tend % MT == 0 || tend == nkt) {
         const int64_t m0 = (tend - 1) / MT * MT;   // first tile of this metadata line
         const int nw = (int)(tend - m0);           // 4-byte words staged per row
+        const int ch = lane & 7;               // 16-byte chunk = 4 words = 4 key tiles
+        u4 mm[QT][4];                          // all staged chunks first, as for the values
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            mm[qt][i] = *reinterpret_cast<const u4*>(sm + (qt * 32 + 8 * i + (lane >> 3)) * MP + ch * 16);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = 8 * i + (lane >> 3);
-            const int ch = lane & 7;           // 16-byte chunk = 4 words = 4 key tiles
-            const int64_t qi = q_wave + qt * 32 + row;
+            const int64_t qi = q_wave + qt * 32 + 8 * i + (lane >> 3);
             if (qi < Lq) {
-              const uint8_t* src = sm + (qt * 32 + row) * MP + ch * 16;
               uint8_t* dst = meta_b + qi * (Lk >> 3) + m0 * 4 + ch * 16;
               if (4 * ch + 4 <= nw && (Lk & 127) == 0) {
-                __builtin_nontemporal_store(*reinterpret_cast<const u4*>(src), reinterpret_cast<u4*>(dst));
+                __builtin_nontemporal_store(mm[qt][i], reinterpret_cast<u4*>(dst));
               } else {
-                for (int w = 4 * ch; w < 4 * ch + 4 && w < nw; ++w)
-                  reinterpret_cast<uint32_t*>(dst)[w - 4 * ch] = reinterpret_cast<const uint32_t*>(src)[w - 4 * ch];
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                  if (4 * ch + w < nw) reinterpret_cast<uint32_t*>(dst)[w] = mm[qt][i][w];
               }
             }
           }
