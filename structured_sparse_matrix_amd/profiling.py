@@ -26,6 +26,15 @@
       (MFMA busy cycles, summed over SIMDs, over the per-XCD GUI-active cycles x CUs x 4
       SIMDs; GRBM_GUI_ACTIVE is summed over the XCDs) and the fp16 matrix operations
       (MOPS x 512). Prints JSON with the wide-kernel source hash.
+
+  python -m structured_sparse_matrix_amd.profiling counters COUNTER_CSV --match NAME
+         [--sources attention|wide|decode] [--workload W] [--command CMD]
+      Per-dispatch means of every counter of one `rocprofv3 --pmc ...` run for the kernels
+      whose name contains NAME (summed over the per-XCD / per-instance rows of a dispatch),
+      with the derived per-wave figures where the counters are present: instructions per
+      wave (SQ_INSTS_* / SQ_WAVES) and the share of wave cycles spent issuing VALU
+      instructions (SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES) or waiting (SQ_WAIT_INST_ANY /
+      SQ_WAVE_CYCLES). Prints JSON with the source hash of the named kernel family.
 """
 from __future__ import annotations
 
@@ -40,6 +49,8 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 DECODE_KERNEL_SOURCES = ("spmm_skinny.hip", "device_common.hpp")
 WIDE_KERNEL_SOURCES = ("spmm_wide.hip", "spmm_vnm_big.hip", "lds_dma.hpp", "wide_layout.hpp", "elem.hpp",
                        "device_common.hpp")
+ATTENTION_KERNEL_SOURCES = ("attention.hip", "elem.hpp", "device_common.hpp")
+SOURCES = {"decode": DECODE_KERNEL_SOURCES, "wide": WIDE_KERNEL_SOURCES, "attention": ATTENTION_KERNEL_SOURCES}
 
 
 def kernel_source_hash(files=DECODE_KERNEL_SOURCES) -> str:
@@ -158,6 +169,34 @@ def mfma(csv_path, match, groups=1, cus=256, xcds=8):
     return {"kernel_match": match, "groups": out, "cus": cus, "xcds": xcds}
 
 
+def counters(csv_path, match):
+    per = {}
+    name = None
+    for r in csv.DictReader(open(csv_path)):
+        if match not in r["Kernel_Name"]:
+            continue
+        name = name or r["Kernel_Name"]
+        d = per.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    rows = [per[i] for i in sorted(per)]
+    keys = sorted({k for r in rows for k in r})
+    mean = {k: statistics.mean(r[k] for r in rows if k in r) for k in keys}
+    out = {"kernel_match": match, "kernel_name": (name or "")[:120], "dispatches": len(rows), "per_dispatch_mean": mean}
+    derived = {}
+    waves = mean.get("SQ_WAVES")
+    if waves:
+        for k in keys:
+            if k.startswith("SQ_INSTS_"):
+                derived[k + "_per_wave"] = mean[k] / waves
+    cyc = mean.get("SQ_WAVE_CYCLES")
+    if cyc:
+        for k in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY"):
+            if k in mean:
+                derived[k + "_share_of_wave_cycles"] = mean[k] / cyc
+    out["derived"] = derived
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -190,10 +229,22 @@ def main(argv=None):
     m.add_argument("--labels", default="", help="comma-separated names of the groups")
     m.add_argument("--workload", default="")
     m.add_argument("--command", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("counters")
+    c.add_argument("--match", required=True)
+    c.add_argument("--sources", choices=tuple(SOURCES), default="attention")
+    c.add_argument("--workload", default="")
+    c.add_argument("--command", default="")
     a = ap.parse_args(argv)
     if a.cmd == "kernels":
         rng = tuple(int(x) for x in a.dispatch.split(":")) if a.dispatch else None
         print(kernels_table(a.trace, a.match, a.skip, a.groups, a.alone, rng))
+    elif a.cmd == "counters":
+        out = counters(a.counters, a.match)
+        out["workload"] = a.workload
+        out["kernel_source_hash"] = kernel_source_hash(SOURCES[a.sources])
+        out["command"] = a.command
+        print(json.dumps(out, indent=1))
     elif a.cmd == "mfma":
         out = mfma(a.counters, a.match, a.groups, a.cus, a.xcds)
         for g, lab in zip(out["groups"], [x for x in a.labels.split(",") if x]):
