@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libsnm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["encode.hip", "spmm.hip", "spmm_skinny.hip", "spmm_splitk.hip", "spmm_wide.hip",
-           "spmm_vnm_big.hip", "attention.hip", "attention_f32.hip", "bitmap.hip", "ceilings.hip",
+           "spmm_vnm_big.hip", "spmm_vnm_big64.hip", "attention.hip", "attention_f32.hip", "bitmap.hip", "ceilings.hip",
            "validate.cpp", "variant.cpp", "abi.cpp"]
 
 COMMON_FLAGS = [

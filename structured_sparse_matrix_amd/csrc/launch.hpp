@@ -80,6 +80,11 @@ bool spmm_vnm_big_eligible(int64_t R, int64_t Kc, int V, int M, const void* B, i
 hipError_t launch_spmm_vnm_big(const void* values, const void* meta, const void* colloc, int64_t R,
                                int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
                                int64_t ldy, bool a_tiled, hipStream_t stream);
+// the same product with 64-row tiles (spmm_vnm_big64.hip): V % 64 == 0
+bool spmm_vnm_big64_eligible(int64_t R, int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb);
+hipError_t launch_spmm_vnm_big64(const void* values, const void* meta, const void* colloc, int64_t R,
+                                 int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb, void* Y,
+                                 int64_t ldy, bool a_tiled, hipStream_t stream);
 // V:2:M product with values and m-indices in the row-group interleaved storage (wide
 // kernel only: V % 32 == 0 and the shape rules of spmm_wide_supported)
 hipError_t launch_spmm_vnm_tiled(const void* values_t, const void* midx_t, const void* colloc,

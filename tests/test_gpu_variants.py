@@ -3,8 +3,9 @@ each setting runs in a child process of its own (one at a time). Every forced va
 give the oracle's product, and SNM_LOG must name the variant that ran.
 
 Shapes: a V:2:16 product with V = 128 whose grid is too small for the large-tile kernel by
-default (so 'large' changes the choice and 'wide' keeps it), and a decode-shaped 2:4 product
-with C = 8 (skinny by default, 'generic' forces the generic tiled kernel)."""
+default (so 'large' changes the choice and 'wide' keeps it), the same for V:2:8 with V = 64
+and the 64-row large-tile kernel (both storages), and a decode-shaped 2:4 product with C = 8
+(skinny by default, 'generic' forces the generic tiled kernel)."""
 import os
 import subprocess
 import sys
@@ -30,7 +31,14 @@ CHILD = textwrap.dedent("""
     import structured_sparse_matrix_amd as snm
     dev = torch.device("cuda:0")
     kind, out = sys.argv[1], sys.argv[2]
-    if kind == "vnm":
+    if kind in ("vnm64", "vnm64t"):   # V = 64, ragged second column tile
+        A = workloads.small_matrix(15, (1024, 2048), 0.02)
+        B = workloads.small_matrix(16, (2048, 264))
+        enc = snm.prune_encode_vnm_tiled if kind == "vnm64t" else snm.prune_encode_vnm
+        mm = snm.spmm_vnm_tiled if kind == "vnm64t" else snm.spmm_vnm
+        v, mi, cl = enc(torch.from_numpy(A).to(dev), 64, 8)
+        Y = mm(v, mi, cl, torch.from_numpy(B).to(dev), 64, 8)
+    elif kind == "vnm":
         A = workloads.small_matrix(11, (1024, 2048), 0.02)
         B = workloads.small_matrix(12, (2048, 512))
         v, mi, cl = snm.prune_encode_vnm(torch.from_numpy(A).to(dev), 128, 16)
@@ -70,6 +78,21 @@ def test_vnm_forced_variant_matches_oracle(force, expect, tmp_path):
     ov, omi, ocl = oracle.prune_encode_vnm(A, 128, 16)
     assert_fp16_close(Y, oracle.spmm_vnm(ov, omi, ocl, 128, 16, B))
     assert any(ln.startswith("snm: spmm_vnm R=1024 K=2048 C=512 -> ") and ln.endswith(expect)
+               for ln in lines), lines
+
+
+@pytest.mark.parametrize("kind", ["vnm64", "vnm64t"])
+@pytest.mark.parametrize("force,expect", [("", "wide 64x128"), ("wide", "wide 64x128"), ("large", "large 64x256")])
+def test_vnm64_forced_variant_matches_oracle(kind, force, expect, tmp_path):
+    """V = 64 (K' = 1024): the default grid (32 tiles of 64 x 256) is below the 64-row
+    large-tile kernel's threshold, 'large' forces it (second column tile ragged: C = 264)."""
+    Y, lines = _run(kind, force, tmp_path)
+    A = workloads.small_matrix(15, (1024, 2048), 0.02)
+    B = workloads.small_matrix(16, (2048, 264))
+    ov, omi, ocl = oracle.prune_encode_vnm(A, 64, 8)
+    assert_fp16_close(Y, oracle.spmm_vnm(ov, omi, ocl, 64, 8, B))
+    op = "spmm_vnm_tiled" if kind == "vnm64t" else "spmm_vnm"
+    assert any(ln.startswith(f"snm: {op} R=1024 K=2048 C=264 -> ") and ln.endswith(expect)
                for ln in lines), lines
 
 
