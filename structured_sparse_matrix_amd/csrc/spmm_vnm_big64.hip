@@ -74,6 +74,7 @@ struct Big64Args {
   int V, M;
   int a_tiled;
   int y_vec;
+  int xcd_remap;   // the workgroup count is a multiple of 8
 };
 
 template <int I>
@@ -103,8 +104,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
 
-  const int64_t ct = (int64_t)blockIdx.x / a.n_row_tiles;
-  const int64_t rt = (int64_t)blockIdx.x - ct * a.n_row_tiles;
+  // tile of this workgroup (XCD-aware: the workgroups resident on one XCD share a run of
+  // column strips of B in its L2)
+  int64_t L = blockIdx.x;
+  if (a.xcd_remap) L = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int64_t ct = L / a.n_row_tiles;
+  const int64_t rt = L - ct * a.n_row_tiles;
   const int64_t row0 = rt * BM;
   const int64_t col0 = ct * BN;
   const int64_t Kc = a.Kc;
@@ -367,6 +372,7 @@ hipError_t launch_spmm_vnm_big64(const void* values, const void* meta, const voi
   a.a_tiled = a_tiled ? 1 : 0;
   a.y_vec = ((uintptr_t)Y & 15) == 0 && ldy % 8 == 0;
   const int64_t tiles = a.n_row_tiles * ((C + BN - 1) / BN);
+  a.xcd_remap = tiles % 8 == 0;
   static std::atomic<uint64_t> lds_set{0};
   if (hipError_t e = ensure_lds_limit(lds_set, (const void*)k_spmm_vnm_big64, kLdsLimit)) return e;
   hipLaunchKernelGGL(k_spmm_vnm_big64, dim3((unsigned)tiles), dim3(THREADS), kLdsLimit, stream, a);

@@ -566,11 +566,11 @@ hipError_t launch_spmm_wide(const void* values, const void* meta, const void* co
       log_variant(op, R, K, C, "large 128x512");
       return launch_spmm_vnm_big(values, meta, colloc, R, Kc, V, M, B, C, ldb, Y, ldy, a_tiled, stream);
     }
-    // its 64-row form where V-blocks are not whole 128-row tiles: one workgroup per V-block
-    // and 256 columns gathers the block's B rows once (the 64 x 128 wide tiles gather them
-    // once per column tile); measured 23.7 against 26.3 us on 11008 x 4096 . 4096 x 256, V = 64
+    // its 64 x 256 form wherever that grid has at least 128 workgroups: measured 23.6
+    // against 26.4 us (wide 64 x 128) on 11008 x 4096 . 4096 x 256 with V = 64, and 7-20 %
+    // faster than the wide tiles on the 1024-row V = 64 and V = 128 products of the sweep
     if (a.batch == 1 && f != Variant::kWide && spmm_vnm_big64_eligible(R, Kc, V, M, B, C, ldb) &&
-        (f == Variant::kLarge || (V % 128 != 0 && (R / 64) * ((C + 255) / 256) >= 128))) {
+        (f == Variant::kLarge || (R / 64) * ((C + 255) / 256) >= 128)) {
       log_variant(op, R, K, C, "large 64x256");
       return launch_spmm_vnm_big64(values, meta, colloc, R, Kc, V, M, B, C, ldb, Y, ldy, a_tiled, stream);
     }
