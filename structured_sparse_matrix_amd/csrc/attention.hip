@@ -55,7 +55,8 @@ template <int D, int QT, bool DENSE, bool RMAX, bool BF>
 __global__ void __launch_bounds__(512)
 k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, int64_t batch,
               int64_t Lq, int64_t Lk, float scale, uint16_t* __restrict__ values,
-              uint16_t* __restrict__ meta, uint16_t* __restrict__ S, float* __restrict__ rowmax) {
+              uint16_t* __restrict__ meta, uint16_t* __restrict__ S, float* __restrict__ rowmax,
+              int xcd_remap) {
   using Cfg = SddmmCfg<D, QT>;
   using E = Elem<BF>;
   constexpr int KSTEPS = Cfg::KSTEPS, KT = Cfg::KT, MT = Cfg::MT, VP = Cfg::VP, MP = Cfg::MP;
@@ -66,10 +67,22 @@ k_sddmm_prune(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Km, i
   const int l32 = lane & 31;
   uint8_t* const sv = smem + wave * Cfg::kWaveV;
   uint8_t* const sm = smem + Cfg::kWaves * Cfg::kWaveV + wave * Cfg::kWaveM;
-  const int64_t q_wave = (int64_t)blockIdx.x * Cfg::kQueries + (int64_t)wave * 32 * QT;
+  // Workgroup -> (query block, batch entry). With xcd_remap the grid is one-dimensional
+  // (query blocks x batch, a multiple of 8) and numbered so that the workgroups resident on
+  // one XCD take consecutive query blocks of the same batch entries: their key tiles are
+  // then fetched into that XCD's L2 once instead of once per XCD.
+  int64_t qblk = blockIdx.x, b0 = blockIdx.y, bstep = gridDim.y;
+  if (xcd_remap) {
+    const int64_t qblocks = (Lq + Cfg::kQueries - 1) / Cfg::kQueries;
+    const int64_t L = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    b0 = L / qblocks;
+    qblk = L - b0 * qblocks;
+    bstep = batch;
+  }
+  const int64_t q_wave = qblk * Cfg::kQueries + (int64_t)wave * 32 * QT;
   const int64_t nkt = Lk >> 5;         // key tiles (Lk % 32 == 0)
 
-  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+  for (int64_t b = b0; b < batch; b += bstep) {
     if (q_wave >= Lq) break;   // whole wave past the end (uniform per wave; no barriers)
     const uint16_t* Qb = Q + b * Lq * D;
     const uint16_t* Kb = Km + b * Lk * D;
@@ -301,11 +314,14 @@ static hipError_t launch_sddmm_cfg1(const uint16_t* q, const uint16_t* k, int64_
                                    float* rmax, hipStream_t stream) {
   using Cfg = SddmmCfg<D, QT>;
   const int64_t qblocks = (Lq + Cfg::kQueries - 1) / Cfg::kQueries;
-  const dim3 grid((unsigned)qblocks, (unsigned)(batch < 65535 ? batch : 65535));
+  const int64_t total = qblocks * batch;
+  const int remap = total % 8 == 0 && total <= 0x7FFFFFFF;
+  const dim3 grid = remap ? dim3((unsigned)total) : dim3((unsigned)qblocks, (unsigned)(batch < 65535 ? batch : 65535));
   auto kern = k_sddmm_prune<D, QT, DENSE, RMAX, BF>;
   static std::atomic<uint64_t> lds_set{0};
   if (hipError_t e = ensure_lds_limit(lds_set, (const void*)kern, Cfg::kLds)) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(64 * Cfg::kWaves), Cfg::kLds, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * Cfg::kWaves), Cfg::kLds, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax,
+                     remap);
   return hipGetLastError();
 }
 template <int D, int QT, bool BF>
