@@ -63,7 +63,8 @@ template <int D, bool DENSE, bool RMAX>
 __global__ void __launch_bounds__(512)
 k_sddmm_1of2_f32(const float* __restrict__ Q, const float* __restrict__ Km, int64_t batch,
                  int64_t Lq, int64_t Lk, float scale, float* __restrict__ values,
-                 uint8_t* __restrict__ meta, float* __restrict__ S, float* __restrict__ rowmax) {
+                 uint8_t* __restrict__ meta, float* __restrict__ S, float* __restrict__ rowmax,
+                 int xcd_remap) {
   using Cfg = Sddmm12Cfg<D>;
   constexpr int KH = Cfg::KH, KT = Cfg::KT, MT = Cfg::MT, VP = Cfg::VP, MP = Cfg::MP;
   constexpr int RING = Cfg::RING;
@@ -74,10 +75,21 @@ k_sddmm_1of2_f32(const float* __restrict__ Q, const float* __restrict__ Km, int6
   const int l32 = lane & 31;
   uint8_t* const sv = smem + wave * Cfg::kWaveV;
   uint8_t* const sm = smem + Cfg::kWaves * Cfg::kWaveV + wave * Cfg::kWaveM;
-  const int64_t q_wave = (int64_t)blockIdx.x * Cfg::kQueries + (int64_t)wave * 32;
+  // workgroup -> (query block, batch entry); with xcd_remap the one-dimensional grid is
+  // numbered so that one XCD's workgroups take consecutive query blocks of the same batch
+  // entries and fetch each entry's key tiles into that XCD's L2 once
+  int64_t qblk = blockIdx.x, b0 = blockIdx.y, bstep = gridDim.y;
+  if (xcd_remap) {
+    const int64_t qblocks = (Lq + Cfg::kQueries - 1) / Cfg::kQueries;
+    const int64_t L = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    b0 = L / qblocks;
+    qblk = L - b0 * qblocks;
+    bstep = batch;
+  }
+  const int64_t q_wave = qblk * Cfg::kQueries + (int64_t)wave * 32;
   const int64_t nkt = Lk >> 5;
 
-  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+  for (int64_t b = b0; b < batch; b += bstep) {
     if (q_wave >= Lq) break;   // uniform per wave; the kernel has no barriers
     const float* Qb = Q + b * Lq * D;
     const float* Kb = Km + b * Lk * D;
@@ -269,8 +281,10 @@ k_spmm_1of2_f32(Spmm12Args a) {
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const int64_t tiles = a.n_row_tiles * a.n_col_tiles;
-  const int64_t bt = blockIdx.x / tiles;
-  const int64_t rem = blockIdx.x - bt * tiles;
+  int64_t L = blockIdx.x;   // XCD-aware: one XCD's workgroups take consecutive tiles (same batch entries)
+  if ((gridDim.x & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int64_t bt = L / tiles;
+  const int64_t rem = L - bt * tiles;
   const int64_t ct = rem / a.n_row_tiles;
   const int64_t rt = rem - ct * a.n_row_tiles;
   const int64_t row0 = rt * 128, col0 = ct * 64;
@@ -376,11 +390,14 @@ static hipError_t launch_sddmm12_cfg(const float* q, const float* k, int64_t bat
                                      float* rmax, hipStream_t stream) {
   using Cfg = Sddmm12Cfg<D>;
   const int64_t qblocks = (Lq + Cfg::kQueries - 1) / Cfg::kQueries;
-  const dim3 grid((unsigned)qblocks, (unsigned)(batch < 65535 ? batch : 65535));
+  const int64_t total = qblocks * batch;
+  const int remap = total % 8 == 0 && total <= 0x7FFFFFFF;
+  const dim3 grid = remap ? dim3((unsigned)total) : dim3((unsigned)qblocks, (unsigned)(batch < 65535 ? batch : 65535));
   auto kern = k_sddmm_1of2_f32<D, DENSE, RMAX>;
   static std::atomic<uint64_t> lds_set{0};
   if (hipError_t e = ensure_lds_limit(lds_set, (const void*)kern, Cfg::kLds)) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(64 * Cfg::kWaves), Cfg::kLds, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * Cfg::kWaves), Cfg::kLds, stream, q, k, batch, Lq, Lk, scale, vv, mm, ss, rmax,
+                     remap);
   return hipGetLastError();
 }
 
