@@ -392,7 +392,7 @@ hipError_t launch_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_
                                 const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                                 int64_t ldy, hipStream_t stream) {
   if (C <= 32 && forced_variant() != Variant::kGeneric) {
-    log_variant("spmm_nm_tiled", R, K, C, "skinny");
+    log_variant("spmm_nm_tiled", R, K, C, skinny_ring_selected(K, B, C, ldb, b_layout) ? "skinny ring" : "skinny");
     return launch_spmm_nm_tiled_skinny(values_t, meta_t, R, K, B, C, ldb, b_layout, Y, ldy, stream);
   }
   log_variant("spmm_nm_tiled", R, K, C, "generic");

@@ -24,6 +24,8 @@
 //     consecutive threads on consecutive columns.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "lds_dma.hpp"
+#include "variant.hpp"
 
 namespace snm {
 
@@ -343,10 +345,185 @@ hipError_t launch_spmm_nm_skinny(const void* values, const void* meta, int64_t R
   return dispatch_skinny<false>(a, b_layout, stream);
 }
 
+// ---------------------------------------------------------------------------------------
+// Column-major B through an LDS ring (operand-major A, one product): the decode regime's
+// other stream. Every workgroup needs all of B (C x K, 256 KiB at C = 32, K = 4096). Loaded
+// straight into the operand registers, each lane takes 16 bytes of one column, so one load
+// instruction touches sixteen 128-byte lines, half of each, and B arrives at about a third
+// of the rate at which whole lines can be copied into LDS. Here B goes global -> LDS by DMA,
+// one whole 1 KiB column slice per instruction, into a ring of NBUF phases of 512 positions;
+// each wave reads its operands back with two 16-byte LDS reads per column tile. A (the HBM
+// stream) is requested in full before the ring starts, as in the register kernel above.
+//   * eight waves; phase p covers positions [512 p, 512 p + 512), wave w the operand chunk
+//     8 p + w (64 positions);
+//   * ring slot: CP column slices of 1 KiB, each padded by 16 bytes so that the sixteen
+//     columns one read touches start in sixteen different 16-byte bank groups;
+//   * copies: wave w copies columns w*D .. w*D + D - 1 of the phase (D = CP / 8); columns
+//     past C are copied from column C - 1 (they feed only output columns that are not
+//     stored), except that a wave whose columns all lie past C copies nothing, so every wave
+//     issues D or 0 copies per phase and counts them exactly;
+//   * one barrier per phase: wait for this wave's copies of phase p, barrier (publishes
+//     phase p, retires every read of phase p - 1), copy phase p + NBUF - 1 into the slot of
+//     phase p - 1, read and multiply phase p.
+namespace sring {
+constexpr int NW = 8, THREADS = 64 * NW;
+constexpr int PK = 64 * NW;                 // positions per phase
+constexpr int NBUF = 4;                     // ring slots
+constexpr int kMaxPhases = 16;              // A of every phase is held in registers
+constexpr int kColBytes = PK * 2;           // one column slice of a phase: one DMA
+constexpr int kPitch = kColBytes + 16;
+template <int CP>
+struct Cfg {
+  static constexpr int CT = CP / 16;
+  static constexpr int D = CP / NW;         // copies per wave per phase
+  static constexpr int kSlot = CP * kPitch;
+  static constexpr int kLds = NBUF * kSlot;
+  static_assert(NW * CT * 64 * 16 <= kLds, "the partial-sum tile fits in the ring");
+};
+// A's loads (two per phase) and the copies of NBUF - 1 phases are outstanding at once
+static_assert(2 * kMaxPhases + (NBUF - 1) * Cfg<32>::D < 64, "vmcnt holds at most 63 outstanding operations");
+}  // namespace sring
+
+template <int CP>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+k_spmm_skinny_ring(SkinnyArgs a) {
+  using namespace sring;
+  using Cf = Cfg<CP>;
+  constexpr int CT = Cf::CT, D = Cf::D;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t lds0 = lds_addr(smem);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4;
+  const int li = lane & 15;
+  const int64_t rt = blockIdx.x;
+  const int64_t row0 = rt * 16;
+  const int nph = (int)(a.Kc / PK);         // 1 .. kMaxPhases
+  const int64_t KC = a.Kc / 64;
+
+  // ---- A: every phase's operand, requested up front --------------------------------------
+  h8 av[kMaxPhases];
+  uint32_t ai[kMaxPhases];
+#pragma unroll
+  for (int p = 0; p < kMaxPhases; ++p) {
+    av[p] = h8{};
+    ai[p] = 0;
+    if (p < nph) {
+      const int64_t blk = rt * KC + p * NW + w;
+      av[p] = *reinterpret_cast<const h8*>(a.values + blk * 512 + lane * 8);
+      ai[p] = *reinterpret_cast<const uint16_t*>(a.meta + (blk * 64 + lane) * 2);
+    }
+  }
+
+  // ---- B copies: this wave's D columns (uniformly none when they all lie past C) -----------
+  const bool copies = (int64_t)w * D < a.C;
+  uint32_t voff[D];
+  uint32_t lcol[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    const int col = w * D + j;
+    const int64_t src = col < a.C ? col : a.C - 1;
+    voff[j] = (uint32_t)((src * a.ldb) * 2 + lane * 16);
+    lcol[j] = (uint32_t)(col * kPitch);
+  }
+  auto copy_phase = [&](int p, int slot) {
+    if (!copies) return;
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      dma_s<16>(a.B + (int64_t)p * PK, voff[j], lds0 + (uint32_t)(slot * Cf::kSlot) + lcol[j]);
+  };
+
+  f4 acc[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+  // LDS byte offset of this lane's first operand half in a slot: column li of tile 0,
+  // positions 64 w + 8 q (the second half is 32 positions on, 64 bytes)
+  const uint32_t rd0 = (uint32_t)(li * kPitch + (64 * w + 8 * q) * 2);
+
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nph) copy_phase(p, p);
+  // phase p (a compile-time constant once unrolled); phase 0 runs unconditionally (nph >= 1)
+  // so that the wait for A it holds covers every later phase on every path
+  auto run_phase = [&](const int p) {
+    if (p + 2 < nph) wait_vmcnt<2 * D>();
+    else if (p + 1 < nph) wait_vmcnt<D>();
+    else wait_vmcnt<0>();
+    if (p == 0) {
+      // A is complete now (its loads are older than the copies still allowed in flight);
+      // a use of every A register here lets the compiler's own wait for them fall before
+      // the copies of phase NBUF - 1 are issued, where it drains only phases 1 .. NBUF - 2
+#pragma unroll
+      for (int i = 0; i < kMaxPhases; ++i) asm volatile("" ::"v"(av[i]), "v"(ai[i]));
+    }
+    lds_barrier();
+    if (p + NBUF - 1 < nph) copy_phase(p + NBUF - 1, (p + NBUF - 1) % NBUF);
+    const uint32_t so = (uint32_t)((p % NBUF) * Cf::kSlot) + rd0;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const uint32_t o = so + (uint32_t)(ct * 16 * kPitch);
+      const h8 lo = *reinterpret_cast<const h8*>(smem + o);
+      const h8 hi = *reinterpret_cast<const h8*>(smem + o + 64);
+      const h16 bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      acc[ct] = smfmac16<0>(av[p], bf, acc[ct], ai[p]);
+    }
+  };
+  run_phase(0);
+#pragma unroll
+  for (int p = 1; p < kMaxPhases; ++p)
+    if (p < nph) run_phase(p);
+
+  // ---- sum the NW partial tiles and store Y --------------------------------------------------
+  lds_barrier();   // every wave is done with the ring
+  f4* red = reinterpret_cast<f4*>(smem);
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) red[(w * CT + ct) * 64 + lane] = acc[ct];
+  __syncthreads();
+  for (int e = tid; e < 16 * CP; e += THREADS) {
+    const int r = e / CP;
+    const int c = e - r * CP;
+    const int ct = c >> 4;
+    const int ln = ((r >> 2) << 4) | (c & 15);
+    const float* rp = reinterpret_cast<const float*>(red);
+    float s = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) s += rp[((ww * CT + ct) * 64 + ln) * 4 + (r & 3)];
+    const int64_t orow = row0 + r;
+    if (orow < a.R && c < a.C) a.Y[orow * a.ldy + c] = f16_bits(to_f16(s));
+  }
+}
+
+// The ring kernel's shape rules: column-major B with 16-byte column slices (ldb % 8, a
+// 16-byte aligned base), whole phases (K % 512), every phase's A in registers (K <= 8192),
+// C <= 32, and 32-bit copy offsets.
+static bool skinny_ring_eligible(int64_t K, const void* B, int64_t C, int64_t ldb) {
+  using namespace sring;
+  if (C < 1 || C > 32 || K < PK || K % PK != 0 || K / PK > kMaxPhases) return false;
+  if (ldb % 8 != 0 || ((uintptr_t)B & 15) != 0) return false;
+  return (C * ldb + K) * 2 < ((int64_t)1 << 31);
+}
+
+bool skinny_ring_selected(int64_t K, const void* B, int64_t C, int64_t ldb, int b_layout) {
+  return b_layout == 1 && forced_variant() != Variant::kDirect && skinny_ring_eligible(K, B, C, ldb);
+}
+
+template <int CP>
+static hipError_t launch_skinny_ring(const SkinnyArgs& a, hipStream_t stream) {
+  auto kern = k_spmm_skinny_ring<CP>;
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit(lds_set, (const void*)kern, sring::Cfg<CP>::kLds)) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)((a.R + 15) / 16)), dim3(sring::THREADS), sring::Cfg<CP>::kLds,
+                     stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_spmm_nm_tiled_skinny(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                                        const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                                        int64_t ldy, hipStream_t stream) {
   const SkinnyArgs a = skinny_args(values_t, meta_t, R, K, B, C, ldb, Y, ldy, 1, 0, 0, 0, 0);
+  if (skinny_ring_selected(K, B, C, ldb, b_layout))
+    return C <= 16 ? launch_skinny_ring<16>(a, stream) : launch_skinny_ring<32>(a, stream);
   return dispatch_skinny<true>(a, b_layout, stream);
 }
 

@@ -10,6 +10,9 @@
 //                          generic  N:M and canonical V:N:M products: the generic tiled kernel
 //                                   (no skinny or wide-tile kernel)
 //                          unsplit  split-reduction decode entry points: never split
+//                          direct   decode products on operand-major A with column-major B: B
+//                                   loaded straight into the operand registers, never
+//                                   through the LDS ring
 #include "variant.hpp"
 
 #include <cstdio>
@@ -37,6 +40,7 @@ const Switches& switches() {
       else if (std::strcmp(f, "large") == 0) s.force = Variant::kLarge;
       else if (std::strcmp(f, "generic") == 0) s.force = Variant::kGeneric;
       else if (std::strcmp(f, "unsplit") == 0) s.force = Variant::kUnsplit;
+      else if (std::strcmp(f, "direct") == 0) s.force = Variant::kDirect;
     }
   });
   return s;

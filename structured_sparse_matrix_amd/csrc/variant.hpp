@@ -5,7 +5,7 @@
 
 namespace snm {
 
-enum class Variant { kNone, kWide, kLarge, kGeneric, kUnsplit };
+enum class Variant { kNone, kWide, kLarge, kGeneric, kUnsplit, kDirect };
 
 // The variant SNM_FORCE_VARIANT names (kNone if unset or unknown).
 Variant forced_variant();

@@ -5,7 +5,8 @@ give the oracle's product, and SNM_LOG must name the variant that ran.
 Shapes: a V:2:16 product with V = 128 whose grid is too small for the large-tile kernel by
 default (so 'large' changes the choice and 'wide' keeps it), the same for V:2:8 with V = 64
 and the 64-row large-tile kernel (both storages), and a decode-shaped 2:4 product with C = 8
-(skinny by default, 'generic' forces the generic tiled kernel)."""
+(skinny by default, 'generic' forces the generic tiled kernel), also on the operand-major
+storage (the LDS-ring kernel by default, 'direct' forces the register kernel)."""
 import os
 import subprocess
 import sys
@@ -43,6 +44,11 @@ CHILD = textwrap.dedent("""
         B = workloads.small_matrix(12, (2048, 512))
         v, mi, cl = snm.prune_encode_vnm(torch.from_numpy(A).to(dev), 128, 16)
         Y = snm.spmm_vnm(v, mi, cl, torch.from_numpy(B).to(dev), 128, 16)
+    elif kind == "nmt":   # operand-major A, column-major B, C <= 32, K % 512 == 0
+        A = workloads.small_matrix(13, (512, 1024), 0.02)
+        X = workloads.small_matrix(14, (8, 1024))
+        vt, mt = snm.prune_encode_nm_tiled(torch.from_numpy(A).to(dev))
+        Y = snm.spmm_nm_tiled(vt, mt, 512, torch.from_numpy(X).to(dev).t())
     else:
         A = workloads.small_matrix(13, (512, 1024), 0.02)
         X = workloads.small_matrix(14, (8, 1024))   # column-major B: activations X[C][K]
@@ -104,3 +110,13 @@ def test_nm_forced_variant_matches_oracle(force, expect, tmp_path):
     ov, om = oracle.prune_encode_nm(A)
     assert_fp16_close(Y, oracle.spmm_nm(ov, om, np.ascontiguousarray(X.T)))
     assert lines == [f"snm: spmm_nm R=512 K=1024 C=8 -> {expect}"], lines
+
+
+@pytest.mark.parametrize("force,expect", [("", "skinny ring"), ("direct", "skinny"), ("generic", "generic")])
+def test_nm_tiled_forced_variant_matches_oracle(force, expect, tmp_path):
+    Y, lines = _run("nmt", force, tmp_path)
+    A = workloads.small_matrix(13, (512, 1024), 0.02)
+    X = workloads.small_matrix(14, (8, 1024))
+    ov, om = oracle.prune_encode_nm(A)
+    assert_fp16_close(Y, oracle.spmm_nm(ov, om, np.ascontiguousarray(X.T)))
+    assert lines == [f"snm: spmm_nm_tiled R=512 K=1024 C=8 -> {expect}"], lines
