@@ -27,6 +27,8 @@
 #include "lds_dma.hpp"
 #include "variant.hpp"
 
+#include <type_traits>
+
 namespace snm {
 
 struct SkinnyArgs {
@@ -353,18 +355,23 @@ hipError_t launch_spmm_nm_skinny(const void* values, const void* meta, int64_t R
 // of the rate at which whole lines can be copied into LDS. Here B goes global -> LDS by DMA,
 // one whole 1 KiB column slice per instruction, into a ring of NBUF phases of 512 positions;
 // each wave reads its operands back with two 16-byte LDS reads per column tile. A (the HBM
-// stream) is requested in full before the ring starts, as in the register kernel above.
+// stream) is requested in full at the start, as in the register kernel above.
 //   * eight waves; phase p covers positions [512 p, 512 p + 512), wave w the operand chunk
-//     8 p + w (64 positions);
+//     8 p + w (64 positions); the phase count NPH = K / 512 is a template parameter, so that
+//     every wait below is an exact count;
 //   * ring slot: CP column slices of 1 KiB, each padded by 16 bytes so that the sixteen
 //     columns one read touches start in sixteen different 16-byte bank groups;
 //   * copies: wave w copies columns w*D .. w*D + D - 1 of the phase (D = CP / 8); columns
 //     past C are copied from column C - 1 (they feed only output columns that are not
-//     stored), except that a wave whose columns all lie past C copies nothing, so every wave
-//     issues D or 0 copies per phase and counts them exactly;
+//     stored), except that a wave whose columns all lie past C copies nothing (its waits
+//     then only cover its own loads of A, which the compiler waits for anyway);
+//   * issue order: the copies of the first NBUF phases (every slot is free), then A, then one
+//     phase of copies per barrier. Loads and copies retire in issue order, so phase p < NBUF
+//     waits for its own copies and A of the phases it needs, not for all of A; the copies of
+//     phase p + NBUF - 1 go out at barrier p >= 1 (every read of phase p - 1, whose slot it
+//     takes, has retired there) while the rest of A is still arriving;
 //   * one barrier per phase: wait for this wave's copies of phase p, barrier (publishes
-//     phase p, retires every read of phase p - 1), copy phase p + NBUF - 1 into the slot of
-//     phase p - 1, read and multiply phase p.
+//     phase p), copy, read and multiply phase p.
 namespace sring {
 constexpr int NW = 8, THREADS = 64 * NW;
 constexpr int PK = 64 * NW;                 // positions per phase
@@ -380,16 +387,39 @@ struct Cfg {
   static constexpr int kLds = NBUF * kSlot;
   static_assert(NW * CT * 64 * 16 <= kLds, "the partial-sum tile fits in the ring");
 };
-// A's loads (two per phase) and the copies of NBUF - 1 phases are outstanding at once
-static_assert(2 * kMaxPhases + (NBUF - 1) * Cfg<32>::D < 64, "vmcnt holds at most 63 outstanding operations");
+// phases copied before A is requested, and whether barrier q issues the copies of q + NBUF - 1
+constexpr int prologue(int nph) { return nph < NBUF ? nph : NBUF; }
+constexpr bool issues_at(int q, int nph) { return q >= 1 && q + NBUF - 1 < nph; }
+// vector-memory operations a copying wave issues after phase p's copies and before its wait
+// at phase p
+constexpr int younger(int p, int nph, int d) {
+  int n = 0;
+  if (p < prologue(nph)) {
+    n += d * (prologue(nph) - 1 - p) + 2 * nph;
+    for (int q = 1; q < p; ++q) n += issues_at(q, nph) ? d : 0;
+  } else {
+    for (int q = p - NBUF + 2; q < p; ++q) n += issues_at(q, nph) ? d : 0;
+  }
+  return n;
+}
+// at most NBUF phases of copies and all of A are outstanding at once
+static_assert(NBUF * Cfg<32>::D + 2 * kMaxPhases + Cfg<32>::D < 64, "vmcnt holds at most 63 outstanding operations");
 }  // namespace sring
 
-template <int CP>
+template <int I, int N, typename F>
+__device__ __forceinline__ void ring_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    ring_for<I + 1, N>(f);
+  }
+}
+
+template <int CP, int NPH>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 k_spmm_skinny_ring(SkinnyArgs a) {
   using namespace sring;
   using Cf = Cfg<CP>;
-  constexpr int CT = Cf::CT, D = Cf::D;
+  constexpr int CT = Cf::CT, D = Cf::D, PRO = prologue(NPH);
   extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t lds0 = lds_addr(smem);
   const int tid = threadIdx.x;
@@ -399,24 +429,9 @@ k_spmm_skinny_ring(SkinnyArgs a) {
   const int li = lane & 15;
   const int64_t rt = blockIdx.x;
   const int64_t row0 = rt * 16;
-  const int nph = (int)(a.Kc / PK);         // 1 .. kMaxPhases
-  const int64_t KC = a.Kc / 64;
+  const int64_t KC = (int64_t)NPH * (PK / 64);
 
-  // ---- A: every phase's operand, requested up front --------------------------------------
-  h8 av[kMaxPhases];
-  uint32_t ai[kMaxPhases];
-#pragma unroll
-  for (int p = 0; p < kMaxPhases; ++p) {
-    av[p] = h8{};
-    ai[p] = 0;
-    if (p < nph) {
-      const int64_t blk = rt * KC + p * NW + w;
-      av[p] = *reinterpret_cast<const h8*>(a.values + blk * 512 + lane * 8);
-      ai[p] = *reinterpret_cast<const uint16_t*>(a.meta + (blk * 64 + lane) * 2);
-    }
-  }
-
-  // ---- B copies: this wave's D columns (uniformly none when they all lie past C) -----------
+  // ---- B copies: this wave's D columns (none when they all lie past C) ---------------------
   const bool copies = (int64_t)w * D < a.C;
   uint32_t voff[D];
   uint32_t lcol[D];
@@ -433,6 +448,18 @@ k_spmm_skinny_ring(SkinnyArgs a) {
     for (int j = 0; j < D; ++j)
       dma_s<16>(a.B + (int64_t)p * PK, voff[j], lds0 + (uint32_t)(slot * Cf::kSlot) + lcol[j]);
   };
+#pragma unroll
+  for (int p = 0; p < PRO; ++p) copy_phase(p, p);
+
+  // ---- A: every phase's operand --------------------------------------------------------------
+  h8 av[NPH];
+  uint32_t ai[NPH];
+#pragma unroll
+  for (int p = 0; p < NPH; ++p) {
+    const int64_t blk = rt * KC + p * NW + w;
+    av[p] = *reinterpret_cast<const h8*>(a.values + blk * 512 + lane * 8);
+    ai[p] = *reinterpret_cast<const uint16_t*>(a.meta + (blk * 64 + lane) * 2);
+  }
 
   f4 acc[CT];
 #pragma unroll
@@ -441,38 +468,21 @@ k_spmm_skinny_ring(SkinnyArgs a) {
   // positions 64 w + 8 q (the second half is 32 positions on, 64 bytes)
   const uint32_t rd0 = (uint32_t)(li * kPitch + (64 * w + 8 * q) * 2);
 
-#pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p)
-    if (p < nph) copy_phase(p, p);
-  // phase p (a compile-time constant once unrolled); phase 0 runs unconditionally (nph >= 1)
-  // so that the wait for A it holds covers every later phase on every path
-  auto run_phase = [&](const int p) {
-    if (p + 2 < nph) wait_vmcnt<2 * D>();
-    else if (p + 1 < nph) wait_vmcnt<D>();
-    else wait_vmcnt<0>();
-    if (p == 0) {
-      // A is complete now (its loads are older than the copies still allowed in flight);
-      // a use of every A register here lets the compiler's own wait for them fall before
-      // the copies of phase NBUF - 1 are issued, where it drains only phases 1 .. NBUF - 2
-#pragma unroll
-      for (int i = 0; i < kMaxPhases; ++i) asm volatile("" ::"v"(av[i]), "v"(ai[i]));
-    }
+  ring_for<0, NPH>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    wait_vmcnt<younger(p, NPH, D)>();
     lds_barrier();
-    if (p + NBUF - 1 < nph) copy_phase(p + NBUF - 1, (p + NBUF - 1) % NBUF);
-    const uint32_t so = (uint32_t)((p % NBUF) * Cf::kSlot) + rd0;
+    if constexpr (issues_at(p, NPH)) copy_phase(p + NBUF - 1, (p + NBUF - 1) % NBUF);
+    constexpr uint32_t so = (uint32_t)((p % NBUF) * Cf::kSlot);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      const uint32_t o = so + (uint32_t)(ct * 16 * kPitch);
+      const uint32_t o = so + rd0 + (uint32_t)(ct * 16 * kPitch);
       const h8 lo = *reinterpret_cast<const h8*>(smem + o);
       const h8 hi = *reinterpret_cast<const h8*>(smem + o + 64);
       const h16 bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
       acc[ct] = smfmac16<0>(av[p], bf, acc[ct], ai[p]);
     }
-  };
-  run_phase(0);
-#pragma unroll
-  for (int p = 1; p < kMaxPhases; ++p)
-    if (p < nph) run_phase(p);
+  });
 
   // ---- sum the NW partial tiles and store Y --------------------------------------------------
   lds_barrier();   // every wave is done with the ring
@@ -508,9 +518,12 @@ bool skinny_ring_selected(int64_t K, const void* B, int64_t C, int64_t ldb, int 
   return b_layout == 1 && forced_variant() != Variant::kDirect && skinny_ring_eligible(K, B, C, ldb);
 }
 
-template <int CP>
-static hipError_t launch_skinny_ring(const SkinnyArgs& a, hipStream_t stream) {
-  auto kern = k_spmm_skinny_ring<CP>;
+template <int CP, int NPH>
+static hipError_t launch_skinny_ring(const SkinnyArgs& a, int nph, hipStream_t stream) {
+  if constexpr (NPH < sring::kMaxPhases) {
+    if (nph != NPH) return launch_skinny_ring<CP, NPH + 1>(a, nph, stream);
+  }
+  auto kern = k_spmm_skinny_ring<CP, NPH>;
   static std::atomic<uint64_t> lds_set{0};
   if (hipError_t e = ensure_lds_limit(lds_set, (const void*)kern, sring::Cfg<CP>::kLds)) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)((a.R + 15) / 16)), dim3(sring::THREADS), sring::Cfg<CP>::kLds,
@@ -522,8 +535,10 @@ hipError_t launch_spmm_nm_tiled_skinny(const void* values_t, const void* meta_t,
                                        const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                                        int64_t ldy, hipStream_t stream) {
   const SkinnyArgs a = skinny_args(values_t, meta_t, R, K, B, C, ldb, Y, ldy, 1, 0, 0, 0, 0);
-  if (skinny_ring_selected(K, B, C, ldb, b_layout))
-    return C <= 16 ? launch_skinny_ring<16>(a, stream) : launch_skinny_ring<32>(a, stream);
+  if (skinny_ring_selected(K, B, C, ldb, b_layout)) {
+    const int nph = (int)(K / sring::PK);
+    return C <= 16 ? launch_skinny_ring<16, 1>(a, nph, stream) : launch_skinny_ring<32, 1>(a, nph, stream);
+  }
   return dispatch_skinny<true>(a, b_layout, stream);
 }
 

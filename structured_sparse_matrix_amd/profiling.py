@@ -46,7 +46,7 @@ import os
 import statistics
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-DECODE_KERNEL_SOURCES = ("spmm_skinny.hip", "device_common.hpp")
+DECODE_KERNEL_SOURCES = ("spmm_skinny.hip", "device_common.hpp", "lds_dma.hpp")
 WIDE_KERNEL_SOURCES = ("spmm_wide.hip", "spmm_vnm_big.hip", "lds_dma.hpp", "wide_layout.hpp", "elem.hpp",
                        "device_common.hpp")
 ATTENTION_KERNEL_SOURCES = ("attention.hip", "elem.hpp", "device_common.hpp")
