@@ -358,7 +358,8 @@ hipError_t launch_spmm_nm_skinny(const void* values, const void* meta, int64_t R
 // stream) is requested in full at the start, as in the register kernel above.
 //   * eight waves; phase p covers positions [512 p, 512 p + 512), wave w the operand chunk
 //     8 p + w (64 positions); the phase count NPH = K / 512 is a template parameter, so that
-//     every wait below is an exact count;
+//     every wait below is an exact count; each workgroup walks the phases from its own
+//     starting phase (the fp32 sums of a row are still in one fixed order per launch shape);
 //   * ring slot: CP column slices of 1 KiB, each padded by 16 bytes so that the sixteen
 //     columns one read touches start in sixteen different 16-byte bank groups;
 //   * copies: wave w copies columns w*D .. w*D + D - 1 of the phase (D = CP / 8); columns
@@ -430,6 +431,12 @@ k_spmm_skinny_ring(SkinnyArgs a) {
   const int64_t rt = blockIdx.x;
   const int64_t row0 = rt * 16;
   const int64_t KC = (int64_t)NPH * (PK / 64);
+  // Phase order rotated per workgroup: consecutive workgroups go to different XCDs, so the
+  // 32 or so of one XCD (every eighth) start at different phases and together request all
+  // of B at once; the later phases of each then find their lines in that XCD's L2. Ring
+  // position p (registers, slot) holds memory phase phys(p).
+  const int rot = (int)((blockIdx.x >> 3) % NPH);
+  auto phys = [&](int p) { const int v = p + rot; return v >= NPH ? v - NPH : v; };
 
   // ---- B copies: this wave's D columns (none when they all lie past C) ---------------------
   const bool copies = (int64_t)w * D < a.C;
@@ -446,7 +453,7 @@ k_spmm_skinny_ring(SkinnyArgs a) {
     if (!copies) return;
 #pragma unroll
     for (int j = 0; j < D; ++j)
-      dma_s<16>(a.B + (int64_t)p * PK, voff[j], lds0 + (uint32_t)(slot * Cf::kSlot) + lcol[j]);
+      dma_s<16>(a.B + (int64_t)phys(p) * PK, voff[j], lds0 + (uint32_t)(slot * Cf::kSlot) + lcol[j]);
   };
 #pragma unroll
   for (int p = 0; p < PRO; ++p) copy_phase(p, p);
@@ -456,7 +463,7 @@ k_spmm_skinny_ring(SkinnyArgs a) {
   uint32_t ai[NPH];
 #pragma unroll
   for (int p = 0; p < NPH; ++p) {
-    const int64_t blk = rt * KC + p * NW + w;
+    const int64_t blk = rt * KC + phys(p) * NW + w;
     av[p] = *reinterpret_cast<const h8*>(a.values + blk * 512 + lane * 8);
     ai[p] = *reinterpret_cast<const uint16_t*>(a.meta + (blk * 64 + lane) * 2);
   }
