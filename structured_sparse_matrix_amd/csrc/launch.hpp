@@ -42,9 +42,10 @@ hipError_t launch_spmm_nm_tiled_splitk(const void* values_t, const void* meta_t,
 hipError_t launch_spmm_nm_tiled_splitk_noalloc(const void* values_t, const void* meta_t, int64_t R,
                                                int64_t K, const void* B, int64_t C, int64_t ldb,
                                                void* Y, int64_t ldy, hipStream_t stream);
-// The decode product on operand-major A takes the LDS-ring kernel (column-major B, C <= 32,
-// K % 512 == 0, K <= 8192, 16-byte column slices) unless SNM_FORCE_VARIANT=direct.
-bool skinny_ring_selected(int64_t K, const void* B, int64_t C, int64_t ldb, int b_layout);
+// A decode product (one product, C <= 32) takes the LDS-ring kernel when B is column-major with
+// 16-byte column slices, K % 512 == 0 (operand-major A) or K % 1024 == 0 (canonical A) and
+// K <= 8192, unless SNM_FORCE_VARIANT=direct.
+bool skinny_ring_selected(int64_t K, const void* B, int64_t C, int64_t ldb, int b_layout, bool a_tiled);
 hipError_t launch_spmm_nm_tiled_skinny(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                                        const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                                        int64_t ldy, hipStream_t stream);

@@ -358,7 +358,8 @@ hipError_t launch_spmm_nm(const void* values, const void* meta, int64_t R, int64
                           int64_t stride_Y, hipStream_t stream) {
   const bool generic = forced_variant() == Variant::kGeneric;
   if (C <= 32 && !generic) {   // decode regime: weight streaming, see spmm_skinny.hip
-    log_variant("spmm_nm", R, K, C, "skinny");
+    log_variant("spmm_nm", R, K, C,
+                batch == 1 && skinny_ring_selected(K, B, C, ldb, b_layout, false) ? "skinny ring" : "skinny");
     return launch_spmm_nm_skinny(values, meta, R, K, B, C, ldb, b_layout, Y, ldy, batch,
                                  stride_values, stride_meta, stride_B, stride_Y, stream);
   }
@@ -392,7 +393,7 @@ hipError_t launch_spmm_nm_tiled(const void* values_t, const void* meta_t, int64_
                                 const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                                 int64_t ldy, hipStream_t stream) {
   if (C <= 32 && forced_variant() != Variant::kGeneric) {
-    log_variant("spmm_nm_tiled", R, K, C, skinny_ring_selected(K, B, C, ldb, b_layout) ? "skinny ring" : "skinny");
+    log_variant("spmm_nm_tiled", R, K, C, skinny_ring_selected(K, B, C, ldb, b_layout, true) ? "skinny ring" : "skinny");
     return launch_spmm_nm_tiled_skinny(values_t, meta_t, R, K, B, C, ldb, b_layout, Y, ldy, stream);
   }
   log_variant("spmm_nm_tiled", R, K, C, "generic");

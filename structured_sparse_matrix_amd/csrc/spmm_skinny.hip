@@ -337,15 +337,6 @@ static SkinnyArgs skinny_args(const void* values, const void* meta, int64_t R, i
   return a;
 }
 
-hipError_t launch_spmm_nm_skinny(const void* values, const void* meta, int64_t R, int64_t K,
-                                 const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
-                                 int64_t ldy, int64_t batch, int64_t stride_values,
-                                 int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
-                                 hipStream_t stream) {
-  const SkinnyArgs a = skinny_args(values, meta, R, K, B, C, ldb, Y, ldy, batch, stride_values,
-                                   stride_meta, stride_B, stride_Y);
-  return dispatch_skinny<false>(a, b_layout, stream);
-}
 
 // ---------------------------------------------------------------------------------------
 // Column-major B through an LDS ring (operand-major A, one product): the decode regime's
@@ -375,36 +366,41 @@ hipError_t launch_spmm_nm_skinny(const void* values, const void* meta, int64_t R
 //     phase p), copy, read and multiply phase p.
 namespace sring {
 constexpr int NW = 8, THREADS = 64 * NW;
-constexpr int PK = 64 * NW;                 // positions per phase
-constexpr int NBUF = 4;                     // ring slots
-constexpr int kMaxPhases = 16;              // A of every phase is held in registers
-constexpr int kColBytes = PK * 2;           // one column slice of a phase: one DMA
-constexpr int kPitch = kColBytes + 16;
-template <int CP>
+// KS: 64-position operands per wave per phase. Operand-major A: 1 (a phase of 512 positions,
+// four ring slots). Canonical A: 2, so that one wave reads both halves of every 128-byte line
+// of its 16 rows (two adjacent chunks) -- concurrent misses of two waves to one line are not
+// merged -- with phases of 1024 positions in two slots (the same bytes in flight).
+template <int CP, int KS>
 struct Cfg {
+  static constexpr int PK = 64 * NW * KS;          // positions per phase
+  static constexpr int NBUF = KS == 1 ? 4 : 2;     // ring slots
+  static constexpr int kMaxPhases = 8192 / PK;     // A of every phase is held in registers
+  static constexpr int kPitch = PK * 2 + 16;       // one padded column slice of a phase
   static constexpr int CT = CP / 16;
-  static constexpr int D = CP / NW;         // copies per wave per phase
+  static constexpr int D = CP / NW * KS;           // copies (1 KiB each) per wave per phase
   static constexpr int kSlot = CP * kPitch;
   static constexpr int kLds = NBUF * kSlot;
   static_assert(NW * CT * 64 * 16 <= kLds, "the partial-sum tile fits in the ring");
-};
-// phases copied before A is requested, and whether barrier q issues the copies of q + NBUF - 1
-constexpr int prologue(int nph) { return nph < NBUF ? nph : NBUF; }
-constexpr bool issues_at(int q, int nph) { return q >= 1 && q + NBUF - 1 < nph; }
-// vector-memory operations a copying wave issues after phase p's copies and before its wait
-// at phase p
-constexpr int younger(int p, int nph, int d) {
-  int n = 0;
-  if (p < prologue(nph)) {
-    n += d * (prologue(nph) - 1 - p) + 2 * nph;
-    for (int q = 1; q < p; ++q) n += issues_at(q, nph) ? d : 0;
-  } else {
-    for (int q = p - NBUF + 2; q < p; ++q) n += issues_at(q, nph) ? d : 0;
+  // at most NBUF + 1 phases of copies and all of A are outstanding at once
+  static_assert((NBUF + 1) * D + 2 * KS * kMaxPhases < 64, "vmcnt holds at most 63 outstanding operations");
+  // phases copied before A is requested, and whether barrier q issues the copies of q + NBUF - 1
+  static constexpr int prologue(int nph) { return nph < NBUF ? nph : NBUF; }
+  static constexpr bool issues_at(int q, int nph) { return q >= 1 && q + NBUF - 1 < nph; }
+  // vector-memory operations a copying wave issues after phase p's copies and before its
+  // wait at phase p
+  static constexpr int younger(int p, int nph) {
+    int n = 0;
+    if (p < prologue(nph)) {
+      n += D * (prologue(nph) - 1 - p) + 2 * KS * nph;
+      for (int q = 1; q < p; ++q) n += issues_at(q, nph) ? D : 0;
+    } else {
+      for (int q = p - NBUF + 2; q < p; ++q) n += issues_at(q, nph) ? D : 0;
+    }
+    return n;
   }
-  return n;
-}
-// at most NBUF phases of copies and all of A are outstanding at once
-static_assert(NBUF * Cfg<32>::D + 2 * kMaxPhases + Cfg<32>::D < 64, "vmcnt holds at most 63 outstanding operations");
+};
+template <bool ATILED>
+constexpr int ks_of() { return ATILED ? 1 : 2; }
 }  // namespace sring
 
 template <int I, int N, typename F>
@@ -415,12 +411,14 @@ __device__ __forceinline__ void ring_for(F&& f) {
   }
 }
 
-template <int CP, int NPH>
+template <int CP, int NPH, bool ATILED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 k_spmm_skinny_ring(SkinnyArgs a) {
   using namespace sring;
-  using Cf = Cfg<CP>;
-  constexpr int CT = Cf::CT, D = Cf::D, PRO = prologue(NPH);
+  constexpr int KS = ks_of<ATILED>();
+  using Cf = Cfg<CP, KS>;
+  constexpr int CT = Cf::CT, D = Cf::D, PK = Cf::PK, NBUF = Cf::NBUF, PRO = Cf::prologue(NPH);
+  constexpr int kPitch = Cf::kPitch;
   extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t lds0 = lds_addr(smem);
   const int tid = threadIdx.x;
@@ -430,7 +428,7 @@ k_spmm_skinny_ring(SkinnyArgs a) {
   const int li = lane & 15;
   const int64_t rt = blockIdx.x;
   const int64_t row0 = rt * 16;
-  const int64_t KC = (int64_t)NPH * (PK / 64);
+  const int64_t KC = (int64_t)NPH * (PK / 64);   // 64-position chunks per row
   // Phase order rotated per workgroup: consecutive workgroups go to different XCDs, so the
   // 32 or so of one XCD (every eighth) start at different phases and together request all
   // of B at once; the later phases of each then find their lines in that XCD's L2. Ring
@@ -438,13 +436,14 @@ k_spmm_skinny_ring(SkinnyArgs a) {
   const int rot = (int)((blockIdx.x >> 3) % NPH);
   auto phys = [&](int p) { const int v = p + rot; return v >= NPH ? v - NPH : v; };
 
-  // ---- B copies: this wave's D columns (none when they all lie past C) ---------------------
-  const bool copies = (int64_t)w * D < a.C;
-  uint32_t voff[D];
-  uint32_t lcol[D];
+  // ---- B copies: this wave's CP / NW columns (none when they all lie past C) --------------
+  constexpr int NCOL = CP / NW;
+  const bool copies = (int64_t)w * NCOL < a.C;
+  uint32_t voff[NCOL];
+  uint32_t lcol[NCOL];
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    const int col = w * D + j;
+  for (int j = 0; j < NCOL; ++j) {
+    const int col = w * NCOL + j;
     const int64_t src = col < a.C ? col : a.C - 1;
     voff[j] = (uint32_t)((src * a.ldb) * 2 + lane * 16);
     lcol[j] = (uint32_t)(col * kPitch);
@@ -452,43 +451,59 @@ k_spmm_skinny_ring(SkinnyArgs a) {
   auto copy_phase = [&](int p, int slot) {
     if (!copies) return;
 #pragma unroll
-    for (int j = 0; j < D; ++j)
-      dma_s<16>(a.B + (int64_t)phys(p) * PK, voff[j], lds0 + (uint32_t)(slot * Cf::kSlot) + lcol[j]);
+    for (int j = 0; j < NCOL; ++j)
+#pragma unroll
+      for (int h = 0; h < KS; ++h)
+        dma_s<16>(a.B + (int64_t)phys(p) * PK + 512 * h, voff[j],
+                  lds0 + (uint32_t)(slot * Cf::kSlot) + lcol[j] + (uint32_t)(1024 * h));
   };
 #pragma unroll
   for (int p = 0; p < PRO; ++p) copy_phase(p, p);
 
-  // ---- A: every phase's operand --------------------------------------------------------------
-  h8 av[NPH];
-  uint32_t ai[NPH];
+  // ---- A: every phase's operands (chunk KS (NW p + w) + t) -------------------------------------
+  h8 av[NPH][KS];
+  uint32_t ai[NPH][KS];
+  // canonical rows past R read row R - 1 (their outputs are not stored), so that every wave
+  // issues the same loads
+  const int64_t crow = row0 + li < a.R ? row0 + li : a.R - 1;
 #pragma unroll
-  for (int p = 0; p < NPH; ++p) {
-    const int64_t blk = rt * KC + phys(p) * NW + w;
-    av[p] = *reinterpret_cast<const h8*>(a.values + blk * 512 + lane * 8);
-    ai[p] = *reinterpret_cast<const uint16_t*>(a.meta + (blk * 64 + lane) * 2);
-  }
+  for (int p = 0; p < NPH; ++p)
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const int64_t chunk = (int64_t)KS * (NW * phys(p) + w) + t;
+      if constexpr (ATILED) {
+        const int64_t blk = rt * KC + chunk;
+        av[p][t] = *reinterpret_cast<const h8*>(a.values + blk * 512 + lane * 8);
+        ai[p][t] = *reinterpret_cast<const uint16_t*>(a.meta + (blk * 64 + lane) * 2);
+      } else {
+        av[p][t] = *reinterpret_cast<const h8*>(a.values + crow * (a.Kc >> 1) + chunk * 32 + 8 * q);
+        ai[p][t] = *reinterpret_cast<const uint16_t*>(a.meta + crow * (a.Kc >> 3) + chunk * 8 + 2 * q);
+      }
+    }
 
   f4 acc[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
   // LDS byte offset of this lane's first operand half in a slot: column li of tile 0,
-  // positions 64 w + 8 q (the second half is 32 positions on, 64 bytes)
-  const uint32_t rd0 = (uint32_t)(li * kPitch + (64 * w + 8 * q) * 2);
+  // positions 64 (KS w + t) + 8 q (the second half is 32 positions on, 64 bytes)
+  const uint32_t rd0 = (uint32_t)(li * kPitch + (64 * KS * w + 8 * q) * 2);
 
   ring_for<0, NPH>([&](auto pc) {
     constexpr int p = decltype(pc)::value;
-    wait_vmcnt<younger(p, NPH, D)>();
+    wait_vmcnt<Cf::younger(p, NPH)>();
     lds_barrier();
-    if constexpr (issues_at(p, NPH)) copy_phase(p + NBUF - 1, (p + NBUF - 1) % NBUF);
+    if constexpr (Cf::issues_at(p, NPH)) copy_phase(p + NBUF - 1, (p + NBUF - 1) % NBUF);
     constexpr uint32_t so = (uint32_t)((p % NBUF) * Cf::kSlot);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const uint32_t o = so + rd0 + (uint32_t)(ct * 16 * kPitch);
-      const h8 lo = *reinterpret_cast<const h8*>(smem + o);
-      const h8 hi = *reinterpret_cast<const h8*>(smem + o + 64);
-      const h16 bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-      acc[ct] = smfmac16<0>(av[p], bf, acc[ct], ai[p]);
-    }
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const uint32_t o = so + rd0 + (uint32_t)(ct * 16 * kPitch + 128 * t);
+        const h8 lo = *reinterpret_cast<const h8*>(smem + o);
+        const h8 hi = *reinterpret_cast<const h8*>(smem + o + 64);
+        const h16 bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+        acc[ct] = smfmac16<0>(av[p][t], bf, acc[ct], ai[p][t]);
+      }
   });
 
   // ---- sum the NW partial tiles and store Y --------------------------------------------------
@@ -512,40 +527,55 @@ k_spmm_skinny_ring(SkinnyArgs a) {
 }
 
 // The ring kernel's shape rules: column-major B with 16-byte column slices (ldb % 8, a
-// 16-byte aligned base), whole phases (K % 512), every phase's A in registers (K <= 8192),
-// C <= 32, and 32-bit copy offsets.
-static bool skinny_ring_eligible(int64_t K, const void* B, int64_t C, int64_t ldb) {
-  using namespace sring;
-  if (C < 1 || C > 32 || K < PK || K % PK != 0 || K / PK > kMaxPhases) return false;
+// 16-byte aligned base), whole phases (K % 512 for operand-major A, K % 1024 for canonical A),
+// every phase's A in registers (K <= 8192), C <= 32, one product, and 32-bit copy offsets.
+static bool skinny_ring_eligible(int64_t K, const void* B, int64_t C, int64_t ldb, bool a_tiled) {
+  const int64_t pk = a_tiled ? sring::Cfg<16, 1>::PK : sring::Cfg<16, 2>::PK;
+  if (C < 1 || C > 32 || K < pk || K % pk != 0 || K > 8192) return false;
   if (ldb % 8 != 0 || ((uintptr_t)B & 15) != 0) return false;
   return (C * ldb + K) * 2 < ((int64_t)1 << 31);
 }
 
-bool skinny_ring_selected(int64_t K, const void* B, int64_t C, int64_t ldb, int b_layout) {
-  return b_layout == 1 && forced_variant() != Variant::kDirect && skinny_ring_eligible(K, B, C, ldb);
+bool skinny_ring_selected(int64_t K, const void* B, int64_t C, int64_t ldb, int b_layout, bool a_tiled) {
+  return b_layout == 1 && forced_variant() != Variant::kDirect && skinny_ring_eligible(K, B, C, ldb, a_tiled);
 }
 
-template <int CP, int NPH>
+template <int CP, bool ATILED, int NPH>
 static hipError_t launch_skinny_ring(const SkinnyArgs& a, int nph, hipStream_t stream) {
-  if constexpr (NPH < sring::kMaxPhases) {
-    if (nph != NPH) return launch_skinny_ring<CP, NPH + 1>(a, nph, stream);
+  using Cf = sring::Cfg<CP, sring::ks_of<ATILED>()>;
+  if constexpr (NPH < Cf::kMaxPhases) {
+    if (nph != NPH) return launch_skinny_ring<CP, ATILED, NPH + 1>(a, nph, stream);
   }
-  auto kern = k_spmm_skinny_ring<CP, NPH>;
+  auto kern = k_spmm_skinny_ring<CP, NPH, ATILED>;
   static std::atomic<uint64_t> lds_set{0};
-  if (hipError_t e = ensure_lds_limit(lds_set, (const void*)kern, sring::Cfg<CP>::kLds)) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)((a.R + 15) / 16)), dim3(sring::THREADS), sring::Cfg<CP>::kLds,
-                     stream, a);
+  if (hipError_t e = ensure_lds_limit(lds_set, (const void*)kern, Cf::kLds)) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)((a.R + 15) / 16)), dim3(sring::THREADS), Cf::kLds, stream, a);
   return hipGetLastError();
+}
+
+template <bool ATILED>
+static hipError_t dispatch_skinny_ring(const SkinnyArgs& a, hipStream_t stream) {
+  const int nph = (int)(a.Kc / sring::Cfg<16, sring::ks_of<ATILED>()>::PK);
+  return a.C <= 16 ? launch_skinny_ring<16, ATILED, 1>(a, nph, stream)
+                   : launch_skinny_ring<32, ATILED, 1>(a, nph, stream);
+}
+
+hipError_t launch_spmm_nm_skinny(const void* values, const void* meta, int64_t R, int64_t K,
+                                 const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
+                                 int64_t ldy, int64_t batch, int64_t stride_values,
+                                 int64_t stride_meta, int64_t stride_B, int64_t stride_Y,
+                                 hipStream_t stream) {
+  const SkinnyArgs a = skinny_args(values, meta, R, K, B, C, ldb, Y, ldy, batch, stride_values,
+                                   stride_meta, stride_B, stride_Y);
+  if (batch == 1 && skinny_ring_selected(K, B, C, ldb, b_layout, false)) return dispatch_skinny_ring<false>(a, stream);
+  return dispatch_skinny<false>(a, b_layout, stream);
 }
 
 hipError_t launch_spmm_nm_tiled_skinny(const void* values_t, const void* meta_t, int64_t R, int64_t K,
                                        const void* B, int64_t C, int64_t ldb, int b_layout, void* Y,
                                        int64_t ldy, hipStream_t stream) {
   const SkinnyArgs a = skinny_args(values_t, meta_t, R, K, B, C, ldb, Y, ldy, 1, 0, 0, 0, 0);
-  if (skinny_ring_selected(K, B, C, ldb, b_layout)) {
-    const int nph = (int)(K / sring::PK);
-    return C <= 16 ? launch_skinny_ring<16, 1>(a, nph, stream) : launch_skinny_ring<32, 1>(a, nph, stream);
-  }
+  if (skinny_ring_selected(K, B, C, ldb, b_layout, true)) return dispatch_skinny_ring<true>(a, stream);
   return dispatch_skinny<true>(a, b_layout, stream);
 }
 

@@ -265,7 +265,7 @@ hipError_t launch_spmm_nm_tiled_splitk(const void* values_t, const void* meta_t,
   const SplitPlan p = splitk_plan(R, K, C);
   if (p.splits < 2 || forced_variant() == Variant::kUnsplit) {
     // the split does not pay here: one workgroup per row tile, all of K
-    log_variant("spmm_nm_tiled_ws", R, K, C, skinny_ring_selected(K, B, C, ldb, 1) ? "skinny ring" : "skinny");
+    log_variant("spmm_nm_tiled_ws", R, K, C, skinny_ring_selected(K, B, C, ldb, 1, true) ? "skinny ring" : "skinny");
     return launch_spmm_nm_tiled_skinny(values_t, meta_t, R, K, B, C, ldb, 1, Y, ldy, stream);
   }
   log_variant("spmm_nm_tiled_ws", R, K, C, p.splits == 2 ? "split 2" : p.splits == 3 ? "split 3" : "split 4");

@@ -5,8 +5,8 @@ give the oracle's product, and SNM_LOG must name the variant that ran.
 Shapes: a V:2:16 product with V = 128 whose grid is too small for the large-tile kernel by
 default (so 'large' changes the choice and 'wide' keeps it), the same for V:2:8 with V = 64
 and the 64-row large-tile kernel (both storages), and a decode-shaped 2:4 product with C = 8
-(skinny by default, 'generic' forces the generic tiled kernel), also on the operand-major
-storage (the LDS-ring kernel by default, 'direct' forces the register kernel)."""
+(the LDS-ring kernel by default, 'direct' forces the register kernel, 'generic' the generic
+tiled kernel), on the canonical and the operand-major storage."""
 import os
 import subprocess
 import sys
@@ -102,7 +102,8 @@ def test_vnm64_forced_variant_matches_oracle(kind, force, expect, tmp_path):
                for ln in lines), lines
 
 
-@pytest.mark.parametrize("force,expect", [("", "skinny"), ("generic", "generic"), ("unknown", "skinny")])
+@pytest.mark.parametrize("force,expect", [("", "skinny ring"), ("direct", "skinny"), ("generic", "generic"),
+                                          ("unknown", "skinny ring")])
 def test_nm_forced_variant_matches_oracle(force, expect, tmp_path):
     Y, lines = _run("nm", force, tmp_path)
     A = workloads.small_matrix(13, (512, 1024), 0.02)
