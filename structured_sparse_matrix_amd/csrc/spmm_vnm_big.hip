@@ -35,8 +35,9 @@
 // those of wide_layout.hpp with BN = 512, KS = 32. The output tile is staged through LDS
 // and written as whole 128-byte lines.
 //
-// Shapes: V % 128 == 0 (R a multiple of 128), K' = 4K/M a multiple of 128 with at least two
-// rounds (K' >= 256), K' <= 12224 (column-loc of the V-block staged after the ring), C >= 256
+// Shapes: V % 128 == 0 (R a multiple of 128), K' = 4K/M a multiple of 32 (whole stages; a
+// ragged last round is padded with stages that are copied but not multiplied) with at least
+// two rounds (K' >= 256), K' <= 12224 (column-loc of the V-block staged after the ring), C >= 256
 // and C % 8 == 0 (a ragged last column tile is clamped on load and masked on store),
 // row-major B with ldb % 8 == 0 and 16-byte rows. The values and m-indices may be in the
 // canonical or the row-group interleaved storage.
@@ -131,7 +132,12 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
   const int64_t row0 = rt * BM;
   const int64_t col0 = ct * BN;
   const int64_t Kc = a.Kc;
-  const int64_t nst = Kc / KS;                  // a multiple of NST, >= 2 NST
+  const int64_t nst = Kc / KS;                  // stages, >= 2 NST
+  // the ring runs in rounds of NST stages: a ragged last round is padded with stages whose
+  // copies repeat stage nst - 1 (so every wait keeps its count and every address stays in
+  // the arrays) and whose products are skipped
+  const int64_t nstp = (nst + NST - 1) / NST * NST;
+  auto src = [&](int64_t s) { return s < nst ? s : nst - 1; };
   const int64_t mrow = Kc >> 3;                 // index bytes per row; a values row is Kc bytes
 
   // column-loc bytes of this V-block after the ring
@@ -181,7 +187,7 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
   uint32_t gw[nB / 4];
   auto fetch_colloc = [&](int64_t s) {
 #pragma unroll
-    for (int w = 0; w < nB / 4; ++w) gw[w] = *reinterpret_cast<const uint32_t*>(smem + kRing + s * KS + xrow0 + 4 * w);
+    for (int w = 0; w < nB / 4; ++w) gw[w] = *reinterpret_cast<const uint32_t*>(smem + kRing + src(s) * KS + xrow0 + 4 * w);
   };
   auto pin_colloc = [&]() {
 #pragma unroll
@@ -195,15 +201,15 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
     constexpr int j = decltype(j_c)::value;
     const uint32_t sb = lds0 + (uint32_t)(slot * kStage);
     if constexpr (j < nB) {
-      const uint16_t* bs = a.B + s * (KS / 4) * a.M * a.ldb;
+      const uint16_t* bs = a.B + src(s) * (KS / 4) * a.M * a.ldb;
       const uint32_t g = (gw[j / 4] >> (8 * (j % 4))) & 0xFFu;
       dma_s<16>(bs, boff[j] + g * ldb2, sb + (uint32_t)((xrow0 + j) * 1024));
     } else if constexpr (WAVES == 4) {
-      if constexpr (j == nB) dma_s<16>(vals + s * a_stage, aoff, sb + (uint32_t)(kAOff + ablk * 1024));
-      else dma_s<2>(meta + s * m_stage, moff, sb + (uint32_t)(kMOff + ablk * 256));
+      if constexpr (j == nB) dma_s<16>(vals + src(s) * a_stage, aoff, sb + (uint32_t)(kAOff + ablk * 1024));
+      else dma_s<2>(meta + src(s) * m_stage, moff, sb + (uint32_t)(kMOff + ablk * 256));
     } else {
-      if (wave < 4) dma_s<16>(vals + s * a_stage, aoff, sb + (uint32_t)(kAOff + ablk * 1024));
-      else dma_s<2>(meta + s * m_stage, moff, sb + (uint32_t)(kMOff + ablk * 256));
+      if (wave < 4) dma_s<16>(vals + src(s) * a_stage, aoff, sb + (uint32_t)(kAOff + ablk * 1024));
+      else dma_s<2>(meta + src(s) * m_stage, moff, sb + (uint32_t)(kMOff + ablk * 256));
     }
   };
   auto copy_all = [&](int64_t s, auto slot_c) {
@@ -300,7 +306,9 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
     static_for<0, kPairs>([&](auto q) {
       constexpr int Q = decltype(q)::value;   // product pair: row tile Q / (TN / 2)
       constexpr int kRd = kPairs / 4;         // pairs per read part
-      if constexpr (MMA) mma_pair(prev, cint<Q / (TN / 2)>{}, cint<2 * (Q % (TN / 2))>{});
+      if constexpr (MMA) {
+        if (s - 1 < nst) mma_pair(prev, cint<Q / (TN / 2)>{}, cint<2 * (Q % (TN / 2))>{});
+      }
       if constexpr (Q % kRd == 0) read_part(cur, sb, cint<Q / kRd>{});
       if constexpr (ISSUE && Q + 2 < kDma) copy(sx, cint<NX>{}, cint<Q + 2>{});
     });
@@ -318,7 +326,7 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
     copy_all((int64_t)P, cint<P>{});
   });
   fetch_colloc(NST - 1);
-  const int64_t rounds = nst / NST;
+  const int64_t rounds = nstp / NST;
   // first round (no products before stage 0); the fetch of column-loc for stage s + NST
   // stays inside column-loc because nst >= 2 NST
   static_for<0, NST>([&](auto u) {
@@ -327,7 +335,7 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
     lds_barrier();
     stage((int64_t)U, cint<U>{}, cint<1>{}, cint<(U > 0)>{});
   });
-  // steady rounds: every stage copies stage s + NST - 1 (< nst)
+  // steady rounds: every stage copies stage s + NST - 1 (< nstp)
   for (int64_t r = 1; r < rounds - 1; ++r) {
     static_for<0, NST>([&](auto u) {
       constexpr int U = decltype(u)::value;
@@ -336,7 +344,7 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
       stage(r * NST + U, cint<U>{}, cint<1>{}, cint<1>{});
     });
   }
-  // last round: only its first stage still copies (stage nst - 1), and it fetches no
+  // last round: only its first stage still copies (stage nstp - 1), and it fetches no
   // column-loc past the V-block's
   static_for<0, NST>([&](auto u) {
     constexpr int U = decltype(u)::value;
@@ -350,10 +358,12 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
     }
     stage(s, cint<U>{}, cint<0>{}, cint<1>{});
   });
-  static_for<0, kPairs>([&](auto q) {   // products of the last stage
-    constexpr int Q = decltype(q)::value;
-    mma_pair(fr[(NST - 1) % 2], cint<Q / (TN / 2)>{}, cint<2 * (Q % (TN / 2))>{});
-  });
+  if (nstp == nst) {   // products of the last stage, unless it is padding
+    static_for<0, kPairs>([&](auto q) {
+      constexpr int Q = decltype(q)::value;
+      mma_pair(fr[(NST - 1) % 2], cint<Q / (TN / 2)>{}, cint<2 * (Q % (TN / 2))>{});
+    });
+  }
   // The epilogue reads the accumulators with ordinary instructions: give the last products
   // 32 wait states first (a 16-pass product needs 18), and route every accumulator through
   // an empty statement after them so that no read is scheduled earlier.
@@ -422,7 +432,7 @@ hipError_t launch_big(const BigArgs& a, int64_t tiles, hipStream_t stream) {
 bool spmm_vnm_big_eligible(int64_t R, int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb) {
   using namespace big;
   if (V <= 0 || V % BM != 0 || R <= 0 || R % BM != 0) return false;
-  if (Kc % (KS * NST) != 0 || Kc < 2 * KS * NST || Kc > kMaxKc) return false;
+  if (Kc % KS != 0 || Kc < 2 * KS * NST || Kc > kMaxKc) return false;
   if (C < BN / 2 || C % 8 != 0 || ldb % 8 != 0 || ((uintptr_t)B & 15) != 0) return false;
   // 32-bit DMA offsets: a tile's rows of values, one stage's gathered B rows
   constexpr int64_t kLim = (int64_t)1 << 31;

@@ -1,8 +1,9 @@
 """GPU parity of the large-tile V:2:M product (spmm_vnm_big.hip: 128 x 512 workgroup tiles,
 accumulators in the AGPR file), which the V:2:M entry points select for V % 128 == 0 when
-K' = 4K/M is a multiple of 128 in [256, 12224] and the grid has at least 256 workgroups.
+K' = 4K/M is a multiple of 32 in [256, 12224] and the grid has at least 256 workgroups.
 Shapes cover the shortest reduction (two rounds of four stages, no steady round), longer
-ones, a ragged last column tile, a grid whose size is not a multiple of 8 (no XCD
+ones, ragged last rounds (K' not a multiple of 128: one to three padding stages whose
+copies repeat the last stage and whose products are skipped), a ragged last column tile, a grid whose size is not a multiple of 8 (no XCD
 renumbering), both storages of A, and the exact decode with B = I. The configuration-5
 workload and the GPT-3 layer shape, which also run this kernel, are checked in
 test_gpu_vnm_tiled.py, test_gpu_spmm.py and test_gpu_vnm_sweep.py."""
@@ -27,6 +28,9 @@ def _snm():
     (4096, 2048, 4088, 16),    # K' = 512: two steady rounds; ragged last column tile
     (4096, 1024, 4096, 8),     # K' = 512, 2:8
     (8576, 512, 1544, 8),      # 67 V-blocks x 4 column tiles = 268 workgroups (no renumbering)
+    (4096, 720, 4096, 10),     # K' = 288: nine stages, the last round padded by three
+    (4096, 1600, 4096, 20),    # K' = 320: ten stages, padded by two
+    (4096, 1408, 4088, 16),    # K' = 352: eleven stages, padded by one; ragged column tile
 ])
 @pytest.mark.parametrize("storage", ["canonical", "interleaved"])
 def test_big_matches_oracle(R, K, C, M, storage):
@@ -45,11 +49,13 @@ def test_big_matches_oracle(R, K, C, M, storage):
 
 
 @pytest.mark.parametrize("storage", ["canonical", "interleaved"])
-def test_big_identity_is_exact_decode(storage):
+@pytest.mark.parametrize("K", [1024, 1408])
+def test_big_identity_is_exact_decode(storage, K):
     # B = I: every output is one product, so the kernel must return the decoded matrix
-    # exactly (16384 x 1024 with 2:16: 128 V-blocks x 2 column tiles = 256 workgroups)
+    # exactly (16384 x 1024 with 2:16: 128 V-blocks x 2 column tiles = 256 workgroups;
+    # K = 1408: K' = 352, a last round with one padding stage, 384 workgroups)
     snm = _snm()
-    R, K, V, M = 16384, 1024, 128, 16
+    R, V, M = 16384, 128, 16
     A = workloads.small_matrix(99, (R, K))
     ov, omi, ocl = oracle.prune_encode_vnm(A, V, M)
     dense = oracle.decode_vnm(ov, omi, ocl, V, M, K)
