@@ -25,7 +25,8 @@
 // those of wide_layout.hpp with BN = 256, KS = 64. The output tile is staged through LDS
 // and written as whole 128-byte lines.
 //
-// Shapes: V % 64 == 0 (R a multiple of 64), K' = 4K/M a multiple of 256 with at least two
+// Shapes: V % 64 == 0 (R a multiple of 64), K' = 4K/M a multiple of 64 (whole stages; a ragged
+// last round is padded with stages that are copied but not multiplied) with at least two
 // rounds (K' >= 512), K' <= 12288 (column-loc staged after the ring), C >= 128 and
 // C % 8 == 0 (a ragged last column tile is clamped on load and masked on store), row-major
 // B with ldb % 8 == 0 and 16-byte rows. Values and m-indices canonical or row-group
@@ -113,7 +114,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
   const int64_t row0 = rt * BM;
   const int64_t col0 = ct * BN;
   const int64_t Kc = a.Kc;
-  const int64_t nst = Kc / KS;                  // a multiple of NST, >= 2 NST
+  const int64_t nst = Kc / KS;                  // stages, >= 2 NST
+  // the ring runs in rounds of NST stages: a ragged last round is padded with stages whose
+  // copies repeat stage nst - 1 (so every wait keeps its count and every address stays in
+  // the arrays) and whose products are skipped
+  const int64_t nstp = (nst + NST - 1) / NST * NST;
+  auto src = [&](int64_t s) { return s < nst ? s : nst - 1; };
   const int64_t mrow = Kc >> 3;                 // index bytes per row; a values row is Kc bytes
 
   // column-loc bytes of this tile's V-block after the ring
@@ -162,7 +168,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
   uint32_t gcl[nB];
   auto fetch_colloc = [&](int64_t s) {
 #pragma unroll
-    for (int j = 0; j < nB; ++j) gcl[j] = smem[kRing + s * KS + bx[j]];
+    for (int j = 0; j < nB; ++j) gcl[j] = smem[kRing + src(s) * KS + bx[j]];
   };
   auto pin_colloc = [&]() {
 #pragma unroll
@@ -175,11 +181,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     constexpr int j = decltype(j_c)::value;
     const uint32_t sb = lds0 + (uint32_t)(slot * kStage);
     if constexpr (j < nB) {
-      const uint16_t* bs = a.B + s * (KS / 4) * a.M * a.ldb;
+      const uint16_t* bs = a.B + src(s) * (KS / 4) * a.M * a.ldb;
       dma_s<16>(bs, boff[j] + gcl[j] * ldb2, sb + (uint32_t)((wave * nB + j) * 1024));
     } else {
-      if (wave < 4) dma_s<16>(vals + s * a_stage, aoff, sb + (uint32_t)(kAOff + ablk * 1024));
-      else dma_s<2>(meta + s * m_stage, moff, sb + (uint32_t)(kMOff + ablk * 256));
+      if (wave < 4) dma_s<16>(vals + src(s) * a_stage, aoff, sb + (uint32_t)(kAOff + ablk * 1024));
+      else dma_s<2>(meta + src(s) * m_stage, moff, sb + (uint32_t)(kMOff + ablk * 256));
     }
   };
   auto copy_all = [&](int64_t s, auto slot_c) {
@@ -255,7 +261,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     static_for64<0, KSTEPS * TM>([&](auto q) {
       constexpr int Q = decltype(q)::value;
       constexpr int KS_ = Q / TM, TM_ = Q % TM;
-      if constexpr (MMA) mma(prev, cint64<KS_>{}, cint64<TM_>{});
+      if constexpr (MMA) {
+        if (s - 1 < nst) mma(prev, cint64<KS_>{}, cint64<TM_>{});
+      }
       read_a(cur, sb, cint64<KS_>{}, cint64<TM_>{});
       if constexpr (TM_ == 0) read_b(cur, sb, cint64<KS_>{});
       if constexpr (ISSUE && Q + 2 < kDma) copy(sx, cint64<NX>{}, cint64<Q + 2>{});
@@ -271,7 +279,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     copy_all((int64_t)P, cint64<P>{});
   });
   fetch_colloc(NST - 1);
-  const int64_t rounds = nst / NST;
+  const int64_t rounds = nstp / NST;
   // first round (no products before stage 0)
   static_for64<0, NST>([&](auto u) {
     constexpr int U = decltype(u)::value;
@@ -279,7 +287,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     lds_barrier();
     stage((int64_t)U, cint64<U>{}, cint64<1>{}, cint64<(U > 0)>{});
   });
-  // steady rounds: every stage copies stage s + NST - 1 (< nst)
+  // steady rounds: every stage copies stage s + NST - 1 (< nstp)
   for (int64_t r = 1; r < rounds - 1; ++r) {
     static_for64<0, NST>([&](auto u) {
       constexpr int U = decltype(u)::value;
@@ -288,7 +296,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
       stage(r * NST + U, cint64<U>{}, cint64<1>{}, cint64<1>{});
     });
   }
-  // last round: only its first stage still copies (stage nst - 1), and it fetches no
+  // last round: only its first stage still copies (stage nstp - 1), and it fetches no
   // column-loc past the V-block's
   static_for64<0, NST>([&](auto u) {
     constexpr int U = decltype(u)::value;
@@ -302,10 +310,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     }
     stage(s, cint64<U>{}, cint64<0>{}, cint64<1>{});
   });
-  static_for64<0, KSTEPS * TM>([&](auto q) {   // products of the last stage
-    constexpr int Q = decltype(q)::value;
-    mma(fr[(NST - 1) % 2], cint64<Q / TM>{}, cint64<Q % TM>{});
-  });
+  if (nstp == nst) {   // products of the last stage, unless it is padding
+    static_for64<0, KSTEPS * TM>([&](auto q) {
+      constexpr int Q = decltype(q)::value;
+      mma(fr[(NST - 1) % 2], cint64<Q / TM>{}, cint64<Q % TM>{});
+    });
+  }
 
   // ---- epilogue: fp32 -> fp16 (RNE) through an LDS tile, whole 128-byte lines out --------
   __syncthreads();   // every wave is done with the ring and column-loc
@@ -347,7 +357,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
 bool spmm_vnm_big64_eligible(int64_t R, int64_t Kc, int V, int M, const void* B, int64_t C, int64_t ldb) {
   using namespace big64;
   if (V <= 0 || V % BM != 0 || R <= 0 || R % BM != 0) return false;
-  if (Kc % (KS * NST) != 0 || Kc < 2 * KS * NST || Kc > kMaxKc) return false;
+  if (Kc % KS != 0 || Kc < 2 * KS * NST || Kc > kMaxKc) return false;
   if (C < BN / 2 || C % 8 != 0 || ldb % 8 != 0 || ((uintptr_t)B & 15) != 0) return false;
   // 32-bit DMA offsets: a tile's rows of values, one stage's gathered B rows
   constexpr int64_t kLim = (int64_t)1 << 31;

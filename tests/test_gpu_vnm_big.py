@@ -66,3 +66,25 @@ def test_big_identity_is_exact_decode(storage, K):
         vt, mt = tile(ov, omi, M)
         Y = snm.spmm_vnm_tiled(to_dev(vt), to_dev(mt), to_dev(ocl), to_dev(B), V, M)
     assert_bits_equal(to_host(Y), dense, f"B = I, {storage}")
+
+
+@pytest.mark.parametrize("R,K,C,V,M", [
+    (1024, 4160, 4096, 64, 20),    # K' = 832: 13 stages of 64, the last round padded by three
+    (1024, 1152, 4096, 64, 8),     # K' = 576: nine stages, padded by three
+    (1024, 2560, 4088, 128, 16),   # K' = 640: ten stages, padded by two; V = 128 on 64-row tiles
+    (1024, 1760, 4096, 64, 10),    # K' = 704: eleven stages, padded by one
+])
+@pytest.mark.parametrize("storage", ["canonical", "interleaved"])
+def test_big64_ragged_rounds_match_oracle(R, K, C, V, M, storage):
+    # the 64-row large-tile kernel (16 x 16 = 256 workgroups, above its 128-workgroup rule)
+    snm = _snm()
+    print(f"big64 {R}x{K}x{C} V{V} M{M} {storage}", flush=True)
+    A = workloads.small_matrix(R + 3 * K + C + M, (R, K), 0.02)
+    B = workloads.small_matrix(R + 5 * K + C, (K, C))
+    ov, omi, ocl = oracle.prune_encode_vnm(A, V, M)
+    if storage == "canonical":
+        Y = snm.spmm_vnm(to_dev(ov), to_dev(omi), to_dev(ocl), to_dev(B), V, M)
+    else:
+        vt, mt = tile(ov, omi, M)
+        Y = snm.spmm_vnm_tiled(to_dev(vt), to_dev(mt), to_dev(ocl), to_dev(B), V, M)
+    assert_fp16_close(to_host(Y), oracle.spmm_vnm(ov, omi, ocl, V, M, B), f"big64 {R}x{K}x{C} M{M} {storage}")
