@@ -226,11 +226,15 @@ k_prune_encode_vnm(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t
 // 32 KiB otherwise (more workgroups per CU to overlap the phases); measured on MI355X.
 constexpr int kVnmTileBytes = 64 * 1024;
 static int vnm_tile_bytes(int V) { return V >= 128 ? kVnmTileBytes : kVnmTileBytes / 2; }
+// Row pitch (elements) of the staged tile for rows of `pitch` elements (a multiple of 8):
+// an odd number of 16-byte chunks.
+__host__ __device__ __forceinline__ int vnm_lds_pitch(int pitch) { return ((pitch >> 3) | 1) << 3; }
 
+template <bool TILED>
 __global__ void __launch_bounds__(kVnmThreads)
 k_prune_encode_vnm_lds(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t lda, int V,
                        int M, int GC, uint16_t* __restrict__ values, uint16_t* __restrict__ midx,
-                       uint8_t* __restrict__ colloc, int tiled) {
+                       uint8_t* __restrict__ colloc) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int64_t G = K / M;
   const int64_t nchunks = (G + GC - 1) / GC;
@@ -238,27 +242,36 @@ k_prune_encode_vnm_lds(const uint16_t* __restrict__ A, int64_t R, int64_t K, int
   const int64_t g0 = (blockIdx.x - vb * nchunks) * GC;
   const int ng = (int)((G - g0) < GC ? (G - g0) : GC);   // groups in this chunk (multiple of 4)
   const int ncols = ng * M;
-  const int pitch = GC * M;                              // elements per staged row
+  const int pitch = GC * M;                              // columns of a full tile
+  // Staged rows are an odd number of 16-byte chunks apart (one pad chunk after rows of an
+  // even number): phase 3 reads one column across consecutive rows (a lane per row), and
+  // with an odd stride sixteen consecutive rows start in sixteen different bank groups
+  // (a 384-byte row, V:2:16 with 12 groups, would otherwise put them on two banks).
+  const int pitchp = vnm_lds_pitch(pitch);
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
-  double* score = reinterpret_cast<double*>(smem + (size_t)V * pitch * 2);
+  double* score = reinterpret_cast<double*>(smem + (size_t)V * pitchp * 2);
   uint8_t* sel = reinterpret_cast<uint8_t*>(score + pitch);   // [group in chunk][4]
   uint8_t* keep = sel + GC * 4;
   const uint16_t* Ablk = A + vb * V * lda + g0 * M;
+  auto tcol = [&](int r, int col) -> int { return r * pitchp + col; };   // element of (r, col)
 
   // ---- stage the tile
   if (ncols == pitch && (((uintptr_t)Ablk) & 15) == 0 && (lda & 7) == 0) {
-    // a full tile is dense in LDS (row pitch = row length): 16-byte chunk ci = row-major
-    // chunk index, so each wave's DMA instruction fills 1 KiB of consecutive chunks and every
-    // copy of the workgroup is in flight at once
+    // a full tile is dense in LDS up to the pad chunks: 16-byte slot ci = row-major slot
+    // index, so each wave's DMA instruction fills 1 KiB of consecutive slots and every copy
+    // of the workgroup is in flight at once; a pad slot takes a second copy of its row's
+    // first chunk
     const int c8 = ncols >> 3;
-    const int n = V * c8;
+    const int c8p = pitchp >> 3;
+    const int n = V * c8p;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint32_t tile_lds = lds_addr(smem);
     for (int b0 = 64 * wave; b0 < n; b0 += kVnmThreads) {
       const int ci = b0 + lane;
       if (ci < n) {   // the last instruction may be partial: its idle lanes write nothing
-        const int r = ci / c8;
-        const int c = (ci - r * c8) * 8;
+        const int r = ci / c8p;
+        const int q = ci - r * c8p;
+        const int c = (q < c8 ? q : 0) * 8;
         dma_v<16>(Ablk + (int64_t)r * lda + c, tile_lds + (uint32_t)b0 * 16u);
       }
     }
@@ -284,7 +297,7 @@ k_prune_encode_vnm_lds(const uint16_t* __restrict__ A, int64_t R, int64_t K, int
         if (i < n) {
           const int r = i / c8;
           const int c = (i - r * c8) * 8;
-          *reinterpret_cast<u4*>(tile + r * pitch + c) = v[t];
+          *reinterpret_cast<u4*>(tile + r * pitchp + c) = v[t];
         }
       }
     }
@@ -292,18 +305,50 @@ k_prune_encode_vnm_lds(const uint16_t* __restrict__ A, int64_t R, int64_t K, int
     for (int i = threadIdx.x; i < V * ncols; i += kVnmThreads) {
       const int r = i / ncols;
       const int c = i - r * ncols;
-      tile[r * pitch + c] = Ablk[(int64_t)r * lda + c];
+      tile[r * pitchp + c] = Ablk[(int64_t)r * lda + c];
     }
   }
   __syncthreads();
-  // ---- phase 1: column scores; eight LDS reads in flight, sums in row order
+  // ---- phase 1: column scores, float64 sums in row order
+  if (V % 16 == 0) {
+    // each lane owns one column: a transpose read (ds_read_b64_tr_b16) gives it four
+    // consecutive rows of that column, so a column of V rows costs V/4 LDS reads instead of
+    // V. Lane gl of a 16-lane group reads row r0 + gl/4, columns cg + 4 (gl % 4) .. + 3; in
+    // a group that straddles the end of the staged columns, the reads past them fall on the
+    // row's pad chunk, the next row or, for the last row, the score array after the tile,
+    // and are never used.
+    const int lane = threadIdx.x & 63;
+    const int gl = lane & 15;
+    const uint32_t tile_lds = lds_addr(smem);
+    for (int cw = (int)(threadIdx.x & ~63); cw < ncols; cw += kVnmThreads) {   // wave-uniform
+      const int cg = cw + (lane & 48);
+      const int c = cg + gl;
+      // first of the four columns this lane reads (a group wholly past the staged columns
+      // reads column 0 instead, unused)
+      const int rc = (cg < ncols ? cg : 0) + 4 * (gl & 3);
+      double s = 0.0;
+      for (int r0 = 0; r0 < V; r0 += 16) {
+        h4 q[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) q[t] = lds_read_tr16(tile_lds + (uint32_t)(tcol(r0 + 4 * t + (gl >> 2), rc) * 2));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const double a = (double)q[t][e];
+            s = __builtin_fma(a, a, s);   // a*a is exact, so this equals s + a*a rounded once
+          }
+      }
+      if (c < ncols) score[c] = s;
+    }
+  } else
   for (int c = threadIdx.x; c < ncols; c += kVnmThreads) {
     double s = 0.0;
     int r = 0;
     for (; r + 8 <= V; r += 8) {
       uint16_t h[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) h[t] = tile[(r + t) * pitch + c];
+      for (int t = 0; t < 8; ++t) h[t] = tile[tcol(r + t, c)];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const double a = (double)bits_f16(h[t]);
@@ -311,7 +356,7 @@ k_prune_encode_vnm_lds(const uint16_t* __restrict__ A, int64_t R, int64_t K, int
       }
     }
     for (; r < V; ++r) {
-      const double a = (double)bits_f16(tile[r * pitch + c]);
+      const double a = (double)bits_f16(tile[tcol(r, c)]);
       s = __builtin_fma(a, a, s);
     }
     score[c] = s;
@@ -364,41 +409,35 @@ k_prune_encode_vnm_lds(const uint16_t* __restrict__ A, int64_t R, int64_t K, int
     }
   }
   __syncthreads();
-  // ---- phase 3: 2:4 among the selected columns, one thread per (row, group), four items
-  // in flight per thread. Consecutive threads take consecutive groups of a row (ng is a
-  // multiple of 4), so the four groups of a metadata word sit in one lane quad and their
-  // codes are combined with two quad permutes.
-  const int nitems = V * ng;
-  const int lane = threadIdx.x & 63;
-  for (int i0 = threadIdx.x; i0 < nitems + 3 * kVnmThreads; i0 += 4 * kVnmThreads) {
-    if (i0 - (int)threadIdx.x >= nitems) break;   // uniform: the whole batch is past the end
-    uint32_t sw[4];
-    int rr[4], gg[4];
+  // ---- phase 3: 2:4 among the selected columns, one thread per (row, four groups): lanes
+  // take consecutive rows of one run of four groups, so the groups' column selections are
+  // the same across the wave, each thread writes one 16-byte piece of values and one index
+  // word, and in the row-group interleaved storage 32 consecutive rows of a run of four
+  // groups are 512 contiguous bytes.
+  const int nw = ng >> 2;
+  const int nitems = V * nw;
+  for (int it = threadIdx.x; it < nitems; it += kVnmThreads) {
+    const int w = it / V;
+    const int r = it - w * V;
+    uint32_t out[4];
+    uint32_t word = 0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int it = i0 + t * kVnmThreads;
-      const int itc = it < nitems ? it : nitems - 1;
-      rr[t] = itc / ng;
-      gg[t] = itc - rr[t] * ng;
-      sw[t] = *reinterpret_cast<const uint32_t*>(sel + gg[t] * 4);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int it = i0 + t * kVnmThreads;
-      const uint16_t* ag = tile + rr[t] * pitch + gg[t] * M;
-      const uint32_t p01 = (uint32_t)ag[sw[t] & 0xFFu] | ((uint32_t)ag[(sw[t] >> 8) & 0xFFu] << 16);
-      const uint32_t p23 = (uint32_t)ag[(sw[t] >> 16) & 0xFFu] | ((uint32_t)ag[sw[t] >> 24] << 16);
+    for (int q = 0; q < 4; ++q) {
+      const int g = 4 * w + q;
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(sel + g * 4);
+      const int cb = g * M;
+      const uint32_t p01 = (uint32_t)tile[tcol(r, cb + (int)(sw & 0xFFu))] |
+                           ((uint32_t)tile[tcol(r, cb + (int)((sw >> 8) & 0xFFu))] << 16);
+      const uint32_t p23 = (uint32_t)tile[tcol(r, cb + (int)((sw >> 16) & 0xFFu))] |
+                           ((uint32_t)tile[tcol(r, cb + (int)(sw >> 24))] << 16);
       uint32_t kept;
-      const uint32_t code = select_2of4_keys(p01, p23, kept);
-      uint32_t w = code << (4 * (lane & 3));
-      w |= (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
-      w |= (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
-      if (it < nitems) {
-        const int64_t row = vb * V + rr[t];
-        *reinterpret_cast<uint32_t*>(values + vnm_value_at(row, g0 + gg[t], G, tiled)) = kept;
-        if ((lane & 3) == 0) midx[vnm_word_at(row, (g0 + gg[t]) >> 2, G, tiled)] = (uint16_t)w;
-      }
+      word |= select_2of4_keys(p01, p23, kept) << (4 * q);
+      out[q] = kept;
     }
+    const int64_t row = vb * V + r;
+    u4 o = {out[0], out[1], out[2], out[3]};
+    *reinterpret_cast<u4*>(values + vnm_value_at(row, g0 + 4 * w, G, TILED)) = o;
+    midx[vnm_word_at(row, (g0 >> 2) + w, G, TILED)] = (uint16_t)word;
   }
 }
 
@@ -450,12 +489,14 @@ hipError_t launch_prune_encode_vnm(const void* A, int64_t R, int64_t K, int64_t 
     const int64_t G = K / M;
     const int64_t nchunks = (G + GL - 1) / GL;
     const int64_t blocks = (R / V) * nchunks;
-    const size_t lds = (size_t)V * GL * M * 2 + (size_t)GL * M * (8 + 1) + (size_t)GL * 4;   // tile, score, sel, keep
+    const size_t lds = (size_t)V * vnm_lds_pitch(GL * M) * 2 + (size_t)GL * M * (8 + 1) + (size_t)GL * 4;   // tile, score, keep, sel
     static std::atomic<uint64_t> lds_set{0};
-    if (hipError_t e = ensure_lds_limit(lds_set, (const void*)k_prune_encode_vnm_lds, 96 * 1024)) return e;
-    hipLaunchKernelGGL(k_prune_encode_vnm_lds, dim3((unsigned)blocks), dim3(kVnmThreads), lds, stream,
+    auto kern = tiled ? k_prune_encode_vnm_lds<true> : k_prune_encode_vnm_lds<false>;
+    static std::atomic<uint64_t> lds_set_t{0};
+    if (hipError_t e = ensure_lds_limit(tiled ? lds_set_t : lds_set, (const void*)kern, 96 * 1024)) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kVnmThreads), lds, stream,
                        (const uint16_t*)A, R, K, lda, V, M, GL, (uint16_t*)values, (uint16_t*)midx,
-                       (uint8_t*)colloc, (int)tiled);
+                       (uint8_t*)colloc);
     return hipGetLastError();
   }
   const int GC = vnm_chunk_groups(M);
