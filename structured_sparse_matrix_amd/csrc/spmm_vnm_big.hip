@@ -400,7 +400,9 @@ __device__ __forceinline__ void spmm_vnm_big_body(const BigArgs& a) {
       const u4 v = *reinterpret_cast<const u4*>(otile + r * kOutPitch + ch * 16);
       uint16_t* dst = a.Y + row * a.ldy + col;
       if (a.y_vec) {
-        *reinterpret_cast<u4*>(dst) = v;
+        // streaming stores: the output is not read again here, and it would otherwise
+        // displace the gathered B rows other workgroups still read from L2
+        __builtin_nontemporal_store(v, reinterpret_cast<u4*>(dst));
       } else {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
