@@ -218,12 +218,14 @@ k_prune_encode_vnm(const uint16_t* __restrict__ A, int64_t R, int64_t K, int64_t
   }
 }
 
-// V:2:M with the workgroup's V x (GC*M) tile of A staged in LDS first (batches of eight
-// 16-byte loads in flight per thread), then the column scores (float64, rows in ascending
-// order), the column-loc selection and the 2:4 encoding all read LDS: one HBM read of A,
-// no dependent global loads. Used whenever a tile of at least one metadata word of groups
-// fits. Tiles of up to 64 KiB for tall blocks (V >= 128: fewer, longer score chains) and
-// 32 KiB otherwise (more workgroups per CU to overlap the phases); measured on MI355X.
+// V:2:M with the workgroup's V x (GC*M) tile of A staged in LDS first (a full tile by the
+// global -> LDS DMA path, every copy of the workgroup in flight; a ragged one by batches of
+// eight 16-byte loads per thread), then the column scores (float64, rows in ascending order,
+// four rows of a column per transpose read), the column-loc selection and the 2:4 encoding
+// (one thread per (row, four groups), lanes on consecutive rows) all read LDS: one HBM read
+// of A, no dependent global loads. Used whenever a tile of at least one metadata word of
+// groups fits. Tiles of up to 64 KiB for tall blocks (V >= 128: fewer, longer score chains)
+// and 32 KiB otherwise (more workgroups per CU to overlap the phases); measured on MI355X.
 constexpr int kVnmTileBytes = 64 * 1024;
 static int vnm_tile_bytes(int V) { return V >= 128 ? kVnmTileBytes : kVnmTileBytes / 2; }
 // Row pitch (elements) of the staged tile for rows of `pitch` elements (a multiple of 8):
