@@ -102,3 +102,56 @@ def test_split_decode_product_graph_replays_match_eager():
         torch.cuda.synchronize()
         for i, y in enumerate(gY):
             assert np.array_equal(to_host(y).view(np.uint16), ref[i]), f"replay {rep}, N={NS[i]}"
+
+
+@pytest.mark.parametrize("R,K,C,V,M", [
+    (2048, 1024, 8192, 128, 16),   # 16 x 16 tiles of 128 x 512: the 128-row large-tile product
+    (2048, 1024, 1024, 64, 8),     # 32 x 4 tiles of 64 x 256: the 64-row large-tile product
+])
+def test_vnm_step_graph_replays_match_eager(R, K, C, V, M):
+    """The V:N:M step the benchmark times (V:2:M prune/encode into the row-group interleaved
+    storage, then the product) captured into a HIP graph: the large-tile products record no
+    memset or allocation, so every replay, with eager work between replays, reproduces the
+    eager results bit for bit."""
+    import torch
+    from structured_sparse_matrix_amd import vnm_sizes
+    from structured_sparse_matrix_amd._lib import load, check
+    lib = load()
+    A = to_dev(workloads.small_matrix(31 + M, (R, K), 0.02))
+    B = to_dev(workloads.small_matrix(32 + M, (K, C)))
+    nv, nm, nc = vnm_sizes(R, K, V, M)
+
+    def buffers():
+        return (torch.empty((nv,), dtype=torch.float16, device="cuda"),
+                torch.empty((nm,), dtype=torch.uint8, device="cuda"),
+                torch.empty((nc,), dtype=torch.uint8, device="cuda"),
+                torch.empty((R, C), dtype=torch.float16, device="cuda"))
+
+    def step(bufs, stream):
+        v, mi, cl, Y = bufs
+        h = stream.cuda_stream
+        check("encode", lib.snm_prune_encode_vnm_tiled(A.data_ptr(), R, K, K, V, 2, M, v.data_ptr(), mi.data_ptr(),
+                                                       cl.data_ptr(), h))
+        check("spmm", lib.snm_spmm_vnm_tiled(v.data_ptr(), mi.data_ptr(), cl.data_ptr(), R, K, V, 2, M, B.data_ptr(),
+                                             C, C, Y.data_ptr(), C, h))
+
+    eager = buffers()
+    step(eager, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = [to_host(t).view(np.uint8).copy() for t in eager]
+
+    graph_bufs = buffers()
+    cap = torch.cuda.Stream()
+    step(graph_bufs, cap)   # first use outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step(graph_bufs, cap)
+    for rep in range(3):
+        graph_bufs[3].fill_(7.0)                                # eager work between replays
+        step(eager, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, t in enumerate(graph_bufs):
+            assert np.array_equal(to_host(t).view(np.uint8), ref[i]), f"replay {rep}, buffer {i}"
