@@ -11,14 +11,16 @@
 //   * the encoder runs in three steps -- per-row bitmaps, padded counts and in-row
 //     offsets; one workgroup scanning the row totals; the final offsets -- then writes
 //     the values in a separate call, once the caller has allocated them.
-//   * the product: one workgroup per 16 rows, eight waves splitting K. Each wave walks its
-//     tiles in phases of 2, software-pipelined: the tiles' bitmaps and offsets are copied
-//     into LDS (global->LDS DMA) two phases ahead, their packed values (16-byte aligned
-//     spans, because every tile starts at a multiple of 8 values) one phase ahead, into
-//     double-buffered per-wave regions whose rows are padded to a 272-byte pitch so that
-//     the 16 rows' reads fall on different LDS banks. Each 8-position chunk is expanded
-//     through its bitmap byte with LDS reads at the computed ranks and fed to a dense
-//     MFMA. Partial sums of the waves are added through LDS.
+//   * the product: one workgroup per 16 rows (or per 32, two row groups sharing each B
+//     operand, with column-major B when those workgroups fit on the CUs at once), eight
+//     waves splitting K. Each wave walks its tiles in phases of 2, software-pipelined: the
+//     tiles' bitmaps and offsets are copied into LDS (global->LDS DMA) two phases ahead,
+//     their packed values (16-byte aligned spans, because every tile starts at a multiple
+//     of 8 values) one phase ahead, into double-buffered per-wave regions whose rows are
+//     padded to a 272-byte pitch so that the 16 rows' reads fall on different LDS banks.
+//     Each 8-position chunk is expanded through its bitmap byte with LDS reads at the
+//     computed ranks and fed to a dense MFMA. Partial sums of the waves are added through
+//     LDS.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "lds_dma.hpp"
@@ -210,8 +212,9 @@ __device__ __forceinline__ f4 mfma16x16x32(const h8& a, const h8& b, const f4& c
 template <int I>
 using cint = std::integral_constant<int, I>;
 
-// One workgroup (kBmWaves waves) per 16-row tile; wave w takes a contiguous 1/kBmWaves of
-// the row's tiles and walks it in phases of kPT tiles. Lane l = 16q + i works on row i; in
+// One workgroup (kBmWaves waves) per RG row groups of 16 rows; wave w takes a contiguous
+// 1/kBmWaves of the rows' tiles and walks it in phases of kPT tiles. Lane l = 16q + i works
+// on row i of every row group (each B operand feeds RG products); in
 // tile t it covers positions 32 blk + 8q + [0, 8), blk = 0, 1 (bitmap byte 4 blk + q) --
 // the dense MFMA A operand of k-block (t, blk).
 // A phase goes through three steps, each overlapped with the previous phase's work:
@@ -234,21 +237,28 @@ constexpr int kBmWaves = 8;
 constexpr int kPT = 2;                                   // tiles per phase
 constexpr int kRowPitch = kPT * kTile * 2 + 16;          // a row's staged values + pad: 17 slots
 constexpr int kSlots = 16 * (kRowPitch / 16);            // 16-byte slots of a value buffer (272)
-constexpr int kValBuf = 16 * kRowPitch;                  // one phase's values (4352 bytes)
-constexpr int kMetaBuf = 448;                            // bitmaps 16 x 16 B, offsets 16 x 12 B
-constexpr int kMetaOffs = 256;                           // offsets within a metadata buffer
-constexpr int kValBase = 2 * kMetaBuf;                   // metadata first: a pair read one value
-                                                         // before a row stays inside the region
-constexpr int kWaveBytes = kValBase + 2 * kValBuf;       // two phases in flight (9600 bytes)
-constexpr int kLutOff = kBmWaves * kWaveBytes;
+constexpr int kRGVal = 16 * kRowPitch;                   // a row group's staged values (4352 bytes)
+constexpr int kRGMeta = 448;                             // a row group's bitmaps 16 x 16 B, offsets 16 x 12 B
+constexpr int kMetaOffs = 256;                           // offsets within a row group's metadata
 constexpr int kLutBytes = 256 * 8 + 16 * 8;              // ranks per byte, keep masks per nibble
-constexpr int kBitmapLds = kLutOff + kLutBytes;          // 77 KiB: two workgroups per CU
-static_assert(kBitmapLds <= 80 * 1024, "two workgroups per CU");
+// Per wave with RG row groups: two metadata buffers, then two value buffers (two phases in
+// flight); metadata first, so that a pair read one value before a row stays inside the
+// wave's region. The expansion tables follow the waves' regions.
+constexpr int bm_wave_bytes(int rg) { return 2 * rg * kRGMeta + 2 * rg * kRGVal; }   // 9600 per group
+constexpr int bm_lds_bytes(int rg) { return kBmWaves * bm_wave_bytes(rg) + kLutBytes; }
+static_assert(bm_lds_bytes(1) <= 80 * 1024, "one row group: two workgroups per CU");
+static_assert(bm_lds_bytes(2) <= 160 * 1024, "two row groups: one workgroup per CU");
 
-template <int CT, bool BCOL>
-__global__ void __launch_bounds__(64 * kBmWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
+template <int CT, bool BCOL, int RG>
+__global__ void __launch_bounds__(64 * kBmWaves) __attribute__((amdgpu_waves_per_eu(4 / RG, 4 / RG)))
 k_spmm_bitmap(BitmapArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];   // per wave 9600 bytes, then the table
+  extern __shared__ __align__(16) uint8_t smem[];   // per wave 9600 bytes per row group, then the table
+  constexpr int kRG = RG;
+  constexpr int kMetaBuf = kRG * kRGMeta;
+  constexpr int kValBuf = kRG * kRGVal;
+  constexpr int kValBase = 2 * kMetaBuf;
+  constexpr int kWaveBytes = bm_wave_bytes(kRG);
+  constexpr int kLutOff = kBmWaves * kWaveBytes;
   // Expansion tables: per bitmap byte m, eight byte offsets 2 rank_e (rank_e = set bits of
   // m below e); per bitmap nibble, two dwords of 16-bit keep masks (0xFFFF where the bit is
   // set). Expanding a chunk is then one add and one 2-byte read per position and one AND
@@ -276,7 +286,7 @@ k_spmm_bitmap(BitmapArgs a) {
   const int w = tid >> 6;
   const int q = lane >> 4;
   const int li = lane & 15;
-  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int64_t row0 = (int64_t)blockIdx.x * 16 * kRG;
   const int64_t T = a.K / kTile;
   const int64_t RT = a.R * T;                          // bitmaps; offsets hold RT + 1
   const int64_t tw = (T + kBmWaves - 1) / kBmWaves;     // tiles per wave
@@ -291,12 +301,16 @@ k_spmm_bitmap(BitmapArgs a) {
   // offsets: R K < 2^31, so every offset into the three arrays fits. The lane parts that do
   // not depend on the phase are computed once here.
   const uint32_t T32 = (uint32_t)T, RT32 = (uint32_t)RT;
-  const int64_t rbm = row0 + (lane >> 2) < a.R ? row0 + (lane >> 2) : a.R - 1;
-  const uint32_t bm_lane = (uint32_t)(rbm * T) * 8u + (uint32_t)(lane & 1) * 4u;
-  const uint32_t bm_t = (uint32_t)((lane >> 1) & 1);
+  uint32_t bm_lane[kRG], of_lane[kRG];
   const int orr = lane < 48 ? lane / 3 : 0;
-  const int64_t rof = row0 + orr < a.R ? row0 + orr : a.R - 1;
-  const uint32_t of_lane = (uint32_t)(rof * T) + (uint32_t)(lane < 48 ? lane - 3 * orr : 0);
+#pragma unroll
+  for (int rg = 0; rg < kRG; ++rg) {
+    const int64_t rbm = row0 + 16 * rg + (lane >> 2) < a.R ? row0 + 16 * rg + (lane >> 2) : a.R - 1;
+    bm_lane[rg] = (uint32_t)(rbm * T) * 8u + (uint32_t)(lane & 1) * 4u;
+    const int64_t rof = row0 + 16 * rg + orr < a.R ? row0 + 16 * rg + orr : a.R - 1;
+    of_lane[rg] = (uint32_t)(rof * T) + (uint32_t)(lane < 48 ? lane - 3 * orr : 0);
+  }
+  const uint32_t bm_t = (uint32_t)((lane >> 1) & 1);
   // a matrix without non-zeros has no values to copy (and its values pointer may be NULL);
   // otherwise the first 16 bytes of values are a readable target for idle lanes. A wave
   // without tiles reads nothing (with K = 0 the arrays may all be NULL).
@@ -310,10 +324,13 @@ k_spmm_bitmap(BitmapArgs a) {
     const uint32_t base = wl_lds + (uint32_t)(kMetaBase + mb * kMetaBuf);
     uint32_t t = kt0 + bm_t;
     t = t < T32 ? t : T32 - 1;
-    dma_s<4>(a.bitmaps, bm_lane + 8u * t, base);
-    uint32_t idx = of_lane + kt0;
-    idx = idx < RT32 ? idx : RT32;
-    if (lane < 48) dma_s<4>(a.offsets, 4u * idx, base + (uint32_t)kMetaOffs);
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) {
+      dma_s<4>(a.bitmaps, bm_lane[rg] + 8u * t, base + (uint32_t)(rg * kRGMeta));
+      uint32_t idx = of_lane[rg] + kt0;
+      idx = idx < RT32 ? idx : RT32;
+      if (lane < 48) dma_s<4>(a.offsets, 4u * idx, base + (uint32_t)(rg * kRGMeta + kMetaOffs));
+    }
   };
   // (2) values of phase p (its metadata in buffer mb) into value buffer vb: DMA b fills the
   // 16-byte slots 64 b .. 64 b + 63 of the buffer, slot = 17 r + c being chunk c of row r
@@ -322,7 +339,9 @@ k_spmm_bitmap(BitmapArgs a) {
     if (!any_values) return;
     const int64_t kt0 = tbeg + p * kPT;
     const int nt = (int)(tend - kt0 < kPT ? tend - kt0 : kPT);
-    const uint8_t* offs = wl + kMetaBase + mb * kMetaBuf + kMetaOffs;
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) {
+    const uint8_t* offs = wl + kMetaBase + mb * kMetaBuf + rg * kRGMeta + kMetaOffs;
 #pragma unroll
     for (int b = 0; b < (kSlots + 63) / 64; ++b) {
       const int slot = 64 * b + lane;
@@ -331,9 +350,10 @@ k_spmm_bitmap(BitmapArgs a) {
       const int rc = r < 16 ? r : 15;
       const uint32_t s0 = *reinterpret_cast<const uint32_t*>(offs + 12 * rc);
       const uint32_t s1 = *reinterpret_cast<const uint32_t*>(offs + 12 * rc + 4 * nt);
-      const bool live = r < 16 && row0 + r < a.R && 8u * ch < s1 - s0;   // ch = 16 is never live
-      const uint32_t dst = wl_lds + (uint32_t)(kValBase + vb * kValBuf + b * 1024);
+      const bool live = r < 16 && row0 + 16 * rg + r < a.R && 8u * ch < s1 - s0;   // ch = 16 is never live
+      const uint32_t dst = wl_lds + (uint32_t)(kValBase + vb * kValBuf + rg * kRGVal + b * 1024);
       if (64 * b + 64 <= kSlots || slot < kSlots) dma_s<16>(a.values, live ? 2u * (s0 + 8u * ch) : 0u, dst);
+    }
     }
   };
   // B operands of phase p. With one column tile and column-major B (16 contiguous bytes per
@@ -382,9 +402,11 @@ k_spmm_bitmap(BitmapArgs a) {
         }
   };
 
-  f4 acc[CT];
+  f4 acc[kRG][CT];
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int rg = 0; rg < kRG; ++rg)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[rg][ct] = f4{0.f, 0.f, 0.f, 0.f};
 
   auto phase = [&](int64_t p, auto par_c) {
     constexpr int P = decltype(par_c)::value;   // p % 2: its value and metadata buffers
@@ -399,12 +421,14 @@ k_spmm_bitmap(BitmapArgs a) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) asm volatile("" : "+v"(bop[PB][t][blk][ct]));
     const uint8_t* mbuf = wl + kMetaBase + P * kMetaBuf;
-    uint64_t bm[kPT];
-    uint32_t off[kPT];
+    uint64_t bm[kRG][kPT];
+    uint32_t off[kRG][kPT];
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg)
 #pragma unroll
     for (int t = 0; t < kPT; ++t) {
-      bm[t] = *reinterpret_cast<const uint64_t*>(mbuf + 16 * li + 8 * t);
-      off[t] = *reinterpret_cast<const uint32_t*>(mbuf + kMetaOffs + 12 * li + 4 * t);
+      bm[rg][t] = *reinterpret_cast<const uint64_t*>(mbuf + rg * kRGMeta + 16 * li + 8 * t);
+      off[rg][t] = *reinterpret_cast<const uint32_t*>(mbuf + rg * kRGMeta + kMetaOffs + 12 * li + 4 * t);
     }
     if (p + 1 < nph) {
       if constexpr (kAheadB) load_b(p + 1, cint<P ^ 1>{});
@@ -415,19 +439,22 @@ k_spmm_bitmap(BitmapArgs a) {
     // (3) expand and multiply
     const int64_t kt0 = tbeg + p * kPT;
     const int nt = (int)(tend - kt0 < kPT ? tend - kt0 : kPT);
-    const uint8_t* rowp = wl + kValBase + P * kValBuf + kRowPitch * li;   // staged row li
-    const uint32_t span0 = off[0];
+
 #pragma unroll
     for (int t = 0; t < kPT; ++t) {
       if (t >= nt) break;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+       for (int rg = 0; rg < kRG; ++rg) {
+        const uint8_t* rowp = wl + kValBase + P * kValBuf + rg * kRGVal + kRowPitch * li;   // staged row li
+        const uint32_t span0 = off[rg][0];
         const int byte = 4 * blk + q;
-        const uint64_t below = byte == 0 ? 0ull : (bm[t] & ((1ull << (8 * byte)) - 1ull));
+        const uint64_t below = byte == 0 ? 0ull : (bm[rg][t] & ((1ull << (8 * byte)) - 1ull));
         // the chunk's first value in the staged row; a position past the last set bit reads
         // at most one value beyond the row's span (byte 256: the row's pad)
-        const uint8_t* cb = rowp + 2u * ((off[t] - span0) + (uint32_t)__popcll(below));
-        const uint32_t m = (uint32_t)(bm[t] >> (8 * byte)) & 0xFFu;
+        const uint8_t* cb = rowp + 2u * ((off[rg][t] - span0) + (uint32_t)__popcll(below));
+        const uint32_t m = (uint32_t)(bm[rg][t] >> (8 * byte)) & 0xFFu;
         const u2 klo = *reinterpret_cast<const u2*>(smem + kLutOff + 2048u + 8u * (m & 15u));
         const u2 khi = *reinterpret_cast<const u2*>(smem + kLutOff + 2048u + 8u * (m >> 4));
         const u4 keep = {klo[0], klo[1], khi[0], khi[1]};
@@ -443,10 +470,11 @@ k_spmm_bitmap(BitmapArgs a) {
         }
         const h8 av = __builtin_bit_cast(h8, pk);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma16x16x32(av, bop[PB][t][blk][ct], acc[ct]);
+        for (int ct = 0; ct < CT; ++ct) acc[rg][ct] = mfma16x16x32(av, bop[PB][t][blk][ct], acc[rg][ct]);
         // scheduling fence: expand block by block (hoisting every block's LDS reads would
         // hold all their results in registers)
         asm volatile("" ::: "memory");
+       }
       }
     }
     // one register set (kAheadB off): the next phase's B operands are requested once this
@@ -473,18 +501,22 @@ k_spmm_bitmap(BitmapArgs a) {
   __syncthreads();
   f4* red = reinterpret_cast<f4*>(smem);
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) red[(w * CT + ct) * 64 + lane] = acc[ct];
+  for (int rg = 0; rg < kRG; ++rg)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) red[((w * kRG + rg) * CT + ct) * 64 + lane] = acc[rg][ct];
   __syncthreads();
   // D layout of the 16x16 MFMA: column l % 16, element r -> row 4 (l / 16) + r
-  for (int e = tid; e < 16 * 16 * CT; e += 64 * kBmWaves) {
+  for (int e = tid; e < 16 * kRG * 16 * CT; e += 64 * kBmWaves) {
     const int rr = e / (16 * CT);
     const int cc = e - rr * 16 * CT;
     const int ct = cc >> 4;
-    const int ln = ((rr >> 2) << 4) | (cc & 15);
+    const int rg = rr >> 4;
+    const int rl = rr & 15;
+    const int ln = ((rl >> 2) << 4) | (cc & 15);
     const float* rp = reinterpret_cast<const float*>(red);
     float s = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kBmWaves; ++ww) s += rp[((ww * CT + ct) * 64 + ln) * 4 + (rr & 3)];
+    for (int ww = 0; ww < kBmWaves; ++ww) s += rp[(((ww * kRG + rg) * CT + ct) * 64 + ln) * 4 + (rl & 3)];
     const int64_t orow = row0 + rr;
     if (orow < a.R && cc < a.C) a.Y[orow * a.ldy + cc] = f16_bits(to_f16(s));
   }
@@ -518,6 +550,21 @@ hipError_t launch_bitmap_values(const void* A, int64_t R, int64_t K, int64_t lda
   return hipGetLastError();
 }
 
+// The current device's compute-unit count, looked up once per device.
+static hipError_t device_cu_count(int* cus) {
+  static std::atomic<int> cache[64] = {};
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) return e;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  *cus = n;
+  return hipSuccess;
+}
+
 hipError_t launch_spmm_bitmap(const uint64_t* bitmaps, const uint32_t* offsets, const void* values,
                               int64_t R, int64_t K, const void* B, int64_t C, int64_t ldb,
                               int b_layout, void* Y, int64_t ldy, hipStream_t stream) {
@@ -529,17 +576,27 @@ hipError_t launch_spmm_bitmap(const uint64_t* bitmaps, const uint32_t* offsets, 
   a.Y = (uint16_t*)Y;
   a.R = R; a.K = K; a.C = C; a.ldb = ldb; a.ldy = ldy;
   a.b_col = b_layout == 1;
-  const unsigned g = (unsigned)((R + 15) / 16);
-  const size_t lds = (size_t)kBitmapLds;   // 77 KiB: two workgroups per CU
+  // Two row groups per wave (32 rows per workgroup) apply every B operand to twice the rows
+  // but leave room for one workgroup per CU (152 KiB of LDS). They are taken with
+  // column-major B when the 32-row workgroups fit in one pass over the CUs; past that the
+  // second pass costs more than the B loads saved. (Row-major B's two-column-tile form would
+  // spill with two row groups.)
+  int cus = 0;
+  if (hipError_t e = device_cu_count(&cus)) return e;
+  const bool two = b_layout == 1 && (R + 31) / 32 <= (int64_t)cus;
+  const int rg = two ? 2 : 1;
+  const unsigned g = (unsigned)((R + 16 * rg - 1) / (16 * rg));
+  const size_t lds = (size_t)bm_lds_bytes(rg);   // 77 KiB (two workgroups per CU) or 152 KiB
   const dim3 blk(64 * kBmWaves);
   auto go = [&](auto kern) -> hipError_t {
-    static std::atomic<uint64_t> lds_set[2][2] = {};
-    if (hipError_t e = ensure_lds_limit(lds_set[C > 16][b_layout == 1], (const void*)kern, (int)lds)) return e;
+    static std::atomic<uint64_t> lds_set[2][2][2] = {};
+    if (hipError_t e = ensure_lds_limit(lds_set[two][C > 16][b_layout == 1], (const void*)kern, (int)lds)) return e;
     hipLaunchKernelGGL(kern, dim3(g), blk, lds, stream, a);
     return hipGetLastError();
   };
-  if (b_layout == 1) return C > 16 ? go(k_spmm_bitmap<2, true>) : go(k_spmm_bitmap<1, true>);
-  return C > 16 ? go(k_spmm_bitmap<2, false>) : go(k_spmm_bitmap<1, false>);
+  if (two) return C > 16 ? go(k_spmm_bitmap<2, true, 2>) : go(k_spmm_bitmap<1, true, 2>);
+  if (b_layout == 1) return C > 16 ? go(k_spmm_bitmap<2, true, 1>) : go(k_spmm_bitmap<1, true, 1>);
+  return C > 16 ? go(k_spmm_bitmap<2, false, 1>) : go(k_spmm_bitmap<1, false, 1>);
 }
 
 }  // namespace snm

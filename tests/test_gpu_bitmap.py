@@ -57,7 +57,7 @@ def test_bitmap_encode_special_values():
 
 @pytest.mark.parametrize("R,K,C,s", [(16, 64, 8, 0.5), (17, 192, 1, 0.3), (100, 640, 16, 0.7),
                                      (64, 4096, 8, 0.5), (130, 64 * 37, 24, 0.6), (48, 1024, 32, 0.0),
-                                     (40, 9216, 8, 0.5), (7, 256, 13, 1.0)])
+                                     (40, 9216, 8, 0.5), (7, 256, 13, 1.0), (8190, 512, 32, 0.5)])
 def test_bitmap_spmm(R, K, C, s):
     snm = _snm()
     rng = np.random.default_rng(R + K + C)
@@ -85,14 +85,15 @@ def test_bitmap_spmm_identity_exact():
         assert np.array_equal(Y.astype(np.float64), A[:, :C].astype(np.float64))
 
 
-@pytest.mark.parametrize("n,s", [(7168, 0.3), (9216, 0.5), (9216, 0.7)])
-def test_bitmap_decode_shapes_sampled(n, s):
-    # the pages' kernel shapes at N = 8; the encoding of the first and last 64 rows against
-    # the oracle (offsets relative to each block's first tile), every column of 96 sampled
-    # output rows against A @ B in float64
+@pytest.mark.parametrize("n,s,N", [(7168, 0.3, 8), (7168, 0.5, 32), (9216, 0.5, 8), (9216, 0.7, 8)])
+def test_bitmap_decode_shapes_sampled(n, s, N):
+    # the pages' kernel shapes (7168 rows take the 32-row workgroups with column-major B,
+    # 9216 the 16-row ones); the encoding of the first and last 64 rows against the oracle
+    # (offsets relative to each block's first tile), every column of 96 sampled output rows
+    # against A @ B in float64
     snm = _snm()
     A = workloads.pruned_unstructured(11, n, n, s)
-    B = workloads.normal_f16(np.random.default_rng(12), (n, 8))
+    B = workloads.normal_f16(np.random.default_rng(12), (n, N))
     bm, off, vals = snm.bitmap_encode(to_dev(A))
     Y = to_host(snm.spmm_bitmap(bm, off, vals, to_dev(np.ascontiguousarray(B.T)).t()))
     bmh, offh, valh = to_host(bm).view(np.uint64), to_host(off).view(np.uint32).astype(np.int64), to_host(vals)
@@ -106,7 +107,7 @@ def test_bitmap_decode_shapes_sampled(n, s):
     rng = np.random.default_rng(13)
     rows = np.unique(np.concatenate([rng.choice(n, 96, replace=False), [0, n - 1]]))
     ref = A[rows].astype(np.float64) @ B.astype(np.float64)
-    assert_fp16_close(Y[rows], ref, f"bitmap {n}x{n} s={s} N=8 sampled rows")
+    assert_fp16_close(Y[rows], ref, f"bitmap {n}x{n} s={s} N={N} sampled rows")
     assert int(offh[-1]) == int(np.sum((np.count_nonzero(A.reshape(n * T, 64), axis=1) + 7) // 8 * 8))
 
 
